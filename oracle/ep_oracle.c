@@ -1,0 +1,314 @@
+/*
+ * CPU oracle for one GPU's share of MoE expert-parallel dispatch and combine.
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU-baseline leg
+ * call this code. It is plain, single-threaded C written from the definitions of the
+ * operations; it shares no code, header, table or helper with the GPU library, and the GPU
+ * library never calls it.
+ *
+ * Sources of the definitions:
+ *  - Dispatch layout (per-expert counts and placement) is the step the "normal" APIs must run
+ *    inside the timed boundary: awsome-distributed-ai PR #1238, "What changed" and the
+ *    author's reply on what latency means.
+ *  - Dispatch expands each token into the expert layout (afdEP-comm validation record,
+ *    kernel_timelines: dispatch_copy_epilogue; the use_expanded_layout patch).
+ *  - The per-token FP8 cast with one scale per 128 channels: PR #1238 review item 1
+ *    (per_token_cast_to_fp8; quantisation inside low_latency_dispatch(use_fp8=True)) and the
+ *    logical-payload accounting there (H + 4*H/128 bytes per FP8 row). The e4m3 format is the
+ *    OCP 8-bit floating point specification (OFP8) E4M3: bias 7, three mantissa bits, no
+ *    infinities, a single NaN code per sign (S.1111.111), largest finite value 448.
+ *  - Combine gathers expert outputs back and reduces them with the top-k weights; combine is
+ *    BF16 in either dispatch dtype (PR #1238 review item 1; afdEP-comm kernel_timelines:
+ *    combine_reduce_epilogue).
+ *  - Readings where the pages are silent: pair order i = t*K + j is "token order"; a
+ *    capacity-C expert keeps its first C pairs in that order; the receive buffer is
+ *    [E][C][H] with expert e = r*(E/R) + l (rank-major); scale = amax / 448 by an IEEE fp32
+ *    division and q = e4m3(x / scale) by a second fp32 division; combine accumulates
+ *    acc = fmaf(w_j, y_j, acc) in fp32 for j ascending from +0 and rounds once to bf16;
+ *    weights of dropped pairs are not renormalised.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fPIC -shared (no -ffast-math, no
+ * FMA contraction: every fp32 operation below is one IEEE operation).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+/* ----------------------------------------------------------------------------------------- */
+/* Number formats                                                                             */
+/* ----------------------------------------------------------------------------------------- */
+
+float oracle_bf16_to_f32(uint16_t b)
+{
+    /* bf16 is the upper half of an fp32 pattern: widening is exact. */
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static uint32_t f32_bits(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return u;
+}
+
+/*
+ * fp32 -> bf16, round to nearest, ties to even, by definition: take the two bf16 values that
+ * bracket f (truncation toward zero, and the next one away from zero), compare the distances
+ * in double precision (exact for fp32 operands), keep the nearer, on a tie keep the one whose
+ * last mantissa bit is 0. Overflow past the largest finite bf16 rounds to infinity as IEEE
+ * round-to-nearest does. NaN stays NaN (quiet, sign kept).
+ */
+uint16_t oracle_bf16_rne(float f)
+{
+    uint32_t u = f32_bits(f);
+    if (isnan(f))
+        return (uint16_t)((u >> 16) | 0x0040u);
+    if (isinf(f))
+        return (uint16_t)(u >> 16);
+    uint16_t lo = (uint16_t)(u >> 16);            /* toward zero */
+    if ((u & 0xFFFFu) == 0)
+        return lo;                                /* exactly representable */
+    uint16_t hi = (uint16_t)(lo + 1);             /* next magnitude (may be +-inf) */
+    double v = fabs((double)f);
+    double dlo = v - fabs((double)oracle_bf16_to_f32(lo));
+    /* Past the largest finite bf16 the next step is infinity, which IEEE rounding treats as
+     * the value 2^128 of an exponent range without bound. */
+    double vhi = ((hi & 0x7FFFu) == 0x7F80u) ? ldexp(1.0, 128)
+                                             : fabs((double)oracle_bf16_to_f32(hi));
+    double dhi = vhi - v;
+    if (dlo < dhi) return lo;
+    if (dhi < dlo) return hi;
+    return (lo & 1u) ? hi : lo;
+}
+
+/* Value of an OCP E4M3 code's magnitude bits (0x00..0x7E); code 0x7F is NaN. */
+double oracle_e4m3_value(uint8_t code)
+{
+    int e = (code >> 3) & 0xF;
+    int m = code & 0x7;
+    double mag;
+    if (e == 0)
+        mag = ldexp((double)m, -9);                     /* subnormal: m/8 * 2^(1-7) */
+    else
+        mag = ldexp(1.0 + (double)m / 8.0, e - 7);     /* normal: (1 + m/8) * 2^(e-7) */
+    return (code & 0x80) ? -mag : mag;
+}
+
+/*
+ * fp32 -> OCP E4M3 with round-to-nearest-even and saturation to +-448 (OFP8 "satfinite"
+ * conversion). The magnitude is matched against the 127 finite non-negative codes
+ * 0x00..0x7E, which increase with their value: find the largest code whose value is <= |v|,
+ * then choose between it and the next code by distance (ties to the code whose last
+ * mantissa bit is 0). Magnitudes at or beyond 448 give 448. The sign bit is copied, so
+ * -0.0 gives 0x80. NaN input gives the NaN code 0x7F with the sign of v.
+ */
+uint8_t oracle_e4m3_rne_sat(float v)
+{
+    uint8_t sign = (f32_bits(v) >> 31) ? 0x80 : 0x00;
+    if (isnan(v))
+        return (uint8_t)(sign | 0x7F);
+    double a = fabs((double)v);
+    if (a >= 448.0)
+        return (uint8_t)(sign | 0x7E);
+    /* binary search for the largest code c in [0, 0x7E] with value(c) <= a */
+    int lo = 0, hi = 0x7E;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) / 2;
+        if (oracle_e4m3_value((uint8_t)mid) <= a) lo = mid;
+        else hi = mid - 1;
+    }
+    int c = lo;
+    double below = oracle_e4m3_value((uint8_t)c);
+    if (below == a)
+        return (uint8_t)(sign | c);
+    double above = oracle_e4m3_value((uint8_t)(c + 1));   /* c < 0x7E since a < 448 */
+    double d0 = a - below, d1 = above - a;
+    if (d1 < d0 || (d1 == d0 && (c & 1)))
+        c = c + 1;
+    return (uint8_t)(sign | c);
+}
+
+/* ----------------------------------------------------------------------------------------- */
+/* Layout                                                                                     */
+/* ----------------------------------------------------------------------------------------- */
+
+/*
+ * Routing layout for T tokens with K choices each over E experts, capacity C per expert,
+ * R virtual ranks of E/R consecutive experts.
+ *
+ *   Pairs are visited in token order i = t*K + j. id == -1 is unrouted; any other id outside
+ *   [0, E) is invalid. Both get slot -1. A routed pair takes the next position of its expert;
+ *   positions >= C are dropped (slot -1). So slot[i] = #{i' < i : id[i'] == id[i]} when that
+ *   is < C, i.e. stable in-order placement under capacity.
+ *
+ *   count[e]  = min(raw[e], C)            kept pairs of expert e
+ *   offset[e] = sum_{e' < e} count[e']   exclusive scan in expert (= rank-major) order
+ *   rank_count[r], rank_offset[r]         the same over the E/R experts of each rank
+ *   stats = {kept, dropped, unrouted, invalid}; the four sum to T*K.
+ *
+ * raw (optional, may be NULL) receives the demand per expert before capacity.
+ */
+void oracle_layout(int T, int K, int E, int C, int R, const int32_t *topk_idx, int32_t *slot,
+                   int32_t *count, int32_t *offset, int32_t *rank_count, int32_t *rank_offset,
+                   int32_t *stats, int32_t *raw)
+{
+    int32_t demand[E > 0 ? E : 1];
+    for (int e = 0; e < E; ++e) demand[e] = 0;
+    int32_t kept = 0, dropped = 0, unrouted = 0, invalid = 0;
+    long n = (long)T * K;
+    for (long i = 0; i < n; ++i) {
+        int32_t e = topk_idx[i];
+        if (e == -1) { slot[i] = -1; ++unrouted; continue; }
+        if (e < 0 || e >= E) { slot[i] = -1; ++invalid; continue; }
+        int32_t p = demand[e]++;
+        if (p < C) { slot[i] = p; ++kept; }
+        else { slot[i] = -1; ++dropped; }
+    }
+    int32_t run = 0;
+    for (int e = 0; e < E; ++e) {
+        count[e] = demand[e] < C ? demand[e] : C;
+        offset[e] = run;
+        run += count[e];
+        if (raw) raw[e] = demand[e];
+    }
+    int EL = E / R;
+    run = 0;
+    for (int r = 0; r < R; ++r) {
+        int32_t s = 0;
+        for (int l = 0; l < EL; ++l) s += count[r * EL + l];
+        if (rank_count) rank_count[r] = s;
+        if (rank_offset) rank_offset[r] = run;
+        run += s;
+    }
+    stats[0] = kept; stats[1] = dropped; stats[2] = unrouted; stats[3] = invalid;
+}
+
+/* A pair takes part in dispatch/combine only if its expert id and slot address a row of the
+ * [E][C][H] buffer; anything else is skipped. */
+static int pair_kept(int32_t e, int32_t s, int E, int C)
+{
+    return e >= 0 && e < E && s >= 0 && s < C;
+}
+
+/* ----------------------------------------------------------------------------------------- */
+/* Dispatch                                                                                   */
+/* ----------------------------------------------------------------------------------------- */
+
+/* recv[e][slot[i]][:] = x[i / K][:] for every kept pair i; every other row is left as it is. */
+void oracle_dispatch(int T, int H, int E, int K, int C, const uint16_t *x,
+                     const int32_t *topk_idx, const int32_t *slot, uint16_t *recv)
+{
+    for (int t = 0; t < T; ++t)
+        for (int j = 0; j < K; ++j) {
+            long i = (long)t * K + j;
+            int32_t e = topk_idx[i], s = slot[i];
+            if (!pair_kept(e, s, E, C)) continue;
+            uint16_t *dst = recv + ((long)e * C + s) * H;
+            for (int h = 0; h < H; ++h) dst[h] = x[(long)t * H + h];
+        }
+}
+
+/*
+ * FP8 dispatch. Token t is quantised once, per block b of 128 channels:
+ *   amax  = max_h |x[t][h]|                    (exact in fp32)
+ *   scale = amax / 448                          (one IEEE fp32 division)
+ *   q[h]  = e4m3_rne_sat(x[t][h] / scale)      (one IEEE fp32 division per element)
+ * If amax == 0 every x in the block is +-0 and q is that signed zero (scale = 0).
+ * Then the q row and the scale row are written to every kept slot of t:
+ *   recv_q[e][s][h] = q[h];  recv_scale[e][s][b] = scale_b.
+ */
+void oracle_dispatch_fp8(int T, int H, int E, int K, int C, const uint16_t *x,
+                         const int32_t *topk_idx, const int32_t *slot, uint8_t *recv_q,
+                         float *recv_scale)
+{
+    int NB = H / 128;
+    uint8_t q[H > 0 ? H : 1];
+    float sc[NB > 0 ? NB : 1];
+    for (int t = 0; t < T; ++t) {
+        const uint16_t *row = x + (long)t * H;
+        for (int b = 0; b < NB; ++b) {
+            float amax = 0.0f;
+            for (int h = 128 * b; h < 128 * b + 128; ++h) {
+                float a = fabsf(oracle_bf16_to_f32(row[h]));
+                if (a > amax) amax = a;
+            }
+            float scale = amax / 448.0f;
+            sc[b] = scale;
+            for (int h = 128 * b; h < 128 * b + 128; ++h) {
+                float v = oracle_bf16_to_f32(row[h]);
+                q[h] = (amax == 0.0f) ? (uint8_t)((row[h] & 0x8000u) ? 0x80 : 0x00)
+                                      : oracle_e4m3_rne_sat(v / scale);
+            }
+        }
+        for (int j = 0; j < K; ++j) {
+            long i = (long)t * K + j;
+            int32_t e = topk_idx[i], s = slot[i];
+            if (!pair_kept(e, s, E, C)) continue;
+            long r = (long)e * C + s;
+            memcpy(recv_q + r * H, q, (size_t)H);
+            memcpy(recv_scale + r * NB, sc, (size_t)NB * sizeof(float));
+        }
+    }
+}
+
+/* ----------------------------------------------------------------------------------------- */
+/* Combine                                                                                    */
+/* ----------------------------------------------------------------------------------------- */
+
+/*
+ * out[t][h] = bf16_rne(acc), acc = +0.0f, then for j = 0 .. K-1 with pair i = t*K + j kept:
+ *   acc = fmaf(w[i], float(y[e_i][slot_i][h]), acc)
+ * Dropped, unrouted and invalid pairs are skipped; the remaining weights are used as given.
+ */
+void oracle_combine(int T, int H, int E, int K, int C, const uint16_t *y,
+                    const int32_t *topk_idx, const int32_t *slot, const float *topk_w,
+                    uint16_t *out)
+{
+    for (int t = 0; t < T; ++t)
+        for (int h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int j = 0; j < K; ++j) {
+                long i = (long)t * K + j;
+                int32_t e = topk_idx[i], s = slot[i];
+                if (!pair_kept(e, s, E, C)) continue;
+                float v = oracle_bf16_to_f32(y[((long)e * C + s) * H + h]);
+                acc = fmaf(topk_w[i], v, acc);
+            }
+            out[(long)t * H + h] = oracle_bf16_rne(acc);
+        }
+}
+
+/* Same as oracle_combine for a subset of tokens: out row n is token tokens[n]. */
+void oracle_combine_tokens(int n_tokens, const int32_t *tokens, int H, int E, int K, int C,
+                           const uint16_t *y, const int32_t *topk_idx, const int32_t *slot,
+                           const float *topk_w, uint16_t *out)
+{
+    for (int n = 0; n < n_tokens; ++n) {
+        int t = tokens[n];
+        for (int h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int j = 0; j < K; ++j) {
+                long i = (long)t * K + j;
+                int32_t e = topk_idx[i], s = slot[i];
+                if (!pair_kept(e, s, E, C)) continue;
+                float v = oracle_bf16_to_f32(y[((long)e * C + s) * H + h]);
+                acc = fmaf(topk_w[i], v, acc);
+            }
+            out[(long)n * H + h] = oracle_bf16_rne(acc);
+        }
+    }
+}
+
+/* Array forms of the two conversions, for the exhaustive format tests. */
+void oracle_bf16_rne_array(const float *in, uint16_t *out, long n)
+{
+    for (long k = 0; k < n; ++k) out[k] = oracle_bf16_rne(in[k]);
+}
+
+void oracle_e4m3_rne_sat_array(const float *in, uint8_t *out, long n)
+{
+    for (long k = 0; k < n; ++k) out[k] = oracle_e4m3_rne_sat(in[k]);
+}

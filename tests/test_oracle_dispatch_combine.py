@@ -1,0 +1,210 @@
+"""Pins for the oracle's dispatch (bf16 and FP8) and combine (CPU only).
+
+Dispatch expands each token into the expert layout (afdEP-comm validation record,
+kernel_timelines: dispatch_copy_epilogue); the FP8 variant quantises each token once per 128
+channels (awsome-distributed-ai PR #1238, review item 1). Combine is the top-k weighted
+reduction back onto the token (combine_reduce_epilogue; BF16 in either dispatch dtype).
+
+Pins used here: a numpy fancy-index scatter (library routine) for dispatch; the round trip of
+every kept pair; the identity law (y = recv, unit weights -> n_kept * x); one-hot weights
+returning a y row exactly; an fp64 bound; and two crafted cases that fix the fp32 fused
+multiply-add and the ascending-j order.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_ep_layout_06_amd import workloads as W
+
+SENTINEL16 = np.uint16(0xDEAD)
+
+
+def small_case(T=37, H=256, E=6, K=3, C=5, R=3, seed=0):
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(-2, E + 1, size=(T, K)).astype(np.int32)   # dupes, unrouted, invalid
+    x = W.f32_to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    w = rng.random((T, K)).astype(np.float32)
+    lay = oracle.layout(idx, E, C, R)
+    return dict(T=T, H=H, E=E, K=K, C=C, R=R, idx=idx, x=x, w=w, slot=lay["slot"], lay=lay)
+
+
+def test_dispatch_matches_numpy_scatter_and_leaves_other_rows():
+    c = small_case()
+    recv = np.full((c["E"], c["C"], c["H"]), SENTINEL16, dtype=np.uint16)
+    oracle.dispatch(c["x"], c["idx"], c["slot"], c["E"], c["C"], recv)
+    want = np.full_like(recv, SENTINEL16)
+    flat_e, flat_s = c["idx"].reshape(-1), c["slot"].reshape(-1)
+    tok = np.repeat(np.arange(c["T"]), c["K"])
+    keep = flat_s >= 0
+    want[flat_e[keep], flat_s[keep]] = c["x"][tok[keep]]
+    assert np.array_equal(recv, want)
+    # rows at or past count[e] still hold the sentinel
+    for e in range(c["E"]):
+        assert (recv[e, c["lay"]["count"][e]:] == SENTINEL16).all()
+
+
+def test_dispatch_round_trip_each_kept_pair_once():
+    cfg = W.get_config("decode_bf16")
+    inp = W.make_inputs(cfg)
+    E, C = cfg.E, 160                       # a smaller C keeps the host buffer small
+    lay = oracle.layout(inp["topk_idx"], E, C, cfg.R)
+    assert lay["stats"]["dropped"] == 0
+    recv = np.zeros((E, C, cfg.H), dtype=np.uint16)
+    oracle.dispatch(inp["x"], inp["topk_idx"], lay["slot"], E, C, recv)
+    seen = np.zeros((E, C), dtype=np.int64)
+    for t in range(cfg.T):
+        for j in range(cfg.K):
+            e, s = inp["topk_idx"][t, j], lay["slot"][t, j]
+            assert np.array_equal(recv[e, s], inp["x"][t])
+            seen[e, s] += 1
+    assert seen.sum() == lay["stats"]["kept"] and seen.max() == 1
+
+
+def test_fp8_dispatch_properties():
+    """Per token and 128-channel block: the scale times 448 is the block amax to within one
+    fp32 rounding; the amax element encodes to +-448; q is torch's e4m3 cast of x / scale;
+    the dequantised row is within the 3-bit-mantissa bound; every kept slot gets the same row."""
+    cfg = W.get_config("decode_fp8")
+    inp = W.make_inputs(cfg)
+    T, H = cfg.T, cfg.H
+    C = 160
+    lay = oracle.layout(inp["topk_idx"], cfg.E, C, cfg.R)
+    q = np.zeros((cfg.E, C, H), dtype=np.uint8)
+    sc = np.zeros((cfg.E, C, H // 128), dtype=np.float32)
+    oracle.dispatch_fp8(inp["x"], inp["topk_idx"], lay["slot"], cfg.E, C, q, sc)
+    xf = W.bf16_bits_to_f32(inp["x"]).reshape(T, H // 128, 128)
+    amax = np.abs(xf).max(axis=2)
+    for t in range(T):
+        e0, s0 = inp["topk_idx"][t, 0], lay["slot"][t, 0]
+        scale, qrow = sc[e0, s0], q[e0, s0]
+        for j in range(1, cfg.K):
+            e, s = inp["topk_idx"][t, j], lay["slot"][t, j]
+            assert np.array_equal(q[e, s], qrow) and np.array_equal(sc[e, s], scale)
+        rel = np.abs(scale.astype(np.float64) * 448 - amax[t]) / amax[t]
+        assert (rel <= 2.0 ** -23).all()
+        blocks = qrow.reshape(H // 128, 128)
+        arg = np.abs(xf[t]).argmax(axis=1)
+        assert ((blocks[np.arange(H // 128), arg] & 0x7F) == 0x7E).all()
+        v = xf[t] / scale[:, None]                               # one fp32 division each
+        want = torch.from_numpy(np.ascontiguousarray(v)).to(torch.float8_e4m3fn) \
+            .view(torch.uint8).numpy()
+        assert np.array_equal(blocks, want)
+    # the outlier workload really exercises large block maxima
+    assert amax.max() > 100
+
+
+def test_fp8_zero_block_gives_signed_zero():
+    H = 256
+    x = np.zeros((1, H), dtype=np.uint16)
+    x[0, 5] = 0x8000                          # -0.0
+    x[0, 130] = W.f32_to_bf16_bits(np.array([3.0], dtype=np.float32))[0]
+    idx = np.array([[0]], dtype=np.int32)
+    lay = oracle.layout(idx, 1, 1, 1)
+    q = np.zeros((1, 1, H), dtype=np.uint8)
+    sc = np.full((1, 1, 2), -1, dtype=np.float32)
+    oracle.dispatch_fp8(x, idx, lay["slot"], 1, 1, q, sc)
+    assert sc[0, 0, 0] == 0.0 and q[0, 0, 5] == 0x80 and (np.delete(q[0, 0, :128], 5) == 0).all()
+    assert sc[0, 0, 1] == np.float32(3.0) / np.float32(448.0) and q[0, 0, 130] == 0x7E
+
+
+def test_combine_identity_law():
+    """y := the bf16 dispatch output, unit weights: out[t] = bf16(n_kept(t) * x[t]); with no
+    drops n = K = 8 and the result is exactly 8 x (a power of two)."""
+    cfg = W.get_config("decode_bf16")
+    inp = W.make_inputs(cfg)
+    C = 160
+    lay = oracle.layout(inp["topk_idx"], cfg.E, C, cfg.R)
+    y = np.zeros((cfg.E, C, cfg.H), dtype=np.uint16)
+    oracle.dispatch(inp["x"], inp["topk_idx"], lay["slot"], cfg.E, C, y)
+    ones = np.ones((cfg.T, cfg.K), dtype=np.float32)
+    out = oracle.combine(y, inp["topk_idx"], lay["slot"], ones)
+    want = W.f32_to_bf16_bits(8.0 * W.bf16_bits_to_f32(inp["x"]))
+    assert np.array_equal(out, want)
+    # with drops and invalid pairs: n_kept(t) * x, n counted per token
+    c = small_case()
+    y = np.zeros((c["E"], c["C"], c["H"]), dtype=np.uint16)
+    oracle.dispatch(c["x"], c["idx"], c["slot"], c["E"], c["C"], y)
+    out = oracle.combine(y, c["idx"], c["slot"], np.ones((c["T"], c["K"]), dtype=np.float32))
+    n = (c["slot"] >= 0).sum(axis=1).astype(np.float32)
+    want = W.f32_to_bf16_bits(n[:, None] * W.bf16_bits_to_f32(c["x"]))
+    want[n == 0] = 0                          # a token with no kept pair is +0, not n * x = -0
+    assert (n == 0).any() and np.array_equal(out, want)
+
+
+def test_combine_one_hot_returns_row():
+    c = small_case(seed=4)
+    rng = np.random.default_rng(5)
+    y = W.f32_to_bf16_bits(rng.standard_normal((c["E"], c["C"], c["H"]), dtype=np.float32))
+    w = np.zeros((c["T"], c["K"]), dtype=np.float32)
+    kept = c["slot"] >= 0
+    tokens = np.nonzero(kept.any(axis=1))[0]
+    jsel = kept.argmax(axis=1)
+    w[np.arange(c["T"]), jsel] = 1.0
+    out = oracle.combine(y, c["idx"], c["slot"], w)
+    for t in tokens:
+        j = jsel[t]
+        assert np.array_equal(out[t], y[c["idx"][t, j], c["slot"][t, j]])
+    for t in np.nonzero(~kept.any(axis=1))[0]:
+        assert (out[t] == 0).all()            # all-dropped token: +0
+
+
+def test_combine_within_one_ulp_of_fp64():
+    cfg = W.get_config("decode_bf16")
+    inp = W.make_inputs(cfg)
+    C = 160
+    lay = oracle.layout(inp["topk_idx"], cfg.E, C, cfg.R)
+    rng = np.random.default_rng(9)
+    y = W.f32_to_bf16_bits(rng.standard_normal((cfg.E, C, cfg.H), dtype=np.float32))
+    out = oracle.combine(y, inp["topk_idx"], lay["slot"], inp["topk_w"])
+    yf = W.bf16_bits_to_f32(y).astype(np.float64)
+    exact = np.zeros((cfg.T, cfg.H))
+    for j in range(cfg.K):
+        exact += inp["topk_w"][:, j:j + 1].astype(np.float64) * yf[inp["topk_idx"][:, j], lay["slot"][:, j]]
+    got = W.bf16_bits_to_f32(out).astype(np.float64)
+    # one bf16 ulp of the exact value (2^-7 relative to its binade), plus a floor for
+    # results near zero where the fp32 running sum can cancel
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(exact), 2.0 ** -30))) - 7)
+    assert (np.abs(got - exact) <= ulp + 2.0 ** -20).all()
+
+
+def test_combine_uses_fused_multiply_add():
+    """w = 1 + 2^-17, y1 = 1 + 2^-7: the product needs 25 bits. After acc = -(1 + 2^-7 + 2^-17)
+    from j = 0, a fused multiply-add leaves 2^-24 and the output is bf16(2^-24); rounding the
+    product first would leave 0."""
+    H = 8
+    y = np.zeros((2, 1, H), dtype=np.uint16)
+    y0 = np.float32(-(1 + 2 ** -7))
+    y[0, 0, :] = W.f32_to_bf16_bits(np.array([y0] * H, dtype=np.float32))
+    y[1, 0, :] = W.f32_to_bf16_bits(np.array([1 + 2 ** -7] * H, dtype=np.float32))
+    idx = np.array([[0, 1]], dtype=np.int32)
+    slot = np.array([[0, 0]], dtype=np.int32)
+    w = np.array([[1 + 2 ** -17, 1 + 2 ** -17]], dtype=np.float32)
+    # j = 0: acc = fl(w0 * y0) = -(1 + 2^-7 + 2^-17); the dropped 2^-24 is a tie to even
+    out = oracle.combine(y, idx, slot, w)
+    assert (W.bf16_bits_to_f32(out) == np.float32(2.0 ** -24)).all()
+
+
+def test_combine_ascending_j_order():
+    """y rows 2^24, 1, -2^24 with unit weights: ascending j gives (2^24 + 1) -> 2^24, then 0;
+    descending j would give 1."""
+    H = 8
+    vals = [2.0 ** 24, 1.0, -(2.0 ** 24)]
+    y = np.zeros((3, 1, H), dtype=np.uint16)
+    for e, v in enumerate(vals):
+        y[e, 0, :] = W.f32_to_bf16_bits(np.full(H, v, dtype=np.float32))
+    idx = np.array([[0, 1, 2]], dtype=np.int32)
+    slot = np.zeros((1, 3), dtype=np.int32)
+    out = oracle.combine(y, idx, slot, np.ones((1, 3), dtype=np.float32))
+    assert (out == 0).all()
+    out_rev = oracle.combine(y, idx[:, ::-1].copy(), slot, np.ones((1, 3), dtype=np.float32))
+    assert (W.bf16_bits_to_f32(out_rev) == 1.0).all()
+
+
+def test_combine_tokens_matches_full():
+    c = small_case(seed=11)
+    rng = np.random.default_rng(12)
+    y = W.f32_to_bf16_bits(rng.standard_normal((c["E"], c["C"], c["H"]), dtype=np.float32))
+    full = oracle.combine(y, c["idx"], c["slot"], c["w"])
+    toks = np.array([0, 5, 36, 5], dtype=np.int32)
+    assert np.array_equal(oracle.combine_tokens(toks, y, c["idx"], c["slot"], c["w"]), full[toks])
