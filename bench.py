@@ -1,0 +1,312 @@
+#!/usr/bin/env python3
+"""Benchmark of one GPU's MoE expert-parallel layout + dispatch + combine on MI355X.
+
+One step is the whole hot path on one batch: ep_layout -> ep_dispatch (bf16) or
+ep_dispatch_fp8 -> ep_combine, enqueued on one stream with the inputs already in HBM. The
+boundary follows the common event boundary of awsome-distributed-ai PR #1238 ("What
+changed"): from route and input ready through the FP8 cast or layout, dispatch and combine
+completion.
+
+Headline (one JSON line on stdout): logical GB/s of the Prefill-like bf16 workload (T=4096,
+H=2048, E=128 experts as 16 virtual ranks of 8, top-8, capacity 4096): the useful payload of the
+PR's accounting (4*T*K*H bytes for bf16) over the measured time per step, with the fraction of
+the HBM roofline (algorithmic bytes / time / 8 TB/s). The same line carries the Decode-like
+(T=128) dispatch+combine latency, the FP8 Prefill-like workload, the dominant kernel's roofline
+and the CPU oracle's time on the host.
+
+Timing: W untimed warm-up steps, then exactly K steps back to back between two
+synchronisations. Every step uses the next of NSETS independent buffer sets (inputs, receive
+buffer, outputs), so consecutive steps never reuse a byte and each step's ~300 MB must come from
+HBM rather than the 256 MB last-level cache. Decode-like latency is single-shot: each step is
+synchronised on its own and timed with an event pair (median of the samples).
+
+``--gpus N`` with N > 1 is refused: this build measures one GPU; inter-GPU transport is not
+part of it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+import numpy as np
+
+METRIC = "dispatch+combine µs at T=128 and logical GB/s (+% HBM roofline) at T=4096"
+NSETS = 4
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="prefill_bf16")
+    ap.add_argument("--latency-samples", type=int, default=200)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget for the oracle's CPU baseline")
+    ap.add_argument("--only", default=None,
+                    help="run only this workload's timed loop (for profiling)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Workload:
+    """NSETS independent buffer sets for one config, all resident on the GPU."""
+
+    def __init__(self, cfg, nsets, torch, B, W):
+        self.cfg, self.torch, self.B = cfg, torch, B
+        dev = torch.device("cuda", 0)
+        self.sets = []
+        for k in range(nsets):
+            inp = W.make_inputs(cfg, seed=cfg.seed + k)
+            s = {}
+            s["x"] = torch.from_numpy(inp["x"].view(np.int16)).to(dev)
+            s["idx"] = torch.from_numpy(inp["topk_idx"]).to(dev)
+            s["w"] = torch.from_numpy(inp["topk_w"]).to(dev)
+            g = torch.Generator(device=dev)
+            g.manual_seed(1000 + cfg.seed + k)
+            y = torch.empty((cfg.E, cfg.C, cfg.H), dtype=torch.bfloat16, device=dev)
+            for e in range(cfg.E):        # expert outputs ~ N(0, 1), one expert at a time
+                y[e].copy_(torch.randn((cfg.C, cfg.H), generator=g, device=dev))
+            s["y"] = y.view(torch.int16)
+            if cfg.fp8:
+                s["recv_q"] = torch.empty((cfg.E, cfg.C, cfg.H), dtype=torch.uint8, device=dev)
+                s["recv_s"] = torch.empty((cfg.E, cfg.C, cfg.H // 128), dtype=torch.float32,
+                                          device=dev)
+            else:
+                s["recv"] = torch.empty((cfg.E, cfg.C, cfg.H), dtype=torch.int16, device=dev)
+            s["out"] = torch.empty((cfg.T, cfg.H), dtype=torch.int16, device=dev)
+            T, K, E, R = cfg.T, cfg.K, cfg.E, cfg.R
+            mk = lambda n: torch.empty(n, dtype=torch.int32, device=dev)
+            s["lay"] = dict(slot=mk((T, K)), expert_count=mk(E), expert_offset=mk(E),
+                            rank_count=mk(R), rank_offset=mk(R), stats=mk(4))
+            self.sets.append(s)
+        torch.cuda.synchronize()
+        self.n_kept = None
+
+    # the three calls of one step
+    def layout(self, s):
+        c = self.cfg
+        self.B.ep_layout(s["idx"], c.E, c.C, c.R, **s["lay"])
+
+    def dispatch(self, s):
+        c = self.cfg
+        if c.fp8:
+            self.B.ep_dispatch_fp8(s["x"], s["idx"], s["lay"]["slot"], s["recv_q"], s["recv_s"], c.C)
+        else:
+            self.B.ep_dispatch(s["x"], s["idx"], s["lay"]["slot"], s["recv"], c.C)
+
+    def combine(self, s):
+        c = self.cfg
+        self.B.ep_combine(s["y"], s["idx"], s["lay"]["slot"], s["w"], c.C, out=s["out"])
+
+    def step(self, k):
+        s = self.sets[k % len(self.sets)]
+        self.layout(s)
+        self.dispatch(s)
+        self.combine(s)
+
+    def kept(self):
+        """Kept pairs per set, read from the GPU layout's stats (after a step ran)."""
+        self.torch.cuda.synchronize()
+        return [int(s["lay"]["stats"][0]) for s in self.sets]
+
+    def timed_loop(self, steps, warmup):
+        torch = self.torch
+        for k in range(warmup):
+            self.step(k)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for k in range(steps):
+            self.step(k)
+        ev1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return ev0.elapsed_time(ev1) / steps, wall / steps * 1e3
+
+    def single_shot(self, samples, flush):
+        """Single-shot latency of one step, cold: each sample first overwrites `flush` (1 GiB,
+        beyond every cache level) outside the event pair. While that fill runs, the host has
+        already enqueued the event pair and the step's three launches, so the pair measures
+        the GPU-side time of the step including the gaps between its kernels, not host-side
+        launch overhead."""
+        torch = self.torch
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for k in range(samples):
+            torch.cuda.synchronize()
+            flush.fill_(k & 0x7F)
+            ev0.record()
+            self.step(k)
+            ev1.record()
+            torch.cuda.synchronize()
+            ts.append(ev0.elapsed_time(ev1) * 1e3)
+        return ts
+
+    def kernel_avg_us(self, which, reps):
+        """Average duration of one kernel, launched `reps` times back to back over the buffer
+        sets (the other two steps ran before, so its inputs are valid), with events on the
+        stream it runs on."""
+        torch = self.torch
+        fn = {"layout": self.layout, "dispatch": self.dispatch, "combine": self.combine}[which]
+        for k in range(len(self.sets)):
+            self.step(k)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for k in range(reps):
+            fn(self.sets[k % len(self.sets)])
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) * 1e3 / reps
+
+
+def cpu_baseline(cfg, budget_s, W, A):
+    """The oracle as it stands, single-threaded on one host core, on whole steps of the same
+    workload, repeated until about `budget_s` seconds of CPU work."""
+    import oracle
+    try:
+        os.sched_setaffinity(0, {min(os.sched_getaffinity(0))})
+    except (AttributeError, OSError):
+        pass
+    inp = W.make_inputs(cfg)
+    x, idx, w = inp["x"], inp["topk_idx"], inp["topk_w"]
+    lay = oracle.layout(idx, cfg.E, cfg.C, cfg.R)
+    slot = lay["slot"]
+    kept_i = np.nonzero(slot.reshape(-1) >= 0)[0]
+    e = idx.reshape(-1)[kept_i]
+    s = slot.reshape(-1)[kept_i]
+    y = np.empty((cfg.E, cfg.C, cfg.H), dtype=np.uint16)
+    y[e, s] = W.y_rows(len(kept_i), cfg.H, cfg.seed)
+    recv = np.empty((cfg.E, cfg.C, cfg.H), dtype=np.uint16)
+    times, t_start = [], time.perf_counter()
+    while time.perf_counter() - t_start < budget_s or not times:
+        t0 = time.perf_counter()
+        lay = oracle.layout(idx, cfg.E, cfg.C, cfg.R)
+        oracle.dispatch(x, idx, lay["slot"], cfg.E, cfg.C, recv)
+        oracle.combine(y, idx, lay["slot"], w)
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    payload = A.logical_payload_bytes(cfg.T, cfg.K, cfg.H, False)
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    return {"value": round(payload / med / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{len(times)} whole steps (layout + bf16 dispatch + combine) of "
+                      f"{cfg.name}, median {med * 1e3:.1f} ms/step, single thread pinned to one "
+                      f"core of {os.cpu_count()} ({cpu})"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path has no "
+              "inter-GPU transport).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from combine_ep_layout_06_amd import accounting as A
+    from combine_ep_layout_06_amd import binding as B
+    from combine_ep_layout_06_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    B.load_library()
+    log(f"library: {B.ep_version()}  device: {torch.cuda.get_device_name(0)}")
+
+    if args.only:
+        cfg = W.get_config(args.only)
+        wl = Workload(cfg, NSETS, torch, B, W)
+        ms, _ = wl.timed_loop(args.steps, args.warmup)
+        log(f"{cfg.name}: {ms * 1e3:.2f} us/step")
+        return
+
+    head_cfg = W.get_config(args.workload)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    results = {}
+    for name in dict.fromkeys([args.workload, "prefill_fp8", "decode_bf16", "decode_fp8"]):
+        cfg = W.get_config(name)
+        wl = Workload(cfg, NSETS, torch, B, W)
+        ms, wall_ms = wl.timed_loop(args.steps, args.warmup)
+        kept = wl.kept()
+        n_kept = kept[0]
+        pay = A.logical_payload_bytes(cfg.T, cfg.K, cfg.H, cfg.fp8)
+        alg = A.step_bytes(cfg.T, cfg.K, cfg.H, n_kept, cfg.fp8)
+        r = {"us_per_step": round(ms * 1e3, 3), "wall_us_per_step": round(wall_ms * 1e3, 3),
+             "logical_GBps": round(pay / (ms * 1e-3) / 1e9, 2),
+             "hbm_frac": round(alg / (ms * 1e-3) / A.HBM_PEAK_BYTES_PER_S, 4),
+             "algorithmic_bytes": alg, "payload_bytes": pay, "kept_pairs": n_kept}
+        if cfg.T <= 256:
+            ss = wl.single_shot(args.latency_samples, flush)
+            r["us_single_shot_median"] = round(statistics.median(ss), 3)
+            r["us_single_shot_min"] = round(min(ss), 3)
+            r["us_single_shot_max"] = round(max(ss), 3)
+        kus = {k: wl.kernel_avg_us(k, args.steps) for k in ("layout", "dispatch", "combine")}
+        r["kernel_avg_us"] = {k: round(v, 3) for k, v in kus.items()}
+        kb = {"layout": A.layout_bytes(cfg.T, cfg.K),
+              "dispatch": A.dispatch_bytes(cfg.T, cfg.K, cfg.H, n_kept, cfg.fp8),
+              "combine": A.combine_bytes(cfg.T, cfg.K, cfg.H, n_kept)}
+        r["kernel_GBps"] = {k: round(kb[k] / (kus[k] * 1e-6) / 1e9, 1) for k in kus}
+        results[name] = (cfg, None, r, kus, kb)
+        log(f"{name}: {json.dumps(r)}")
+        del wl
+        torch.cuda.empty_cache()
+
+    cfg, _, r, kus, kb = results[args.workload]
+    dom = max(("dispatch", "combine"), key=lambda k: kus[k])
+    achieved = kb[dom] / (kus[dom] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": A.HBM_PEAK_BYTES_PER_S / 1e9, "unit": "GB/s",
+                "frac": round(achieved / (A.HBM_PEAK_BYTES_PER_S / 1e9), 4),
+                "traffic": None, "avg_launch_us": round(kus[dom], 3),
+                "bytes_per_launch": kb[dom]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        cpu = cpu_baseline(head_cfg, args.cpu_seconds, W, A)
+
+    def brief(name):
+        c, _, rr, _, _ = results[name]
+        keys = ("us_per_step", "us_single_shot_median", "logical_GBps", "hbm_frac",
+                "kernel_avg_us")
+        return {k: rr[k] for k in keys if k in rr}
+
+    line = {
+        "metric": METRIC, "value": r["logical_GBps"], "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["us_per_step"] / 1e3, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; inputs resident in HBM; 4 rotating buffer sets)",
+        "config": {"workload": f"{cfg.name}: T={cfg.T} H={cfg.H} E={cfg.E} K={cfg.K} "
+                               f"C={cfg.C} R={cfg.R} ({cfg.route} distinct top-{cfg.K})",
+                   "T": cfg.T, "H": cfg.H, "E": cfg.E, "K": cfg.K, "C": cfg.C, "R": cfg.R,
+                   "parallelism": "single GPU"},
+        "hbm_roofline_frac": r["hbm_frac"],
+        "us_per_step": r["us_per_step"],
+        "t128_us": {n: brief(n) for n in ("decode_bf16", "decode_fp8") if n in results},
+        "prefill_fp8": brief("prefill_fp8") if "prefill_fp8" in results else None,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "library": B.ep_version(),
+        "torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+        "host": platform.node(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,201 @@
+"""ctypes binding of libep_mi355x.so (include/ep.h) for torch tensors.
+
+Argument marshalling only: each function checks dtypes, devices, sizes and contiguity, then
+passes ``data_ptr()`` values and torch's current HIP stream to the C entry point of the same
+name. Every step of the computation runs in the library's gfx950 kernels; there is no other
+code path. If the library is missing the functions raise instead of computing anything.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB
+
+EP_OK, EP_ERR_INVALID, EP_ERR_ALIGN, EP_ERR_UNSUPPORTED, EP_ERR_HIP = 0, -1, -2, -3, -4
+EP_STATS_LEN = 4
+EP_MAX_EXPERTS = 1024
+EP_MAX_TOPK = 256
+EP_FP8_BLOCK = 128
+
+#: every entry point the header declares
+EXPORTED = ("ep_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_combine", "ep_error_string",
+            "ep_last_error", "ep_version")
+
+
+class EpShape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("C", ctypes.c_int32), ("R", ctypes.c_int32)]
+
+
+class EpError(RuntimeError):
+    def __init__(self, fn: str, code: int, detail: str):
+        super().__init__(f"{fn} failed with {code}: {detail}")
+        self.code = code
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.environ.get("EP_MI355X_LIB", LIB)
+
+
+def load_library():
+    """Load the HIP library once. Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
+                               "`python -m combine_ep_layout_06_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(path)
+        vp, sp = ctypes.c_void_p, ctypes.POINTER(EpShape)
+        L.ep_layout.argtypes = [sp] + [vp] * 7 + [vp]
+        L.ep_dispatch.argtypes = [sp, vp, vp, vp, vp, vp]
+        L.ep_dispatch_fp8.argtypes = [sp, vp, vp, vp, vp, vp, vp]
+        L.ep_combine.argtypes = [sp, vp, vp, vp, vp, vp, vp]
+        for fn in ("ep_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_combine"):
+            getattr(L, fn).restype = ctypes.c_int
+        L.ep_error_string.argtypes = [ctypes.c_int]
+        L.ep_error_string.restype = ctypes.c_char_p
+        L.ep_last_error.argtypes = []
+        L.ep_last_error.restype = ctypes.c_char_p
+        L.ep_version.argtypes = []
+        L.ep_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def ep_version() -> str:
+    return load_library().ep_version().decode()
+
+
+def ep_error_string(code: int) -> str:
+    return load_library().ep_error_string(code).decode()
+
+
+def _check(fn: str, rc: int):
+    if rc != EP_OK:
+        raise EpError(fn, rc, load_library().ep_last_error().decode())
+
+
+def _shape(T, H, E, K, C, R) -> EpShape:
+    return EpShape(int(T), int(H), int(E), int(K), int(C), int(R))
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, numel: int, device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name}: expected {numel} elements, got {t.numel()}")
+
+
+def _bf16(t: torch.Tensor) -> torch.dtype:
+    # bf16 rows may be passed as torch.bfloat16 or as their int16/uint16 bit patterns
+    return t.dtype if t.dtype in (torch.bfloat16, torch.int16, torch.uint16) else torch.bfloat16
+
+
+def ep_layout(topk_idx: torch.Tensor, E: int, C: int, R: int, *, slot=None, expert_count=None,
+              expert_offset=None, rank_count=None, rank_offset=None, stats=None, stream=None):
+    """Routing layout. ``topk_idx`` int32 [T, K] on the GPU. Returns a dict of the outputs
+    (``slot`` [T, K], ``expert_count`` [E], ``expert_offset`` [E], ``rank_count`` [R],
+    ``rank_offset`` [R], ``stats`` [4] = kept, dropped, unrouted, invalid); any of them may be
+    passed in preallocated."""
+    dev = topk_idx.device
+    T, K = topk_idx.shape
+    mk = lambda n: torch.empty(n, dtype=torch.int32, device=dev)
+    slot = mk((T, K)) if slot is None else slot
+    expert_count = mk(E) if expert_count is None else expert_count
+    expert_offset = mk(E) if expert_offset is None else expert_offset
+    rank_count = mk(R) if rank_count is None else rank_count
+    rank_offset = mk(R) if rank_offset is None else rank_offset
+    stats = mk(EP_STATS_LEN) if stats is None else stats
+    _need(topk_idx, "topk_idx", torch.int32, T * K, dev)
+    _need(slot, "slot", torch.int32, T * K, dev)
+    for name, t, n in (("expert_count", expert_count, E), ("expert_offset", expert_offset, E),
+                       ("rank_count", rank_count, R), ("rank_offset", rank_offset, R),
+                       ("stats", stats, EP_STATS_LEN)):
+        _need(t, name, torch.int32, n, dev)
+    sh = _shape(T, 1, E, K, C, R)
+    rc = load_library().ep_layout(ctypes.byref(sh), _ptr(topk_idx), _ptr(slot),
+                                  _ptr(expert_count), _ptr(expert_offset), _ptr(rank_count),
+                                  _ptr(rank_offset), _ptr(stats), _stream(stream))
+    _check("ep_layout", rc)
+    return dict(slot=slot, expert_count=expert_count, expert_offset=expert_offset,
+                rank_count=rank_count, rank_offset=rank_offset, stats=stats)
+
+
+def ep_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, slot: torch.Tensor, recv: torch.Tensor,
+                C: int, *, stream=None):
+    """bf16 dispatch: ``x`` [T, H] bf16 -> ``recv`` [E, C, H] bf16 (written in place)."""
+    dev = x.device
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    E = recv.numel() // (C * H)
+    _need(x, "x", _bf16(x), T * H, dev)
+    _need(topk_idx, "topk_idx", torch.int32, T * K, dev)
+    _need(slot, "slot", torch.int32, T * K, dev)
+    _need(recv, "recv", _bf16(recv), E * C * H, dev)
+    sh = _shape(T, H, E, K, C, 1)
+    rc = load_library().ep_dispatch(ctypes.byref(sh), _ptr(x), _ptr(topk_idx), _ptr(slot),
+                                    _ptr(recv), _stream(stream))
+    _check("ep_dispatch", rc)
+    return recv
+
+
+def ep_dispatch_fp8(x: torch.Tensor, topk_idx: torch.Tensor, slot: torch.Tensor,
+                    recv_q: torch.Tensor, recv_scale: torch.Tensor, C: int, *, stream=None):
+    """FP8 dispatch: ``x`` [T, H] bf16 -> ``recv_q`` [E, C, H] uint8 (OCP E4M3 codes) and
+    ``recv_scale`` [E, C, H/128] float32 (written in place)."""
+    dev = x.device
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    E = recv_q.numel() // (C * H)
+    _need(x, "x", _bf16(x), T * H, dev)
+    _need(topk_idx, "topk_idx", torch.int32, T * K, dev)
+    _need(slot, "slot", torch.int32, T * K, dev)
+    _need(recv_q, "recv_q", recv_q.dtype if recv_q.dtype in (torch.uint8, torch.float8_e4m3fn)
+          else torch.uint8, E * C * H, dev)
+    _need(recv_scale, "recv_scale", torch.float32, E * C * (H // EP_FP8_BLOCK), dev)
+    sh = _shape(T, H, E, K, C, 1)
+    rc = load_library().ep_dispatch_fp8(ctypes.byref(sh), _ptr(x), _ptr(topk_idx), _ptr(slot),
+                                        _ptr(recv_q), _ptr(recv_scale), _stream(stream))
+    _check("ep_dispatch_fp8", rc)
+    return recv_q, recv_scale
+
+
+def ep_combine(y: torch.Tensor, topk_idx: torch.Tensor, slot: torch.Tensor,
+               topk_w: torch.Tensor, C: int, *, out=None, stream=None):
+    """Combine: ``y`` [E, C, H] bf16 -> ``out`` [T, H] bf16."""
+    dev = y.device
+    T, K = topk_idx.shape
+    H = y.shape[-1]
+    E = y.numel() // (C * H)
+    out = torch.empty((T, H), dtype=_bf16(y), device=dev) if out is None else out
+    _need(y, "y", _bf16(y), E * C * H, dev)
+    _need(topk_idx, "topk_idx", torch.int32, T * K, dev)
+    _need(slot, "slot", torch.int32, T * K, dev)
+    _need(topk_w, "topk_w", torch.float32, T * K, dev)
+    _need(out, "out", _bf16(out), T * H, dev)
+    sh = _shape(T, H, E, K, C, 1)
+    rc = load_library().ep_combine(ctypes.byref(sh), _ptr(y), _ptr(topk_idx), _ptr(slot),
+                                   _ptr(topk_w), _ptr(out), _stream(stream))
+    _check("ep_combine", rc)
+    return out

@@ -1,0 +1,149 @@
+// C ABI of libep_mi355x: argument checks on the host, then the gfx950 kernel launches.
+// Every entry point is declared and documented in include/ep.h.
+#include <stdint.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "ep.h"
+#include "ep_internal.h"
+
+#ifndef EP_VERSION_STRING
+#define EP_VERSION_STRING "0.1.0"
+#endif
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string &what)
+{
+    g_last_error = what;
+    return code;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape rules common to every call. On failure returns a negative code and records why.
+int check_shape(const ep_shape_t *s, const char *fn)
+{
+    std::string f(fn);
+    if (!s) return fail(EP_ERR_INVALID, f + ": shape is NULL");
+    if (s->T < 0 || s->H < 1 || s->E < 1 || s->K < 1 || s->C < 1 || s->R < 1)
+        return fail(EP_ERR_INVALID, f + ": need T >= 0 and H, E, K, C, R >= 1");
+    if (s->E % s->R != 0) return fail(EP_ERR_INVALID, f + ": E must be a multiple of R");
+    if ((int64_t)s->T * s->K > INT32_MAX) return fail(EP_ERR_INVALID, f + ": T*K exceeds INT32_MAX");
+    if ((int64_t)s->E * s->C > INT32_MAX) return fail(EP_ERR_INVALID, f + ": E*C exceeds INT32_MAX");
+    return EP_OK;
+}
+
+// Limits of the dispatch and combine kernels: 16-byte rows, and the K pairs of a token staged
+// in one workgroup's LDS.
+int check_rows(const ep_shape_t *s, const char *fn, int h_multiple)
+{
+    if (s->H % h_multiple != 0)
+        return fail(EP_ERR_UNSUPPORTED, std::string(fn) + ": H must be a multiple of " +
+                                            std::to_string(h_multiple));
+    if (s->K > EP_MAX_TOPK)
+        return fail(EP_ERR_UNSUPPORTED, std::string(fn) + ": K exceeds EP_MAX_TOPK");
+    return EP_OK;
+}
+
+int hip_status(hipError_t e, const char *fn)
+{
+    if (e == hipSuccess) {
+        g_last_error.clear();
+        return EP_OK;
+    }
+    return fail(EP_ERR_HIP, std::string(fn) + ": " + hipGetErrorName(e) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int ep_layout(const ep_shape_t *shape, const int32_t *topk_idx, int32_t *slot,
+              int32_t *expert_count, int32_t *expert_offset, int32_t *rank_count,
+              int32_t *rank_offset, int32_t *stats, hipStream_t stream)
+{
+    if (int rc = check_shape(shape, "ep_layout")) return rc;
+    if (shape->E > EP_MAX_EXPERTS)
+        return fail(EP_ERR_UNSUPPORTED, "ep_layout: E exceeds EP_MAX_EXPERTS");
+    const bool empty = (int64_t)shape->T * shape->K == 0;
+    if ((!empty && (!topk_idx || !slot)) || !expert_count || !expert_offset || !stats)
+        return fail(EP_ERR_INVALID, "ep_layout: NULL required pointer");
+    return hip_status(ep::launch_layout(*shape, topk_idx, slot, expert_count, expert_offset,
+                                        rank_count, rank_offset, stats, stream),
+                      "ep_layout");
+}
+
+int ep_dispatch(const ep_shape_t *shape, const uint16_t *x, const int32_t *topk_idx,
+                const int32_t *slot, uint16_t *recv, hipStream_t stream)
+{
+    if (int rc = check_shape(shape, "ep_dispatch")) return rc;
+    if (int rc = check_rows(shape, "ep_dispatch", 8)) return rc;
+    if (shape->T == 0) return hip_status(hipSuccess, "ep_dispatch");
+    if (!x || !topk_idx || !slot || !recv)
+        return fail(EP_ERR_INVALID, "ep_dispatch: NULL required pointer");
+    if (!aligned(x, 16) || !aligned(recv, 16))
+        return fail(EP_ERR_ALIGN, "ep_dispatch: x and recv must be 16-byte aligned");
+    return hip_status(ep::launch_dispatch_bf16(*shape, x, topk_idx, slot, recv, stream),
+                      "ep_dispatch");
+}
+
+int ep_dispatch_fp8(const ep_shape_t *shape, const uint16_t *x, const int32_t *topk_idx,
+                    const int32_t *slot, uint8_t *recv_q, float *recv_scale, hipStream_t stream)
+{
+    if (int rc = check_shape(shape, "ep_dispatch_fp8")) return rc;
+    if (int rc = check_rows(shape, "ep_dispatch_fp8", EP_FP8_BLOCK)) return rc;
+    if (shape->T == 0) return hip_status(hipSuccess, "ep_dispatch_fp8");
+    if (!x || !topk_idx || !slot || !recv_q || !recv_scale)
+        return fail(EP_ERR_INVALID, "ep_dispatch_fp8: NULL required pointer");
+    if (!aligned(x, 16) || !aligned(recv_q, 16) || !aligned(recv_scale, 4))
+        return fail(EP_ERR_ALIGN, "ep_dispatch_fp8: x and recv_q must be 16-byte aligned, "
+                                  "recv_scale 4-byte aligned");
+    return hip_status(ep::launch_dispatch_fp8(*shape, x, topk_idx, slot, recv_q, recv_scale,
+                                              stream),
+                      "ep_dispatch_fp8");
+}
+
+int ep_combine(const ep_shape_t *shape, const uint16_t *y, const int32_t *topk_idx,
+               const int32_t *slot, const float *topk_w, uint16_t *out, hipStream_t stream)
+{
+    if (int rc = check_shape(shape, "ep_combine")) return rc;
+    if (int rc = check_rows(shape, "ep_combine", 8)) return rc;
+    if (shape->T == 0) return hip_status(hipSuccess, "ep_combine");
+    if (!y || !topk_idx || !slot || !topk_w || !out)
+        return fail(EP_ERR_INVALID, "ep_combine: NULL required pointer");
+    if (!aligned(y, 16) || !aligned(out, 16))
+        return fail(EP_ERR_ALIGN, "ep_combine: y and out must be 16-byte aligned");
+    return hip_status(ep::launch_combine(*shape, y, topk_idx, slot, topk_w, out, stream),
+                      "ep_combine");
+}
+
+const char *ep_error_string(int code)
+{
+    switch (code) {
+    case EP_OK: return "EP_OK: success";
+    case EP_ERR_INVALID: return "EP_ERR_INVALID: invalid shape or NULL pointer";
+    case EP_ERR_ALIGN: return "EP_ERR_ALIGN: buffer not aligned";
+    case EP_ERR_UNSUPPORTED: return "EP_ERR_UNSUPPORTED: shape not supported by the kernels";
+    case EP_ERR_HIP: return "EP_ERR_HIP: HIP runtime error";
+    default: return "unknown ep error code";
+    }
+}
+
+const char *ep_last_error(void) { return g_last_error.c_str(); }
+
+const char *ep_version(void)
+{
+    static const std::string v = [] {
+        char buf[96];
+        snprintf(buf, sizeof buf, "libep_mi355x %s (gfx950; HIP %d.%d.%d)", EP_VERSION_STRING,
+                 HIP_VERSION_MAJOR, HIP_VERSION_MINOR, HIP_VERSION_PATCH);
+        return std::string(buf);
+    }();
+    return v.c_str();
+}
+
+}  // extern "C"

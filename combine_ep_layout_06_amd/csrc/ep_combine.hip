@@ -1,0 +1,176 @@
+// Combine on gfx950: gather each token's kept expert-output rows and form the top-k weighted
+// sum in fp32, in ascending j, rounding once to bf16.
+//
+// Combine reduces the expert outputs with the top-k weights on the token's side (afdEP-comm
+// validation record, kernel_timelines: combine_reduce_epilogue), in BF16 whatever the dispatch
+// dtype (awsome-distributed-ai PR #1238, review item 1). Traffic: each kept y row is read once
+// (2*H), the output row written once (2*H per token).
+//
+// Work split. A workgroup of 4 wavefronts owns `tpb` consecutive tokens and first stages the
+// receive-row numbers and weights of their tpb*K pairs in LDS with one coalesced pass. A
+// wavefront item is one token and one row segment; each lane owns U 16-byte chunks (8 bf16
+// channels each, lane-contiguous, so one load instruction covers 1 KiB of a row).
+//
+// Memory-level parallelism. For a group of KG pairs (KG = K rounded up to a power of two, at
+// most 8) the wavefront issues every row load first, as straight-line code with clamped
+// addresses (a pair that is not kept loads row 0 and its result is discarded by a select), and
+// only then folds the rows in j order with fmaf. The K row fetches of a token are therefore
+// in flight together; a branch around any load would make the compiler wait for earlier
+// loads before issuing the next one. Loads of y and stores of out are non-temporal: each byte
+// is touched once.
+#include "ep_device.h"
+#include "ep_internal.h"
+
+#ifndef EP_COMBINE_U
+#define EP_COMBINE_U 0      // 16-byte chunks per lane per item (0 = choose from the shape)
+#endif
+#ifndef EP_COMBINE_TPB
+#define EP_COMBINE_TPB 0    // tokens per workgroup (0 = choose from the shape)
+#endif
+
+namespace ep {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kStage = 256;        // staged pairs per workgroup (tpb * K <= kStage)
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// KG: pairs per group (K <= KG unless MULTI); U: chunks per lane per item.
+template <int KG, int U, bool MULTI>
+__global__ __launch_bounds__(kThreads) void combine_kernel(
+    const u32x4 *__restrict__ y, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ slot, const float *__restrict__ topk_w,
+    u32x4 *__restrict__ out, int T, int H8, int E, int C, int K, int tpb, int nseg)
+{
+    __shared__ int32_t rows[kStage];
+    __shared__ float wts[kStage];
+    const int tid = threadIdx.x;
+    const int t0 = blockIdx.x * tpb;
+    const int nt = min(tpb, T - t0);
+    for (int k = tid; k < nt * K; k += kThreads) {
+        const size_t i = (size_t)t0 * K + k;
+        const int e = idx[i], s = slot[i];
+        rows[k] = ((unsigned)e < (unsigned)E && (unsigned)s < (unsigned)C) ? e * C + s : -1;
+        wts[k] = topk_w[i];
+    }
+    __syncthreads();
+
+    const int wave = uniform(tid / kWave);
+    const int lane = tid & (kWave - 1);
+    for (int item = wave; item < nt * nseg; item += kWaves) {
+        const int tl = item / nseg;
+        const int seg = item - tl * nseg;
+        int cidx[U];          // chunk of the row this lane reads (clamped) and whether it is real
+        bool cok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = (seg * U + u) * kWave + lane;
+            cok[u] = c < H8;
+            cidx[u] = cok[u] ? c : H8 - 1;
+        }
+        float acc[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[u][k] = 0.0f;
+
+        const int ngroups = MULTI ? (K + KG - 1) / KG : 1;
+        for (int grp = 0; grp < ngroups; ++grp) {
+            int r[KG];
+            float wj[KG];
+            u32x4 v[KG][U];
+#pragma unroll
+            for (int g = 0; g < KG; ++g) {
+                const int j = grp * KG + g;
+                const int k = tl * K + (j < K ? j : K - 1);
+                const int rr = uniform(rows[k]);
+                r[g] = j < K ? rr : -1;
+                wj[g] = __int_as_float(uniform(__float_as_int(wts[k])));
+                const u32x4 *src = y + (size_t)(r[g] >= 0 ? r[g] : 0) * H8;
+#pragma unroll
+                for (int u = 0; u < U; ++u) v[g][u] = load16_stream(src + cidx[u]);
+            }
+            // keep the scheduler from pulling any use of a row above the last row load
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int g = 0; g < KG; ++g) {
+                const bool keep = r[g] >= 0;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const uint32_t wd[4] = {v[g][u].x, v[g][u].y, v[g][u].z, v[g][u].w};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const float lo = __builtin_fmaf(wj[g], bf16_lo(wd[k]), acc[u][2 * k]);
+                        const float hi = __builtin_fmaf(wj[g], bf16_hi(wd[k]), acc[u][2 * k + 1]);
+                        acc[u][2 * k] = keep ? lo : acc[u][2 * k];
+                        acc[u][2 * k + 1] = keep ? hi : acc[u][2 * k + 1];
+                    }
+                }
+            }
+        }
+        u32x4 *dst = out + (size_t)(t0 + tl) * H8;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (!cok[u]) continue;
+            u32x4 o;
+            o.x = bf16_rne(acc[u][0]) | (bf16_rne(acc[u][1]) << 16);
+            o.y = bf16_rne(acc[u][2]) | (bf16_rne(acc[u][3]) << 16);
+            o.z = bf16_rne(acc[u][4]) | (bf16_rne(acc[u][5]) << 16);
+            o.w = bf16_rne(acc[u][6]) | (bf16_rne(acc[u][7]) << 16);
+            store16_stream(dst + cidx[u], o);
+        }
+    }
+}
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+int pick_u(int T, int H8)
+{
+    if (EP_COMBINE_U) return EP_COMBINE_U;
+    if ((long)T * ceil_div(H8, 2 * kWave) >= 8192) return 2;
+    return 1;
+}
+
+int pick_tpb(int T, int K, int nseg)
+{
+    int tpb = EP_COMBINE_TPB ? EP_COMBINE_TPB : (T >= 2048 ? 2 : 1) * (nseg == 1 ? 2 : 1);
+    while (tpb > 1 && tpb * K > kStage) --tpb;
+    return tpb;
+}
+
+template <int U>
+hipError_t launch_u(const ep_shape_t &s, const u32x4 *y, const int32_t *idx, const int32_t *slot,
+                    const float *w, u32x4 *out, int H8, int tpb, int nseg, hipStream_t stream)
+{
+    const dim3 grid(ceil_div(s.T, tpb)), block(kThreads);
+#define EP_COMBINE_LAUNCH(KG, MULTI)                                                            \
+    return launch(combine_kernel<KG, U, MULTI>, grid, block, 0, stream, y, idx, slot, w, out,   \
+                  s.T, H8, s.E, s.C, s.K, tpb, nseg)
+    if (s.K > 8) EP_COMBINE_LAUNCH(8, true);
+    if (s.K > 4) EP_COMBINE_LAUNCH(8, false);
+    if (s.K > 2) EP_COMBINE_LAUNCH(4, false);
+    if (s.K > 1) EP_COMBINE_LAUNCH(2, false);
+    EP_COMBINE_LAUNCH(1, false);
+#undef EP_COMBINE_LAUNCH
+}
+
+}  // namespace
+
+hipError_t launch_combine(const ep_shape_t &s, const uint16_t *y, const int32_t *idx,
+                          const int32_t *slot, const float *w, uint16_t *out, hipStream_t stream)
+{
+    if (s.T == 0) return hipSuccess;
+    const int H8 = s.H / 8;
+    const int U = pick_u(s.T, H8) >= 2 ? 2 : 1;
+    const int nseg = ceil_div(H8, U * kWave);
+    const int tpb = pick_tpb(s.T, s.K, nseg);
+    const u32x4 *yv = reinterpret_cast<const u32x4 *>(y);
+    u32x4 *ov = reinterpret_cast<u32x4 *>(out);
+    if (U == 2) return launch_u<2>(s, yv, idx, slot, w, ov, H8, tpb, nseg, stream);
+    return launch_u<1>(s, yv, idx, slot, w, ov, H8, tpb, nseg, stream);
+}
+
+}  // namespace ep

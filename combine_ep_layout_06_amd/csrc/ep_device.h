@@ -1,0 +1,84 @@
+// Device helpers shared by the gfx950 kernels of libep_mi355x (internal header).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ep {
+
+constexpr int kWave = 64;   // CDNA wavefront width
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// A 16-byte chunk: 8 bf16 channels, or 16 FP8 codes.
+__device__ __forceinline__ u32x4 load16(const u32x4 *p) { return *p; }
+
+__device__ __forceinline__ u32x4 load16_stream(const u32x4 *p)
+{
+    return __builtin_nontemporal_load(p);
+}
+
+__device__ __forceinline__ void store16_stream(u32x4 *p, u32x4 v)
+{
+    __builtin_nontemporal_store(v, p);
+}
+
+// bf16 pattern in the low / high half of a 32-bit word -> fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 pattern, round to nearest even. Adding 0x7FFF plus the kept LSB carries into
+// the upper half exactly when the dropped half is above the midpoint, or at it with an odd
+// LSB; overflow past the largest finite value carries into the infinity pattern. NaN is
+// returned quiet with its sign.
+__device__ __forceinline__ uint32_t bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? ((u >> 16) | 0x40u) : r;
+}
+
+// fp32 -> OCP E4M3 code, round to nearest even, saturating at +-448 (NaN -> S.1111.111).
+//  * |v| >= 448 (or inf): 0x7E.
+//  * normal range [2^-6, 448): keep 3 mantissa bits by adding half an E4M3 ulp (2^19 in the
+//    fp32 mantissa) minus one plus the kept LSB, then shifting; a carry moves into the
+//    exponent, which is then rebiased from 127 to 7 (subtract 120 << 3).
+//  * below 2^-6 the E4M3 step is 2^-9: the code is the integer nearest to |v| * 2^9 (exact
+//    scaling), rounded half to even by v_rndne; 8 gives 0x08, the smallest normal.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float v)
+{
+    uint32_t u = __float_as_uint(v);
+    uint32_t sign = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t code;
+    if (a > 0x7F800000u) {
+        code = 0x7Fu;
+    } else if (a >= 0x43E00000u) {              // 448.0f
+        code = 0x7Eu;
+    } else if (a >= 0x3C800000u) {              // 2^-6
+        uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
+        code = r - (120u << 3);
+    } else {
+        code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+    }
+    return sign | code;
+}
+
+// Lanes [0, lane) of the wavefront.
+__device__ __forceinline__ uint64_t lanemask_lt(int lane)
+{
+    return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Max over aligned groups of 8 lanes, with DPP moves: swap neighbours (quad_perm 1,0,3,2),
+// swap pairs (quad_perm 2,3,0,1), then mirror within each half-row of 8 lanes.
+__device__ __forceinline__ float group8_max(float v)
+{
+    int x = __float_as_int(v);
+    x = max(x, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));
+    x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));
+    x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false));
+    return __int_as_float(x);   // inputs are non-negative floats: integer order = value order
+}
+
+}  // namespace ep

@@ -1,0 +1,243 @@
+// Dispatch on gfx950: scatter each token row to the receive slot of every expert it selected,
+// as bf16, or cast once per token to OCP E4M3 with one fp32 scale per 128 channels.
+//
+// The receiving side of expert-parallel dispatch expands tokens into the per-expert layout
+// (afdEP-comm validation record, kernel_timelines: dispatch_copy_epilogue). Here the tokens
+// are local, so dispatch reads each row of x ONCE and stores it K times: HBM traffic is
+// 2*H per token read plus 2*H (bf16) or H + 4*H/128 (FP8) per kept pair written.
+//
+// Work split. A workgroup of 4 wavefronts owns `tpb` consecutive tokens. It first stages the
+// receive-row numbers (e*C + slot, or -1 for a pair that is not kept) of its tpb*K pairs in
+// LDS with one coalesced pass, so no wavefront waits on a global load before its row copy.
+// A wavefront item is one token and one segment of the row; each lane moves 16-byte chunks
+// (8 bf16), lane-contiguous so every load and store instruction covers 1 KiB of one row.
+// Row stores are non-temporal: the receive buffer is not read again by this step.
+//
+// FP8: a lane owns 16 consecutive channels (two 16-byte loads, one 16-byte store of codes),
+// so a 128-channel block is 8 lanes; the block amax is a DPP max over those 8 lanes. The scale
+// and the codes use IEEE fp32 divisions (HIP's default, correctly rounded) exactly as the
+// definition states: scale = amax / 448, q = e4m3(x / scale).
+#include "ep_device.h"
+#include "ep_internal.h"
+
+#ifndef EP_DISPATCH_U
+#define EP_DISPATCH_U 0     // 16-byte chunks per lane per item (0 = choose from the shape)
+#endif
+#ifndef EP_DISPATCH_TPB
+#define EP_DISPATCH_TPB 0   // tokens per workgroup (0 = choose from the shape)
+#endif
+
+namespace ep {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kStage = 256;        // staged pairs per workgroup (tpb * K <= kStage)
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Row number of pair (e, s) in the [E][C] receive buffer, or -1 if it is not kept.
+__device__ __forceinline__ int recv_row(int e, int s, int E, int C)
+{
+    return ((unsigned)e < (unsigned)E && (unsigned)s < (unsigned)C) ? e * C + s : -1;
+}
+
+// The receive rows of up to KG pairs of token tl, read from LDS together (uniform values).
+template <int KG>
+__device__ __forceinline__ void token_rows(const int32_t *rows, int tl, int j0, int K, int (&r)[KG])
+{
+#pragma unroll
+    for (int g = 0; g < KG; ++g) {
+        const int j = j0 + g;
+        const int v = uniform(rows[tl * K + (j < K ? j : K - 1)]);
+        r[g] = j < K ? v : -1;
+    }
+}
+
+// KG: pairs per group (K <= KG unless MULTI); U: 16-byte chunks per lane per item.
+template <int KG, int U, bool MULTI>
+__global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
+    const u32x4 *__restrict__ x, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ slot, u32x4 *__restrict__ recv, int T, int H8, int E, int C,
+    int K, int tpb, int nseg)
+{
+    __shared__ int32_t rows[kStage];
+    const int tid = threadIdx.x;
+    const int t0 = blockIdx.x * tpb;
+    const int nt = min(tpb, T - t0);
+    for (int k = tid; k < nt * K; k += kThreads) {
+        const size_t i = (size_t)t0 * K + k;
+        rows[k] = recv_row(idx[i], slot[i], E, C);
+    }
+    __syncthreads();
+
+    const int wave = uniform(tid / kWave);
+    const int lane = tid & (kWave - 1);
+    for (int item = wave; item < nt * nseg; item += kWaves) {
+        const int tl = item / nseg;
+        const int seg = item - tl * nseg;
+        const u32x4 *src = x + (size_t)(t0 + tl) * H8;
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = (seg * U + u) * kWave + lane;
+            v[u] = load16_stream(src + (c < H8 ? c : H8 - 1));
+        }
+        const int ngroups = MULTI ? (K + KG - 1) / KG : 1;
+        for (int grp = 0; grp < ngroups; ++grp) {
+            int r[KG];
+            token_rows<KG>(rows, tl, grp * KG, K, r);
+#pragma unroll
+            for (int g = 0; g < KG; ++g) {
+                if (r[g] < 0) continue;
+                u32x4 *dst = recv + (size_t)r[g] * H8;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = (seg * U + u) * kWave + lane;
+                    if (c < H8) store16_stream(dst + c, v[u]);
+                }
+            }
+        }
+    }
+}
+
+template <int KG, bool MULTI>
+__global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
+    const u32x4 *__restrict__ x, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ slot, u32x4 *__restrict__ recv_q, float *__restrict__ recv_scale,
+    int T, int H, int E, int C, int K, int tpb, int nseg)
+{
+    __shared__ int32_t rows[kStage];
+    const int tid = threadIdx.x;
+    const int t0 = blockIdx.x * tpb;
+    const int nt = min(tpb, T - t0);
+    for (int k = tid; k < nt * K; k += kThreads) {
+        const size_t i = (size_t)t0 * K + k;
+        rows[k] = recv_row(idx[i], slot[i], E, C);
+    }
+    __syncthreads();
+
+    const int H8 = H / 8, H16 = H / 16, NB = H / 128;
+    const int wave = uniform(tid / kWave);
+    const int lane = tid & (kWave - 1);
+    for (int item = wave; item < nt * nseg; item += kWaves) {
+        const int tl = item / nseg;
+        const int seg = item - tl * nseg;
+        const int h0 = seg * (16 * kWave) + lane * 16;     // first channel of this lane
+        const bool act = h0 < H;                           // whole 8-lane groups (H % 128 == 0)
+        u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+        if (act) {
+            const u32x4 *src = x + (size_t)(t0 + tl) * H8 + h0 / 8;
+            a = load16_stream(src);
+            b = load16_stream(src + 1);
+        }
+        uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        float f[16];
+        uint32_t m = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            f[2 * k] = bf16_lo(w[k]);
+            f[2 * k + 1] = bf16_hi(w[k]);
+            m = max(m, (w[k] << 16) & 0x7FFFFFFFu);
+            m = max(m, w[k] & 0x7FFF0000u);
+        }
+        const float amax = group8_max(__uint_as_float(m));   // |x| bits: integer order
+        const float scale = amax / 448.0f;
+        uint32_t q[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const uint32_t code = (amax == 0.0f) ? ((__float_as_uint(f[k]) >> 24) & 0x80u)
+                                                 : e4m3_rne_sat(f[k] / scale);
+            q[k / 4] |= code << (8 * (k % 4));
+        }
+        const u32x4 qv = {q[0], q[1], q[2], q[3]};
+        const int ngroups = MULTI ? (K + KG - 1) / KG : 1;
+        for (int grp = 0; grp < ngroups; ++grp) {
+            int r[KG];
+            token_rows<KG>(rows, tl, grp * KG, K, r);
+#pragma unroll
+            for (int g = 0; g < KG; ++g) {
+                if (r[g] < 0 || !act) continue;
+                store16_stream(recv_q + (size_t)r[g] * H16 + h0 / 16, qv);
+                if ((lane & 7) == 0) recv_scale[(size_t)r[g] * NB + h0 / 128] = scale;
+            }
+        }
+    }
+}
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Chunks per lane: the widest item that still leaves at least 8192 wavefront items.
+int pick_u(int T, int H8)
+{
+    if (EP_DISPATCH_U) return EP_DISPATCH_U;
+    for (int u : {4, 2})
+        if ((long)T * ceil_div(H8, u * kWave) >= 8192) return u;
+    return 1;
+}
+
+int pick_tpb(int T, int K, int nseg)
+{
+    int tpb = EP_DISPATCH_TPB ? EP_DISPATCH_TPB : (T >= 2048 ? 2 : 1) * (nseg == 1 ? 2 : 1);
+    while (tpb > 1 && tpb * K > kStage) --tpb;
+    return tpb;
+}
+
+#define EP_BY_K(K, LAUNCH)                                                                  \
+    do {                                                                                    \
+        if ((K) > 8) LAUNCH(8, true);                                                       \
+        if ((K) > 4) LAUNCH(8, false);                                                      \
+        if ((K) > 2) LAUNCH(4, false);                                                      \
+        if ((K) > 1) LAUNCH(2, false);                                                      \
+        LAUNCH(1, false);                                                                   \
+    } while (0)
+
+template <int U>
+hipError_t launch_bf16_u(const ep_shape_t &s, const u32x4 *x, const int32_t *idx,
+                         const int32_t *slot, u32x4 *recv, int H8, int tpb, int nseg,
+                         hipStream_t stream)
+{
+    const dim3 grid(ceil_div(s.T, tpb)), block(kThreads);
+#define EP_LAUNCH_BF16(KG, MULTI)                                                            \
+    return launch(dispatch_bf16_kernel<KG, U, MULTI>, grid, block, 0, stream, x, idx, slot,  \
+                  recv, s.T, H8, s.E, s.C, s.K, tpb, nseg)
+    EP_BY_K(s.K, EP_LAUNCH_BF16);
+#undef EP_LAUNCH_BF16
+}
+
+}  // namespace
+
+hipError_t launch_dispatch_bf16(const ep_shape_t &s, const uint16_t *x, const int32_t *idx,
+                                const int32_t *slot, uint16_t *recv, hipStream_t stream)
+{
+    if (s.T == 0) return hipSuccess;
+    const int H8 = s.H / 8;
+    const int U = pick_u(s.T, H8);
+    const int nseg = ceil_div(H8, U * kWave);
+    const int tpb = pick_tpb(s.T, s.K, nseg);
+    const u32x4 *xv = reinterpret_cast<const u32x4 *>(x);
+    u32x4 *rv = reinterpret_cast<u32x4 *>(recv);
+    if (U >= 4) return launch_bf16_u<4>(s, xv, idx, slot, rv, H8, tpb, nseg, stream);
+    if (U == 2) return launch_bf16_u<2>(s, xv, idx, slot, rv, H8, tpb, nseg, stream);
+    return launch_bf16_u<1>(s, xv, idx, slot, rv, H8, tpb, nseg, stream);
+}
+
+hipError_t launch_dispatch_fp8(const ep_shape_t &s, const uint16_t *x, const int32_t *idx,
+                               const int32_t *slot, uint8_t *recv_q, float *recv_scale,
+                               hipStream_t stream)
+{
+    if (s.T == 0) return hipSuccess;
+    const int nseg = ceil_div(s.H, 16 * kWave);
+    const int tpb = pick_tpb(s.T, s.K, nseg);
+    const dim3 grid(ceil_div(s.T, tpb)), block(kThreads);
+    const u32x4 *xv = reinterpret_cast<const u32x4 *>(x);
+    u32x4 *qv = reinterpret_cast<u32x4 *>(recv_q);
+#define EP_LAUNCH_FP8(KG, MULTI)                                                             \
+    return launch(dispatch_fp8_kernel<KG, MULTI>, grid, block, 0, stream, xv, idx, slot, qv, \
+                  recv_scale, s.T, s.H, s.E, s.C, s.K, tpb, nseg)
+    EP_BY_K(s.K, EP_LAUNCH_FP8);
+#undef EP_LAUNCH_FP8
+}
+
+}  // namespace ep

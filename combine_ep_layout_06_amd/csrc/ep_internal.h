@@ -1,0 +1,50 @@
+// Host-side declarations shared by the kernel launchers and the C ABI (internal header).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <tuple>
+#include <utility>
+
+#include "ep.h"
+
+namespace ep {
+
+// Launch `kernel` with hipLaunchKernel, which returns the launch status itself (so an error
+// left behind by an unrelated earlier call is neither reported nor cleared). Arguments are
+// converted to the kernel's parameter types first.
+template <typename... KArgs, size_t... I>
+inline void fill_argv(void **argv, std::tuple<KArgs...> &t, std::index_sequence<I...>)
+{
+    ((argv[I] = static_cast<void *>(&std::get<I>(t))), ...);
+}
+
+template <typename... KArgs, typename... Args>
+inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
+                         hipStream_t stream, Args... args)
+{
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+    std::tuple<KArgs...> typed(static_cast<KArgs>(args)...);
+    void *argv[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
+    fill_argv(argv, typed, std::index_sequence_for<KArgs...>{});
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, shmem,
+                           stream);
+}
+
+hipError_t launch_layout(const ep_shape_t &s, const int32_t *idx, int32_t *slot, int32_t *count,
+                         int32_t *offset, int32_t *rank_count, int32_t *rank_offset,
+                         int32_t *stats, hipStream_t stream);
+
+hipError_t launch_dispatch_bf16(const ep_shape_t &s, const uint16_t *x, const int32_t *idx,
+                                const int32_t *slot, uint16_t *recv, hipStream_t stream);
+
+hipError_t launch_dispatch_fp8(const ep_shape_t &s, const uint16_t *x, const int32_t *idx,
+                               const int32_t *slot, uint8_t *recv_q, float *recv_scale,
+                               hipStream_t stream);
+
+hipError_t launch_combine(const ep_shape_t &s, const uint16_t *y, const int32_t *idx,
+                          const int32_t *slot, const float *w, uint16_t *out,
+                          hipStream_t stream);
+
+}  // namespace ep

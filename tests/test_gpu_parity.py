@@ -1,0 +1,217 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle on the same
+seeded inputs.
+
+Bars: layout, dispatch and the FP8 cast bit-exact; combine within 1 bf16 ulp per element (and,
+by construction, expected bit-exact: both sides fold fmaf in ascending j from +0).
+
+Full-size workloads run in the launch configuration the benchmark uses (the library picks it
+from the shape). Their receive buffers are 1-2 GiB, so dispatch is checked row by row on every
+kept pair plus a sentinel check of all other rows; combine is compared on every output element.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_ep_layout_06_amd import binding as B
+from combine_ep_layout_06_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+import gpu_cases as G  # noqa: E402  (tests/ is on sys.path under pytest)
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.load_library()
+
+
+FULL_CONFIGS = ["decode_bf16", "decode_fp8", "skew_zipf", "skew_zipf_c1024", "skew_zipf_c256",
+                "prefill_bf16", "prefill_fp8", "balanced_stride"]
+
+
+@pytest.mark.parametrize("name", FULL_CONFIGS)
+def test_config_full_path(name):
+    cfg = W.get_config(name)
+    print(f"[parity] {name} T={cfg.T} H={cfg.H} E={cfg.E} K={cfg.K} C={cfg.C} R={cfg.R}",
+          flush=True)
+    case = G.Case.from_config(cfg)
+    if cfg.fp8:
+        case.check_dispatch_fp8(full=False)
+    else:
+        case.check_dispatch_bf16(full=False)
+    got, want = case.check_combine()
+    assert np.array_equal(got, want), "combine not bit-exact"
+    if name.startswith("skew_zipf_c"):
+        assert case.lay["stats"]["dropped"] > 0
+
+
+@pytest.mark.parametrize("name", ["decode_bf16", "prefill_fp8"])
+def test_config_other_dispatch_dtype(name):
+    """The dispatch dtype a workload does not use in the benchmark, for coverage."""
+    cfg = W.get_config(name)
+    case = G.Case.from_config(cfg)
+    if cfg.fp8:
+        case.check_dispatch_bf16(full=False)
+    else:
+        case.check_dispatch_fp8(full=False)
+
+
+# small shapes that span several tiles and ragged tails, compared on whole buffers
+SMALL = [
+    # T, H, E, K, C, R
+    (1, 8, 1, 1, 1, 1),
+    (3, 24, 4, 2, 2, 2),
+    (37, 256, 6, 3, 5, 3),
+    (100, 520, 16, 4, 9, 4),          # H/8 = 65 chunks: one lane past a full wavefront
+    (257, 1024, 32, 8, 40, 8),
+    (1500, 128, 64, 6, 100, 4),       # T*K = 9000: nine layout tiles, a ragged last tile
+    (300, 384, 128, 16, 24, 16),      # K = 16: two groups of 8 pairs
+    (2049, 256, 8, 1, 300, 2),        # K = 1
+]
+
+
+@pytest.mark.parametrize("T,H,E,K,C,R", SMALL)
+def test_small_random_routes(T, H, E, K, C, R):
+    """Random ids in [-2, E]: duplicates, unrouted (-1), invalid (-2 and E), and drops."""
+    print(f"[parity] small T={T} H={H} E={E} K={K} C={C} R={R}", flush=True)
+    case = G.Case.random(T, H, E, K, C, R, seed=T + H)
+    case.check_dispatch_bf16(full=True)
+    if H % 128 == 0:
+        case.check_dispatch_fp8(full=True)
+    got, want = case.check_combine()
+    assert np.array_equal(got, want)
+
+
+def test_empty_tokens():
+    idx = torch.zeros((0, 8), dtype=torch.int32, device="cuda")
+    g = B.ep_layout(idx, 16, 4, 4)
+    torch.cuda.synchronize()
+    assert G.to_np(g["expert_count"]).tolist() == [0] * 16
+    assert G.to_np(g["expert_offset"]).tolist() == [0] * 16
+    assert G.to_np(g["stats"]).tolist() == [0, 0, 0, 0]
+    x = torch.zeros((0, 256), dtype=torch.int16, device="cuda")
+    recv = torch.full((16, 4, 256), G.SENTINEL16, dtype=torch.int16, device="cuda")
+    B.ep_dispatch(x, idx, g["slot"], recv, 4)
+    out = B.ep_combine(recv, idx, g["slot"], torch.zeros((0, 8), device="cuda"), 4)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 256) and int((recv != G.SENTINEL16).sum()) == 0
+
+
+def test_all_unrouted_and_all_to_one_expert():
+    T, H, E, K, C, R = 64, 128, 8, 4, 3, 2
+    rng = np.random.default_rng(1)
+    x = W.f32_to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    w = rng.random((T, K)).astype(np.float32)
+    case = G.Case(T, H, E, K, C, R, x, np.full((T, K), -1, np.int32), w)
+    assert case.lay["stats"]["unrouted"] == T * K
+    case.check_dispatch_bf16(full=True)
+    got, _ = case.check_combine()
+    assert (got == 0).all()
+    case = G.Case(T, H, E, K, C, R, x, np.full((T, K), 5, np.int32), w)
+    assert case.lay["stats"]["dropped"] == T * K - C
+    case.check_dispatch_bf16(full=True)
+    case.check_dispatch_fp8(full=True)
+    case.check_combine()
+
+
+def test_max_experts_and_many_pairs():
+    """E at its maximum (EP_MAX_EXPERTS) and 2^17 pairs (128 layout tiles), with drops."""
+    cfg = W.EpConfig("max_e", T=16384, H=128, E=B.EP_MAX_EXPERTS, K=8, C=100, R=8)
+    inp = W.make_inputs(cfg)
+    case = G.Case(cfg.T, cfg.H, cfg.E, cfg.K, cfg.C, cfg.R, inp["x"], inp["topk_idx"],
+                  inp["topk_w"])
+    assert case.lay["stats"]["dropped"] > 0
+    case.check_dispatch_bf16(full=False)
+    case.check_combine()
+
+
+def test_balanced_route_counts_closed_form():
+    cfg = W.get_config("balanced_stride")
+    case = G.Case.from_config(cfg)
+    per = cfg.T * cfg.K // cfg.E
+    assert G.to_np(case.g["expert_count"]).tolist() == [per] * cfg.E
+
+
+def test_fp8_every_bf16_value_through_the_quantiser():
+    """Blocks whose amax is 448 have scale exactly 1, so the kernel's codes are e4m3(x) for
+    every finite bf16 x with |x| <= 448 (both signs); a second pass with amax 3 exercises the
+    division on the same values scaled into range."""
+    vals = np.arange(0, 0x43E1, dtype=np.uint32)                     # +0 .. 448 as bf16 bits
+    vals = np.concatenate([vals, vals | 0x8000]).astype(np.uint16)
+    for amax_bits in (0x43E0, 0x4040):                                # 448.0, 3.0
+        amax = W.bf16_bits_to_f32(np.array([amax_bits], np.uint16))[0]
+        keep = W.bf16_bits_to_f32(vals)
+        v = vals[np.abs(keep) <= amax]
+        per_block = 127
+        nblk = -(-v.size // per_block)
+        blocks = np.zeros((nblk, 128), dtype=np.uint16)
+        flat = np.zeros(nblk * per_block, dtype=np.uint16)
+        flat[:v.size] = v
+        blocks[:, 1:] = flat.reshape(nblk, per_block)
+        blocks[:, 0] = amax_bits
+        H = 2048
+        T = -(-nblk // (H // 128))
+        x = np.zeros((T * (H // 128), 128), dtype=np.uint16)
+        x[:nblk] = blocks
+        x[nblk:, 0] = amax_bits
+        x = x.reshape(T, H)
+        idx = (np.arange(T, dtype=np.int32) % 4)[:, None]
+        case = G.Case(T, H, 4, 1, T, 1, x, idx, np.ones((T, 1), np.float32))
+        case.check_dispatch_fp8(full=True)
+
+
+def test_fp8_degenerate_blocks():
+    """All-zero blocks (scale 0, signed-zero codes), bf16 subnormals, a tiny amax."""
+    H = 512
+    x = np.zeros((3, H), dtype=np.uint16)
+    x[0, :128] = 0x8000                                   # -0 block
+    x[0, 128:256] = 0x0001                                # smallest bf16 subnormal
+    x[0, 256] = 0x0080                                    # smallest bf16 normal, rest zero
+    x[0, 257] = 0x8001
+    x[1] = W.f32_to_bf16_bits(np.linspace(-1e-38, 1e-38, H).astype(np.float32))
+    x[2] = W.f32_to_bf16_bits(np.linspace(-3e4, 3e4, H).astype(np.float32))
+    idx = np.array([[0, 1], [1, 0], [0, 1]], dtype=np.int32)
+    case = G.Case(3, H, 2, 2, 4, 1, x, idx, np.ones((3, 2), np.float32))
+    case.check_dispatch_fp8(full=True)
+
+
+def test_combine_identity_law_on_gpu():
+    """y := the GPU's own bf16 dispatch output, unit weights: out = bf16(n_kept * x), checked
+    against the oracle (bit-exact) and, for tokens with all K pairs kept, against 8x."""
+    cfg = W.get_config("decode_bf16")
+    case = G.Case.from_config(cfg)
+    recv = torch.full((cfg.E, cfg.C, cfg.H), G.BF16_NAN, dtype=torch.int16, device="cuda")
+    B.ep_dispatch(case.x_d, case.idx_d, case.g["slot"], recv, cfg.C)
+    ones = torch.ones((cfg.T, cfg.K), dtype=torch.float32, device="cuda")
+    out = B.ep_combine(recv, case.idx_d, case.g["slot"], ones, cfg.C)
+    torch.cuda.synchronize()
+    want = W.f32_to_bf16_bits(8.0 * W.bf16_bits_to_f32(case.x))
+    assert np.array_equal(G.to_np(out).view(np.uint16), want)
+
+
+def test_deterministic_repeat():
+    cfg = W.get_config("skew_zipf_c256")
+    case = G.Case.from_config(cfg)
+    y_host, y = case.make_y()
+    outs = []
+    for _ in range(3):
+        g = B.ep_layout(case.idx_d, cfg.E, cfg.C, cfg.R)
+        outs.append(G.to_np(B.ep_combine(y, case.idx_d, g["slot"], case.w_d, cfg.C)).copy())
+        assert np.array_equal(G.to_np(g["slot"]), case.lay["slot"])
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+def test_non_default_stream():
+    cfg = W.get_config("decode_bf16")
+    case = G.Case.from_config(cfg)
+    y_host, y = case.make_y()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        g = B.ep_layout(case.idx_d, cfg.E, cfg.C, cfg.R)
+        out = B.ep_combine(y, case.idx_d, g["slot"], case.w_d, cfg.C)
+    s.synchronize()
+    want = oracle.combine(y_host, case.idx, case.lay["slot"], case.w)
+    assert np.array_equal(G.to_np(out).view(np.uint16), want)
