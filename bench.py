@@ -15,10 +15,12 @@ the HBM roofline (algorithmic bytes / time / 8 TB/s). The same line carries the 
 and the CPU oracle's time on the host.
 
 Timing: W untimed warm-up steps, then exactly K steps back to back between two
-synchronisations. Every step uses the next of NSETS independent buffer sets (inputs, receive
-buffer, outputs), so consecutive steps never reuse a byte and each step's ~300 MB must come from
-HBM rather than the 256 MB last-level cache. Decode-like latency is single-shot: each step is
-synchronised on its own and timed with an event pair (median of the samples).
+synchronisations. Every step takes the next of NSETS input batches (x, route, weights) and
+writes the layer's persistent buffers (receive buffer, output), reading its persistent expert
+outputs, as an MoE layer does. A variant where every batch also has its own buffers
+("rotating_all_buffers": ~16 GiB touched in turn, so page translations are cold each step) is
+reported beside it. Decode-like latency is single-shot: each sample first overwrites 1 GiB
+(beyond every cache) outside the event pair, then times one step (median of the samples).
 
 ``--gpus N`` with N > 1 is refused: this build measures one GPU; inter-GPU transport is not
 part of it.
@@ -50,7 +52,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget for the oracle's CPU baseline")
     ap.add_argument("--only", default=None,
-                    help="run only this workload's timed loop (for profiling)")
+                    help="run only this workload's timed loop (for profiling); 'copy_probe' "
+                         "runs a plain 256 MiB device copy instead, the reference kernel for "
+                         "scaling HBM byte counters")
     return ap.parse_args()
 
 
@@ -59,38 +63,51 @@ def log(msg):
 
 
 class Workload:
-    """NSETS independent buffer sets for one config, all resident on the GPU."""
+    """One config on the GPU: NSETS input sets (x, topk_idx, topk_w: a new batch of tokens per
+    step) and the layer's persistent buffers (expert outputs y, receive buffer, output, layout
+    outputs), allocated once and reused by every step as an MoE layer reuses its workspace.
+    With ``rotate_all`` every set also gets its own persistent buffers, so consecutive steps
+    touch disjoint memory (and disjoint page translations) throughout."""
 
-    def __init__(self, cfg, nsets, torch, B, W):
+    def __init__(self, cfg, nsets, torch, B, W, rotate_all=False):
         self.cfg, self.torch, self.B = cfg, torch, B
         dev = torch.device("cuda", 0)
         self.sets = []
+        bufs = None
         for k in range(nsets):
             inp = W.make_inputs(cfg, seed=cfg.seed + k)
             s = {}
             s["x"] = torch.from_numpy(inp["x"].view(np.int16)).to(dev)
             s["idx"] = torch.from_numpy(inp["topk_idx"]).to(dev)
             s["w"] = torch.from_numpy(inp["topk_w"]).to(dev)
-            g = torch.Generator(device=dev)
-            g.manual_seed(1000 + cfg.seed + k)
-            y = torch.empty((cfg.E, cfg.C, cfg.H), dtype=torch.bfloat16, device=dev)
-            for e in range(cfg.E):        # expert outputs ~ N(0, 1), one expert at a time
-                y[e].copy_(torch.randn((cfg.C, cfg.H), generator=g, device=dev))
-            s["y"] = y.view(torch.int16)
-            if cfg.fp8:
-                s["recv_q"] = torch.empty((cfg.E, cfg.C, cfg.H), dtype=torch.uint8, device=dev)
-                s["recv_s"] = torch.empty((cfg.E, cfg.C, cfg.H // 128), dtype=torch.float32,
-                                          device=dev)
-            else:
-                s["recv"] = torch.empty((cfg.E, cfg.C, cfg.H), dtype=torch.int16, device=dev)
-            s["out"] = torch.empty((cfg.T, cfg.H), dtype=torch.int16, device=dev)
+            if bufs is None or rotate_all:
+                bufs = self._buffers(cfg, dev, seed=1000 + cfg.seed + k)
+            s.update(bufs)
+            # the layout's outputs are per batch (the handle dispatch and combine reuse)
             T, K, E, R = cfg.T, cfg.K, cfg.E, cfg.R
             mk = lambda n: torch.empty(n, dtype=torch.int32, device=dev)
             s["lay"] = dict(slot=mk((T, K)), expert_count=mk(E), expert_offset=mk(E),
                             rank_count=mk(R), rank_offset=mk(R), stats=mk(4))
             self.sets.append(s)
         torch.cuda.synchronize()
-        self.n_kept = None
+
+    def _buffers(self, cfg, dev, seed):
+        torch = self.torch
+        b = {}
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        y = torch.empty((cfg.E, cfg.C, cfg.H), dtype=torch.bfloat16, device=dev)
+        for e in range(cfg.E):            # expert outputs ~ N(0, 1), one expert at a time
+            y[e].copy_(torch.randn((cfg.C, cfg.H), generator=g, device=dev))
+        b["y"] = y.view(torch.int16)
+        if cfg.fp8:
+            b["recv_q"] = torch.empty((cfg.E, cfg.C, cfg.H), dtype=torch.uint8, device=dev)
+            b["recv_s"] = torch.empty((cfg.E, cfg.C, cfg.H // 128), dtype=torch.float32,
+                                      device=dev)
+        else:
+            b["recv"] = torch.empty((cfg.E, cfg.C, cfg.H), dtype=torch.int16, device=dev)
+        b["out"] = torch.empty((cfg.T, cfg.H), dtype=torch.int16, device=dev)
+        return b
 
     # the three calls of one step
     def layout(self, s):
@@ -115,9 +132,13 @@ class Workload:
         self.combine(s)
 
     def kept(self):
-        """Kept pairs per set, read from the GPU layout's stats (after a step ran)."""
-        self.torch.cuda.synchronize()
-        return [int(s["lay"]["stats"][0]) for s in self.sets]
+        """Kept pairs per input set: run each set's layout and read its stats."""
+        out = []
+        for s in self.sets:
+            self.layout(s)
+            self.torch.cuda.synchronize()
+            out.append(int(s["lay"]["stats"][0]))
+        return out
 
     def timed_loop(self, steps, warmup):
         torch = self.torch
@@ -153,22 +174,55 @@ class Workload:
             ts.append(ev0.elapsed_time(ev1) * 1e3)
         return ts
 
-    def kernel_avg_us(self, which, reps):
-        """Average duration of one kernel, launched `reps` times back to back over the buffer
-        sets (the other two steps ran before, so its inputs are valid), with events on the
-        stream it runs on."""
+    def kernel_avg_us(self, reps):
+        """Average duration of each kernel inside whole steps: an event is recorded on the
+        stream the kernels run on before the layout, between the calls and after the combine,
+        for `reps` steps; each kernel's time is the mean gap between its two events."""
         torch = self.torch
-        fn = {"layout": self.layout, "dispatch": self.dispatch, "combine": self.combine}[which]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
         for k in range(len(self.sets)):
             self.step(k)
         torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record()
         for k in range(reps):
-            fn(self.sets[k % len(self.sets)])
-        ev1.record()
+            s = self.sets[k % len(self.sets)]
+            e = evs[k]
+            e[0].record()
+            self.layout(s)
+            e[1].record()
+            self.dispatch(s)
+            e[2].record()
+            self.combine(s)
+            e[3].record()
         torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1) * 1e3 / reps
+        names = ("layout", "dispatch", "combine")
+        return {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) * 1e3 / reps
+                for i, n in enumerate(names)}
+
+
+def counter_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter record
+    (profiles/hbm_traffic.json: rocprofv3 FETCH_SIZE and WRITE_SIZE passes, each scaled by what
+    the same counter reads for a plain device copy of known size). None if there is no record
+    or the kernel's sources changed since the counters were taken."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    for r in rec.get("records", []):
+        if r.get("kernel") != kernel or r.get("workload") != workload:
+            continue
+        h = hashlib.sha256()
+        for src in r["sources"]:
+            with open(os.path.join(root, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != r["sources_sha256"]:
+            return None
+        return r["traffic_bytes"]
+    return None
 
 
 def cpu_baseline(cfg, budget_s, W, A):
@@ -228,6 +282,15 @@ def main():
     B.load_library()
     log(f"library: {B.ep_version()}  device: {torch.cuda.get_device_name(0)}")
 
+    if args.only == "copy_probe":
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy_probe: {args.warmup + args.steps} copies of {n} bytes")
+        return
     if args.only:
         cfg = W.get_config(args.only)
         wl = Workload(cfg, NSETS, torch, B, W)
@@ -255,16 +318,25 @@ def main():
             r["us_single_shot_median"] = round(statistics.median(ss), 3)
             r["us_single_shot_min"] = round(min(ss), 3)
             r["us_single_shot_max"] = round(max(ss), 3)
-        kus = {k: wl.kernel_avg_us(k, args.steps) for k in ("layout", "dispatch", "combine")}
+        kus = wl.kernel_avg_us(args.steps)
         r["kernel_avg_us"] = {k: round(v, 3) for k, v in kus.items()}
         kb = {"layout": A.layout_bytes(cfg.T, cfg.K),
               "dispatch": A.dispatch_bytes(cfg.T, cfg.K, cfg.H, n_kept, cfg.fp8),
               "combine": A.combine_bytes(cfg.T, cfg.K, cfg.H, n_kept)}
         r["kernel_GBps"] = {k: round(kb[k] / (kus[k] * 1e-6) / 1e9, 1) for k in kus}
-        results[name] = (cfg, None, r, kus, kb)
-        log(f"{name}: {json.dumps(r)}")
         del wl
         torch.cuda.empty_cache()
+        if name == args.workload:
+            wl = Workload(cfg, NSETS, torch, B, W, rotate_all=True)
+            ms_all, _ = wl.timed_loop(args.steps, args.warmup)
+            r["rotating_all_buffers"] = {
+                "us_per_step": round(ms_all * 1e3, 3),
+                "logical_GBps": round(pay / (ms_all * 1e-3) / 1e9, 2),
+                "hbm_frac": round(alg / (ms_all * 1e-3) / A.HBM_PEAK_BYTES_PER_S, 4)}
+            del wl
+            torch.cuda.empty_cache()
+        results[name] = (cfg, None, r, kus, kb)
+        log(f"{name}: {json.dumps(r)}")
 
     cfg, _, r, kus, kb = results[args.workload]
     dom = max(("dispatch", "combine"), key=lambda k: kus[k])
@@ -272,7 +344,7 @@ def main():
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": A.HBM_PEAK_BYTES_PER_S / 1e9, "unit": "GB/s",
                 "frac": round(achieved / (A.HBM_PEAK_BYTES_PER_S / 1e9), 4),
-                "traffic": None, "avg_launch_us": round(kus[dom], 3),
+                "traffic": counter_traffic(dom, cfg.name), "avg_launch_us": round(kus[dom], 3),
                 "bytes_per_launch": kb[dom]}
 
     cpu = None
@@ -290,13 +362,15 @@ def main():
         "metric": METRIC, "value": r["logical_GBps"], "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["us_per_step"] / 1e3, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded; inputs resident in HBM; 4 rotating buffer sets)",
+        "data": "synthetic (seeded; resident in HBM; 4 rotating input batches, persistent "
+                "layer buffers)",
         "config": {"workload": f"{cfg.name}: T={cfg.T} H={cfg.H} E={cfg.E} K={cfg.K} "
                                f"C={cfg.C} R={cfg.R} ({cfg.route} distinct top-{cfg.K})",
                    "T": cfg.T, "H": cfg.H, "E": cfg.E, "K": cfg.K, "C": cfg.C, "R": cfg.R,
                    "parallelism": "single GPU"},
         "hbm_roofline_frac": r["hbm_frac"],
         "us_per_step": r["us_per_step"],
+        "rotating_all_buffers": r.get("rotating_all_buffers"),
         "t128_us": {n: brief(n) for n in ("decode_bf16", "decode_fp8") if n in results},
         "prefill_fp8": brief("prefill_fp8") if "prefill_fp8" in results else None,
         "roofline": roofline,

@@ -72,6 +72,8 @@ int ep_layout(const ep_shape_t *shape, const int32_t *topk_idx, int32_t *slot,
     const bool empty = (int64_t)shape->T * shape->K == 0;
     if ((!empty && (!topk_idx || !slot)) || !expert_count || !expert_offset || !stats)
         return fail(EP_ERR_INVALID, "ep_layout: NULL required pointer");
+    if (!aligned(topk_idx, 16))
+        return fail(EP_ERR_ALIGN, "ep_layout: topk_idx must be 16-byte aligned");
     return hip_status(ep::launch_layout(*shape, topk_idx, slot, expert_count, expert_offset,
                                         rank_count, rank_offset, stats, stream),
                       "ep_layout");

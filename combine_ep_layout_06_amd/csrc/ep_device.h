@@ -10,17 +10,20 @@ constexpr int kWave = 64;   // CDNA wavefront width
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// A 16-byte chunk: 8 bf16 channels, or 16 FP8 codes.
-__device__ __forceinline__ u32x4 load16(const u32x4 *p) { return *p; }
-
-__device__ __forceinline__ u32x4 load16_stream(const u32x4 *p)
+// A 16-byte chunk: 8 bf16 channels, or 16 FP8 codes. NT selects the non-temporal form, which
+// streams past the caches; whether it pays depends on the access pattern (measured per kernel).
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const u32x4 *p)
 {
-    return __builtin_nontemporal_load(p);
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
 }
 
-__device__ __forceinline__ void store16_stream(u32x4 *p, u32x4 v)
+template <bool NT>
+__device__ __forceinline__ void store16(u32x4 *p, u32x4 v)
 {
-    __builtin_nontemporal_store(v, p);
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
 }
 
 // bf16 pattern in the low / high half of a 32-bit word -> fp32 (exact).
@@ -64,10 +67,38 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float v)
     return sign | code;
 }
 
-// Lanes [0, lane) of the wavefront.
-__device__ __forceinline__ uint64_t lanemask_lt(int lane)
+// Number of set bits of `mask` in lanes below this one (v_mbcnt).
+__device__ __forceinline__ int count_below(uint64_t mask)
 {
-    return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// DPP move of `v` from the lane n below within the same row of 16 lanes; 0 past the row start.
+template <int N>
+__device__ __forceinline__ int row_shr(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, 0x110 + N, 0xF, 0xF, true);
+}
+
+// Inclusive prefix sum within each row of 16 lanes (4 DPP steps, no LDS).
+__device__ __forceinline__ int row16_inclusive_sum(int v)
+{
+    v += row_shr<1>(v);
+    v += row_shr<2>(v);
+    v += row_shr<4>(v);
+    v += row_shr<8>(v);
+    return v;
+}
+
+// Inclusive prefix sum across the 64 lanes: per-row scans, then the last lane of row 0 (row
+// 2) is broadcast into row 1 (row 3) and the last lane of row 1 into rows 2 and 3.
+__device__ __forceinline__ int wave_inclusive_sum(int v)
+{
+    v = row16_inclusive_sum(v);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31
+    return v;
 }
 
 // Max over aligned groups of 8 lanes, with DPP moves: swap neighbours (quad_perm 1,0,3,2),

@@ -6,12 +6,16 @@
 // are local, so dispatch reads each row of x ONCE and stores it K times: HBM traffic is
 // 2*H per token read plus 2*H (bf16) or H + 4*H/128 (FP8) per kept pair written.
 //
-// Work split. A workgroup of 4 wavefronts owns `tpb` consecutive tokens. It first stages the
-// receive-row numbers (e*C + slot, or -1 for a pair that is not kept) of its tpb*K pairs in
-// LDS with one coalesced pass, so no wavefront waits on a global load before its row copy.
-// A wavefront item is one token and one segment of the row; each lane moves 16-byte chunks
-// (8 bf16), lane-contiguous so every load and store instruction covers 1 KiB of one row.
-// Row stores are non-temporal: the receive buffer is not read again by this step.
+// Work split. Tokens are cut into groups of `tpb`; a workgroup of 4 wavefronts takes groups in
+// a grid-stride loop. For each group it first stages the receive-row numbers (e*C + slot, or
+// -1 for a pair that is not kept) of the group's tpb*K pairs in LDS with one coalesced pass, so
+// no wavefront waits on a dependent global load before its row copy. A wavefront item is one
+// token and one segment of its row; each lane moves 16-byte chunks (8 bf16), lane-contiguous,
+// so every load and store instruction covers 1 KiB of one row. The KG receive rows of a token
+// are read from LDS together, then the row pieces are stored.
+//
+// x loads are non-temporal (read once). Row stores are plain stores: for this one-row-to-K-rows
+// scatter, non-temporal stores measured slower on MI355X.
 //
 // FP8: a lane owns 16 consecutive channels (two 16-byte loads, one 16-byte store of codes),
 // so a 128-channel block is 8 lanes; the block amax is a DPP max over those 8 lanes. The scale
@@ -21,10 +25,19 @@
 #include "ep_internal.h"
 
 #ifndef EP_DISPATCH_U
-#define EP_DISPATCH_U 0     // 16-byte chunks per lane per item (0 = choose from the shape)
+#define EP_DISPATCH_U 0          // 16-byte chunks per lane per item (0 = choose from the shape)
 #endif
 #ifndef EP_DISPATCH_TPB
-#define EP_DISPATCH_TPB 0   // tokens per workgroup (0 = choose from the shape)
+#define EP_DISPATCH_TPB 0        // tokens per group (0 = choose from the shape)
+#endif
+#ifndef EP_DISPATCH_MAX_BLOCKS
+#define EP_DISPATCH_MAX_BLOCKS 0 // grid cap; groups beyond it are taken in a grid-stride loop
+#endif
+#ifndef EP_DISPATCH_NT_LOAD
+#define EP_DISPATCH_NT_LOAD 1
+#endif
+#ifndef EP_DISPATCH_NT_STORE
+#define EP_DISPATCH_NT_STORE 0
 #endif
 
 namespace ep {
@@ -33,7 +46,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kStage = 256;        // staged pairs per workgroup (tpb * K <= kStage)
+constexpr int kStage = 256;        // staged pairs per group (tpb * K <= kStage)
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -43,9 +56,21 @@ __device__ __forceinline__ int recv_row(int e, int s, int E, int C)
     return ((unsigned)e < (unsigned)E && (unsigned)s < (unsigned)C) ? e * C + s : -1;
 }
 
+// Stage the receive rows of tokens [t0, t0 + nt) into rows[] (one coalesced pass).
+__device__ __forceinline__ void stage_rows(int32_t *rows, const int32_t *__restrict__ idx,
+                                           const int32_t *__restrict__ slot, int t0, int nt,
+                                           int K, int E, int C)
+{
+    for (int k = threadIdx.x; k < nt * K; k += kThreads) {
+        const size_t i = (size_t)t0 * K + k;
+        rows[k] = recv_row(idx[i], slot[i], E, C);
+    }
+}
+
 // The receive rows of up to KG pairs of token tl, read from LDS together (uniform values).
 template <int KG>
-__device__ __forceinline__ void token_rows(const int32_t *rows, int tl, int j0, int K, int (&r)[KG])
+__device__ __forceinline__ void token_rows(const int32_t *rows, int tl, int j0, int K,
+                                           int (&r)[KG])
 {
 #pragma unroll
     for (int g = 0; g < KG; ++g) {
@@ -63,39 +88,38 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
     int K, int tpb, int nseg)
 {
     __shared__ int32_t rows[kStage];
-    const int tid = threadIdx.x;
-    const int t0 = blockIdx.x * tpb;
-    const int nt = min(tpb, T - t0);
-    for (int k = tid; k < nt * K; k += kThreads) {
-        const size_t i = (size_t)t0 * K + k;
-        rows[k] = recv_row(idx[i], slot[i], E, C);
-    }
-    __syncthreads();
-
-    const int wave = uniform(tid / kWave);
-    const int lane = tid & (kWave - 1);
-    for (int item = wave; item < nt * nseg; item += kWaves) {
-        const int tl = item / nseg;
-        const int seg = item - tl * nseg;
-        const u32x4 *src = x + (size_t)(t0 + tl) * H8;
-        u32x4 v[U];
+    const int wave = uniform(threadIdx.x / kWave);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int ntg = (T + tpb - 1) / tpb;
+    for (int tg = blockIdx.x; tg < ntg; tg += gridDim.x) {
+        const int t0 = tg * tpb;
+        const int nt = min(tpb, T - t0);
+        __syncthreads();                     // the previous group is done with rows[]
+        stage_rows(rows, idx, slot, t0, nt, K, E, C);
+        __syncthreads();
+        for (int item = wave; item < nt * nseg; item += kWaves) {
+            const int tl = item / nseg;
+            const int seg = item - tl * nseg;
+            const u32x4 *src = x + (size_t)(t0 + tl) * H8;
+            u32x4 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = (seg * U + u) * kWave + lane;
-            v[u] = load16_stream(src + (c < H8 ? c : H8 - 1));
-        }
-        const int ngroups = MULTI ? (K + KG - 1) / KG : 1;
-        for (int grp = 0; grp < ngroups; ++grp) {
-            int r[KG];
-            token_rows<KG>(rows, tl, grp * KG, K, r);
+            for (int u = 0; u < U; ++u) {
+                const int c = (seg * U + u) * kWave + lane;
+                v[u] = load16<EP_DISPATCH_NT_LOAD>(src + (c < H8 ? c : H8 - 1));
+            }
+            const int npg = MULTI ? (K + KG - 1) / KG : 1;
+            for (int pg = 0; pg < npg; ++pg) {
+                int r[KG];
+                token_rows<KG>(rows, tl, pg * KG, K, r);
 #pragma unroll
-            for (int g = 0; g < KG; ++g) {
-                if (r[g] < 0) continue;
-                u32x4 *dst = recv + (size_t)r[g] * H8;
+                for (int g = 0; g < KG; ++g) {
+                    if (r[g] < 0) continue;
+                    u32x4 *dst = recv + (size_t)r[g] * H8;
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int c = (seg * U + u) * kWave + lane;
-                    if (c < H8) store16_stream(dst + c, v[u]);
+                    for (int u = 0; u < U; ++u) {
+                        const int c = (seg * U + u) * kWave + lane;
+                        if (c < H8) store16<EP_DISPATCH_NT_STORE>(dst + c, v[u]);
+                    }
                 }
             }
         }
@@ -105,62 +129,61 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
 template <int KG, bool MULTI>
 __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
     const u32x4 *__restrict__ x, const int32_t *__restrict__ idx,
-    const int32_t *__restrict__ slot, u32x4 *__restrict__ recv_q, float *__restrict__ recv_scale,
-    int T, int H, int E, int C, int K, int tpb, int nseg)
+    const int32_t *__restrict__ slot, u32x4 *__restrict__ recv_q,
+    float *__restrict__ recv_scale, int T, int H, int E, int C, int K, int tpb, int nseg)
 {
     __shared__ int32_t rows[kStage];
-    const int tid = threadIdx.x;
-    const int t0 = blockIdx.x * tpb;
-    const int nt = min(tpb, T - t0);
-    for (int k = tid; k < nt * K; k += kThreads) {
-        const size_t i = (size_t)t0 * K + k;
-        rows[k] = recv_row(idx[i], slot[i], E, C);
-    }
-    __syncthreads();
-
     const int H8 = H / 8, H16 = H / 16, NB = H / 128;
-    const int wave = uniform(tid / kWave);
-    const int lane = tid & (kWave - 1);
-    for (int item = wave; item < nt * nseg; item += kWaves) {
-        const int tl = item / nseg;
-        const int seg = item - tl * nseg;
-        const int h0 = seg * (16 * kWave) + lane * 16;     // first channel of this lane
-        const bool act = h0 < H;                           // whole 8-lane groups (H % 128 == 0)
-        u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-        if (act) {
-            const u32x4 *src = x + (size_t)(t0 + tl) * H8 + h0 / 8;
-            a = load16_stream(src);
-            b = load16_stream(src + 1);
-        }
-        uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        float f[16];
-        uint32_t m = 0;
+    const int wave = uniform(threadIdx.x / kWave);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int ntg = (T + tpb - 1) / tpb;
+    for (int tg = blockIdx.x; tg < ntg; tg += gridDim.x) {
+        const int t0 = tg * tpb;
+        const int nt = min(tpb, T - t0);
+        __syncthreads();
+        stage_rows(rows, idx, slot, t0, nt, K, E, C);
+        __syncthreads();
+        for (int item = wave; item < nt * nseg; item += kWaves) {
+            const int tl = item / nseg;
+            const int seg = item - tl * nseg;
+            const int h0 = seg * (16 * kWave) + lane * 16;   // first channel of this lane
+            const bool act = h0 < H;                         // whole 8-lane groups (H % 128 == 0)
+            u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+            if (act) {
+                const u32x4 *src = x + (size_t)(t0 + tl) * H8 + h0 / 8;
+                a = load16<EP_DISPATCH_NT_LOAD>(src);
+                b = load16<EP_DISPATCH_NT_LOAD>(src + 1);
+            }
+            const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            float f[16];
+            uint32_t m = 0;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            f[2 * k] = bf16_lo(w[k]);
-            f[2 * k + 1] = bf16_hi(w[k]);
-            m = max(m, (w[k] << 16) & 0x7FFFFFFFu);
-            m = max(m, w[k] & 0x7FFF0000u);
-        }
-        const float amax = group8_max(__uint_as_float(m));   // |x| bits: integer order
-        const float scale = amax / 448.0f;
-        uint32_t q[4] = {0u, 0u, 0u, 0u};
+            for (int k = 0; k < 8; ++k) {
+                f[2 * k] = bf16_lo(w[k]);
+                f[2 * k + 1] = bf16_hi(w[k]);
+                m = max(m, (w[k] << 16) & 0x7FFFFFFFu);
+                m = max(m, w[k] & 0x7FFF0000u);
+            }
+            const float amax = group8_max(__uint_as_float(m));   // |x| bits: integer order
+            const float scale = amax / 448.0f;
+            uint32_t q[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const uint32_t code = (amax == 0.0f) ? ((__float_as_uint(f[k]) >> 24) & 0x80u)
-                                                 : e4m3_rne_sat(f[k] / scale);
-            q[k / 4] |= code << (8 * (k % 4));
-        }
-        const u32x4 qv = {q[0], q[1], q[2], q[3]};
-        const int ngroups = MULTI ? (K + KG - 1) / KG : 1;
-        for (int grp = 0; grp < ngroups; ++grp) {
-            int r[KG];
-            token_rows<KG>(rows, tl, grp * KG, K, r);
+            for (int k = 0; k < 16; ++k) {
+                const uint32_t code = (amax == 0.0f) ? ((__float_as_uint(f[k]) >> 24) & 0x80u)
+                                                     : e4m3_rne_sat(f[k] / scale);
+                q[k / 4] |= code << (8 * (k % 4));
+            }
+            const u32x4 qv = {q[0], q[1], q[2], q[3]};
+            const int npg = MULTI ? (K + KG - 1) / KG : 1;
+            for (int pg = 0; pg < npg; ++pg) {
+                int r[KG];
+                token_rows<KG>(rows, tl, pg * KG, K, r);
 #pragma unroll
-            for (int g = 0; g < KG; ++g) {
-                if (r[g] < 0 || !act) continue;
-                store16_stream(recv_q + (size_t)r[g] * H16 + h0 / 16, qv);
-                if ((lane & 7) == 0) recv_scale[(size_t)r[g] * NB + h0 / 128] = scale;
+                for (int g = 0; g < KG; ++g) {
+                    if (r[g] < 0 || !act) continue;
+                    store16<EP_DISPATCH_NT_STORE>(recv_q + (size_t)r[g] * H16 + h0 / 16, qv);
+                    if ((lane & 7) == 0) recv_scale[(size_t)r[g] * NB + h0 / 128] = scale;
+                }
             }
         }
     }
@@ -168,12 +191,13 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// Chunks per lane: the widest item that still leaves at least 8192 wavefront items.
+// Chunks per lane: the widest item that still leaves at least 4096 wavefront items (measured
+// on MI355X: wide items win on prefill-sized batches, one chunk per lane on small ones).
 int pick_u(int T, int H8)
 {
     if (EP_DISPATCH_U) return EP_DISPATCH_U;
     for (int u : {4, 2})
-        if ((long)T * ceil_div(H8, u * kWave) >= 8192) return u;
+        if ((long)T * ceil_div(H8, u * kWave) >= 4096) return u;
     return 1;
 }
 
@@ -182,6 +206,12 @@ int pick_tpb(int T, int K, int nseg)
     int tpb = EP_DISPATCH_TPB ? EP_DISPATCH_TPB : (T >= 2048 ? 2 : 1) * (nseg == 1 ? 2 : 1);
     while (tpb > 1 && tpb * K > kStage) --tpb;
     return tpb;
+}
+
+dim3 grid_for(int T, int tpb)
+{
+    const int groups = ceil_div(T, tpb);
+    return dim3(EP_DISPATCH_MAX_BLOCKS ? min(groups, EP_DISPATCH_MAX_BLOCKS) : groups);
 }
 
 #define EP_BY_K(K, LAUNCH)                                                                  \
@@ -198,7 +228,7 @@ hipError_t launch_bf16_u(const ep_shape_t &s, const u32x4 *x, const int32_t *idx
                          const int32_t *slot, u32x4 *recv, int H8, int tpb, int nseg,
                          hipStream_t stream)
 {
-    const dim3 grid(ceil_div(s.T, tpb)), block(kThreads);
+    const dim3 grid = grid_for(s.T, tpb), block(kThreads);
 #define EP_LAUNCH_BF16(KG, MULTI)                                                            \
     return launch(dispatch_bf16_kernel<KG, U, MULTI>, grid, block, 0, stream, x, idx, slot,  \
                   recv, s.T, H8, s.E, s.C, s.K, tpb, nseg)
@@ -230,7 +260,7 @@ hipError_t launch_dispatch_fp8(const ep_shape_t &s, const uint16_t *x, const int
     if (s.T == 0) return hipSuccess;
     const int nseg = ceil_div(s.H, 16 * kWave);
     const int tpb = pick_tpb(s.T, s.K, nseg);
-    const dim3 grid(ceil_div(s.T, tpb)), block(kThreads);
+    const dim3 grid = grid_for(s.T, tpb), block(kThreads);
     const u32x4 *xv = reinterpret_cast<const u32x4 *>(x);
     u32x4 *qv = reinterpret_cast<u32x4 *>(recv_q);
 #define EP_LAUNCH_FP8(KG, MULTI)                                                             \

@@ -6,20 +6,24 @@
 // #{i' < i : id[i'] == e}; positions >= C are dropped.
 //
 // Design. Pairs are cut into tiles of 1024, one workgroup of 16 wavefronts per tile, one pair
-// per lane, so lane order is pair order.
-//  1. Each workgroup counts, per bin, the pairs of all EARLIER tiles (LDS histogram with
-//     atomics; the counts do not depend on the order of the atomics). Bins are the E experts,
-//     then "unrouted" (id -1) and "invalid" (any other id outside [0, E)).
-//  2. Inside its tile, each wavefront finds, for every lane, the mask of lanes holding the same
-//     bin with one ballot per bit of the bin number (bit-sliced match). The lane's rank is the
-//     popcount of that mask below it; the lowest lane of each group writes the group size into
-//     a per-wavefront histogram in LDS.
-//  3. A scan over the 16 wavefronts, per bin, turns those histograms into per-wavefront bases,
-//     starting from the earlier-tile count of step 1, so slot = base + rank, or -1 past C.
-//  4. The last workgroup, which now holds the totals of every bin, writes count = min(total, C),
-//     the exclusive scan of count (an LDS block scan), the per-rank sums and the stats.
+// per lane, so lane order is pair order. Bins are the E experts, then two bins that are never
+// ranked: E for invalid ids (outside [0, E) and not -1) and E+1 for unrouted ones (-1).
+//  1. Each workgroup counts, per bin, the pairs of all EARLIER tiles: 16-byte id vectors, all in
+//     flight at once, then one LDS atomic per id (the counts do not depend on the order of the
+//     atomics).
+//  2. Inside its tile, each wavefront finds, for every routed lane, the mask of lanes holding
+//     the same expert with one ballot per bit of the expert number (bit-sliced match). The
+//     lane's rank is the number of mask bits below it (v_mbcnt); the lowest lane of each group
+//     writes the group size into a per-wavefront histogram in LDS.
+//  3. A scan over the 16 wavefronts, per expert (16 lanes = one DPP row per expert), turns those
+//     histograms into per-wavefront bases starting from the earlier-tile count, so
+//     slot = base + rank, or -1 past C.
+//  4. The last workgroup, which now holds the total of every expert, writes
+//     count = min(total, C), its exclusive scan (DPP wave scans plus wave totals), the per-rank
+//     sums and the stats; dropped = routed - kept.
 // No workgroup waits on another and no result depends on scheduling: the outputs are
-// deterministic and need no workspace.
+// deterministic and need no workspace. The cost is the last workgroup's pass over all earlier
+// ids, which is one memory round trip plus ~T*K/1024 LDS atomics per lane.
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -30,10 +34,12 @@ namespace {
 constexpr int kLayoutThreads = 1024;
 constexpr int kLayoutWaves = kLayoutThreads / kWave;
 constexpr int kMaxBins = EP_MAX_EXPERTS + 2;
+constexpr int kPrefixVec = 8;     // 16-byte id vectors in flight per lane in step 1
 
+// Bin of an id: itself for an expert, E for an invalid id, E+1 for -1 (unrouted).
 __device__ __forceinline__ int bin_of(int e, int E)
 {
-    return ((unsigned)e < (unsigned)E) ? e : (e == -1 ? E : E + 1);
+    return (int)min((unsigned)e, (unsigned)E) + (e == -1 ? 1 : 0);
 }
 
 __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
@@ -46,89 +52,94 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
     __shared__ int32_t wcnt[kLayoutWaves][kMaxBins];    // per-wavefront counts, then bases
     __shared__ int32_t scan[EP_MAX_EXPERTS + 1];        // exclusive scan of count, then total
     __shared__ int32_t wsum[kLayoutWaves];
-    __shared__ int32_t dropped_total;
 
-    const int NB = E + 2;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const int tile_begin = blockIdx.x * kLayoutThreads;
+    const bool last = blockIdx.x == gridDim.x - 1;
 
-    for (int k = tid; k < NB; k += kLayoutThreads) {
+    // this lane's own pair, loaded first so its latency overlaps the prefix histogram
+    const int p = tile_begin + tid;
+    const bool in = p < TK;
+    const int own = in ? idx[p] : -1;
+
+    for (int k = tid; k < E + 2; k += kLayoutThreads) {
         base[k] = 0;
 #pragma unroll
         for (int w = 0; w < kLayoutWaves; ++w) wcnt[w][k] = 0;
     }
-    if (tid == 0) dropped_total = 0;
     __syncthreads();
 
-    // 1. histogram of the earlier tiles, eight independent loads in flight per lane
-    {
-        int p = tid;
-        for (; p + 7 * kLayoutThreads < tile_begin; p += 8 * kLayoutThreads) {
-            int v[8];
+    // 1. histogram of the earlier tiles. A tile is 4 KiB of ids, so the prefix is whole 16-byte
+    //    vectors; up to kPrefixVec of them per lane are in flight together. Addresses past the
+    //    prefix are clamped to its last vector and their counts skipped.
+    if (tile_begin > 0) {
+        const int4 *idx4 = reinterpret_cast<const int4 *>(idx);
+        const int nvec = tile_begin / 4;
+        for (int q0 = tid; q0 < nvec; q0 += kPrefixVec * kLayoutThreads) {
+            int4 v[kPrefixVec];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = idx[p + u * kLayoutThreads];
+            for (int u = 0; u < kPrefixVec; ++u) {
+                const int q = q0 + u * kLayoutThreads;
+                v[u] = idx4[q < nvec ? q : nvec - 1];
+            }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) atomicAdd(&base[bin_of(v[u], E)], 1);
+            for (int u = 0; u < kPrefixVec; ++u) {
+                const bool ok = q0 + u * kLayoutThreads < nvec;
+                const int e4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (ok) atomicAdd(&base[bin_of(e4[c], E)], 1);
+            }
         }
-        for (; p < tile_begin; p += kLayoutThreads) atomicAdd(&base[bin_of(idx[p], E)], 1);
     }
 
-    // 2. ranks inside the wavefront by bit-sliced ballot matching
-    const int p = tile_begin + tid;
-    const bool in = p < TK;
-    const int b = in ? bin_of(idx[p], E) : 0;
-    uint64_t same = __ballot(in);
+    // 2. ranks of the routed lanes inside the wavefront by bit-sliced ballot matching
+    const bool routed = in && (unsigned)own < (unsigned)E;
+    if (last) {                     // this tile's pairs in the two non-expert bins, for the stats
+        const int unrouted = __popcll(__ballot(in && own == -1));
+        const int invalid = __popcll(__ballot(in && own != -1 && !routed));
+        if (lane == 0 && unrouted) atomicAdd(&base[E + 1], unrouted);
+        if (lane == 0 && invalid) atomicAdd(&base[E], invalid);
+    }
+    uint64_t same = __ballot(routed);
     for (int k = 0; k < nbits; ++k) {
-        const bool bit = (b >> k) & 1;
+        const bool bit = (own >> k) & 1;
         const uint64_t m = __ballot(bit);
         same &= bit ? m : ~m;
     }
-    const int rank = __popcll(same & lanemask_lt(lane));
-    if (in && rank == 0) wcnt[wave][b] = __popcll(same);
+    const int rank = count_below(same);
+    if (routed && rank == 0) wcnt[wave][own] = __popcll(same);
     __syncthreads();
 
-    // 3. per-bin scan over wavefronts, from the earlier-tile base
-    for (int k = tid; k < NB; k += kLayoutThreads) {
-        int run = base[k];
-#pragma unroll
-        for (int w = 0; w < kLayoutWaves; ++w) {
-            const int c = wcnt[w][k];
-            wcnt[w][k] = run;
-            run += c;
-        }
-        base[k] = run;
+    // 3. per-expert exclusive scan over the 16 wavefronts, from the earlier-tile base: the 16
+    //    counts of an expert sit in one DPP row of 16 lanes
+    for (int k = tid; k < E * kLayoutWaves; k += kLayoutThreads) {
+        const int e = k / kLayoutWaves, w = k % kLayoutWaves;
+        const int c = wcnt[w][e];
+        const int incl = row16_inclusive_sum(c);
+        const int b0 = base[e];
+        wcnt[w][e] = b0 + incl - c;
+        // the 16 lanes of an expert are in one wavefront and read b0 before this write
+        if (w == kLayoutWaves - 1) base[e] = b0 + incl;
     }
     __syncthreads();
     if (in) {
         int s = -1;
-        if (b < E) {
-            const int pos = wcnt[wave][b] + rank;
+        if (routed) {
+            const int pos = wcnt[wave][own] + rank;
             s = pos < C ? pos : -1;
         }
         slot[p] = s;
     }
-    if (blockIdx.x != gridDim.x - 1) return;
+    if (!last) return;
 
-    // 4. last tile: totals are complete; counts, offsets, ranks and stats
-    int cnt = 0, drop = 0;
-    for (int e = tid; e < E; e += kLayoutThreads) {   // E <= kLayoutThreads: one expert per lane
-        const int d = base[e];
-        cnt = d < C ? d : C;
-        drop = d - cnt;
-    }
-    int incl = cnt;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int v = __shfl_up(incl, o);
-        if (lane >= o) incl += v;
-    }
-    int wdrop = drop;
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) wdrop += __shfl_xor(wdrop, o);
+    // 4. last tile: base[e] is the total of expert e. count = min(total, C), its exclusive
+    //    scan in expert order, per-rank sums, stats. Every routed pair is kept or dropped.
+    const int cnt = tid < E ? min(base[tid], C) : 0;     // E <= kLayoutThreads
+    const int incl = wave_inclusive_sum(cnt);
     if (lane == kWave - 1) wsum[wave] = incl;
-    if (lane == 0 && wdrop) atomicAdd(&dropped_total, wdrop);
     __syncthreads();
     int wbase = 0;
     for (int w = 0; w < wave; ++w) wbase += wsum[w];
@@ -138,11 +149,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
         offset[tid] = excl;
         scan[tid] = excl;
     }
-    if (tid == 0) {
-        int total = 0;
-        for (int w = 0; w < kLayoutWaves; ++w) total += wsum[w];
-        scan[E] = total;
-    }
+    if (tid == E - 1) scan[E] = excl + cnt;             // total kept
     __syncthreads();
     const int EL = E / R;
     for (int r = tid; r < R; r += kLayoutThreads) {
@@ -151,10 +158,11 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
         if (rank_offset) rank_offset[r] = lo;
     }
     if (tid == 0) {
-        stats[0] = scan[E];
-        stats[1] = dropped_total;
-        stats[2] = base[E];
-        stats[3] = base[E + 1];
+        const int kept = scan[E], unrouted = base[E + 1], invalid = base[E];
+        stats[0] = kept;
+        stats[1] = TK - unrouted - invalid - kept;
+        stats[2] = unrouted;
+        stats[3] = invalid;
     }
 }
 
@@ -167,7 +175,7 @@ hipError_t launch_layout(const ep_shape_t &s, const int32_t *idx, int32_t *slot,
     const int TK = s.T * s.K;
     const int tiles = TK > 0 ? (TK + kLayoutThreads - 1) / kLayoutThreads : 1;
     int nbits = 0;
-    while ((1 << nbits) < s.E + 2) ++nbits;   // bins 0 .. E+1
+    while ((1 << nbits) < s.E) ++nbits;   // expert numbers 0 .. E-1
     return launch(layout_kernel, dim3(tiles), dim3(kLayoutThreads), 0, stream, idx, TK, s.E,
                   s.C, s.R, nbits, slot, count, offset, rank_count, rank_offset, stats);
 }

@@ -68,6 +68,7 @@ enum {
  *
  *   topk_idx      [T*K] int32 in   expert of pair i; -1 = unrouted; other ids outside [0, E)
  *                                   are invalid. Both get slot -1 and are counted in stats.
+ *                                   16-byte aligned (else EP_ERR_ALIGN).
  *   slot          [T*K] int32 out  #{i' < i : topk_idx[i'] == topk_idx[i]} if that is < C,
  *                                   else -1 (dropped: each expert keeps its first C pairs in
  *                                   token order). This is the handle dispatch and combine use.

@@ -76,6 +76,10 @@ def test_layout_rejects_bad_shapes(lib, kw, code):
     assert lib.ep_last_error().decode().startswith("ep_layout")
 
 
+def test_layout_rejects_misaligned_route(lib):
+    assert lib.ep_layout(shape(), A16 + 4, A16, A16, A16, None, None, A16, None) == B.EP_ERR_ALIGN
+
+
 def test_layout_rejects_null_pointers(lib):
     assert lib.ep_layout(None, A16, A16, A16, A16, None, None, A16, None) == B.EP_ERR_INVALID
     assert lib.ep_layout(shape(), None, A16, A16, A16, None, None, A16, None) == B.EP_ERR_INVALID
