@@ -19,7 +19,7 @@ synchronisations. Every step takes the next of NSETS input batches (x, route, we
 writes the layer's persistent buffers (receive buffer, output), reading its persistent expert
 outputs, as an MoE layer does. A variant where every batch also has its own buffers
 ("rotating_all_buffers": ~16 GiB touched in turn, so page translations are cold each step) is
-reported beside it. Decode-like latency is single-shot: each sample first overwrites 1 GiB
+reported beside it. Decode-like latency is single-shot: each sample first overwrites 2 GiB
 (beyond every cache) outside the event pair, then times one step (median of the samples).
 
 ``--gpus N`` with N > 1 is refused: this build measures one GPU; inter-GPU transport is not
@@ -156,7 +156,7 @@ class Workload:
         return ev0.elapsed_time(ev1) / steps, wall / steps * 1e3
 
     def single_shot(self, samples, flush):
-        """Single-shot latency of one step, cold: each sample first overwrites `flush` (1 GiB,
+        """Single-shot latency of one step, cold: each sample first overwrites `flush` (2 GiB,
         beyond every cache level) outside the event pair. While that fill runs, the host has
         already enqueued the event pair and the step's three launches, so the pair measures
         the GPU-side time of the step including the gaps between its kernels, not host-side
@@ -174,29 +174,33 @@ class Workload:
             ts.append(ev0.elapsed_time(ev1) * 1e3)
         return ts
 
-    def kernel_avg_us(self, reps):
-        """Average duration of each kernel inside whole steps: an event is recorded on the
-        stream the kernels run on before the layout, between the calls and after the combine,
-        for `reps` steps; each kernel's time is the mean gap between its two events."""
+    def kernel_avg_us(self, flush, runs=25, per_run=8):
+        """Average duration of each kernel launched back to back: per run, a 2 GiB fill of
+        `flush` is enqueued first, and while it executes the host enqueues an event, `per_run`
+        launches of the one kernel (rotating over the input batches) and a second event, so
+        the launches reach the GPU already queued. The per-launch time is the event gap over
+        `per_run`; the result is the median over `runs`. The batches' layouts are computed
+        first, so dispatch and combine read valid slots."""
         torch = self.torch
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
         for k in range(len(self.sets)):
             self.step(k)
         torch.cuda.synchronize()
-        for k in range(reps):
-            s = self.sets[k % len(self.sets)]
-            e = evs[k]
-            e[0].record()
-            self.layout(s)
-            e[1].record()
-            self.dispatch(s)
-            e[2].record()
-            self.combine(s)
-            e[3].record()
-        torch.cuda.synchronize()
-        names = ("layout", "dispatch", "combine")
-        return {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) * 1e3 / reps
-                for i, n in enumerate(names)}
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        out = {}
+        for name, fn in (("layout", self.layout), ("dispatch", self.dispatch),
+                         ("combine", self.combine)):
+            ts = []
+            for r in range(runs):
+                torch.cuda.synchronize()
+                flush.fill_(r & 0x7F)
+                ev0.record()
+                for k in range(per_run):
+                    fn(self.sets[k % len(self.sets)])
+                ev1.record()
+                torch.cuda.synchronize()
+                ts.append(ev0.elapsed_time(ev1) * 1e3 / per_run)
+            out[name] = statistics.median(ts)
+        return out
 
 
 def counter_traffic(kernel, workload):
@@ -299,7 +303,7 @@ def main():
         return
 
     head_cfg = W.get_config(args.workload)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")   # beyond every cache
     results = {}
     for name in dict.fromkeys([args.workload, "prefill_fp8", "decode_bf16", "decode_fp8"]):
         cfg = W.get_config(name)
@@ -318,7 +322,7 @@ def main():
             r["us_single_shot_median"] = round(statistics.median(ss), 3)
             r["us_single_shot_min"] = round(min(ss), 3)
             r["us_single_shot_max"] = round(max(ss), 3)
-        kus = wl.kernel_avg_us(args.steps)
+        kus = wl.kernel_avg_us(flush)
         r["kernel_avg_us"] = {k: round(v, 3) for k, v in kus.items()}
         kb = {"layout": A.layout_bytes(cfg.T, cfg.K),
               "dispatch": A.dispatch_bytes(cfg.T, cfg.K, cfg.H, n_kept, cfg.fp8),
