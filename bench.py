@@ -1,8 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark of one GPU's MoE expert-parallel layout + dispatch + combine on MI355X.
 
-One step is the whole hot path on one batch: ep_layout -> ep_dispatch (bf16) or
-ep_dispatch_fp8 -> ep_combine, enqueued on one stream with the inputs already in HBM. The
+One step is the whole hot path on one batch: ep_layout_dispatch (the layout and the bf16 or
+FP8 dispatch in one launch) -> ep_combine, enqueued on one stream with the inputs already in
+HBM; the same pass as three calls (ep_layout -> ep_dispatch[_fp8] -> ep_combine) is reported
+beside it. The
 boundary follows the common event boundary of awsome-distributed-ai PR #1238 ("What
 changed"): from route and input ready through the FP8 cast or layout, dispatch and combine
 completion.
@@ -109,7 +111,15 @@ class Workload:
         b["out"] = torch.empty((cfg.T, cfg.H), dtype=torch.int16, device=dev)
         return b
 
-    # the three calls of one step
+    # the calls of one step: layout_dispatch + combine (or layout, dispatch, combine)
+    def layout_dispatch(self, s):
+        c = self.cfg
+        if c.fp8:
+            self.B.ep_layout_dispatch_fp8(s["x"], s["idx"], s["recv_q"], s["recv_s"], c.E, c.C,
+                                          c.R, **s["lay"])
+        else:
+            self.B.ep_layout_dispatch(s["x"], s["idx"], s["recv"], c.E, c.C, c.R, **s["lay"])
+
     def layout(self, s):
         c = self.cfg
         self.B.ep_layout(s["idx"], c.E, c.C, c.R, **s["lay"])
@@ -126,6 +136,13 @@ class Workload:
         self.B.ep_combine(s["y"], s["idx"], s["lay"]["slot"], s["w"], c.C, out=s["out"])
 
     def step(self, k):
+        """One pass of the hot path: the fused layout + dispatch, then combine."""
+        s = self.sets[k % len(self.sets)]
+        self.layout_dispatch(s)
+        self.combine(s)
+
+    def step3(self, k):
+        """The same pass as three separate calls: layout, dispatch, combine."""
         s = self.sets[k % len(self.sets)]
         self.layout(s)
         self.dispatch(s)
@@ -140,35 +157,37 @@ class Workload:
             out.append(int(s["lay"]["stats"][0]))
         return out
 
-    def timed_loop(self, steps, warmup):
+    def timed_loop(self, steps, warmup, step=None):
         torch = self.torch
+        step = step or self.step
         for k in range(warmup):
-            self.step(k)
+            step(k)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ev0.record()
         for k in range(steps):
-            self.step(k)
+            step(k)
         ev1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         return ev0.elapsed_time(ev1) / steps, wall / steps * 1e3
 
-    def single_shot(self, samples, flush):
+    def single_shot(self, samples, flush, step=None):
         """Single-shot latency of one step, cold: each sample first overwrites `flush` (2 GiB,
         beyond every cache level) outside the event pair. While that fill runs, the host has
         already enqueued the event pair and the step's three launches, so the pair measures
         the GPU-side time of the step including the gaps between its kernels, not host-side
         launch overhead."""
         torch = self.torch
+        step = step or self.step
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ts = []
         for k in range(samples):
             torch.cuda.synchronize()
             flush.fill_(k & 0x7F)
             ev0.record()
-            self.step(k)
+            step(k)
             ev1.record()
             torch.cuda.synchronize()
             ts.append(ev0.elapsed_time(ev1) * 1e3)
@@ -187,8 +206,8 @@ class Workload:
         torch.cuda.synchronize()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         out = {}
-        for name, fn in (("layout", self.layout), ("dispatch", self.dispatch),
-                         ("combine", self.combine)):
+        for name, fn in (("layout_dispatch", self.layout_dispatch), ("combine", self.combine),
+                         ("layout", self.layout), ("dispatch", self.dispatch)):
             ts = []
             for r in range(runs):
                 torch.cuda.synchronize()
@@ -309,6 +328,7 @@ def main():
         cfg = W.get_config(name)
         wl = Workload(cfg, NSETS, torch, B, W)
         ms, wall_ms = wl.timed_loop(args.steps, args.warmup)
+        ms3, _ = wl.timed_loop(args.steps, args.warmup, step=wl.step3)
         kept = wl.kept()
         n_kept = kept[0]
         pay = A.logical_payload_bytes(cfg.T, cfg.K, cfg.H, cfg.fp8)
@@ -316,9 +336,13 @@ def main():
         r = {"us_per_step": round(ms * 1e3, 3), "wall_us_per_step": round(wall_ms * 1e3, 3),
              "logical_GBps": round(pay / (ms * 1e-3) / 1e9, 2),
              "hbm_frac": round(alg / (ms * 1e-3) / A.HBM_PEAK_BYTES_PER_S, 4),
-             "algorithmic_bytes": alg, "payload_bytes": pay, "kept_pairs": n_kept}
+             "algorithmic_bytes": alg, "payload_bytes": pay, "kept_pairs": n_kept,
+             "three_call_step": {"us_per_step": round(ms3 * 1e3, 3),
+                                 "hbm_frac": round(alg / (ms3 * 1e-3) / A.HBM_PEAK_BYTES_PER_S, 4)}}
         if cfg.T <= 256:
             ss = wl.single_shot(args.latency_samples, flush)
+            ss3 = wl.single_shot(args.latency_samples, flush, step=wl.step3)
+            r["three_call_step"]["us_single_shot_median"] = round(statistics.median(ss3), 3)
             r["us_single_shot_median"] = round(statistics.median(ss), 3)
             r["us_single_shot_min"] = round(min(ss), 3)
             r["us_single_shot_max"] = round(max(ss), 3)
@@ -327,6 +351,7 @@ def main():
         kb = {"layout": A.layout_bytes(cfg.T, cfg.K),
               "dispatch": A.dispatch_bytes(cfg.T, cfg.K, cfg.H, n_kept, cfg.fp8),
               "combine": A.combine_bytes(cfg.T, cfg.K, cfg.H, n_kept)}
+        kb["layout_dispatch"] = kb["layout"] + kb["dispatch"]
         r["kernel_GBps"] = {k: round(kb[k] / (kus[k] * 1e-6) / 1e9, 1) for k in kus}
         del wl
         torch.cuda.empty_cache()
@@ -343,7 +368,7 @@ def main():
         log(f"{name}: {json.dumps(r)}")
 
     cfg, _, r, kus, kb = results[args.workload]
-    dom = max(("dispatch", "combine"), key=lambda k: kus[k])
+    dom = max(("layout_dispatch", "combine"), key=lambda k: kus[k])   # the step's two kernels
     achieved = kb[dom] / (kus[dom] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": A.HBM_PEAK_BYTES_PER_S / 1e9, "unit": "GB/s",
@@ -359,7 +384,7 @@ def main():
     def brief(name):
         c, _, rr, _, _ = results[name]
         keys = ("us_per_step", "us_single_shot_median", "logical_GBps", "hbm_frac",
-                "kernel_avg_us")
+                "kernel_avg_us", "three_call_step")
         return {k: rr[k] for k in keys if k in rr}
 
     line = {
@@ -375,6 +400,7 @@ def main():
         "hbm_roofline_frac": r["hbm_frac"],
         "us_per_step": r["us_per_step"],
         "rotating_all_buffers": r.get("rotating_all_buffers"),
+        "three_call_step": r.get("three_call_step"),
         "t128_us": {n: brief(n) for n in ("decode_bf16", "decode_fp8") if n in results},
         "prefill_fp8": brief("prefill_fp8") if "prefill_fp8" in results else None,
         "roofline": roofline,

@@ -5,7 +5,8 @@ The compute runs in hand-written gfx950 HIP kernels behind a C ABI (``include/ep
 and the current HIP stream only). ``workloads`` draws the seeded synthetic inputs and
 ``accounting`` counts bytes.
 """
-_BINDING_NAMES = ("ep_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_combine", "ep_version",
+_BINDING_NAMES = ("ep_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_layout_dispatch",
+                  "ep_layout_dispatch_fp8", "ep_combine", "ep_version",
                   "ep_error_string", "EpError", "library_path", "load_library")
 
 

@@ -21,8 +21,9 @@ EP_MAX_TOPK = 256
 EP_FP8_BLOCK = 128
 
 #: every entry point the header declares
-EXPORTED = ("ep_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_combine", "ep_error_string",
-            "ep_last_error", "ep_version")
+EXPORTED = ("ep_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_layout_dispatch",
+            "ep_layout_dispatch_fp8", "ep_combine", "ep_error_string", "ep_last_error",
+            "ep_version")
 
 
 class EpShape(ctypes.Structure):
@@ -57,7 +58,10 @@ def load_library():
         L.ep_dispatch.argtypes = [sp, vp, vp, vp, vp, vp]
         L.ep_dispatch_fp8.argtypes = [sp, vp, vp, vp, vp, vp, vp]
         L.ep_combine.argtypes = [sp, vp, vp, vp, vp, vp, vp]
-        for fn in ("ep_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_combine"):
+        L.ep_layout_dispatch.argtypes = [sp] + [vp] * 10
+        L.ep_layout_dispatch_fp8.argtypes = [sp] + [vp] * 11
+        for fn in ("ep_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_layout_dispatch",
+                   "ep_layout_dispatch_fp8", "ep_combine"):
             getattr(L, fn).restype = ctypes.c_int
         L.ep_error_string.argtypes = [ctypes.c_int]
         L.ep_error_string.restype = ctypes.c_char_p
@@ -140,6 +144,71 @@ def ep_layout(topk_idx: torch.Tensor, E: int, C: int, R: int, *, slot=None, expe
     _check("ep_layout", rc)
     return dict(slot=slot, expert_count=expert_count, expert_offset=expert_offset,
                 rank_count=rank_count, rank_offset=rank_offset, stats=stats)
+
+
+def _layout_outputs(dev, T, K, E, R, slot, expert_count, expert_offset, rank_count,
+                    rank_offset, stats):
+    mk = lambda n: torch.empty(n, dtype=torch.int32, device=dev)
+    out = dict(slot=mk((T, K)) if slot is None else slot,
+               expert_count=mk(E) if expert_count is None else expert_count,
+               expert_offset=mk(E) if expert_offset is None else expert_offset,
+               rank_count=mk(R) if rank_count is None else rank_count,
+               rank_offset=mk(R) if rank_offset is None else rank_offset,
+               stats=mk(EP_STATS_LEN) if stats is None else stats)
+    _need(out["slot"], "slot", torch.int32, T * K, dev)
+    for name, n in (("expert_count", E), ("expert_offset", E), ("rank_count", R),
+                    ("rank_offset", R), ("stats", EP_STATS_LEN)):
+        _need(out[name], name, torch.int32, n, dev)
+    return out
+
+
+def _layout_ptrs(lay):
+    return [_ptr(lay[k]) for k in ("slot", "expert_count", "expert_offset", "rank_count",
+                                    "rank_offset", "stats")]
+
+
+def ep_layout_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, recv: torch.Tensor, E: int,
+                       C: int, R: int, *, slot=None, expert_count=None, expert_offset=None,
+                       rank_count=None, rank_offset=None, stats=None, stream=None):
+    """ep_layout + bf16 dispatch in one launch. Returns the layout dict (as ep_layout);
+    ``recv`` [E, C, H] is written in place."""
+    dev = x.device
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    lay = _layout_outputs(dev, T, K, E, R, slot, expert_count, expert_offset, rank_count,
+                          rank_offset, stats)
+    _need(x, "x", _bf16(x), T * H, dev)
+    _need(topk_idx, "topk_idx", torch.int32, T * K, dev)
+    _need(recv, "recv", _bf16(recv), E * C * H, dev)
+    sh = _shape(T, H, E, K, C, R)
+    rc = load_library().ep_layout_dispatch(ctypes.byref(sh), _ptr(x), _ptr(topk_idx),
+                                           *_layout_ptrs(lay), _ptr(recv), _stream(stream))
+    _check("ep_layout_dispatch", rc)
+    return lay
+
+
+def ep_layout_dispatch_fp8(x: torch.Tensor, topk_idx: torch.Tensor, recv_q: torch.Tensor,
+                           recv_scale: torch.Tensor, E: int, C: int, R: int, *, slot=None,
+                           expert_count=None, expert_offset=None, rank_count=None,
+                           rank_offset=None, stats=None, stream=None):
+    """ep_layout + FP8 dispatch in one launch. Returns the layout dict; ``recv_q`` and
+    ``recv_scale`` are written in place."""
+    dev = x.device
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    lay = _layout_outputs(dev, T, K, E, R, slot, expert_count, expert_offset, rank_count,
+                          rank_offset, stats)
+    _need(x, "x", _bf16(x), T * H, dev)
+    _need(topk_idx, "topk_idx", torch.int32, T * K, dev)
+    _need(recv_q, "recv_q", recv_q.dtype if recv_q.dtype in (torch.uint8, torch.float8_e4m3fn)
+          else torch.uint8, E * C * H, dev)
+    _need(recv_scale, "recv_scale", torch.float32, E * C * (H // EP_FP8_BLOCK), dev)
+    sh = _shape(T, H, E, K, C, R)
+    rc = load_library().ep_layout_dispatch_fp8(ctypes.byref(sh), _ptr(x), _ptr(topk_idx),
+                                               *_layout_ptrs(lay), _ptr(recv_q),
+                                               _ptr(recv_scale), _stream(stream))
+    _check("ep_layout_dispatch_fp8", rc)
+    return lay
 
 
 def ep_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, slot: torch.Tensor, recv: torch.Tensor,

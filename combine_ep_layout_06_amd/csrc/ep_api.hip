@@ -58,6 +58,22 @@ int hip_status(hipError_t e, const char *fn)
     return fail(EP_ERR_HIP, std::string(fn) + ": " + hipGetErrorName(e) + ": " + hipGetErrorString(e));
 }
 
+// Checks shared by every call that computes the layout.
+int check_layout_args(const ep_shape_t *shape, const int32_t *topk_idx, const int32_t *slot,
+                      const int32_t *expert_count, const int32_t *expert_offset,
+                      const int32_t *stats, const char *fn)
+{
+    const std::string f(fn);
+    if (int rc = check_shape(shape, fn)) return rc;
+    if (shape->E > EP_MAX_EXPERTS) return fail(EP_ERR_UNSUPPORTED, f + ": E exceeds EP_MAX_EXPERTS");
+    const bool empty = (int64_t)shape->T * shape->K == 0;
+    if ((!empty && (!topk_idx || !slot)) || !expert_count || !expert_offset || !stats)
+        return fail(EP_ERR_INVALID, f + ": NULL required pointer");
+    if (!aligned(topk_idx, 16))
+        return fail(EP_ERR_ALIGN, f + ": topk_idx must be 16-byte aligned");
+    return EP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -66,17 +82,50 @@ int ep_layout(const ep_shape_t *shape, const int32_t *topk_idx, int32_t *slot,
               int32_t *expert_count, int32_t *expert_offset, int32_t *rank_count,
               int32_t *rank_offset, int32_t *stats, hipStream_t stream)
 {
-    if (int rc = check_shape(shape, "ep_layout")) return rc;
-    if (shape->E > EP_MAX_EXPERTS)
-        return fail(EP_ERR_UNSUPPORTED, "ep_layout: E exceeds EP_MAX_EXPERTS");
-    const bool empty = (int64_t)shape->T * shape->K == 0;
-    if ((!empty && (!topk_idx || !slot)) || !expert_count || !expert_offset || !stats)
-        return fail(EP_ERR_INVALID, "ep_layout: NULL required pointer");
-    if (!aligned(topk_idx, 16))
-        return fail(EP_ERR_ALIGN, "ep_layout: topk_idx must be 16-byte aligned");
+    if (int rc = check_layout_args(shape, topk_idx, slot, expert_count, expert_offset, stats,
+                                   "ep_layout"))
+        return rc;
     return hip_status(ep::launch_layout(*shape, topk_idx, slot, expert_count, expert_offset,
                                         rank_count, rank_offset, stats, stream),
                       "ep_layout");
+}
+
+int ep_layout_dispatch(const ep_shape_t *shape, const uint16_t *x, const int32_t *topk_idx,
+                       int32_t *slot, int32_t *expert_count, int32_t *expert_offset,
+                       int32_t *rank_count, int32_t *rank_offset, int32_t *stats,
+                       uint16_t *recv, hipStream_t stream)
+{
+    if (int rc = check_layout_args(shape, topk_idx, slot, expert_count, expert_offset, stats,
+                                   "ep_layout_dispatch"))
+        return rc;
+    if (int rc = check_rows(shape, "ep_layout_dispatch", 8)) return rc;
+    if (shape->T > 0 && (!x || !recv))
+        return fail(EP_ERR_INVALID, "ep_layout_dispatch: NULL required pointer");
+    if (!aligned(x, 16) || !aligned(recv, 16))
+        return fail(EP_ERR_ALIGN, "ep_layout_dispatch: x and recv must be 16-byte aligned");
+    const ep::LayoutOut o{slot, expert_count, expert_offset, rank_count, rank_offset, stats};
+    return hip_status(ep::launch_layout_dispatch_bf16(*shape, x, topk_idx, o, recv, stream),
+                      "ep_layout_dispatch");
+}
+
+int ep_layout_dispatch_fp8(const ep_shape_t *shape, const uint16_t *x, const int32_t *topk_idx,
+                           int32_t *slot, int32_t *expert_count, int32_t *expert_offset,
+                           int32_t *rank_count, int32_t *rank_offset, int32_t *stats,
+                           uint8_t *recv_q, float *recv_scale, hipStream_t stream)
+{
+    if (int rc = check_layout_args(shape, topk_idx, slot, expert_count, expert_offset, stats,
+                                   "ep_layout_dispatch_fp8"))
+        return rc;
+    if (int rc = check_rows(shape, "ep_layout_dispatch_fp8", EP_FP8_BLOCK)) return rc;
+    if (shape->T > 0 && (!x || !recv_q || !recv_scale))
+        return fail(EP_ERR_INVALID, "ep_layout_dispatch_fp8: NULL required pointer");
+    if (!aligned(x, 16) || !aligned(recv_q, 16) || !aligned(recv_scale, 4))
+        return fail(EP_ERR_ALIGN, "ep_layout_dispatch_fp8: x and recv_q must be 16-byte aligned, "
+                                  "recv_scale 4-byte aligned");
+    const ep::LayoutOut o{slot, expert_count, expert_offset, rank_count, rank_offset, stats};
+    return hip_status(ep::launch_layout_dispatch_fp8(*shape, x, topk_idx, o, recv_q, recv_scale,
+                                                     stream),
+                      "ep_layout_dispatch_fp8");
 }
 
 int ep_dispatch(const ep_shape_t *shape, const uint16_t *x, const int32_t *topk_idx,

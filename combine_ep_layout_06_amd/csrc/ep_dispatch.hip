@@ -1,27 +1,14 @@
 // Dispatch on gfx950: scatter each token row to the receive slot of every expert it selected,
-// as bf16, or cast once per token to OCP E4M3 with one fp32 scale per 128 channels.
-//
-// The receiving side of expert-parallel dispatch expands tokens into the per-expert layout
-// (afdEP-comm validation record, kernel_timelines: dispatch_copy_epilogue). Here the tokens
-// are local, so dispatch reads each row of x ONCE and stores it K times: HBM traffic is
-// 2*H per token read plus 2*H (bf16) or H + 4*H/128 (FP8) per kept pair written.
+// as bf16, or cast once per token to OCP E4M3 with one fp32 scale per 128 channels. The row
+// work is dispatch_item_bf16 / dispatch_item_fp8 (ep_dispatch_item.h).
 //
 // Work split. Tokens are cut into groups of `tpb`; a workgroup of 4 wavefronts takes groups in
 // a grid-stride loop. For each group it first stages the receive-row numbers (e*C + slot, or
 // -1 for a pair that is not kept) of the group's tpb*K pairs in LDS with one coalesced pass, so
 // no wavefront waits on a dependent global load before its row copy. A wavefront item is one
-// token and one segment of its row; each lane moves 16-byte chunks (8 bf16), lane-contiguous,
-// so every load and store instruction covers 1 KiB of one row. The KG receive rows of a token
-// are read from LDS together, then the row pieces are stored.
-//
-// x loads are non-temporal (read once). Row stores are plain stores: for this one-row-to-K-rows
-// scatter, non-temporal stores measured slower on MI355X.
-//
-// FP8: a lane owns 16 consecutive channels (two 16-byte loads, one 16-byte store of codes),
-// so a 128-channel block is 8 lanes; the block amax is a DPP max over those 8 lanes. The scale
-// and the codes use IEEE fp32 divisions (HIP's default, correctly rounded) exactly as the
-// definition states: scale = amax / 448, q = e4m3(x / scale).
-#include "ep_device.h"
+// token and one segment of its row. HBM traffic: 2*H per token read plus 2*H (bf16) or
+// H + 4*H/128 (FP8) per kept pair written.
+#include "ep_dispatch_item.h"
 #include "ep_internal.h"
 
 #ifndef EP_DISPATCH_U
@@ -33,12 +20,6 @@
 #ifndef EP_DISPATCH_MAX_BLOCKS
 #define EP_DISPATCH_MAX_BLOCKS 0 // grid cap; groups beyond it are taken in a grid-stride loop
 #endif
-#ifndef EP_DISPATCH_NT_LOAD
-#define EP_DISPATCH_NT_LOAD 1
-#endif
-#ifndef EP_DISPATCH_NT_STORE
-#define EP_DISPATCH_NT_STORE 0
-#endif
 
 namespace ep {
 
@@ -47,14 +28,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kStage = 256;        // staged pairs per group (tpb * K <= kStage)
-
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-// Row number of pair (e, s) in the [E][C] receive buffer, or -1 if it is not kept.
-__device__ __forceinline__ int recv_row(int e, int s, int E, int C)
-{
-    return ((unsigned)e < (unsigned)E && (unsigned)s < (unsigned)C) ? e * C + s : -1;
-}
 
 // Stage the receive rows of tokens [t0, t0 + nt) into rows[] (one coalesced pass).
 __device__ __forceinline__ void stage_rows(int32_t *rows, const int32_t *__restrict__ idx,
@@ -67,20 +40,6 @@ __device__ __forceinline__ void stage_rows(int32_t *rows, const int32_t *__restr
     }
 }
 
-// The receive rows of up to KG pairs of token tl, read from LDS together (uniform values).
-template <int KG>
-__device__ __forceinline__ void token_rows(const int32_t *rows, int tl, int j0, int K,
-                                           int (&r)[KG])
-{
-#pragma unroll
-    for (int g = 0; g < KG; ++g) {
-        const int j = j0 + g;
-        const int v = uniform(rows[tl * K + (j < K ? j : K - 1)]);
-        r[g] = j < K ? v : -1;
-    }
-}
-
-// KG: pairs per group (K <= KG unless MULTI); U: 16-byte chunks per lane per item.
 template <int KG, int U, bool MULTI>
 __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
     const u32x4 *__restrict__ x, const int32_t *__restrict__ idx,
@@ -88,8 +47,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
     int K, int tpb, int nseg)
 {
     __shared__ int32_t rows[kStage];
-    const int wave = uniform(threadIdx.x / kWave);
-    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = wave_uniform(threadIdx.x / kWave);
     const int ntg = (T + tpb - 1) / tpb;
     for (int tg = blockIdx.x; tg < ntg; tg += gridDim.x) {
         const int t0 = tg * tpb;
@@ -99,29 +57,8 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
         __syncthreads();
         for (int item = wave; item < nt * nseg; item += kWaves) {
             const int tl = item / nseg;
-            const int seg = item - tl * nseg;
-            const u32x4 *src = x + (size_t)(t0 + tl) * H8;
-            u32x4 v[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = (seg * U + u) * kWave + lane;
-                v[u] = load16<EP_DISPATCH_NT_LOAD>(src + (c < H8 ? c : H8 - 1));
-            }
-            const int npg = MULTI ? (K + KG - 1) / KG : 1;
-            for (int pg = 0; pg < npg; ++pg) {
-                int r[KG];
-                token_rows<KG>(rows, tl, pg * KG, K, r);
-#pragma unroll
-                for (int g = 0; g < KG; ++g) {
-                    if (r[g] < 0) continue;
-                    u32x4 *dst = recv + (size_t)r[g] * H8;
-#pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        const int c = (seg * U + u) * kWave + lane;
-                        if (c < H8) store16<EP_DISPATCH_NT_STORE>(dst + c, v[u]);
-                    }
-                }
-            }
+            dispatch_item_bf16<KG, U, MULTI>(x, recv, rows, t0 + tl, tl, item - tl * nseg, H8,
+                                             K);
         }
     }
 }
@@ -133,9 +70,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
     float *__restrict__ recv_scale, int T, int H, int E, int C, int K, int tpb, int nseg)
 {
     __shared__ int32_t rows[kStage];
-    const int H8 = H / 8, H16 = H / 16, NB = H / 128;
-    const int wave = uniform(threadIdx.x / kWave);
-    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = wave_uniform(threadIdx.x / kWave);
     const int ntg = (T + tpb - 1) / tpb;
     for (int tg = blockIdx.x; tg < ntg; tg += gridDim.x) {
         const int t0 = tg * tpb;
@@ -145,46 +80,8 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
         __syncthreads();
         for (int item = wave; item < nt * nseg; item += kWaves) {
             const int tl = item / nseg;
-            const int seg = item - tl * nseg;
-            const int h0 = seg * (16 * kWave) + lane * 16;   // first channel of this lane
-            const bool act = h0 < H;                         // whole 8-lane groups (H % 128 == 0)
-            u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-            if (act) {
-                const u32x4 *src = x + (size_t)(t0 + tl) * H8 + h0 / 8;
-                a = load16<EP_DISPATCH_NT_LOAD>(src);
-                b = load16<EP_DISPATCH_NT_LOAD>(src + 1);
-            }
-            const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-            float f[16];
-            uint32_t m = 0;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                f[2 * k] = bf16_lo(w[k]);
-                f[2 * k + 1] = bf16_hi(w[k]);
-                m = max(m, (w[k] << 16) & 0x7FFFFFFFu);
-                m = max(m, w[k] & 0x7FFF0000u);
-            }
-            const float amax = group8_max(__uint_as_float(m));   // |x| bits: integer order
-            const float scale = amax / 448.0f;
-            uint32_t q[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const uint32_t code = (amax == 0.0f) ? ((__float_as_uint(f[k]) >> 24) & 0x80u)
-                                                     : e4m3_rne_sat(f[k] / scale);
-                q[k / 4] |= code << (8 * (k % 4));
-            }
-            const u32x4 qv = {q[0], q[1], q[2], q[3]};
-            const int npg = MULTI ? (K + KG - 1) / KG : 1;
-            for (int pg = 0; pg < npg; ++pg) {
-                int r[KG];
-                token_rows<KG>(rows, tl, pg * KG, K, r);
-#pragma unroll
-                for (int g = 0; g < KG; ++g) {
-                    if (r[g] < 0 || !act) continue;
-                    store16<EP_DISPATCH_NT_STORE>(recv_q + (size_t)r[g] * H16 + h0 / 16, qv);
-                    if ((lane & 7) == 0) recv_scale[(size_t)r[g] * NB + h0 / 128] = scale;
-                }
-            }
+            dispatch_item_fp8<KG, MULTI>(x, recv_q, recv_scale, rows, t0 + tl, tl,
+                                         item - tl * nseg, H, K);
         }
     }
 }
@@ -213,15 +110,6 @@ dim3 grid_for(int T, int tpb)
     const int groups = ceil_div(T, tpb);
     return dim3(EP_DISPATCH_MAX_BLOCKS ? min(groups, EP_DISPATCH_MAX_BLOCKS) : groups);
 }
-
-#define EP_BY_K(K, LAUNCH)                                                                  \
-    do {                                                                                    \
-        if ((K) > 8) LAUNCH(8, true);                                                       \
-        if ((K) > 4) LAUNCH(8, false);                                                      \
-        if ((K) > 2) LAUNCH(4, false);                                                      \
-        if ((K) > 1) LAUNCH(2, false);                                                      \
-        LAUNCH(1, false);                                                                   \
-    } while (0)
 
 template <int U>
 hipError_t launch_bf16_u(const ep_shape_t &s, const u32x4 *x, const int32_t *idx,

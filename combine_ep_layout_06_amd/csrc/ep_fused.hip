@@ -1,0 +1,137 @@
+// Layout and dispatch fused into one kernel on gfx950.
+//
+// The "normal" EP APIs compute the dispatch layout before dispatch inside one boundary
+// (awsome-distributed-ai PR #1238, "What changed"). Here each workgroup of 1024 lanes owns a
+// tile of TT tokens (TT*K pairs): it computes the slots of its own pairs exactly as the
+// standalone layout does (layout_tile: a histogram of all earlier pairs, then ballot ranks
+// inside the tile; no workgroup waits on another), keeps their receive rows in LDS, and
+// immediately copies (bf16) or quantises and copies (FP8) its tokens' rows into the receive
+// buffer. The workgroup of the last tile also writes counts, offsets, per-rank sums and stats.
+// The results are identical to ep_layout followed by ep_dispatch / ep_dispatch_fp8.
+//
+// Why: the standalone layout is a separate launch (~2.5 µs of launch floor on MI355X) whose
+// latency the row copies then wait for. Fused, each tile starts copying as soon as its own
+// slots are known, so the layout of later tiles overlaps the copies of earlier ones.
+#include "ep_dispatch_item.h"
+#include "ep_internal.h"
+#include "ep_layout_tile.h"
+
+#ifndef EP_FUSED_TT
+#define EP_FUSED_TT 0        // tokens per tile (0 = choose from the shape)
+#endif
+
+namespace ep {
+
+namespace {
+
+template <int KG, int U, bool MULTI>
+__global__ __launch_bounds__(kTileThreads) void layout_dispatch_bf16_kernel(
+    const u32x4 *__restrict__ x, const int32_t *__restrict__ idx, LayoutOut o,
+    u32x4 *__restrict__ recv, int T, int H8, int E, int C, int K, int R, int nbits, int TT,
+    int nseg)
+{
+    __shared__ LayoutLds L;
+    __shared__ int32_t rows[kTileThreads];
+    const int TK = T * K;
+    const bool last = blockIdx.x == gridDim.x - 1;
+    const int t0 = blockIdx.x * TT;
+    const int nt = min(TT, T - t0);
+    layout_tile(idx, TK, E, C, nbits, t0 * K, TT * K, last, L, o.slot, rows);
+    const int wave = wave_uniform(threadIdx.x / kWave);
+    for (int item = wave; item < nt * nseg; item += kTileWaves) {
+        const int tl = item / nseg;
+        dispatch_item_bf16<KG, U, MULTI>(x, recv, rows, t0 + tl, tl, item - tl * nseg, H8, K);
+    }
+    if (last) layout_finish(TK, E, C, R, L, o);
+}
+
+template <int KG, bool MULTI>
+__global__ __launch_bounds__(kTileThreads) void layout_dispatch_fp8_kernel(
+    const u32x4 *__restrict__ x, const int32_t *__restrict__ idx, LayoutOut o,
+    u32x4 *__restrict__ recv_q, float *__restrict__ recv_scale, int T, int H, int E, int C,
+    int K, int R, int nbits, int TT, int nseg)
+{
+    __shared__ LayoutLds L;
+    __shared__ int32_t rows[kTileThreads];
+    const int TK = T * K;
+    const bool last = blockIdx.x == gridDim.x - 1;
+    const int t0 = blockIdx.x * TT;
+    const int nt = min(TT, T - t0);
+    layout_tile(idx, TK, E, C, nbits, t0 * K, TT * K, last, L, o.slot, rows);
+    const int wave = wave_uniform(threadIdx.x / kWave);
+    for (int item = wave; item < nt * nseg; item += kTileWaves) {
+        const int tl = item / nseg;
+        dispatch_item_fp8<KG, MULTI>(x, recv_q, recv_scale, rows, t0 + tl, tl, item - tl * nseg,
+                                     H, K);
+    }
+    if (last) layout_finish(TK, E, C, R, L, o);
+}
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Tokens per tile: a multiple of 4 (tile starts stay 16-byte aligned in topk_idx) with
+// TT*K <= 1024 pairs; small batches use small tiles so more workgroups share the copies.
+int pick_tt(int T, int K)
+{
+    int tt = EP_FUSED_TT ? EP_FUSED_TT : (T >= 2048 ? 16 : 4);
+    while (tt > 4 && tt * K > kTileThreads) tt -= 4;
+    return tt;
+}
+
+// Chunks per lane so that a tile has about one item per wavefront.
+int pick_u(int TT, int H8)
+{
+    const int nseg_target = TT >= kTileWaves ? 1 : kTileWaves / TT;
+    const int u = ceil_div(H8, kWave * nseg_target);
+    return u >= 4 ? 4 : (u >= 2 ? 2 : 1);
+}
+
+template <int U>
+hipError_t launch_bf16_u(const ep_shape_t &s, const u32x4 *x, const int32_t *idx,
+                         const LayoutOut &o, u32x4 *recv, int H8, int TT, int nseg,
+                         hipStream_t stream)
+{
+    const dim3 grid(s.T > 0 ? ceil_div(s.T, TT) : 1), block(kTileThreads);
+    const int nbits = expert_bits(s.E);
+#define EP_LAUNCH_FUSED_BF16(KG, MULTI)                                                         \
+    return launch(layout_dispatch_bf16_kernel<KG, U, MULTI>, grid, block, 0, stream, x, idx, o, \
+                  recv, s.T, H8, s.E, s.C, s.K, s.R, nbits, TT, nseg)
+    EP_BY_K(s.K, EP_LAUNCH_FUSED_BF16);
+#undef EP_LAUNCH_FUSED_BF16
+}
+
+}  // namespace
+
+hipError_t launch_layout_dispatch_bf16(const ep_shape_t &s, const uint16_t *x,
+                                       const int32_t *idx, const LayoutOut &o, uint16_t *recv,
+                                       hipStream_t stream)
+{
+    const int H8 = s.H / 8;
+    const int TT = pick_tt(s.T, s.K);
+    const int U = pick_u(TT, H8);
+    const int nseg = ceil_div(H8, U * kWave);
+    const u32x4 *xv = reinterpret_cast<const u32x4 *>(x);
+    u32x4 *rv = reinterpret_cast<u32x4 *>(recv);
+    if (U >= 4) return launch_bf16_u<4>(s, xv, idx, o, rv, H8, TT, nseg, stream);
+    if (U == 2) return launch_bf16_u<2>(s, xv, idx, o, rv, H8, TT, nseg, stream);
+    return launch_bf16_u<1>(s, xv, idx, o, rv, H8, TT, nseg, stream);
+}
+
+hipError_t launch_layout_dispatch_fp8(const ep_shape_t &s, const uint16_t *x, const int32_t *idx,
+                                      const LayoutOut &o, uint8_t *recv_q, float *recv_scale,
+                                      hipStream_t stream)
+{
+    const int TT = pick_tt(s.T, s.K);
+    const int nseg = ceil_div(s.H, 16 * kWave);
+    const dim3 grid(s.T > 0 ? ceil_div(s.T, TT) : 1), block(kTileThreads);
+    const int nbits = expert_bits(s.E);
+    const u32x4 *xv = reinterpret_cast<const u32x4 *>(x);
+    u32x4 *qv = reinterpret_cast<u32x4 *>(recv_q);
+#define EP_LAUNCH_FUSED_FP8(KG, MULTI)                                                          \
+    return launch(layout_dispatch_fp8_kernel<KG, MULTI>, grid, block, 0, stream, xv, idx, o,   \
+                  qv, recv_scale, s.T, s.H, s.E, s.C, s.K, s.R, nbits, TT, nseg)
+    EP_BY_K(s.K, EP_LAUNCH_FUSED_FP8);
+#undef EP_LAUNCH_FUSED_FP8
+}
+
+}  // namespace ep

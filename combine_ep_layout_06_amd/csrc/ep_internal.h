@@ -32,6 +32,11 @@ inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t
                            stream);
 }
 
+// Outputs of the layout (see ep_layout in ep.h); rank_count / rank_offset may be null.
+struct LayoutOut {
+    int32_t *slot, *count, *offset, *rank_count, *rank_offset, *stats;
+};
+
 hipError_t launch_layout(const ep_shape_t &s, const int32_t *idx, int32_t *slot, int32_t *count,
                          int32_t *offset, int32_t *rank_count, int32_t *rank_offset,
                          int32_t *stats, hipStream_t stream);
@@ -42,6 +47,14 @@ hipError_t launch_dispatch_bf16(const ep_shape_t &s, const uint16_t *x, const in
 hipError_t launch_dispatch_fp8(const ep_shape_t &s, const uint16_t *x, const int32_t *idx,
                                const int32_t *slot, uint8_t *recv_q, float *recv_scale,
                                hipStream_t stream);
+
+hipError_t launch_layout_dispatch_bf16(const ep_shape_t &s, const uint16_t *x,
+                                       const int32_t *idx, const LayoutOut &o, uint16_t *recv,
+                                       hipStream_t stream);
+
+hipError_t launch_layout_dispatch_fp8(const ep_shape_t &s, const uint16_t *x, const int32_t *idx,
+                                      const LayoutOut &o, uint8_t *recv_q, float *recv_scale,
+                                      hipStream_t stream);
 
 hipError_t launch_combine(const ep_shape_t &s, const uint16_t *y, const int32_t *idx,
                           const int32_t *slot, const float *w, uint16_t *out,

@@ -128,6 +128,32 @@ int ep_dispatch_fp8(const ep_shape_t *shape, const uint16_t *x, const int32_t *t
                     hipStream_t stream);
 
 /*
+ * ep_layout_dispatch -- ep_layout and ep_dispatch in one launch.
+ *
+ * The layout is computed inside the same boundary as dispatch, as the "normal" EP APIs require
+ * (awsome-distributed-ai PR #1238, "What changed"). Every output (slot, expert_count,
+ * expert_offset, rank_count, rank_offset, stats, recv) is bit-identical to calling ep_layout
+ * and then ep_dispatch with the same arguments. Each workgroup computes the slots of its own
+ * tile of tokens and copies those tokens' rows at once, so there is no second launch and no
+ * wait for the whole layout. Arguments, layouts, alignment and limits are the union of the two
+ * calls' (E <= EP_MAX_EXPERTS, K <= EP_MAX_TOPK, H % 8 == 0, topk_idx / x / recv 16-byte
+ * aligned).
+ */
+int ep_layout_dispatch(const ep_shape_t *shape, const uint16_t *x, const int32_t *topk_idx,
+                       int32_t *slot, int32_t *expert_count, int32_t *expert_offset,
+                       int32_t *rank_count, int32_t *rank_offset, int32_t *stats,
+                       uint16_t *recv, hipStream_t stream);
+
+/*
+ * ep_layout_dispatch_fp8 -- ep_layout and ep_dispatch_fp8 in one launch; bit-identical to the
+ * two calls in sequence. Requires H % 128 == 0 in addition; recv_scale 4-byte aligned.
+ */
+int ep_layout_dispatch_fp8(const ep_shape_t *shape, const uint16_t *x, const int32_t *topk_idx,
+                           int32_t *slot, int32_t *expert_count, int32_t *expert_offset,
+                           int32_t *rank_count, int32_t *rank_offset, int32_t *stats,
+                           uint8_t *recv_q, float *recv_scale, hipStream_t stream);
+
+/*
  * ep_combine -- top-k weighted gather-reduce of expert outputs back onto each token.
  *
  * Combine gathers the expert outputs and reduces them with the top-k weights on the token's

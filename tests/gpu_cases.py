@@ -143,6 +143,48 @@ class Case:
         sc.view(E * C, NB).index_fill_(0, rows, SENTINEL_F32)
         assert int((q != SENTINEL8).sum()) == 0 and int((sc != SENTINEL_F32).sum()) == 0
 
+    def check_fused(self, fp8: bool, full: bool):
+        """ep_layout_dispatch[_fp8]: every layout output bit-equal to the oracle's, and the
+        receive buffers exactly as the separate dispatch must leave them."""
+        E, C, H, R = self.E, self.C, self.H, self.R
+        i, s = kept_pairs(self.lay)
+        e = self.idx.reshape(-1)[i]
+        rows = torch.from_numpy((e.astype(np.int64) * C + s)).to(dev())
+        if fp8:
+            NB = H // 128
+            q = torch.full((E, C, H), SENTINEL8, dtype=torch.uint8, device=dev())
+            sc = torch.full((E, C, NB), SENTINEL_F32, dtype=torch.float32, device=dev())
+            g = B.ep_layout_dispatch_fp8(self.x_d, self.idx_d, q, sc, E, C, R)
+        else:
+            recv = torch.full((E, C, H), SENTINEL16, dtype=torch.int16, device=dev())
+            g = B.ep_layout_dispatch(self.x_d, self.idx_d, recv, E, C, R)
+        torch.cuda.synchronize()
+        check_layout(self.idx, E, C, R, g)
+        if fp8:
+            wq = np.full((E, C, H), SENTINEL8, dtype=np.uint8) if full else np.empty((E, C, H), np.uint8)
+            ws = (np.full((E, C, NB), SENTINEL_F32, dtype=np.float32) if full
+                  else np.empty((E, C, NB), np.float32))
+            oracle.dispatch_fp8(self.x, self.idx, self.lay["slot"], E, C, wq, ws)
+            if full:
+                assert np.array_equal(to_np(q), wq) and np.array_equal(to_np(sc).view(np.uint32), ws.view(np.uint32))
+                return
+            assert np.array_equal(to_np(q.view(E * C, H).index_select(0, rows)), wq[e, s])
+            assert np.array_equal(to_np(sc.view(E * C, NB).index_select(0, rows)).view(np.uint32),
+                                  ws[e, s].view(np.uint32))
+            q.view(E * C, H).index_fill_(0, rows, SENTINEL8)
+            sc.view(E * C, NB).index_fill_(0, rows, SENTINEL_F32)
+            assert int((q != SENTINEL8).sum()) == 0 and int((sc != SENTINEL_F32).sum()) == 0
+        else:
+            want = np.full((E, C, H), SENTINEL16, dtype=np.uint16) if full else np.empty((E, C, H), np.uint16)
+            oracle.dispatch(self.x, self.idx, self.lay["slot"], E, C, want)
+            if full:
+                assert np.array_equal(to_np(recv).view(np.uint16), want)
+                return
+            got = to_np(recv.view(E * C, H).index_select(0, rows)).view(np.uint16)
+            assert np.array_equal(got, want[e, s])
+            recv.view(E * C, H).index_fill_(0, rows, SENTINEL16)
+            assert int((recv != SENTINEL16).sum()) == 0
+
     def make_y(self):
         """y on host and device: kept rows from the seeded expert-output stream, in pair
         order; every other row NaN on the device (and never read by the oracle)."""

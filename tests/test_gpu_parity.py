@@ -48,6 +48,16 @@ def test_config_full_path(name):
         assert case.lay["stats"]["dropped"] > 0
 
 
+@pytest.mark.parametrize("name", FULL_CONFIGS)
+def test_config_fused_layout_dispatch(name):
+    """ep_layout_dispatch[_fp8] on the full workloads, in both dispatch dtypes."""
+    cfg = W.get_config(name)
+    print(f"[parity] fused {name}", flush=True)
+    case = G.Case.from_config(cfg)
+    case.check_fused(fp8=False, full=False)
+    case.check_fused(fp8=True, full=False)
+
+
 @pytest.mark.parametrize("name", ["decode_bf16", "prefill_fp8"])
 def test_config_other_dispatch_dtype(name):
     """The dispatch dtype a workload does not use in the benchmark, for coverage."""
@@ -79,8 +89,10 @@ def test_small_random_routes(T, H, E, K, C, R):
     print(f"[parity] small T={T} H={H} E={E} K={K} C={C} R={R}", flush=True)
     case = G.Case.random(T, H, E, K, C, R, seed=T + H)
     case.check_dispatch_bf16(full=True)
+    case.check_fused(fp8=False, full=True)
     if H % 128 == 0:
         case.check_dispatch_fp8(full=True)
+        case.check_fused(fp8=True, full=True)
     got, want = case.check_combine()
     assert np.array_equal(got, want)
 
@@ -94,6 +106,11 @@ def test_empty_tokens():
     assert G.to_np(g["stats"]).tolist() == [0, 0, 0, 0]
     x = torch.zeros((0, 256), dtype=torch.int16, device="cuda")
     recv = torch.full((16, 4, 256), G.SENTINEL16, dtype=torch.int16, device="cuda")
+    gf = B.ep_layout_dispatch(x, idx, recv, 16, 4, 4,
+                              expert_count=torch.full((16,), 7, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert G.to_np(gf["expert_count"]).tolist() == [0] * 16
+    assert G.to_np(gf["stats"]).tolist() == [0, 0, 0, 0]
     B.ep_dispatch(x, idx, g["slot"], recv, 4)
     out = B.ep_combine(recv, idx, g["slot"], torch.zeros((0, 8), device="cuda"), 4)
     torch.cuda.synchronize()
@@ -114,6 +131,8 @@ def test_all_unrouted_and_all_to_one_expert():
     assert case.lay["stats"]["dropped"] == T * K - C
     case.check_dispatch_bf16(full=True)
     case.check_dispatch_fp8(full=True)
+    case.check_fused(fp8=False, full=True)
+    case.check_fused(fp8=True, full=True)
     case.check_combine()
 
 
@@ -125,6 +144,7 @@ def test_max_experts_and_many_pairs():
                   inp["topk_w"])
     assert case.lay["stats"]["dropped"] > 0
     case.check_dispatch_bf16(full=False)
+    case.check_fused(fp8=False, full=False)
     case.check_combine()
 
 
@@ -161,6 +181,7 @@ def test_fp8_every_bf16_value_through_the_quantiser():
         idx = (np.arange(T, dtype=np.int32) % 4)[:, None]
         case = G.Case(T, H, 4, 1, T, 1, x, idx, np.ones((T, 1), np.float32))
         case.check_dispatch_fp8(full=True)
+        case.check_fused(fp8=True, full=True)
 
 
 def test_fp8_degenerate_blocks():
@@ -176,6 +197,7 @@ def test_fp8_degenerate_blocks():
     idx = np.array([[0, 1], [1, 0], [0, 1]], dtype=np.int32)
     case = G.Case(3, H, 2, 2, 4, 1, x, idx, np.ones((3, 2), np.float32))
     case.check_dispatch_fp8(full=True)
+    case.check_fused(fp8=True, full=True)
 
 
 def test_combine_identity_law_on_gpu():
