@@ -399,6 +399,8 @@ def main():
                    "parallelism": "single GPU"},
         "hbm_roofline_frac": r["hbm_frac"],
         "us_per_step": r["us_per_step"],
+        "kernel_avg_us": r["kernel_avg_us"],
+        "kernel_GBps": r["kernel_GBps"],
         "rotating_all_buffers": r.get("rotating_all_buffers"),
         "three_call_step": r.get("three_call_step"),
         "t128_us": {n: brief(n) for n in ("decode_bf16", "decode_fp8") if n in results},

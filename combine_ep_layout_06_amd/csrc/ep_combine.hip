@@ -23,7 +23,8 @@
 // Measured on MI355X, this kernel reaches ~94% of a bare probe of the same access pattern
 // (eight random 4 KiB rows read per contiguous row written); a per-wavefront variant that
 // prefetched the next token's metadata through scalar loads instead of LDS staging was no
-// faster.
+// faster, and neither was a wave-uniform branch around each pair's fold in place of the
+// per-element select.
 #include "ep_device.h"
 #include "ep_internal.h"
 

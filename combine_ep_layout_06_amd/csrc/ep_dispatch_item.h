@@ -50,21 +50,35 @@ __device__ __forceinline__ void token_rows(const int32_t *rows, int tl, int j0, 
     }
 }
 
-// bf16: segment `seg` (U chunks per lane) of token t (local index tl).
-// KG: pairs per group (K <= KG unless MULTI).
-template <int KG, int U, bool MULTI>
-__device__ __forceinline__ void dispatch_item_bf16(const u32x4 *__restrict__ x,
-                                                   u32x4 *__restrict__ recv, const int32_t *rows,
-                                                   int t, int tl, int seg, int H8, int K)
+// bf16 item, split in two so a caller can issue the loads before it knows the slots:
+// segment `seg` (U chunks per lane) of token t (local index tl).
+template <int U>
+struct RowPiece {
+    u32x4 v[U];
+};
+
+template <int U>
+__device__ __forceinline__ RowPiece<U> load_item_bf16(const u32x4 *__restrict__ x, int t,
+                                                      int seg, int H8)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const u32x4 *src = x + (size_t)t * H8;
-    u32x4 v[U];
+    RowPiece<U> p;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int c = (seg * U + u) * kWave + lane;
-        v[u] = load16<EP_DISPATCH_NT_LOAD>(src + (c < H8 ? c : H8 - 1));
+        p.v[u] = load16<EP_DISPATCH_NT_LOAD>(src + (c < H8 ? c : H8 - 1));
     }
+    return p;
+}
+
+// KG: pairs per group (K <= KG unless MULTI).
+template <int KG, int U, bool MULTI>
+__device__ __forceinline__ void store_item_bf16(const RowPiece<U> &p, u32x4 *__restrict__ recv,
+                                                const int32_t *rows, int tl, int seg, int H8,
+                                                int K)
+{
+    const int lane = threadIdx.x & (kWave - 1);
     const int npg = MULTI ? (K + KG - 1) / KG : 1;
     for (int pg = 0; pg < npg; ++pg) {
         int r[KG];
@@ -76,31 +90,54 @@ __device__ __forceinline__ void dispatch_item_bf16(const u32x4 *__restrict__ x,
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int c = (seg * U + u) * kWave + lane;
-                if (c < H8) store16<EP_DISPATCH_NT_STORE>(dst + c, v[u]);
+                if (c < H8) store16<EP_DISPATCH_NT_STORE>(dst + c, p.v[u]);
             }
         }
     }
 }
 
-// FP8: segment `seg` (1024 channels) of token t (local index tl); H % 128 == 0.
-template <int KG, bool MULTI>
-__device__ __forceinline__ void dispatch_item_fp8(const u32x4 *__restrict__ x,
-                                                  u32x4 *__restrict__ recv_q,
-                                                  float *__restrict__ recv_scale,
-                                                  const int32_t *rows, int t, int tl, int seg,
-                                                  int H, int K)
+template <int KG, int U, bool MULTI>
+__device__ __forceinline__ void dispatch_item_bf16(const u32x4 *__restrict__ x,
+                                                   u32x4 *__restrict__ recv, const int32_t *rows,
+                                                   int t, int tl, int seg, int H8, int K)
+{
+    store_item_bf16<KG, U, MULTI>(load_item_bf16<U>(x, t, seg, H8), recv, rows, tl, seg, H8, K);
+}
+
+// FP8 item, split in three: the row load, the cast (which needs only the row) and the stores
+// (which need the slots). Segment `seg` (1024 channels) of token t; H % 128 == 0.
+struct RawPieceFp8 {
+    u32x4 a, b;       // this lane's 16 channels, zero where it has none
+    bool act;         // this lane's channels exist (whole 8-lane groups)
+};
+
+struct QuantPiece {
+    u32x4 q;          // 16 codes of this lane's channels
+    float scale;      // scale of this lane's 128-channel block
+    bool act;
+};
+
+__device__ __forceinline__ RawPieceFp8 load_item_fp8(const u32x4 *__restrict__ x, int t, int seg,
+                                                     int H)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int H8 = H / 8, H16 = H / 16, NB = H / 128;
     const int h0 = seg * (16 * kWave) + lane * 16;   // first channel of this lane
-    const bool act = h0 < H;                         // whole 8-lane groups (H % 128 == 0)
-    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (act) {
-        const u32x4 *src = x + (size_t)t * H8 + h0 / 8;
-        a = load16<EP_DISPATCH_NT_LOAD>(src);
-        b = load16<EP_DISPATCH_NT_LOAD>(src + 1);
+    RawPieceFp8 r;
+    r.act = h0 < H;
+    r.a = u32x4{0u, 0u, 0u, 0u};
+    r.b = r.a;
+    if (r.act) {
+        const u32x4 *src = x + (size_t)t * (H / 8) + h0 / 8;
+        r.a = load16<EP_DISPATCH_NT_LOAD>(src);
+        r.b = load16<EP_DISPATCH_NT_LOAD>(src + 1);
     }
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    return r;
+}
+
+// All 64 lanes take part (the block amax is a DPP max over 8 lanes).
+__device__ __forceinline__ QuantPiece cast_item_fp8(const RawPieceFp8 &r)
+{
+    const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
     float f[16];
     uint32_t m = 0;
 #pragma unroll
@@ -111,26 +148,56 @@ __device__ __forceinline__ void dispatch_item_fp8(const u32x4 *__restrict__ x,
         m = max(m, w[k] & 0x7FFF0000u);
     }
     const float amax = group8_max(__uint_as_float(m));   // |x| bits: integer order
-    const float scale = amax / 448.0f;
+    QuantPiece p;
+    p.act = r.act;
+    p.scale = amax / 448.0f;
     uint32_t q[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
         const uint32_t code = (amax == 0.0f) ? ((__float_as_uint(f[k]) >> 24) & 0x80u)
-                                             : e4m3_rne_sat(f[k] / scale);
+                                             : e4m3_rne_sat(f[k] / p.scale);
         q[k / 4] |= code << (8 * (k % 4));
     }
-    const u32x4 qv = {q[0], q[1], q[2], q[3]};
+    p.q = u32x4{q[0], q[1], q[2], q[3]};
+    return p;
+}
+
+__device__ __forceinline__ QuantPiece quant_item_fp8(const u32x4 *__restrict__ x, int t, int seg,
+                                                     int H)
+{
+    return cast_item_fp8(load_item_fp8(x, t, seg, H));
+}
+
+template <int KG, bool MULTI>
+__device__ __forceinline__ void store_item_fp8(const QuantPiece &p, u32x4 *__restrict__ recv_q,
+                                               float *__restrict__ recv_scale,
+                                               const int32_t *rows, int tl, int seg, int H, int K)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int H16 = H / 16, NB = H / 128;
+    const int h0 = seg * (16 * kWave) + lane * 16;
     const int npg = MULTI ? (K + KG - 1) / KG : 1;
     for (int pg = 0; pg < npg; ++pg) {
         int r[KG];
         token_rows<KG>(rows, tl, pg * KG, K, r);
 #pragma unroll
         for (int g = 0; g < KG; ++g) {
-            if (r[g] < 0 || !act) continue;
-            store16<EP_DISPATCH_NT_STORE>(recv_q + (size_t)r[g] * H16 + h0 / 16, qv);
-            if ((lane & 7) == 0) recv_scale[(size_t)r[g] * NB + h0 / 128] = scale;
+            if (r[g] < 0 || !p.act) continue;
+            store16<EP_DISPATCH_NT_STORE>(recv_q + (size_t)r[g] * H16 + h0 / 16, p.q);
+            if ((lane & 7) == 0) recv_scale[(size_t)r[g] * NB + h0 / 128] = p.scale;
         }
     }
+}
+
+template <int KG, bool MULTI>
+__device__ __forceinline__ void dispatch_item_fp8(const u32x4 *__restrict__ x,
+                                                  u32x4 *__restrict__ recv_q,
+                                                  float *__restrict__ recv_scale,
+                                                  const int32_t *rows, int t, int tl, int seg,
+                                                  int H, int K)
+{
+    store_item_fp8<KG, MULTI>(quant_item_fp8(x, t, seg, H), recv_q, recv_scale, rows, tl, seg, H,
+                              K);
 }
 
 // Instantiate LAUNCH(KG, MULTI) for the pair-group size that fits K.

@@ -11,7 +11,9 @@
 //
 // Why: the standalone layout is a separate launch (~2.5 µs of launch floor on MI355X) whose
 // latency the row copies then wait for. Fused, each tile starts copying as soon as its own
-// slots are known, so the layout of later tiles overlaps the copies of earlier ones.
+// slots are known, so the layout of later tiles overlaps the copies of earlier ones; and in the
+// bf16 kernel each wavefront issues its first row piece's loads together with the layout's own
+// loads, since only the stores need the slots.
 #include "ep_dispatch_item.h"
 #include "ep_internal.h"
 #include "ep_layout_tile.h"
@@ -27,53 +29,68 @@ namespace {
 template <int KG, int U, bool MULTI>
 __global__ __launch_bounds__(kTileThreads) void layout_dispatch_bf16_kernel(
     const u32x4 *__restrict__ x, const int32_t *__restrict__ idx, LayoutOut o,
-    u32x4 *__restrict__ recv, int T, int H8, int E, int C, int K, int R, int nbits, int TT,
-    int nseg)
+    u32x4 *__restrict__ recv, int T, int H8, int E, int C, int K, int R, int nbits, int lg_nc,
+    int TT, int nseg)
 {
-    __shared__ LayoutLds L;
+    extern __shared__ __align__(16) int32_t lds[];
     __shared__ int32_t rows[kTileThreads];
+    const LayoutLdsMap m = layout_lds_map(E, lg_nc);
     const int TK = T * K;
     const bool last = blockIdx.x == gridDim.x - 1;
     const int t0 = blockIdx.x * TT;
     const int nt = min(TT, T - t0);
-    layout_tile(idx, TK, E, C, nbits, t0 * K, TT * K, last, L, o.slot, rows);
     const int wave = wave_uniform(threadIdx.x / kWave);
-    for (int item = wave; item < nt * nseg; item += kTileWaves) {
+    const int nitems = nt * nseg;
+    // the first item's row loads do not depend on the slots: they are issued before the
+    // layout's own loads (which the layout waits for in full), so both round trips overlap
+    RowPiece<U> first;
+    if (wave < nitems) first = load_item_bf16<U>(x, t0 + wave / nseg, wave % nseg, H8);
+    const TileIds ids = layout_tile_loads(idx, TK, t0 * K, TT * K);
+    layout_tile(ids, idx, TK, E, C, nbits, t0 * K, TT * K, last, lds, m, o.slot, rows);
+    if (wave < nitems)
+        store_item_bf16<KG, U, MULTI>(first, recv, rows, wave / nseg, wave % nseg, H8, K);
+    for (int item = wave + kTileWaves; item < nitems; item += kTileWaves) {
         const int tl = item / nseg;
         dispatch_item_bf16<KG, U, MULTI>(x, recv, rows, t0 + tl, tl, item - tl * nseg, H8, K);
     }
-    if (last) layout_finish(TK, E, C, R, L, o);
+    if (last) layout_finish(TK, E, C, R, lds, m, o);
 }
 
 template <int KG, bool MULTI>
 __global__ __launch_bounds__(kTileThreads) void layout_dispatch_fp8_kernel(
     const u32x4 *__restrict__ x, const int32_t *__restrict__ idx, LayoutOut o,
     u32x4 *__restrict__ recv_q, float *__restrict__ recv_scale, int T, int H, int E, int C,
-    int K, int R, int nbits, int TT, int nseg)
+    int K, int R, int nbits, int lg_nc, int TT, int nseg)
 {
-    __shared__ LayoutLds L;
+    extern __shared__ __align__(16) int32_t lds[];
     __shared__ int32_t rows[kTileThreads];
+    const LayoutLdsMap m = layout_lds_map(E, lg_nc);
     const int TK = T * K;
     const bool last = blockIdx.x == gridDim.x - 1;
     const int t0 = blockIdx.x * TT;
     const int nt = min(TT, T - t0);
-    layout_tile(idx, TK, E, C, nbits, t0 * K, TT * K, last, L, o.slot, rows);
     const int wave = wave_uniform(threadIdx.x / kWave);
-    for (int item = wave; item < nt * nseg; item += kTileWaves) {
+    const int nitems = nt * nseg;
+    // (loading the first row before the layout, as the bf16 kernel does, measured slower here)
+    const TileIds ids = layout_tile_loads(idx, TK, t0 * K, TT * K);
+    layout_tile(ids, idx, TK, E, C, nbits, t0 * K, TT * K, last, lds, m, o.slot, rows);
+    for (int item = wave; item < nitems; item += kTileWaves) {
         const int tl = item / nseg;
         dispatch_item_fp8<KG, MULTI>(x, recv_q, recv_scale, rows, t0 + tl, tl, item - tl * nseg,
                                      H, K);
     }
-    if (last) layout_finish(TK, E, C, R, L, o);
+    if (last) layout_finish(TK, E, C, R, lds, m, o);
 }
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Tokens per tile: a multiple of 4 (tile starts stay 16-byte aligned in topk_idx) with
-// TT*K <= 1024 pairs; small batches use small tiles so more workgroups share the copies.
-int pick_tt(int T, int K)
+// TT*K <= 1024 pairs. Small batches use small tiles so more workgroups share the copies; on
+// large ones (measured on MI355X at T = 4096) bf16 rows do best at 8 tokens per tile (two
+// workgroups per CU, one copying while the other is in its layout), FP8 rows at 16.
+int pick_tt(int T, int K, bool fp8)
 {
-    int tt = EP_FUSED_TT ? EP_FUSED_TT : (T >= 2048 ? 16 : 4);
+    int tt = EP_FUSED_TT ? EP_FUSED_TT : (T >= 2048 ? (fp8 ? 16 : 8) : 4);
     while (tt > 4 && tt * K > kTileThreads) tt -= 4;
     return tt;
 }
@@ -92,10 +109,11 @@ hipError_t launch_bf16_u(const ep_shape_t &s, const u32x4 *x, const int32_t *idx
                          hipStream_t stream)
 {
     const dim3 grid(s.T > 0 ? ceil_div(s.T, TT) : 1), block(kTileThreads);
-    const int nbits = expert_bits(s.E);
+    const int nbits = expert_bits(s.E), lg_nc = layout_lg_nc(s.E);
+    const size_t lds = layout_lds_bytes(s.E, lg_nc);
 #define EP_LAUNCH_FUSED_BF16(KG, MULTI)                                                         \
-    return launch(layout_dispatch_bf16_kernel<KG, U, MULTI>, grid, block, 0, stream, x, idx, o, \
-                  recv, s.T, H8, s.E, s.C, s.K, s.R, nbits, TT, nseg)
+    return launch(layout_dispatch_bf16_kernel<KG, U, MULTI>, grid, block, lds, stream, x, idx,  \
+                  o, recv, s.T, H8, s.E, s.C, s.K, s.R, nbits, lg_nc, TT, nseg)
     EP_BY_K(s.K, EP_LAUNCH_FUSED_BF16);
 #undef EP_LAUNCH_FUSED_BF16
 }
@@ -107,7 +125,7 @@ hipError_t launch_layout_dispatch_bf16(const ep_shape_t &s, const uint16_t *x,
                                        hipStream_t stream)
 {
     const int H8 = s.H / 8;
-    const int TT = pick_tt(s.T, s.K);
+    const int TT = pick_tt(s.T, s.K, false);
     const int U = pick_u(TT, H8);
     const int nseg = ceil_div(H8, U * kWave);
     const u32x4 *xv = reinterpret_cast<const u32x4 *>(x);
@@ -121,15 +139,16 @@ hipError_t launch_layout_dispatch_fp8(const ep_shape_t &s, const uint16_t *x, co
                                       const LayoutOut &o, uint8_t *recv_q, float *recv_scale,
                                       hipStream_t stream)
 {
-    const int TT = pick_tt(s.T, s.K);
+    const int TT = pick_tt(s.T, s.K, true);
     const int nseg = ceil_div(s.H, 16 * kWave);
     const dim3 grid(s.T > 0 ? ceil_div(s.T, TT) : 1), block(kTileThreads);
-    const int nbits = expert_bits(s.E);
+    const int nbits = expert_bits(s.E), lg_nc = layout_lg_nc(s.E);
+    const size_t lds = layout_lds_bytes(s.E, lg_nc);
     const u32x4 *xv = reinterpret_cast<const u32x4 *>(x);
     u32x4 *qv = reinterpret_cast<u32x4 *>(recv_q);
 #define EP_LAUNCH_FUSED_FP8(KG, MULTI)                                                          \
-    return launch(layout_dispatch_fp8_kernel<KG, MULTI>, grid, block, 0, stream, xv, idx, o,   \
-                  qv, recv_scale, s.T, s.H, s.E, s.C, s.K, s.R, nbits, TT, nseg)
+    return launch(layout_dispatch_fp8_kernel<KG, MULTI>, grid, block, lds, stream, xv, idx, o, \
+                  qv, recv_scale, s.T, s.H, s.E, s.C, s.K, s.R, nbits, lg_nc, TT, nseg)
     EP_BY_K(s.K, EP_LAUNCH_FUSED_FP8);
 #undef EP_LAUNCH_FUSED_FP8
 }

@@ -10,13 +10,17 @@ namespace {
 
 __global__ __launch_bounds__(kTileThreads) void layout_kernel(const int32_t *__restrict__ idx,
                                                                int TK, int E, int C, int R,
-                                                               int nbits, LayoutOut o)
+                                                               int nbits, int lg_nc,
+                                                               LayoutOut o)
 {
-    __shared__ LayoutLds L;
+    extern __shared__ __align__(16) int32_t lds[];
+    const LayoutLdsMap m = layout_lds_map(E, lg_nc);
     const bool last = blockIdx.x == gridDim.x - 1;
-    layout_tile(idx, TK, E, C, nbits, blockIdx.x * kTileThreads, kTileThreads, last, L, o.slot,
+    const int tile_begin = blockIdx.x * kTileThreads;
+    const TileIds ids = layout_tile_loads(idx, TK, tile_begin, kTileThreads);
+    layout_tile(ids, idx, TK, E, C, nbits, tile_begin, kTileThreads, last, lds, m, o.slot,
                 nullptr);
-    if (last) layout_finish(TK, E, C, R, L, o);
+    if (last) layout_finish(TK, E, C, R, lds, m, o);
 }
 
 }  // namespace
@@ -28,8 +32,9 @@ hipError_t launch_layout(const ep_shape_t &s, const int32_t *idx, int32_t *slot,
     const int TK = s.T * s.K;
     const int tiles = TK > 0 ? (TK + kTileThreads - 1) / kTileThreads : 1;
     const LayoutOut o{slot, count, offset, rank_count, rank_offset, stats};
-    return launch(layout_kernel, dim3(tiles), dim3(kTileThreads), 0, stream, idx, TK, s.E, s.C,
-                  s.R, expert_bits(s.E), o);
+    const int lg_nc = layout_lg_nc(s.E);
+    return launch(layout_kernel, dim3(tiles), dim3(kTileThreads), layout_lds_bytes(s.E, lg_nc),
+                  stream, idx, TK, s.E, s.C, s.R, expert_bits(s.E), lg_nc, o);
 }
 
 }  // namespace ep

@@ -7,22 +7,30 @@
 // A tile is the pairs [tile_begin, tile_begin + P), P <= 1024 and a multiple of 4, one pair per
 // lane so lane order is pair order. Bins are the E experts, then two bins that are never ranked:
 // E for invalid ids (outside [0, E) and not -1) and E+1 for unrouted ones (-1).
-//  1. The workgroup counts, per bin, the pairs of all EARLIER tiles: 16-byte id vectors, all in
-//     flight at once, then one LDS atomic per id (the counts do not depend on the order of the
-//     atomics).
+//  0. Every global load the layout needs is issued first, in one go: the ids of the earlier
+//     tiles (16-byte vectors, up to kPrefixVec per lane) and the lane's own id, so the tile pays
+//     one memory round trip before its LDS work.
+//  1. The workgroup counts, per bin, the pairs of all EARLIER tiles with one LDS atomic per id
+//     (the counts do not depend on the order of the atomics) into a replicated histogram: NC
+//     copies of every bin, interleaved, and lane l adds into copy l % NC, so lanes that hit the
+//     same bin hit different banks (on MI355X a single histogram costs ~2.3x more than
+//     conflict-free atomics: random bins collide in the banks; 16 copies bring it to ~1.1x).
 //  2. Inside the tile, each wavefront finds, for every routed lane, the mask of lanes holding
 //     the same expert with one ballot per bit of the expert number (bit-sliced match). The
 //     lane's rank is the number of mask bits below it (v_mbcnt); the lowest lane of each group
 //     writes the group size into a per-wavefront histogram in LDS.
-//  3. A scan over the 16 wavefronts, per expert (16 lanes = one DPP row per expert), turns those
-//     histograms into per-wavefront bases starting from the earlier-tile count, so
+//  3. Per expert, 16 lanes (one DPP row) fold the NC copies into the earlier-tile count and
+//     scan the 16 per-wavefront counts from it, so each wavefront gets its base;
 //     slot = base + rank, or -1 past C.
 // The workgroup of the last tile then holds the total of every bin and finishes the layout:
 //  4. count = min(total, C), its exclusive scan in expert order (DPP wave scans plus wave
 //     totals), the per-rank sums and the stats; dropped = routed - kept.
 // No workgroup waits on another and no result depends on scheduling: the outputs are
 // deterministic and need no workspace. The cost is the pass over all earlier ids, one memory
-// round trip plus ~tile_begin/1024 LDS atomics per lane.
+// round trip plus ~tile_begin/1024 conflict-free LDS atomics per lane.
+//
+// LDS is the launch's dynamic shared memory, carved by layout_lds_map(E, lg_nc); its size grows
+// with E (17 KB at E = 128, 140 KB at E = 1024).
 #pragma once
 
 #include "ep_device.h"
@@ -32,15 +40,57 @@ namespace ep {
 
 constexpr int kTileThreads = 1024;
 constexpr int kTileWaves = kTileThreads / kWave;
-constexpr int kTileMaxBins = EP_MAX_EXPERTS + 2;
-constexpr int kPrefixVec = 8;      // 16-byte id vectors in flight per lane in step 1
+constexpr int kPrefixVec = 8;      // 16-byte id vectors per lane issued up front in step 0
+constexpr int kHistWords = (EP_MAX_EXPERTS + 2) * 16;   // budget of the replicated histogram
 
-struct LayoutLds {
-    int32_t base[kTileMaxBins];                 // earlier-tile counts, then running totals
-    int32_t wcnt[kTileWaves][kTileMaxBins];     // per-wavefront counts, then bases
-    int32_t scan[EP_MAX_EXPERTS + 1];           // exclusive scan of count, then total
-    int32_t wsum[kTileWaves];
+// Copies per bin of the replicated histogram (a power of two, 16..64). More copies spread the
+// atomics of one instruction over more banks but cost more LDS to clear and fold; 16 measured
+// best on MI355X across the batch sizes here.
+#ifndef EP_LAYOUT_NC
+#define EP_LAYOUT_NC 16
+#endif
+
+// Word offsets of the layout's LDS arrays, from E and the histogram copies (the same on host
+// and device).
+struct LayoutLdsMap {
+    int B;        // bins: E experts, invalid, unrouted
+    int lg_nc;    // log2 of the histogram copies per bin (4, 5 or 6)
+    int wcnt;     // [kTileWaves][B]: per-wavefront counts, then bases
+    int hist;     // [B][NC]: replicated earlier-tile histogram
+    int base;     // [B]: running totals (earlier tiles + this tile) of the experts
+    int scan;     // [E + 1]: exclusive scan of count, then the total kept
+    int wsum;     // [kTileWaves], then the invalid and unrouted totals
+    int words;    // total
 };
+
+// log2 of the copies for E experts: EP_LAYOUT_NC, fewer if the histogram would not fit.
+inline int layout_lg_nc(int E)
+{
+    int lg = 4;
+    while ((2 << lg) <= EP_LAYOUT_NC && lg < 6) ++lg;
+    while (lg > 4 && ((E + 2) << lg) > kHistWords) --lg;
+    return lg;
+}
+
+__host__ __device__ inline LayoutLdsMap layout_lds_map(int E, int lg_nc)
+{
+    LayoutLdsMap m;
+    m.B = E + 2;
+    m.lg_nc = lg_nc;
+    const int wcnt_words = (kTileWaves * m.B + 3) & ~3;   // keep hist 16-byte aligned
+    m.wcnt = 0;
+    m.hist = wcnt_words;
+    m.base = m.hist + (m.B << m.lg_nc);
+    m.scan = m.base + ((m.B + 3) & ~3);
+    m.wsum = m.scan + ((E + 1 + 3) & ~3);
+    m.words = m.wsum + kTileWaves + 2;
+    return m;
+}
+
+inline size_t layout_lds_bytes(int E, int lg_nc)
+{
+    return (size_t)layout_lds_map(E, lg_nc).words * 4;
+}
 
 // Bin of an id: itself for an expert, E for an invalid id, E+1 for -1 (unrouted).
 __device__ __forceinline__ int layout_bin(int e, int E)
@@ -48,37 +98,87 @@ __device__ __forceinline__ int layout_bin(int e, int E)
     return (int)min((unsigned)e, (unsigned)E) + (e == -1 ? 1 : 0);
 }
 
-// Steps 1-3 for the tile [tile_begin, tile_begin + P). Writes slot[] for the tile's pairs and,
-// if rows is not null, rows[k] = e*C + slot (or -1 for a pair that is not kept) for local pair
-// k. `last` marks the workgroup that will call layout_finish. Ends with a barrier.
-__device__ __forceinline__ void layout_tile(const int32_t *__restrict__ idx, int TK, int E, int C,
-                                            int nbits, int tile_begin, int P, bool last,
-                                            LayoutLds &L, int32_t *__restrict__ slot,
-                                            int32_t *rows)
+// Sum over each row of 16 lanes, in every lane of the row (DPP butterfly: swap neighbours,
+// swap pairs, mirror the half-rows, mirror the row).
+__device__ __forceinline__ int row16_total(int v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
+    return v;
+}
+
+// Step 0: the global loads of a tile, issued before anything waits on memory.
+struct TileIds {
+    int4 v[kPrefixVec];   // earlier-tile id vectors tid + u*1024 (clamped; see layout_tile)
+    int own;              // this lane's pair, -1 past the tile or the batch
+};
+
+__device__ __forceinline__ TileIds layout_tile_loads(const int32_t *__restrict__ idx, int TK,
+                                                     int tile_begin, int P)
+{
+    TileIds t;
+    const int tid = threadIdx.x;
+    const int p = tile_begin + tid;
+    t.own = (tid < P && p < TK) ? idx[p] : -1;
+    const int nvec = tile_begin / 4;      // tile_begin is a multiple of 4: whole vectors
+    // a batch is issued only if some lane of the wavefront needs it: the load pipe of a CU
+    // moves ~64 bytes per clock, so clamped duplicates would still cost issue time
+    const int wave_q0 = __builtin_amdgcn_readfirstlane(tid & ~(kWave - 1));
+    const int4 *idx4 = reinterpret_cast<const int4 *>(idx);
+#pragma unroll
+    for (int u = 0; u < kPrefixVec; ++u) {
+        t.v[u] = int4{0, 0, 0, 0};
+        if (wave_q0 + u * kTileThreads < nvec) {
+            const int q = tid + u * kTileThreads;
+            t.v[u] = idx4[q < nvec ? q : nvec - 1];
+        }
+    }
+    return t;
+}
+
+// Steps 1-3 for the tile [tile_begin, tile_begin + P), with its loads `ids` from
+// layout_tile_loads. Writes slot[] for the tile's pairs and, if rows is not null,
+// rows[k] = e*C + slot (or -1 for a pair that is not kept) for local pair k. `last` marks the
+// workgroup that will call layout_finish. Ends with a barrier.
+__device__ __forceinline__ void layout_tile(const TileIds &ids, const int32_t *__restrict__ idx,
+                                            int TK, int E, int C, int nbits, int tile_begin,
+                                            int P, bool last, int32_t *lds,
+                                            const LayoutLdsMap &m,
+                                            int32_t *__restrict__ slot, int32_t *rows)
 {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
+    const int B = m.B, NC = 1 << m.lg_nc;
+    int32_t *wcnt = lds + m.wcnt, *hist = lds + m.hist, *base = lds + m.base;
 
-    // this lane's own pair, loaded first so its latency overlaps the prefix histogram
-    const int p = tile_begin + tid;
-    const bool in = tid < P && p < TK;
-    const int own = in ? idx[p] : -1;
-
-    for (int k = tid; k < E + 2; k += kTileThreads) {
-        L.base[k] = 0;
-#pragma unroll
-        for (int w = 0; w < kTileWaves; ++w) L.wcnt[w][k] = 0;
+    // zero the per-wavefront counts and the histogram copies (adjacent, 16-byte aligned)
+    {
+        int4 *z = reinterpret_cast<int4 *>(lds + m.wcnt);
+        const int n4 = (m.base - m.wcnt) / 4;
+        for (int k = tid; k < n4; k += kTileThreads) z[k] = int4{0, 0, 0, 0};
     }
     __syncthreads();
 
-    // 1. histogram of the earlier tiles. tile_begin is a multiple of 4, so the prefix is whole
-    //    16-byte vectors; up to kPrefixVec of them per lane are in flight together. Addresses
-    //    past the prefix are clamped to its last vector and their counts skipped.
-    if (tile_begin > 0) {
+    // 1. earlier tiles into the replicated histogram. Vectors past the prefix were clamped to
+    //    its last one; their counts are skipped.
+    const int nvec = tile_begin / 4;
+    const int copy = lane & (NC - 1);
+    if (nvec > 0) {
+#pragma unroll
+        for (int u = 0; u < kPrefixVec; ++u) {
+            const bool ok = tid + u * kTileThreads < nvec;
+            const int e4[4] = {ids.v[u].x, ids.v[u].y, ids.v[u].z, ids.v[u].w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (ok) atomicAdd(&hist[(layout_bin(e4[c], E) << m.lg_nc) + copy], 1);
+        }
+        // prefixes longer than kPrefixVec*4096 ids: the rest in further batches
         const int4 *idx4 = reinterpret_cast<const int4 *>(idx);
-        const int nvec = tile_begin / 4;
-        for (int q0 = tid; q0 < nvec; q0 += kPrefixVec * kTileThreads) {
+        for (int q0 = tid + kPrefixVec * kTileThreads; q0 < nvec;
+             q0 += kPrefixVec * kTileThreads) {
             int4 v[kPrefixVec];
 #pragma unroll
             for (int u = 0; u < kPrefixVec; ++u) {
@@ -91,45 +191,59 @@ __device__ __forceinline__ void layout_tile(const int32_t *__restrict__ idx, int
                 const int e4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    if (ok) atomicAdd(&L.base[layout_bin(e4[c], E)], 1);
+                    if (ok) atomicAdd(&hist[(layout_bin(e4[c], E) << m.lg_nc) + copy], 1);
             }
         }
     }
 
     // 2. ranks of the routed lanes inside the wavefront by bit-sliced ballot matching
+    const int p = tile_begin + tid;
+    const bool in = tid < P && p < TK;
+    const int own = ids.own;
     const bool routed = in && (unsigned)own < (unsigned)E;
     if (last) {                     // this tile's pairs in the two non-expert bins, for the stats
         const int unrouted = __popcll(__ballot(in && own == -1));
         const int invalid = __popcll(__ballot(in && own != -1 && !routed));
-        if (lane == 0 && unrouted) atomicAdd(&L.base[E + 1], unrouted);
-        if (lane == 0 && invalid) atomicAdd(&L.base[E], invalid);
+        if (lane == 0 && unrouted) atomicAdd(&hist[(E + 1) << m.lg_nc], unrouted);
+        if (lane == 0 && invalid) atomicAdd(&hist[E << m.lg_nc], invalid);
     }
     uint64_t same = __ballot(routed);
     for (int k = 0; k < nbits; ++k) {
         const bool bit = (own >> k) & 1;
-        const uint64_t m = __ballot(bit);
-        same &= bit ? m : ~m;
+        const uint64_t mk = __ballot(bit);
+        same &= bit ? mk : ~mk;
     }
     const int rank = count_below(same);
-    if (routed && rank == 0) L.wcnt[wave][own] = __popcll(same);
+    if (routed && rank == 0) wcnt[wave * B + own] = __popcll(same);
     __syncthreads();
 
-    // 3. per-expert exclusive scan over the 16 wavefronts, from the earlier-tile base: the 16
-    //    counts of an expert sit in one DPP row of 16 lanes
+    // 3. per expert, one DPP row of 16 lanes: fold the NC copies (NC/16 words per lane) into
+    //    the earlier-tile count b0, then the exclusive scan of the 16 wavefront counts from b0
+    //    (the two non-expert bins are folded by layout_finish, which alone needs them)
     for (int k = tid; k < E * kTileWaves; k += kTileThreads) {
         const int e = k / kTileWaves, w = k % kTileWaves;
-        const int c = L.wcnt[w][e];
+        const int32_t *h = hist + (e << m.lg_nc) + (w << (m.lg_nc - 4));
+        int part;
+        if (m.lg_nc == 6) {
+            const int4 q = *reinterpret_cast<const int4 *>(h);
+            part = (q.x + q.y) + (q.z + q.w);
+        } else if (m.lg_nc == 5) {
+            const int2 q = *reinterpret_cast<const int2 *>(h);
+            part = q.x + q.y;
+        } else {
+            part = h[0];
+        }
+        const int b0 = row16_total(part);
+        const int c = wcnt[w * B + e];
         const int incl = row16_inclusive_sum(c);
-        const int b0 = L.base[e];
-        L.wcnt[w][e] = b0 + incl - c;
-        // the 16 lanes of an expert are in one wavefront and read b0 before this write
-        if (w == kTileWaves - 1) L.base[e] = b0 + incl;
+        wcnt[w * B + e] = b0 + incl - c;
+        if (w == kTileWaves - 1) base[e] = b0 + incl;
     }
     __syncthreads();
     if (in) {
         int s = -1;
         if (routed) {
-            const int pos = L.wcnt[wave][own] + rank;
+            const int pos = wcnt[wave * B + own] + rank;
             s = pos < C ? pos : -1;
         }
         slot[p] = s;
@@ -138,36 +252,47 @@ __device__ __forceinline__ void layout_tile(const int32_t *__restrict__ idx, int
     __syncthreads();
 }
 
-// Step 4, by the workgroup of the last tile after layout_tile: L.base[e] is the total of
-// expert e, L.base[E] / L.base[E+1] the invalid / unrouted totals.
-__device__ __forceinline__ void layout_finish(int TK, int E, int C, int R, LayoutLds &L,
-                                              const LayoutOut &o)
+// Step 4, by the workgroup of the last tile after layout_tile: base[e] is the total of expert
+// e; the histogram copies of bins E and E+1 hold the invalid and unrouted totals.
+__device__ __forceinline__ void layout_finish(int TK, int E, int C, int R, int32_t *lds,
+                                              const LayoutLdsMap &m, const LayoutOut &o)
 {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    const int cnt = tid < E ? min(L.base[tid], C) : 0;     // E <= kTileThreads
+    const int32_t *base = lds + m.base, *hist = lds + m.hist;
+    int32_t *scan = lds + m.scan, *wsum = lds + m.wsum;
+    const int cnt = tid < E ? min(base[tid], C) : 0;     // E <= kTileThreads
     const int incl = wave_inclusive_sum(cnt);
-    if (lane == kWave - 1) L.wsum[wave] = incl;
+    if (lane == kWave - 1) wsum[wave] = incl;
+    if (wave == 0) {          // invalid (bin E) and unrouted (bin E+1) totals: sum of the copies
+        const int NC = 1 << m.lg_nc;
+        const int inv = wave_inclusive_sum(lane < NC ? hist[(E << m.lg_nc) + lane] : 0);
+        const int unr = wave_inclusive_sum(lane < NC ? hist[((E + 1) << m.lg_nc) + lane] : 0);
+        if (lane == kWave - 1) {
+            wsum[kTileWaves] = inv;
+            wsum[kTileWaves + 1] = unr;
+        }
+    }
     __syncthreads();
     int wbase = 0;
-    for (int w = 0; w < wave; ++w) wbase += L.wsum[w];
+    for (int w = 0; w < wave; ++w) wbase += wsum[w];
     const int excl = wbase + incl - cnt;
     if (tid < E) {
         o.count[tid] = cnt;
         o.offset[tid] = excl;
-        L.scan[tid] = excl;
+        scan[tid] = excl;
     }
-    if (tid == E - 1) L.scan[E] = excl + cnt;             // total kept
+    if (tid == E - 1) scan[E] = excl + cnt;             // total kept
     __syncthreads();
     const int EL = E / R;
     for (int r = tid; r < R; r += kTileThreads) {
-        const int lo = L.scan[r * EL], hi = L.scan[(r + 1) * EL];
+        const int lo = scan[r * EL], hi = scan[(r + 1) * EL];
         if (o.rank_count) o.rank_count[r] = hi - lo;
         if (o.rank_offset) o.rank_offset[r] = lo;
     }
     if (tid == 0) {
-        const int kept = L.scan[E], unrouted = L.base[E + 1], invalid = L.base[E];
+        const int kept = scan[E], invalid = wsum[kTileWaves], unrouted = wsum[kTileWaves + 1];
         o.stats[0] = kept;
         o.stats[1] = TK - unrouted - invalid - kept;
         o.stats[2] = unrouted;
