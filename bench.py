@@ -193,6 +193,35 @@ class Workload:
             ts.append(ev0.elapsed_time(ev1) * 1e3)
         return ts
 
+    def graph_single_shot(self, samples, flush):
+        """Cold single-shot latency of one step replayed from a HIP graph: the step's launches
+        (fused layout + dispatch, then combine, on input batch 0) are captured once, and each
+        sample replays the graph after a 2 GiB fill, between an event pair."""
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                self.step(0)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step(0)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for k in range(samples):
+            torch.cuda.synchronize()
+            flush.fill_(k & 0x7F)
+            ev0.record()
+            g.replay()
+            ev1.record()
+            torch.cuda.synchronize()
+            ts.append(ev0.elapsed_time(ev1) * 1e3)
+        del g
+        return ts
+
     def kernel_avg_us(self, flush, runs=25, per_run=8):
         """Average duration of each kernel launched back to back: per run, a 2 GiB fill of
         `flush` is enqueued first, and while it executes the host enqueues an event, `per_run`
@@ -288,6 +317,29 @@ def cpu_baseline(cfg, budget_s, W, A):
                       f"core of {os.cpu_count()} ({cpu})"}
 
 
+def launch_floor(samples, flush, torch, B):
+    """The latency floor of the step's structure, measured like the T=128 single-shot: one and
+    two back-to-back launches of the library's layout kernel on an empty batch (one workgroup
+    that clears its counts), each sample after a 2 GiB fill."""
+    idx = torch.zeros((0, 8), dtype=torch.int32, device="cuda")
+    lay = B.ep_layout(idx, 16, 4, 4)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {}
+    for n in (1, 2):
+        ts = []
+        for k in range(samples):
+            torch.cuda.synchronize()
+            flush.fill_(k & 0x7F)
+            ev0.record()
+            for _ in range(n):
+                B.ep_layout(idx, 16, 4, 4, **lay)
+            ev1.record()
+            torch.cuda.synchronize()
+            ts.append(ev0.elapsed_time(ev1) * 1e3)
+        out[f"{n}_launch{'es' if n > 1 else ''}_us"] = round(statistics.median(ts), 3)
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -350,6 +402,8 @@ def main():
         if cfg.T <= 256:
             ss = wl.single_shot(args.latency_samples, flush)
             ss3 = wl.single_shot(args.latency_samples, flush, step=wl.step3)
+            r["graph_us_single_shot_median"] = round(
+                statistics.median(wl.graph_single_shot(args.latency_samples, flush)), 3)
             r["three_call_step"]["us_single_shot_median"] = round(statistics.median(ss3), 3)
             r["us_single_shot_median"] = round(statistics.median(ss), 3)
             r["us_single_shot_min"] = round(min(ss), 3)
@@ -375,6 +429,9 @@ def main():
         results[name] = (cfg, None, r, kus, kb)
         log(f"{name}: {json.dumps(r)}")
 
+    floor = launch_floor(args.latency_samples, flush, torch, B)
+    log(f"launch floor: {floor}")
+
     cfg, _, r, kus, kb = results[args.workload]
     dom = max(("layout_dispatch", "combine"), key=lambda k: kus[k])   # the step's two kernels
     achieved = kb[dom] / (kus[dom] * 1e-6) / 1e9
@@ -391,8 +448,9 @@ def main():
 
     def brief(name):
         c, _, rr, _, _ = results[name]
-        keys = ("us_per_step", "us_single_shot_median", "logical_GBps", "hbm_frac",
-                "cold_single_shot", "kernel_avg_us", "three_call_step")
+        keys = ("us_per_step", "us_single_shot_median", "graph_us_single_shot_median",
+                "logical_GBps", "hbm_frac", "cold_single_shot", "kernel_avg_us",
+                "three_call_step")
         return {k: rr[k] for k in keys if k in rr}
 
     line = {
@@ -413,6 +471,7 @@ def main():
         "rotating_all_buffers": r.get("rotating_all_buffers"),
         "three_call_step": r.get("three_call_step"),
         "t128_us": {n: brief(n) for n in ("decode_bf16", "decode_fp8") if n in results},
+        "launch_floor_us": floor,
         "prefill_fp8": brief("prefill_fp8") if "prefill_fp8" in results else None,
         "roofline": roofline,
         "cpu_baseline": cpu,
