@@ -7,7 +7,10 @@ with gcc by ``oracle/build.py``) with numpy arrays. It shares nothing with the G
 Every function here is pinned by the ``-m "not gpu"`` tests against something other than
 itself: brute-force enumeration and a stable sort for the layout, a numpy scatter for the
 dispatch, torch's CPU casts and an exhaustive table search for the number formats, the
-identity/one-hot laws and an fp64 bound for combine.
+identity/one-hot laws and an fp64 bound for combine. The two-stage path is pinned by its
+reductions to the pinned one-stage functions (one expert per rank, a single rank), by the
+composed dispatch being the one-stage dispatch, and by closed forms (identity law, one expert
+per rank).
 """
 from __future__ import annotations
 
@@ -56,6 +59,21 @@ def lib():
         L.oracle_combine_tokens.argtypes = ([_c_int, _i32p] + [_c_int] * 4
                                             + [_u16p, _i32p, _i32p, _f32p, _u16p])
         L.oracle_combine_tokens.restype = None
+        L.oracle_rank_layout.argtypes = [_c_int] * 4 + [_i32p, _i32p, _i32p]
+        L.oracle_rank_layout.restype = None
+        L.oracle_dispatch_ranks.argtypes = [_c_int] * 3 + [_u16p, _i32p, _u16p]
+        L.oracle_dispatch_ranks.restype = None
+        L.oracle_dispatch_ranks_fp8.argtypes = [_c_int] * 3 + [_u16p, _i32p, _u8p, _f32p]
+        L.oracle_dispatch_ranks_fp8.restype = None
+        L.oracle_dispatch_expand.argtypes = [_c_int] * 6 + [_u16p, _i32p, _i32p, _i32p, _u16p]
+        L.oracle_dispatch_expand.restype = None
+        L.oracle_dispatch_expand_fp8.argtypes = ([_c_int] * 6
+                                                 + [_u8p, _f32p, _i32p, _i32p, _i32p, _u8p, _f32p])
+        L.oracle_dispatch_expand_fp8.restype = None
+        L.oracle_combine_ranks.argtypes = [_c_int] * 6 + [_u16p, _i32p, _i32p, _i32p, _f32p, _u16p]
+        L.oracle_combine_ranks.restype = None
+        L.oracle_combine_reduce.argtypes = [_c_int] * 3 + [_u16p, _i32p, _u16p]
+        L.oracle_combine_reduce.restype = None
         L.oracle_bf16_rne_array.argtypes = [_f32p, _u16p, _c_long]
         L.oracle_bf16_rne_array.restype = None
         L.oracle_e4m3_rne_sat_array.argtypes = [_f32p, _u8p, _c_long]
@@ -165,3 +183,87 @@ def combine_tokens(tokens: np.ndarray, y: np.ndarray, topk_idx: np.ndarray, slot
                                 np.ascontiguousarray(topk_idx), np.ascontiguousarray(slot),
                                 np.ascontiguousarray(topk_w, dtype=np.float32), out)
     return out
+
+
+# ------------------------------------------------------------------------------------------
+# the two-stage path: one copy per (token, virtual rank), then the rank's own expansion
+# ------------------------------------------------------------------------------------------
+
+def _c(a, dtype=None):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def rank_layout(topk_idx: np.ndarray, E: int, R: int) -> dict:
+    """Which virtual ranks each token goes to. Returns ``rank_slot`` int32 [T, R] (the token's
+    position among the rank's tokens, -1 if not sent) and ``rank_tokens`` int32 [R]."""
+    idx = _c(topk_idx, np.int32)
+    T, K = idx.shape
+    rank_slot = np.empty((T, R), dtype=np.int32)
+    rank_tokens = np.empty(R, dtype=np.int32)
+    lib().oracle_rank_layout(T, K, E, R, idx, rank_slot, rank_tokens)
+    return dict(rank_slot=rank_slot, rank_tokens=rank_tokens)
+
+
+def dispatch_ranks(x: np.ndarray, rank_slot: np.ndarray, stage: np.ndarray) -> np.ndarray:
+    """Stage 1 of dispatch into ``stage`` (uint16 [R, T, H]), in place."""
+    T, H = x.shape
+    R = rank_slot.shape[1]
+    assert stage.shape == (R, T, H) and stage.dtype == np.uint16 and stage.flags.c_contiguous
+    lib().oracle_dispatch_ranks(T, H, R, _c(x), _c(rank_slot), stage)
+    return stage
+
+
+def dispatch_ranks_fp8(x: np.ndarray, rank_slot: np.ndarray, stage_q: np.ndarray,
+                       stage_scale: np.ndarray):
+    """FP8 stage 1 into ``stage_q`` (uint8 [R, T, H]) and ``stage_scale`` (float32 [R, T, H/128])."""
+    T, H = x.shape
+    R = rank_slot.shape[1]
+    assert H % 128 == 0
+    assert stage_q.shape == (R, T, H) and stage_q.dtype == np.uint8
+    assert stage_scale.shape == (R, T, H // 128) and stage_scale.dtype == np.float32
+    lib().oracle_dispatch_ranks_fp8(T, H, R, _c(x), _c(rank_slot), stage_q, stage_scale)
+    return stage_q, stage_scale
+
+
+def dispatch_expand(stage: np.ndarray, topk_idx: np.ndarray, slot: np.ndarray,
+                    rank_slot: np.ndarray, E: int, C: int, recv: np.ndarray) -> np.ndarray:
+    """Stage 2 of dispatch from ``stage`` [R, T, H] into ``recv`` (uint16 [E, C, H]), in place."""
+    R, T, H = stage.shape
+    K = topk_idx.shape[1]
+    assert recv.shape == (E, C, H) and recv.dtype == np.uint16 and recv.flags.c_contiguous
+    lib().oracle_dispatch_expand(T, H, E, K, C, R, _c(stage), _c(topk_idx), _c(slot),
+                                 _c(rank_slot), recv)
+    return recv
+
+
+def dispatch_expand_fp8(stage_q, stage_scale, topk_idx, slot, rank_slot, E, C, recv_q,
+                        recv_scale):
+    """FP8 stage 2 into ``recv_q`` [E, C, H] and ``recv_scale`` [E, C, H/128], in place."""
+    R, T, H = stage_q.shape
+    K = topk_idx.shape[1]
+    assert recv_q.shape == (E, C, H) and recv_scale.shape == (E, C, H // 128)
+    lib().oracle_dispatch_expand_fp8(T, H, E, K, C, R, _c(stage_q), _c(stage_scale),
+                                     _c(topk_idx), _c(slot), _c(rank_slot), recv_q, recv_scale)
+    return recv_q, recv_scale
+
+
+def combine_ranks(y: np.ndarray, topk_idx: np.ndarray, slot: np.ndarray, rank_slot: np.ndarray,
+                  topk_w: np.ndarray) -> np.ndarray:
+    """Stage 1 of combine: per-rank partial rows, uint16 [R, T, H]; rows of tokens a rank did
+    not receive are left as zero here (the kernels leave them untouched)."""
+    E, C, H = y.shape
+    T, K = topk_idx.shape
+    R = rank_slot.shape[1]
+    part = np.zeros((R, T, H), dtype=np.uint16)
+    lib().oracle_combine_ranks(T, H, E, K, C, R, _c(y), _c(topk_idx), _c(slot), _c(rank_slot),
+                               _c(topk_w, np.float32), part)
+    return part
+
+
+def combine_reduce(part: np.ndarray, rank_slot: np.ndarray) -> np.ndarray:
+    """Stage 2 of combine: out uint16 [T, H] from the partial rows ``part`` [R, T, H]."""
+    R, T, H = part.shape
+    out = np.empty((T, H), dtype=np.uint16)
+    lib().oracle_combine_reduce(T, H, R, _c(part), _c(rank_slot), out)
+    return out
+

@@ -20,12 +20,21 @@
  *  - Combine gathers expert outputs back and reduces them with the top-k weights; combine is
  *    BF16 in either dispatch dtype (PR #1238 review item 1; afdEP-comm kernel_timelines:
  *    combine_reduce_epilogue).
+ *  - The two-stage path mirrors the pages' kernel chain (afdEP-comm kernel_timelines:
+ *    dispatch_impl then dispatch_copy_epilogue; combine_impl then combine_reduce_epilogue):
+ *    a token goes to each virtual rank once, the rank expands it into its experts' rows, and
+ *    on the way back each rank returns one partial row per token.
  *  - Readings where the pages are silent: pair order i = t*K + j is "token order"; a
  *    capacity-C expert keeps its first C pairs in that order; the receive buffer is
  *    [E][C][H] with expert e = r*(E/R) + l (rank-major); scale = amax / 448 by an IEEE fp32
  *    division and q = e4m3(x / scale) by a second fp32 division; combine accumulates
  *    acc = fmaf(w_j, y_j, acc) in fp32 for j ascending from +0 and rounds once to bf16;
- *    weights of dropped pairs are not renormalised.
+ *    weights of dropped pairs are not renormalised. Two-stage path: a token is sent to rank r
+ *    if any of its valid ids is an expert of r (the sender sees only the routing; capacity is
+ *    applied to the experts' rows on the receiving side); a rank's tokens keep token order; the
+ *    per-rank partial is the same fmaf fold over the token's kept pairs of that rank, rounded
+ *    once to bf16 (the combine payload is bf16); the final row is the fp32 sum of the
+ *    partials in ascending rank, rounded once to bf16.
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fPIC -shared (no -ffast-math, no
  * FMA contraction: every fp32 operation below is one IEEE operation).
@@ -220,6 +229,24 @@ void oracle_dispatch(int T, int H, int E, int K, int C, const uint16_t *x,
  * Then the q row and the scale row are written to every kept slot of t:
  *   recv_q[e][s][h] = q[h];  recv_scale[e][s][b] = scale_b.
  */
+static void quantise_token(int H, const uint16_t *row, uint8_t *q, float *sc)
+{
+    for (int b = 0; b < H / 128; ++b) {
+        float amax = 0.0f;
+        for (int h = 128 * b; h < 128 * b + 128; ++h) {
+            float a = fabsf(oracle_bf16_to_f32(row[h]));
+            if (a > amax) amax = a;
+        }
+        float scale = amax / 448.0f;
+        sc[b] = scale;
+        for (int h = 128 * b; h < 128 * b + 128; ++h) {
+            float v = oracle_bf16_to_f32(row[h]);
+            q[h] = (amax == 0.0f) ? (uint8_t)((row[h] & 0x8000u) ? 0x80 : 0x00)
+                                  : oracle_e4m3_rne_sat(v / scale);
+        }
+    }
+}
+
 void oracle_dispatch_fp8(int T, int H, int E, int K, int C, const uint16_t *x,
                          const int32_t *topk_idx, const int32_t *slot, uint8_t *recv_q,
                          float *recv_scale)
@@ -228,21 +255,7 @@ void oracle_dispatch_fp8(int T, int H, int E, int K, int C, const uint16_t *x,
     uint8_t q[H > 0 ? H : 1];
     float sc[NB > 0 ? NB : 1];
     for (int t = 0; t < T; ++t) {
-        const uint16_t *row = x + (long)t * H;
-        for (int b = 0; b < NB; ++b) {
-            float amax = 0.0f;
-            for (int h = 128 * b; h < 128 * b + 128; ++h) {
-                float a = fabsf(oracle_bf16_to_f32(row[h]));
-                if (a > amax) amax = a;
-            }
-            float scale = amax / 448.0f;
-            sc[b] = scale;
-            for (int h = 128 * b; h < 128 * b + 128; ++h) {
-                float v = oracle_bf16_to_f32(row[h]);
-                q[h] = (amax == 0.0f) ? (uint8_t)((row[h] & 0x8000u) ? 0x80 : 0x00)
-                                      : oracle_e4m3_rne_sat(v / scale);
-            }
-        }
+        quantise_token(H, x + (long)t * H, q, sc);
         for (int j = 0; j < K; ++j) {
             long i = (long)t * K + j;
             int32_t e = topk_idx[i], s = slot[i];
@@ -276,6 +289,152 @@ void oracle_combine(int T, int H, int E, int K, int C, const uint16_t *y,
                 if (!pair_kept(e, s, E, C)) continue;
                 float v = oracle_bf16_to_f32(y[((long)e * C + s) * H + h]);
                 acc = fmaf(topk_w[i], v, acc);
+            }
+            out[(long)t * H + h] = oracle_bf16_rne(acc);
+        }
+}
+
+/* ----------------------------------------------------------------------------------------- */
+/* Two-stage path: one copy per (token, virtual rank), then the rank's own expansion           */
+/* ----------------------------------------------------------------------------------------- */
+
+/*
+ * Rank layout. Expert e belongs to virtual rank e / (E/R). Token t is sent to rank r if any of
+ * its pairs holds a valid id (0 <= id < E) of an expert of r, whatever the capacity decides.
+ *   rank_slot[t][r] = #{t' < t : t' is sent to r} if t is sent to r, else -1
+ *   rank_tokens[r]  = #{t : t is sent to r}
+ */
+void oracle_rank_layout(int T, int K, int E, int R, const int32_t *topk_idx, int32_t *rank_slot,
+                        int32_t *rank_tokens)
+{
+    int EL = E / R;
+    for (int r = 0; r < R; ++r) rank_tokens[r] = 0;
+    for (int t = 0; t < T; ++t) {
+        int32_t *rs = rank_slot + (long)t * R;
+        for (int r = 0; r < R; ++r) rs[r] = -1;
+        for (int j = 0; j < K; ++j) {
+            int32_t e = topk_idx[(long)t * K + j];
+            if (e < 0 || e >= E) continue;
+            int r = e / EL;
+            if (rs[r] < 0) rs[r] = rank_tokens[r]++;
+        }
+    }
+}
+
+/* Stage 1 of dispatch: stage[r][rank_slot[t][r]][:] = x[t][:] for every rank t is sent to
+ * (stage is [R][T][H]); every other row is left as it is. */
+void oracle_dispatch_ranks(int T, int H, int R, const uint16_t *x, const int32_t *rank_slot,
+                           uint16_t *stage)
+{
+    for (int t = 0; t < T; ++t)
+        for (int r = 0; r < R; ++r) {
+            int32_t p = rank_slot[(long)t * R + r];
+            if (p < 0) continue;
+            memcpy(stage + ((long)r * T + p) * H, x + (long)t * H, (size_t)H * sizeof(uint16_t));
+        }
+}
+
+/* FP8 stage 1: token t quantised once (as in oracle_dispatch_fp8), its codes and scales
+ * written to stage_q[r][p] ([R][T][H]) and stage_scale[r][p] ([R][T][H/128]). */
+void oracle_dispatch_ranks_fp8(int T, int H, int R, const uint16_t *x, const int32_t *rank_slot,
+                               uint8_t *stage_q, float *stage_scale)
+{
+    int NB = H / 128;
+    uint8_t q[H > 0 ? H : 1];
+    float sc[NB > 0 ? NB : 1];
+    for (int t = 0; t < T; ++t) {
+        quantise_token(H, x + (long)t * H, q, sc);
+        for (int r = 0; r < R; ++r) {
+            int32_t p = rank_slot[(long)t * R + r];
+            if (p < 0) continue;
+            memcpy(stage_q + ((long)r * T + p) * H, q, (size_t)H);
+            memcpy(stage_scale + ((long)r * T + p) * NB, sc, (size_t)NB * sizeof(float));
+        }
+    }
+}
+
+/* Stage 2 of dispatch, the rank's own expansion: for every kept pair i = t*K + j of expert e
+ * (rank r = e / (E/R)), recv[e][slot[i]][:] = stage[r][rank_slot[t][r]][:]. */
+void oracle_dispatch_expand(int T, int H, int E, int K, int C, int R, const uint16_t *stage,
+                            const int32_t *topk_idx, const int32_t *slot,
+                            const int32_t *rank_slot, uint16_t *recv)
+{
+    int EL = E / R;
+    for (int t = 0; t < T; ++t)
+        for (int j = 0; j < K; ++j) {
+            long i = (long)t * K + j;
+            int32_t e = topk_idx[i], s = slot[i];
+            if (!pair_kept(e, s, E, C)) continue;
+            int r = e / EL;
+            int32_t p = rank_slot[(long)t * R + r];
+            if (p < 0) continue;
+            memcpy(recv + ((long)e * C + s) * H, stage + ((long)r * T + p) * H,
+                   (size_t)H * sizeof(uint16_t));
+        }
+}
+
+/* FP8 stage 2: codes and scales of the staged row copied to every kept pair's row. */
+void oracle_dispatch_expand_fp8(int T, int H, int E, int K, int C, int R, const uint8_t *stage_q,
+                                const float *stage_scale, const int32_t *topk_idx,
+                                const int32_t *slot, const int32_t *rank_slot, uint8_t *recv_q,
+                                float *recv_scale)
+{
+    int EL = E / R, NB = H / 128;
+    for (int t = 0; t < T; ++t)
+        for (int j = 0; j < K; ++j) {
+            long i = (long)t * K + j;
+            int32_t e = topk_idx[i], s = slot[i];
+            if (!pair_kept(e, s, E, C)) continue;
+            int r = e / EL;
+            int32_t p = rank_slot[(long)t * R + r];
+            if (p < 0) continue;
+            long dst = (long)e * C + s, src = (long)r * T + p;
+            memcpy(recv_q + dst * H, stage_q + src * H, (size_t)H);
+            memcpy(recv_scale + dst * NB, stage_scale + src * NB, (size_t)NB * sizeof(float));
+        }
+}
+
+/*
+ * Stage 1 of combine, on each rank: one partial row per token sent to the rank,
+ *   part[r][rank_slot[t][r]][h] = bf16_rne(acc), acc = +0.0f, then for j = 0 .. K-1 with pair
+ *   i = t*K + j kept and its expert in rank r: acc = fmaf(w[i], float(y[e_i][slot_i][h]), acc).
+ * A token sent to r whose pairs there were all dropped gets a +0 row.
+ */
+void oracle_combine_ranks(int T, int H, int E, int K, int C, int R, const uint16_t *y,
+                          const int32_t *topk_idx, const int32_t *slot,
+                          const int32_t *rank_slot, const float *topk_w, uint16_t *part)
+{
+    int EL = E / R;
+    for (int t = 0; t < T; ++t)
+        for (int r = 0; r < R; ++r) {
+            int32_t p = rank_slot[(long)t * R + r];
+            if (p < 0) continue;
+            uint16_t *dst = part + ((long)r * T + p) * H;
+            for (int h = 0; h < H; ++h) {
+                float acc = 0.0f;
+                for (int j = 0; j < K; ++j) {
+                    long i = (long)t * K + j;
+                    int32_t e = topk_idx[i], s = slot[i];
+                    if (!pair_kept(e, s, E, C) || e / EL != r) continue;
+                    acc = fmaf(topk_w[i], oracle_bf16_to_f32(y[((long)e * C + s) * H + h]), acc);
+                }
+                dst[h] = oracle_bf16_rne(acc);
+            }
+        }
+}
+
+/* Stage 2 of combine, on the token's side: out[t][h] = bf16_rne(acc), acc = +0.0f, then for
+ * r = 0 .. R-1 with t sent to r: acc = acc + float(part[r][rank_slot[t][r]][h]). */
+void oracle_combine_reduce(int T, int H, int R, const uint16_t *part, const int32_t *rank_slot,
+                           uint16_t *out)
+{
+    for (int t = 0; t < T; ++t)
+        for (int h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int r = 0; r < R; ++r) {
+                int32_t p = rank_slot[(long)t * R + r];
+                if (p < 0) continue;
+                acc = acc + oracle_bf16_to_f32(part[((long)r * T + p) * H + h]);
             }
             out[(long)t * H + h] = oracle_bf16_rne(acc);
         }
