@@ -222,7 +222,65 @@ class Workload:
         del g
         return ts
 
-    def kernel_avg_us(self, flush, runs=25, per_run=8):
+    # the two-stage, rank-deduplicated pass: expert layout, rank layout, staging copy, the
+    # rank's expansion; per-rank partial combine, then the reduction on the token's side
+    def enable_two_stage(self):
+        torch, c = self.torch, self.cfg
+        dev = torch.device("cuda", 0)
+        b = {}
+        if c.fp8:
+            b["stage_q"] = torch.empty((c.R, c.T, c.H), dtype=torch.uint8, device=dev)
+            b["stage_s"] = torch.empty((c.R, c.T, c.H // 128), dtype=torch.float32, device=dev)
+        else:
+            b["stage"] = torch.empty((c.R, c.T, c.H), dtype=torch.int16, device=dev)
+        b["part"] = torch.empty((c.R, c.T, c.H), dtype=torch.int16, device=dev)
+        for s in self.sets:
+            s.update(b)
+            s["rl"] = dict(rank_slot=torch.empty((c.T, c.R), dtype=torch.int32, device=dev),
+                           rank_tokens=torch.empty(c.R, dtype=torch.int32, device=dev))
+        for k in range(len(self.sets)):
+            self.step2(k)
+        torch.cuda.synchronize()
+        return [int(s["rl"]["rank_tokens"].sum()) for s in self.sets]
+
+    def rank_layout(self, s):
+        c = self.cfg
+        self.B.ep_rank_layout(s["idx"], c.E, c.R, **s["rl"])
+
+    def dispatch_ranks(self, s):
+        if self.cfg.fp8:
+            self.B.ep_dispatch_ranks_fp8(s["x"], s["rl"]["rank_slot"], s["stage_q"], s["stage_s"])
+        else:
+            self.B.ep_dispatch_ranks(s["x"], s["rl"]["rank_slot"], s["stage"])
+
+    def expand(self, s):
+        c = self.cfg
+        if c.fp8:
+            self.B.ep_dispatch_expand_fp8(s["stage_q"], s["stage_s"], s["idx"], s["lay"]["slot"],
+                                          s["rl"]["rank_slot"], s["recv_q"], s["recv_s"], c.C)
+        else:
+            self.B.ep_dispatch_expand(s["stage"], s["idx"], s["lay"]["slot"],
+                                      s["rl"]["rank_slot"], s["recv"], c.C)
+
+    def combine_ranks(self, s):
+        c = self.cfg
+        self.B.ep_combine_ranks(s["y"], s["idx"], s["lay"]["slot"], s["rl"]["rank_slot"], s["w"],
+                                c.C, part=s["part"])
+
+    def combine_reduce(self, s):
+        self.B.ep_combine_reduce(s["part"], s["rl"]["rank_slot"], self.cfg.K, out=s["out"])
+
+    def step2(self, k):
+        """One two-stage pass: six launches."""
+        s = self.sets[k % len(self.sets)]
+        self.layout(s)
+        self.rank_layout(s)
+        self.dispatch_ranks(s)
+        self.expand(s)
+        self.combine_ranks(s)
+        self.combine_reduce(s)
+
+    def kernel_avg_us(self, flush, runs=25, per_run=8, kernels=None):
         """Average duration of each kernel launched back to back: per run, a 2 GiB fill of
         `flush` is enqueued first, and while it executes the host enqueues an event, `per_run`
         launches of the one kernel (rotating over the input batches) and a second event, so
@@ -235,8 +293,9 @@ class Workload:
         torch.cuda.synchronize()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         out = {}
-        for name, fn in (("layout_dispatch", self.layout_dispatch), ("combine", self.combine),
-                         ("layout", self.layout), ("dispatch", self.dispatch)):
+        kernels = kernels or (("layout_dispatch", self.layout_dispatch), ("combine", self.combine),
+                              ("layout", self.layout), ("dispatch", self.dispatch))
+        for name, fn in kernels:
             ts = []
             for r in range(runs):
                 torch.cuda.synchronize()
@@ -315,6 +374,37 @@ def cpu_baseline(cfg, budget_s, W, A):
             "sample": f"{len(times)} whole steps (layout + bf16 dispatch + combine) of "
                       f"{cfg.name}, median {med * 1e3:.1f} ms/step, single thread pinned to one "
                       f"core of {os.cpu_count()} ({cpu})"}
+
+
+def two_stage_report(cfg, flush, args, torch, B, W, A):
+    """The two-stage, rank-deduplicated pass on one workload: each kernel back to back, the
+    whole six-launch pass pipelined, bytes per kernel, and the rows that would cross ranks."""
+    wl = Workload(cfg, NSETS, torch, B, W)
+    n_kept = wl.kept()[0]
+    n_tr = wl.enable_two_stage()[0]
+    ms, _ = wl.timed_loop(args.steps, args.warmup, step=wl.step2)
+    kus = wl.kernel_avg_us(flush, kernels=(
+        ("rank_layout", wl.rank_layout), ("dispatch_ranks", wl.dispatch_ranks),
+        ("dispatch_expand", wl.expand), ("combine_ranks", wl.combine_ranks),
+        ("combine_reduce", wl.combine_reduce)))
+    T, K, H, R = cfg.T, cfg.K, cfg.H, cfg.R
+    kb = {"rank_layout": A.rank_layout_bytes(T, K, R),
+          "dispatch_ranks": A.dispatch_ranks_bytes(T, R, H, n_tr, cfg.fp8),
+          "dispatch_expand": A.dispatch_expand_bytes(T, K, R, H, n_tr, n_kept, cfg.fp8),
+          "combine_ranks": A.combine_ranks_bytes(T, K, R, H, n_tr, n_kept),
+          "combine_reduce": A.combine_reduce_bytes(T, R, H, n_tr)}
+    alg = A.layout_bytes(T, K) + sum(kb.values())
+    out = {"workload": cfg.name, "us_per_pass": round(ms * 1e3, 3),
+           "hbm_frac": round(alg / (ms * 1e-3) / A.HBM_PEAK_BYTES_PER_S, 4),
+           "algorithmic_bytes": alg,
+           "rows_crossing_ranks": n_tr, "kept_pairs": n_kept,
+           "dedup_ratio": round(n_tr / max(n_kept, 1), 4),
+           "kernel_avg_us": {k: round(v, 3) for k, v in kus.items()},
+           "kernel_hbm_frac": {k: round(kb[k] / (kus[k] * 1e-6) / A.HBM_PEAK_BYTES_PER_S, 4)
+                               for k in kus}}
+    del wl
+    torch.cuda.empty_cache()
+    return out
 
 
 def launch_floor(samples, flush, torch, B):
@@ -429,6 +519,9 @@ def main():
         results[name] = (cfg, None, r, kus, kb)
         log(f"{name}: {json.dumps(r)}")
 
+    two_stage = {n: two_stage_report(W.get_config(n), flush, args, torch, B, W, A)
+                 for n in (args.workload, "prefill_fp8")}
+    log(f"two-stage: {json.dumps(two_stage)}")
     floor = launch_floor(args.latency_samples, flush, torch, B)
     log(f"launch floor: {floor}")
 
@@ -472,6 +565,7 @@ def main():
         "three_call_step": r.get("three_call_step"),
         "t128_us": {n: brief(n) for n in ("decode_bf16", "decode_fp8") if n in results},
         "launch_floor_us": floor,
+        "two_stage": two_stage,
         "prefill_fp8": brief("prefill_fp8") if "prefill_fp8" in results else None,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -47,3 +47,38 @@ def step_bytes(T: int, K: int, H: int, n_kept: int, fp8: bool) -> int:
     """Algorithmic HBM bytes of layout + dispatch + combine."""
     return (layout_bytes(T, K) + dispatch_bytes(T, K, H, n_kept, fp8)
             + combine_bytes(T, K, H, n_kept))
+
+
+# ------------------------------------------------------------------------------------------
+# two-stage, rank-deduplicated path: N_tr = sum over ranks of the tokens sent there (one staging
+# row and one partial row each), N_kept = kept pairs
+# ------------------------------------------------------------------------------------------
+
+def rank_layout_bytes(T: int, K: int, R: int) -> int:
+    """Rank layout: read topk_idx, write rank_slot [T, R]."""
+    return 4 * T * K + 4 * T * R
+
+
+def dispatch_ranks_bytes(T: int, R: int, H: int, n_tr: int, fp8: bool) -> int:
+    """Stage 1: read x once and rank_slot, write one staging row (and scale row) per (token,
+    rank)."""
+    row = H + 4 * (H // 128) if fp8 else 2 * H
+    return 2 * T * H + row * n_tr + 4 * T * R
+
+
+def dispatch_expand_bytes(T: int, K: int, R: int, H: int, n_tr: int, n_kept: int,
+                          fp8: bool) -> int:
+    """Stage 2: read each staging row once, write one row per kept pair; idx, slot, rank_slot."""
+    row = H + 4 * (H // 128) if fp8 else 2 * H
+    return row * (n_tr + n_kept) + 8 * T * K + 4 * T * R
+
+
+def combine_ranks_bytes(T: int, K: int, R: int, H: int, n_tr: int, n_kept: int) -> int:
+    """Stage 1 of combine: read each kept y row, write one partial row per (token, rank)."""
+    return 2 * H * (n_kept + n_tr) + 12 * T * K + 4 * T * R
+
+
+def combine_reduce_bytes(T: int, R: int, H: int, n_tr: int) -> int:
+    """Stage 2 of combine: read each partial row once, write out once."""
+    return 2 * H * n_tr + 2 * T * H + 4 * T * R
+

@@ -19,10 +19,13 @@ EP_STATS_LEN = 4
 EP_MAX_EXPERTS = 1024
 EP_MAX_TOPK = 256
 EP_FP8_BLOCK = 128
+EP_MAX_RANKS = 64
 
 #: every entry point the header declares
 EXPORTED = ("ep_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_layout_dispatch",
-            "ep_layout_dispatch_fp8", "ep_combine", "ep_error_string", "ep_last_error",
+            "ep_layout_dispatch_fp8", "ep_combine", "ep_rank_layout", "ep_dispatch_ranks",
+            "ep_dispatch_ranks_fp8", "ep_dispatch_expand", "ep_dispatch_expand_fp8",
+            "ep_combine_ranks", "ep_combine_reduce", "ep_error_string", "ep_last_error",
             "ep_version")
 
 
@@ -60,9 +63,17 @@ def load_library():
         L.ep_combine.argtypes = [sp, vp, vp, vp, vp, vp, vp]
         L.ep_layout_dispatch.argtypes = [sp] + [vp] * 10
         L.ep_layout_dispatch_fp8.argtypes = [sp] + [vp] * 11
-        for fn in ("ep_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_layout_dispatch",
-                   "ep_layout_dispatch_fp8", "ep_combine"):
-            getattr(L, fn).restype = ctypes.c_int
+        L.ep_rank_layout.argtypes = [sp, vp, vp, vp, vp]
+        L.ep_dispatch_ranks.argtypes = [sp, vp, vp, vp, vp]
+        L.ep_dispatch_ranks_fp8.argtypes = [sp, vp, vp, vp, vp, vp]
+        L.ep_dispatch_expand.argtypes = [sp] + [vp] * 6
+        L.ep_dispatch_expand_fp8.argtypes = [sp] + [vp] * 8
+        L.ep_combine_ranks.argtypes = [sp] + [vp] * 7
+        L.ep_combine_reduce.argtypes = [sp] + [vp] * 4
+        for fn in EXPORTED:
+            if fn.startswith("ep_") and fn not in ("ep_error_string", "ep_last_error",
+                                                   "ep_version"):
+                getattr(L, fn).restype = ctypes.c_int
         L.ep_error_string.argtypes = [ctypes.c_int]
         L.ep_error_string.restype = ctypes.c_char_p
         L.ep_last_error.argtypes = []
@@ -268,3 +279,147 @@ def ep_combine(y: torch.Tensor, topk_idx: torch.Tensor, slot: torch.Tensor,
                                    _ptr(topk_w), _ptr(out), _stream(stream))
     _check("ep_combine", rc)
     return out
+
+
+# ------------------------------------------------------------------------------------------
+# two-stage, rank-deduplicated path (stage buffers are [R, T, ...])
+# ------------------------------------------------------------------------------------------
+
+def ep_rank_layout(topk_idx: torch.Tensor, E: int, R: int, *, rank_slot=None, rank_tokens=None,
+                   stream=None):
+    """Which virtual ranks each token goes to: ``rank_slot`` int32 [T, R] (position among the
+    rank's tokens, -1 if not sent) and ``rank_tokens`` int32 [R]."""
+    dev = topk_idx.device
+    T, K = topk_idx.shape
+    rank_slot = torch.empty((T, R), dtype=torch.int32, device=dev) if rank_slot is None else rank_slot
+    rank_tokens = (torch.empty(R, dtype=torch.int32, device=dev) if rank_tokens is None
+                   else rank_tokens)
+    _need(topk_idx, "topk_idx", torch.int32, T * K, dev)
+    _need(rank_slot, "rank_slot", torch.int32, T * R, dev)
+    _need(rank_tokens, "rank_tokens", torch.int32, R, dev)
+    sh = _shape(T, 1, E, K, 1, R)
+    rc = load_library().ep_rank_layout(ctypes.byref(sh), _ptr(topk_idx), _ptr(rank_slot),
+                                       _ptr(rank_tokens), _stream(stream))
+    _check("ep_rank_layout", rc)
+    return dict(rank_slot=rank_slot, rank_tokens=rank_tokens)
+
+
+def ep_dispatch_ranks(x: torch.Tensor, rank_slot: torch.Tensor, stage: torch.Tensor, *,
+                      stream=None):
+    """Stage 1 of dispatch: ``x`` [T, H] bf16 -> ``stage`` [R, T, H] bf16 (in place)."""
+    dev = x.device
+    T, H = x.shape
+    R = rank_slot.shape[1]
+    _need(x, "x", _bf16(x), T * H, dev)
+    _need(rank_slot, "rank_slot", torch.int32, T * R, dev)
+    _need(stage, "stage", _bf16(stage), R * T * H, dev)
+    sh = _shape(T, H, R, 1, 1, R)
+    rc = load_library().ep_dispatch_ranks(ctypes.byref(sh), _ptr(x), _ptr(rank_slot), _ptr(stage),
+                                          _stream(stream))
+    _check("ep_dispatch_ranks", rc)
+    return stage
+
+
+def ep_dispatch_ranks_fp8(x: torch.Tensor, rank_slot: torch.Tensor, stage_q: torch.Tensor,
+                          stage_scale: torch.Tensor, *, stream=None):
+    """FP8 stage 1: ``stage_q`` [R, T, H] uint8 and ``stage_scale`` [R, T, H/128] float32."""
+    dev = x.device
+    T, H = x.shape
+    R = rank_slot.shape[1]
+    _need(x, "x", _bf16(x), T * H, dev)
+    _need(rank_slot, "rank_slot", torch.int32, T * R, dev)
+    _need(stage_q, "stage_q", torch.uint8, R * T * H, dev)
+    _need(stage_scale, "stage_scale", torch.float32, R * T * (H // EP_FP8_BLOCK), dev)
+    sh = _shape(T, H, R, 1, 1, R)
+    rc = load_library().ep_dispatch_ranks_fp8(ctypes.byref(sh), _ptr(x), _ptr(rank_slot),
+                                              _ptr(stage_q), _ptr(stage_scale), _stream(stream))
+    _check("ep_dispatch_ranks_fp8", rc)
+    return stage_q, stage_scale
+
+
+def ep_dispatch_expand(stage: torch.Tensor, topk_idx: torch.Tensor, slot: torch.Tensor,
+                       rank_slot: torch.Tensor, recv: torch.Tensor, C: int, *, stream=None):
+    """Stage 2 of dispatch: ``stage`` [R, T, H] -> ``recv`` [E, C, H] bf16 (in place)."""
+    dev = stage.device
+    R, T, H = stage.shape
+    K = topk_idx.shape[1]
+    E = recv.numel() // (C * H)
+    _need(stage, "stage", _bf16(stage), R * T * H, dev)
+    _need(topk_idx, "topk_idx", torch.int32, T * K, dev)
+    _need(slot, "slot", torch.int32, T * K, dev)
+    _need(rank_slot, "rank_slot", torch.int32, T * R, dev)
+    _need(recv, "recv", _bf16(recv), E * C * H, dev)
+    sh = _shape(T, H, E, K, C, R)
+    rc = load_library().ep_dispatch_expand(ctypes.byref(sh), _ptr(stage), _ptr(topk_idx),
+                                           _ptr(slot), _ptr(rank_slot), _ptr(recv),
+                                           _stream(stream))
+    _check("ep_dispatch_expand", rc)
+    return recv
+
+
+def ep_dispatch_expand_fp8(stage_q: torch.Tensor, stage_scale: torch.Tensor,
+                           topk_idx: torch.Tensor, slot: torch.Tensor, rank_slot: torch.Tensor,
+                           recv_q: torch.Tensor, recv_scale: torch.Tensor, C: int, *,
+                           stream=None):
+    """FP8 stage 2: codes and scales of the staged rows -> ``recv_q`` [E, C, H] and
+    ``recv_scale`` [E, C, H/128] (in place)."""
+    dev = stage_q.device
+    R, T, H = stage_q.shape
+    K = topk_idx.shape[1]
+    E = recv_q.numel() // (C * H)
+    NB = H // EP_FP8_BLOCK
+    _need(stage_q, "stage_q", torch.uint8, R * T * H, dev)
+    _need(stage_scale, "stage_scale", torch.float32, R * T * NB, dev)
+    _need(topk_idx, "topk_idx", torch.int32, T * K, dev)
+    _need(slot, "slot", torch.int32, T * K, dev)
+    _need(rank_slot, "rank_slot", torch.int32, T * R, dev)
+    _need(recv_q, "recv_q", torch.uint8, E * C * H, dev)
+    _need(recv_scale, "recv_scale", torch.float32, E * C * NB, dev)
+    sh = _shape(T, H, E, K, C, R)
+    rc = load_library().ep_dispatch_expand_fp8(ctypes.byref(sh), _ptr(stage_q), _ptr(stage_scale),
+                                               _ptr(topk_idx), _ptr(slot), _ptr(rank_slot),
+                                               _ptr(recv_q), _ptr(recv_scale), _stream(stream))
+    _check("ep_dispatch_expand_fp8", rc)
+    return recv_q, recv_scale
+
+
+def ep_combine_ranks(y: torch.Tensor, topk_idx: torch.Tensor, slot: torch.Tensor,
+                     rank_slot: torch.Tensor, topk_w: torch.Tensor, C: int, *, part=None,
+                     stream=None):
+    """Stage 1 of combine: ``y`` [E, C, H] bf16 -> per-rank partial rows ``part`` [R, T, H]."""
+    dev = y.device
+    T, K = topk_idx.shape
+    R = rank_slot.shape[1]
+    H = y.shape[-1]
+    E = y.numel() // (C * H)
+    part = torch.empty((R, T, H), dtype=_bf16(y), device=dev) if part is None else part
+    _need(y, "y", _bf16(y), E * C * H, dev)
+    _need(topk_idx, "topk_idx", torch.int32, T * K, dev)
+    _need(slot, "slot", torch.int32, T * K, dev)
+    _need(rank_slot, "rank_slot", torch.int32, T * R, dev)
+    _need(topk_w, "topk_w", torch.float32, T * K, dev)
+    _need(part, "part", _bf16(part), R * T * H, dev)
+    sh = _shape(T, H, E, K, C, R)
+    rc = load_library().ep_combine_ranks(ctypes.byref(sh), _ptr(y), _ptr(topk_idx), _ptr(slot),
+                                         _ptr(rank_slot), _ptr(topk_w), _ptr(part),
+                                         _stream(stream))
+    _check("ep_combine_ranks", rc)
+    return part
+
+
+def ep_combine_reduce(part: torch.Tensor, rank_slot: torch.Tensor, K: int, *, out=None,
+                      stream=None):
+    """Stage 2 of combine: ``part`` [R, T, H] -> ``out`` [T, H] bf16. K (the top-k of the
+    routing) bounds the ranks a token reaches."""
+    dev = part.device
+    R, T, H = part.shape
+    out = torch.empty((T, H), dtype=_bf16(part), device=dev) if out is None else out
+    _need(part, "part", _bf16(part), R * T * H, dev)
+    _need(rank_slot, "rank_slot", torch.int32, T * R, dev)
+    _need(out, "out", _bf16(out), T * H, dev)
+    sh = _shape(T, H, R, K, 1, R)
+    rc = load_library().ep_combine_reduce(ctypes.byref(sh), _ptr(part), _ptr(rank_slot), _ptr(out),
+                                          _stream(stream))
+    _check("ep_combine_reduce", rc)
+    return out
+

@@ -74,6 +74,16 @@ int check_layout_args(const ep_shape_t *shape, const int32_t *topk_idx, const in
     return EP_OK;
 }
 
+// Limits of the two-stage calls: ranks as 64-bit sets, staging rows r*T + p in int32.
+int check_ranks(const ep_shape_t *s, const char *fn)
+{
+    if (s->R > EP_MAX_RANKS)
+        return fail(EP_ERR_UNSUPPORTED, std::string(fn) + ": R exceeds EP_MAX_RANKS");
+    if ((int64_t)s->R * s->T > INT32_MAX)
+        return fail(EP_ERR_UNSUPPORTED, std::string(fn) + ": R*T exceeds INT32_MAX");
+    return EP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -170,6 +180,124 @@ int ep_combine(const ep_shape_t *shape, const uint16_t *y, const int32_t *topk_i
         return fail(EP_ERR_ALIGN, "ep_combine: y and out must be 16-byte aligned");
     return hip_status(ep::launch_combine(*shape, y, topk_idx, slot, topk_w, out, stream),
                       "ep_combine");
+}
+
+int ep_rank_layout(const ep_shape_t *shape, const int32_t *topk_idx, int32_t *rank_slot,
+                   int32_t *rank_tokens, hipStream_t stream)
+{
+    const char *fn = "ep_rank_layout";
+    if (int rc = check_shape(shape, fn)) return rc;
+    if (int rc = check_ranks(shape, fn)) return rc;
+    if ((shape->T > 0 && (!topk_idx || !rank_slot)) || !rank_tokens)
+        return fail(EP_ERR_INVALID, "ep_rank_layout: NULL required pointer");
+    if (!aligned(topk_idx, 16) || !aligned(rank_slot, 16))
+        return fail(EP_ERR_ALIGN, "ep_rank_layout: topk_idx and rank_slot must be 16-byte aligned");
+    return hip_status(ep::launch_rank_layout(*shape, topk_idx, rank_slot, rank_tokens, stream),
+                      fn);
+}
+
+int ep_dispatch_ranks(const ep_shape_t *shape, const uint16_t *x, const int32_t *rank_slot,
+                      uint16_t *stage, hipStream_t stream)
+{
+    const char *fn = "ep_dispatch_ranks";
+    if (int rc = check_shape(shape, fn)) return rc;
+    if (int rc = check_rows(shape, fn, 8)) return rc;
+    if (int rc = check_ranks(shape, fn)) return rc;
+    if (shape->T == 0) return hip_status(hipSuccess, fn);
+    if (!x || !rank_slot || !stage) return fail(EP_ERR_INVALID, "ep_dispatch_ranks: NULL required pointer");
+    if (!aligned(x, 16) || !aligned(stage, 16))
+        return fail(EP_ERR_ALIGN, "ep_dispatch_ranks: x and stage must be 16-byte aligned");
+    return hip_status(ep::launch_dispatch_ranks_bf16(*shape, x, rank_slot, stage, stream), fn);
+}
+
+int ep_dispatch_ranks_fp8(const ep_shape_t *shape, const uint16_t *x, const int32_t *rank_slot,
+                          uint8_t *stage_q, float *stage_scale, hipStream_t stream)
+{
+    const char *fn = "ep_dispatch_ranks_fp8";
+    if (int rc = check_shape(shape, fn)) return rc;
+    if (int rc = check_rows(shape, fn, EP_FP8_BLOCK)) return rc;
+    if (int rc = check_ranks(shape, fn)) return rc;
+    if (shape->T == 0) return hip_status(hipSuccess, fn);
+    if (!x || !rank_slot || !stage_q || !stage_scale)
+        return fail(EP_ERR_INVALID, "ep_dispatch_ranks_fp8: NULL required pointer");
+    if (!aligned(x, 16) || !aligned(stage_q, 16) || !aligned(stage_scale, 4))
+        return fail(EP_ERR_ALIGN, "ep_dispatch_ranks_fp8: x and stage_q must be 16-byte aligned, "
+                                  "stage_scale 4-byte aligned");
+    return hip_status(ep::launch_dispatch_ranks_fp8(*shape, x, rank_slot, stage_q, stage_scale,
+                                                    stream),
+                      fn);
+}
+
+int ep_dispatch_expand(const ep_shape_t *shape, const uint16_t *stage, const int32_t *topk_idx,
+                       const int32_t *slot, const int32_t *rank_slot, uint16_t *recv,
+                       hipStream_t stream)
+{
+    const char *fn = "ep_dispatch_expand";
+    if (int rc = check_shape(shape, fn)) return rc;
+    if (int rc = check_rows(shape, fn, 8)) return rc;
+    if (int rc = check_ranks(shape, fn)) return rc;
+    if (shape->T == 0) return hip_status(hipSuccess, fn);
+    if (!stage || !topk_idx || !slot || !rank_slot || !recv)
+        return fail(EP_ERR_INVALID, "ep_dispatch_expand: NULL required pointer");
+    if (!aligned(stage, 16) || !aligned(recv, 16))
+        return fail(EP_ERR_ALIGN, "ep_dispatch_expand: stage and recv must be 16-byte aligned");
+    return hip_status(ep::launch_dispatch_expand_bf16(*shape, stage, topk_idx, slot, rank_slot,
+                                                      recv, stream),
+                      fn);
+}
+
+int ep_dispatch_expand_fp8(const ep_shape_t *shape, const uint8_t *stage_q,
+                           const float *stage_scale, const int32_t *topk_idx,
+                           const int32_t *slot, const int32_t *rank_slot, uint8_t *recv_q,
+                           float *recv_scale, hipStream_t stream)
+{
+    const char *fn = "ep_dispatch_expand_fp8";
+    if (int rc = check_shape(shape, fn)) return rc;
+    if (int rc = check_rows(shape, fn, EP_FP8_BLOCK)) return rc;
+    if (int rc = check_ranks(shape, fn)) return rc;
+    if (shape->T == 0) return hip_status(hipSuccess, fn);
+    if (!stage_q || !stage_scale || !topk_idx || !slot || !rank_slot || !recv_q || !recv_scale)
+        return fail(EP_ERR_INVALID, "ep_dispatch_expand_fp8: NULL required pointer");
+    if (!aligned(stage_q, 16) || !aligned(recv_q, 16) || !aligned(stage_scale, 4) ||
+        !aligned(recv_scale, 4))
+        return fail(EP_ERR_ALIGN, "ep_dispatch_expand_fp8: stage_q and recv_q must be 16-byte "
+                                  "aligned, the scale buffers 4-byte aligned");
+    return hip_status(ep::launch_dispatch_expand_fp8(*shape, stage_q, stage_scale, topk_idx, slot,
+                                                     rank_slot, recv_q, recv_scale, stream),
+                      fn);
+}
+
+int ep_combine_ranks(const ep_shape_t *shape, const uint16_t *y, const int32_t *topk_idx,
+                     const int32_t *slot, const int32_t *rank_slot, const float *topk_w,
+                     uint16_t *part, hipStream_t stream)
+{
+    const char *fn = "ep_combine_ranks";
+    if (int rc = check_shape(shape, fn)) return rc;
+    if (int rc = check_rows(shape, fn, 8)) return rc;
+    if (int rc = check_ranks(shape, fn)) return rc;
+    if (shape->T == 0) return hip_status(hipSuccess, fn);
+    if (!y || !topk_idx || !slot || !rank_slot || !topk_w || !part)
+        return fail(EP_ERR_INVALID, "ep_combine_ranks: NULL required pointer");
+    if (!aligned(y, 16) || !aligned(part, 16))
+        return fail(EP_ERR_ALIGN, "ep_combine_ranks: y and part must be 16-byte aligned");
+    return hip_status(ep::launch_combine_ranks(*shape, y, topk_idx, slot, rank_slot, topk_w,
+                                               part, stream),
+                      fn);
+}
+
+int ep_combine_reduce(const ep_shape_t *shape, const uint16_t *part, const int32_t *rank_slot,
+                      uint16_t *out, hipStream_t stream)
+{
+    const char *fn = "ep_combine_reduce";
+    if (int rc = check_shape(shape, fn)) return rc;
+    if (int rc = check_rows(shape, fn, 8)) return rc;
+    if (int rc = check_ranks(shape, fn)) return rc;
+    if (shape->T == 0) return hip_status(hipSuccess, fn);
+    if (!part || !rank_slot || !out)
+        return fail(EP_ERR_INVALID, "ep_combine_reduce: NULL required pointer");
+    if (!aligned(part, 16) || !aligned(out, 16))
+        return fail(EP_ERR_ALIGN, "ep_combine_reduce: part and out must be 16-byte aligned");
+    return hip_status(ep::launch_combine_reduce(*shape, part, rank_slot, out, stream), fn);
 }
 
 const char *ep_error_string(int code)

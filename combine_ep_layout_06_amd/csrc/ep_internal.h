@@ -60,4 +60,33 @@ hipError_t launch_combine(const ep_shape_t &s, const uint16_t *y, const int32_t 
                           const int32_t *slot, const float *w, uint16_t *out,
                           hipStream_t stream);
 
+// two-stage, rank-deduplicated path
+hipError_t launch_rank_layout(const ep_shape_t &s, const int32_t *idx, int32_t *rank_slot,
+                              int32_t *rank_tokens, hipStream_t stream);
+
+hipError_t launch_dispatch_ranks_bf16(const ep_shape_t &s, const uint16_t *x,
+                                      const int32_t *rank_slot, uint16_t *stage,
+                                      hipStream_t stream);
+
+hipError_t launch_dispatch_ranks_fp8(const ep_shape_t &s, const uint16_t *x,
+                                     const int32_t *rank_slot, uint8_t *stage_q,
+                                     float *stage_scale, hipStream_t stream);
+
+hipError_t launch_dispatch_expand_bf16(const ep_shape_t &s, const uint16_t *stage,
+                                       const int32_t *idx, const int32_t *slot,
+                                       const int32_t *rank_slot, uint16_t *recv,
+                                       hipStream_t stream);
+
+hipError_t launch_dispatch_expand_fp8(const ep_shape_t &s, const uint8_t *stage_q,
+                                      const float *stage_scale, const int32_t *idx,
+                                      const int32_t *slot, const int32_t *rank_slot,
+                                      uint8_t *recv_q, float *recv_scale, hipStream_t stream);
+
+hipError_t launch_combine_ranks(const ep_shape_t &s, const uint16_t *y, const int32_t *idx,
+                                const int32_t *slot, const int32_t *rank_slot, const float *w,
+                                uint16_t *part, hipStream_t stream);
+
+hipError_t launch_combine_reduce(const ep_shape_t &s, const uint16_t *part,
+                                 const int32_t *rank_slot, uint16_t *out, hipStream_t stream);
+
 }  // namespace ep

@@ -1,0 +1,849 @@
+// Two-stage, rank-deduplicated dispatch and combine on gfx950.
+//
+// The pages' kernel chain moves a token to each virtual rank once (dispatch_impl) and lets the
+// rank expand it into its experts' rows (dispatch_copy_epilogue); on the way back each rank
+// reduces per token (combine_impl) before the top-k reduction on the token's side
+// (combine_reduce_epilogue) (afdEP-comm validation record, kernel_timelines). The staging
+// buffer stage[R][T][row] stands in for the transport; every definition is in ep.h.
+//
+// Kernels:
+//  * rank_layout: one workgroup of 1024 lanes per 1024 tokens, one token per lane. A token's
+//    rank set is a 64-bit mask (R <= 64) built from its K ids (16-byte vectors for K = 4, 8,
+//    12, 16; the ids of several earlier tokens and the lane's own are all in flight together).
+//    Earlier tiles are counted per rank with one ballot per rank per 64 tokens, summed with
+//    scalar adds (LDS atomics on the set bits measured no faster, and slower for few ranks);
+//    the tile's own tokens are ranked with a ballot + v_mbcnt per rank and a 16-lane DPP scan
+//    over the wavefronts, like the expert layout.
+//  * dispatch_ranks (bf16 / FP8): the dispatch work items of ep_dispatch_item.h with the R
+//    staging rows of a token in place of its K expert rows.
+//  * expand (bf16 / FP8): per kept pair, the staged row of the pair's rank is copied to the
+//    pair's expert row; all of a token's row loads are issued before its stores (pairs of one
+//    rank load the same row, which the second time comes from the cache).
+//  * combine_ranks: a token's K expert rows are loaded once (straight-line, as in combine);
+//    then for each rank, in order of its first pair, its pairs are folded in ascending j with
+//    fmaf and the partial is rounded to bf16 and stored. K > 8 takes a sequential path.
+//  * combine_reduce: the token's partial rows, listed in ascending rank in LDS, are gathered
+//    and summed in that order in fp32, then rounded once.
+#include "ep_dispatch_item.h"
+#include "ep_internal.h"
+
+#ifndef EP_TWO_STAGE_U
+#define EP_TWO_STAGE_U 0        // 16-byte chunks per lane per item (0 = choose from the shape)
+#endif
+
+namespace ep {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kStage = 256;          // staged entries per token group (tpb*K, tpb*R <= kStage)
+constexpr int kRankTile = 1024;      // rank layout: tokens per workgroup, one per lane
+constexpr int kRankWaves = kRankTile / kWave;
+constexpr int kRankBatch = 4;        // earlier tokens per lane whose ids are loaded together
+
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// ------------------------------------------------------------------------------------------
+// rank layout
+// ------------------------------------------------------------------------------------------
+
+// Bit of id e's rank (e / EL) if e is a valid expert (0 <= e < E), else 0. Branch-free: the
+// division is unsigned and its result is masked before the shift.
+__device__ __forceinline__ uint64_t rank_bit(int e, int E, int EL)
+{
+    const unsigned r = (unsigned)e / (unsigned)EL;
+    return (unsigned)e < (unsigned)E ? (1ull << (r & 63u)) : 0ull;
+}
+
+__device__ __forceinline__ uint64_t ranks_of(const int4 *v, int nv, int E, int EL)
+{
+    uint64_t m = 0;
+    for (int j = 0; j < nv; ++j)
+        m |= rank_bit(v[j].x, E, EL) | rank_bit(v[j].y, E, EL) | rank_bit(v[j].z, E, EL) |
+             rank_bit(v[j].w, E, EL);
+    return m;
+}
+
+// Rank set of token t for any K, one id at a time.
+__device__ __forceinline__ uint64_t token_ranks_any(const int32_t *__restrict__ idx, int t, int K,
+                                                    int E, int EL)
+{
+    uint64_t m = 0;
+    for (int j = 0; j < K; ++j) m |= rank_bit(idx[(size_t)t * K + j], E, EL);
+    return m;
+}
+
+// KV > 0: K = 4*KV ids per token, read as KV 16-byte vectors; KV = 0: any K.
+template <int KV>
+__global__ __launch_bounds__(kRankTile) void rank_layout_kernel(
+    const int32_t *__restrict__ idx, int T, int K, int E, int R, int32_t *__restrict__ rank_slot,
+    int32_t *__restrict__ rank_tokens)
+{
+    __shared__ int32_t wcnt[kRankWaves][EP_MAX_RANKS];   // counts, then per-wavefront bases
+    __shared__ int32_t base[EP_MAX_RANKS];               // earlier-tile counts
+    __shared__ int4 out16[kRankTile][4];                 // 16 ranks of each token's output row
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int EL = E / R;
+    const int t0 = blockIdx.x * kRankTile;
+    const int t = t0 + tid;
+    const int q_first = wave * kWave + lane;     // this lane's token in each earlier tile
+
+    // 1. the lane's own token and the earlier tiles, 64 tokens per wavefront step (t0 is a
+    //    multiple of 1024, so a step is whole or absent). The first kRankBatch tiles and the
+    //    own token are loaded straight-line, all in flight together; per rank, the wavefront
+    //    sums the ballot counts of its tokens (scalar adds) and lane r keeps rank r's total.
+    uint64_t own = 0;
+    uint64_t m[kRankBatch];
+    if constexpr (KV > 0) {
+        int4 vo[KV], v[kRankBatch][KV];
+        if (t < T) {
+#pragma unroll
+            for (int j = 0; j < KV; ++j) vo[j] = reinterpret_cast<const int4 *>(idx + (size_t)t * K)[j];
+        }
+#pragma unroll
+        for (int b = 0; b < kRankBatch; ++b)
+            if (b * kRankTile < t0) {
+#pragma unroll
+                for (int j = 0; j < KV; ++j)
+                    v[b][j] = reinterpret_cast<const int4 *>(
+                        idx + (size_t)(q_first + b * kRankTile) * K)[j];
+            }
+        own = t < T ? ranks_of(vo, KV, E, EL) : 0;
+#pragma unroll
+        for (int b = 0; b < kRankBatch; ++b) m[b] = b * kRankTile < t0 ? ranks_of(v[b], KV, E, EL) : 0;
+    } else {
+        own = t < T ? token_ranks_any(idx, t, K, E, EL) : 0;
+#pragma unroll
+        for (int b = 0; b < kRankBatch; ++b)
+            m[b] = b * kRankTile < t0 ? token_ranks_any(idx, q_first + b * kRankTile, K, E, EL) : 0;
+    }
+    int acc = 0;
+    for (int b0 = 0;; b0 += kRankBatch) {
+        const int nb = min(kRankBatch, t0 / kRankTile - b0);     // tiles in this batch
+        uint32_t lo[kRankBatch], hi[kRankBatch];
+#pragma unroll
+        for (int b = 0; b < kRankBatch; ++b) {
+            lo[b] = (uint32_t)m[b];
+            hi[b] = (uint32_t)(m[b] >> 32);
+        }
+        for (int r = 0; r < R && nb > 0; ++r) {
+            int c = 0;
+#pragma unroll
+            for (int b = 0; b < kRankBatch; ++b)
+                if (b < nb) c += __popcll(__ballot((((r < 32 ? lo[b] : hi[b]) >> (r & 31)) & 1u) != 0));
+            acc = lane == r ? acc + c : acc;
+        }
+        if ((b0 + kRankBatch) * kRankTile >= t0) break;
+        // prefixes longer than kRankBatch tiles (T > 5*1024): further batches
+        const int bn = b0 + kRankBatch;
+        if constexpr (KV > 0) {
+            int4 v[kRankBatch][KV];
+#pragma unroll
+            for (int b = 0; b < kRankBatch; ++b)
+                if ((bn + b) * kRankTile < t0) {
+#pragma unroll
+                    for (int j = 0; j < KV; ++j)
+                        v[b][j] = reinterpret_cast<const int4 *>(
+                            idx + (size_t)(q_first + (bn + b) * kRankTile) * K)[j];
+                }
+#pragma unroll
+            for (int b = 0; b < kRankBatch; ++b)
+                m[b] = (bn + b) * kRankTile < t0 ? ranks_of(v[b], KV, E, EL) : 0;
+        } else {
+#pragma unroll
+            for (int b = 0; b < kRankBatch; ++b)
+                m[b] = (bn + b) * kRankTile < t0
+                           ? token_ranks_any(idx, q_first + (bn + b) * kRankTile, K, E, EL) : 0;
+        }
+    }
+    if (lane < R) wcnt[wave][lane] = acc;
+    __syncthreads();
+    if (tid < R) {
+        int sum = 0;
+        for (int w = 0; w < kRankWaves; ++w) sum += wcnt[w][tid];
+        base[tid] = sum;
+    }
+    __syncthreads();
+
+    // 2. this tile: per wavefront, how many of its tokens go to each rank
+    int own_cnt = 0;
+    for (int r = 0; r < R; ++r) {
+        const int c = __popcll(__ballot((own >> r) & 1));
+        own_cnt = lane == r ? c : own_cnt;
+    }
+    if (lane < R) wcnt[wave][lane] = own_cnt;
+    __syncthreads();
+
+    // 3. per rank, the 16 wavefront counts sit in one DPP row: exclusive scan from the
+    //    earlier-tile count gives each wavefront's base; the last tile writes the totals
+    if (tid < R * kRankWaves) {
+        const int r = tid / kRankWaves, w = tid % kRankWaves;
+        const int c = wcnt[w][r];
+        const int incl = row16_inclusive_sum(c);
+        const int b0 = base[r];
+        wcnt[w][r] = b0 + incl - c;
+        if (w == kRankWaves - 1 && blockIdx.x == gridDim.x - 1) rank_tokens[r] = b0 + incl;
+    }
+    __syncthreads();
+
+    // 4. the tile's rows of rank_slot, 16 ranks at a time through LDS so that consecutive lanes
+    //    store consecutive 16-byte pieces (R % 4 == 0; otherwise one value per store)
+    for (int r0 = 0; r0 < R; r0 += 16) {
+        int v[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int r = r0 + q;
+            const bool sent = r < R && ((own >> r) & 1);
+            const int pos = wcnt[wave][r < R ? r : 0] + count_below(__ballot(sent));
+            v[q] = sent ? pos : -1;
+        }
+        if ((R & 3) != 0) {
+            if (t < T)
+                for (int q = 0; q < 16 && r0 + q < R; ++q) rank_slot[(size_t)t * R + r0 + q] = v[q];
+            continue;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) out16[tid][q] = int4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+        __syncthreads();
+        const int nq = min(16, R - r0) / 4;               // 16-byte pieces per token in this pass
+        for (int k = tid; k < kRankTile * nq; k += kRankTile) {
+            const int tl = k / nq, q = k % nq;
+            if (t0 + tl < T)
+                *reinterpret_cast<int4 *>(rank_slot + (size_t)(t0 + tl) * R + r0 + 4 * q) =
+                    out16[tl][q];
+        }
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// dispatch, stage 1: one staging row per (token, rank)
+// ------------------------------------------------------------------------------------------
+
+// rows[tl*R + r] = r*T + rank_slot[t0 + tl][r], or -1 (not sent, or out of range)
+__device__ __forceinline__ void stage_rank_rows(int32_t *rows, const int32_t *__restrict__ rank_slot,
+                                                int t0, int nt, int R, int T)
+{
+    for (int k = threadIdx.x; k < nt * R; k += kThreads) {
+        const int p = rank_slot[(size_t)t0 * R + k];
+        rows[k] = (unsigned)p < (unsigned)T ? (k % R) * T + p : -1;
+    }
+}
+
+template <int KG, int U, bool MULTI>
+__global__ __launch_bounds__(kThreads) void dispatch_ranks_bf16_kernel(
+    const u32x4 *__restrict__ x, const int32_t *__restrict__ rank_slot, u32x4 *__restrict__ stage,
+    int T, int H8, int R, int tpb, int nseg)
+{
+    __shared__ int32_t rows[kStage];
+    const int wave = wave_uniform(threadIdx.x / kWave);
+    const int ntg = ceil_div(T, tpb);
+    for (int tg = blockIdx.x; tg < ntg; tg += gridDim.x) {
+        const int t0 = tg * tpb, nt = min(tpb, T - t0);
+        __syncthreads();
+        stage_rank_rows(rows, rank_slot, t0, nt, R, T);
+        __syncthreads();
+        for (int item = wave; item < nt * nseg; item += kWaves) {
+            const int tl = item / nseg;
+            dispatch_item_bf16<KG, U, MULTI>(x, stage, rows, t0 + tl, tl, item - tl * nseg, H8, R);
+        }
+    }
+}
+
+template <int KG, bool MULTI>
+__global__ __launch_bounds__(kThreads) void dispatch_ranks_fp8_kernel(
+    const u32x4 *__restrict__ x, const int32_t *__restrict__ rank_slot,
+    u32x4 *__restrict__ stage_q, float *__restrict__ stage_scale, int T, int H, int R, int tpb,
+    int nseg)
+{
+    __shared__ int32_t rows[kStage];
+    const int wave = wave_uniform(threadIdx.x / kWave);
+    const int ntg = ceil_div(T, tpb);
+    for (int tg = blockIdx.x; tg < ntg; tg += gridDim.x) {
+        const int t0 = tg * tpb, nt = min(tpb, T - t0);
+        __syncthreads();
+        stage_rank_rows(rows, rank_slot, t0, nt, R, T);
+        __syncthreads();
+        for (int item = wave; item < nt * nseg; item += kWaves) {
+            const int tl = item / nseg;
+            dispatch_item_fp8<KG, MULTI>(x, stage_q, stage_scale, rows, t0 + tl, tl,
+                                         item - tl * nseg, H, R);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// per-pair staging shared by the expansion and the partial combine
+// ------------------------------------------------------------------------------------------
+
+// For the pairs of tokens [t0, t0 + nt): the staging row of the pair's rank (src), its expert
+// row if kept (dst), its rank, and its weight. A pair takes part only if its id is a valid
+// expert whose rank row is known; dst additionally needs a slot below C. The group's
+// rank_slot rows are read into LDS first (coalesced), next to the pairs' ids and slots.
+struct PairLds {
+    int32_t rs[kStage];      // rank_slot rows of the group's tokens
+    int32_t src[kStage];
+    int32_t dst[kStage];
+    int32_t rnk[kStage];
+    float w[kStage];
+};
+
+__device__ __forceinline__ void stage_pairs(PairLds &L, const int32_t *__restrict__ idx,
+                                            const int32_t *__restrict__ slot,
+                                            const int32_t *__restrict__ rank_slot,
+                                            const float *__restrict__ w, int t0, int nt, int T,
+                                            int E, int C, int K, int R)
+{
+    for (int k = threadIdx.x; k < nt * R; k += kThreads) L.rs[k] = rank_slot[(size_t)t0 * R + k];
+    int e[2], s[2];
+    float wk[2];
+    const int EL = E / R;
+    // pairs per thread: nt*K <= kStage = 2*kThreads... loads first, then the LDS reads
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int k = threadIdx.x + u * kThreads;
+        const bool in = k < nt * K;
+        const size_t i = (size_t)t0 * K + (in ? k : 0);
+        e[u] = in ? idx[i] : -1;
+        s[u] = in ? slot[i] : -1;
+        wk[u] = (in && w) ? w[i] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int k = threadIdx.x + u * kThreads;
+        if (k >= nt * K) continue;
+        const bool valid = (unsigned)e[u] < (unsigned)E;
+        const int r = valid ? e[u] / EL : 0;
+        const int p = valid ? L.rs[(k / K) * R + r] : -1;
+        const bool ok = valid && (unsigned)p < (unsigned)T;
+        L.rnk[k] = ok ? r : -1;
+        L.src[k] = ok ? r * T + p : -1;
+        L.dst[k] = ok && (unsigned)s[u] < (unsigned)C ? e[u] * C + s[u] : -1;
+        L.w[k] = wk[u];
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// dispatch, stage 2: the rank's own expansion into its experts' rows
+// ------------------------------------------------------------------------------------------
+
+template <int KG, int U, bool MULTI>
+__global__ __launch_bounds__(kThreads) void expand_bf16_kernel(
+    const u32x4 *__restrict__ stage, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ slot, const int32_t *__restrict__ rank_slot,
+    u32x4 *__restrict__ recv, int T, int H8, int E, int C, int K, int R, int tpb, int nseg)
+{
+    __shared__ PairLds L;
+    const int wave = wave_uniform(threadIdx.x / kWave);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int ntg = ceil_div(T, tpb);
+    for (int tg = blockIdx.x; tg < ntg; tg += gridDim.x) {
+        const int t0 = tg * tpb, nt = min(tpb, T - t0);
+        __syncthreads();
+        stage_pairs(L, idx, slot, rank_slot, nullptr, t0, nt, T, E, C, K, R);
+        __syncthreads();
+        for (int item = wave; item < nt * nseg; item += kWaves) {
+            const int tl = item / nseg, seg = item - tl * nseg;
+            int cidx[U];
+            bool cok[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = (seg * U + u) * kWave + lane;
+                cok[u] = c < H8;
+                cidx[u] = cok[u] ? c : H8 - 1;
+            }
+            const int npg = MULTI ? ceil_div(K, KG) : 1;
+            for (int pg = 0; pg < npg; ++pg) {
+                int d[KG];
+                u32x4 v[KG][U];
+#pragma unroll
+                for (int g = 0; g < KG; ++g) {
+                    const int j = pg * KG + g;
+                    const int k = tl * K + (j < K ? j : K - 1);
+                    const int sr = wave_uniform(L.src[k]);
+                    d[g] = j < K ? wave_uniform(L.dst[k]) : -1;
+                    const u32x4 *src = stage + (size_t)(sr >= 0 ? sr : 0) * H8;
+#pragma unroll
+                    for (int u = 0; u < U; ++u) v[g][u] = src[cidx[u]];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int g = 0; g < KG; ++g) {
+                    if (d[g] < 0) continue;
+                    u32x4 *dst = recv + (size_t)d[g] * H8;
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        if (cok[u]) store16<EP_DISPATCH_NT_STORE>(dst + cidx[u], v[g][u]);
+                }
+            }
+        }
+    }
+}
+
+// FP8: a lane owns 16 codes (one 16-byte chunk) of a 1024-channel segment; the first lane of
+// each 8-lane group (one 128-channel block) also carries the block's scale.
+template <int KG, bool MULTI>
+__global__ __launch_bounds__(kThreads) void expand_fp8_kernel(
+    const u32x4 *__restrict__ stage_q, const float *__restrict__ stage_scale,
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ slot,
+    const int32_t *__restrict__ rank_slot, u32x4 *__restrict__ recv_q,
+    float *__restrict__ recv_scale, int T, int H, int E, int C, int K, int R, int tpb, int nseg)
+{
+    __shared__ PairLds L;
+    const int wave = wave_uniform(threadIdx.x / kWave);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int H16 = H / 16, NB = H / 128;
+    const int ntg = ceil_div(T, tpb);
+    for (int tg = blockIdx.x; tg < ntg; tg += gridDim.x) {
+        const int t0 = tg * tpb, nt = min(tpb, T - t0);
+        __syncthreads();
+        stage_pairs(L, idx, slot, rank_slot, nullptr, t0, nt, T, E, C, K, R);
+        __syncthreads();
+        for (int item = wave; item < nt * nseg; item += kWaves) {
+            const int tl = item / nseg, seg = item - tl * nseg;
+            const int h0 = seg * (16 * kWave) + lane * 16;
+            const bool act = h0 < H;
+            const bool lead = act && (lane & 7) == 0;
+            const int cq = act ? h0 / 16 : 0, cs = act ? h0 / 128 : 0;
+            const int npg = MULTI ? ceil_div(K, KG) : 1;
+            for (int pg = 0; pg < npg; ++pg) {
+                int d[KG];
+                u32x4 q[KG];
+                float sc[KG];
+#pragma unroll
+                for (int g = 0; g < KG; ++g) {
+                    const int j = pg * KG + g;
+                    const int k = tl * K + (j < K ? j : K - 1);
+                    const int sr = wave_uniform(L.src[k]);
+                    d[g] = j < K ? wave_uniform(L.dst[k]) : -1;
+                    const size_t row = (size_t)(sr >= 0 ? sr : 0);
+                    q[g] = stage_q[row * H16 + cq];
+                    sc[g] = stage_scale[row * NB + cs];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int g = 0; g < KG; ++g) {
+                    if (d[g] < 0) continue;
+                    if (act) recv_q[(size_t)d[g] * H16 + cq] = q[g];
+                    if (lead) recv_scale[(size_t)d[g] * NB + cs] = sc[g];
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// combine, stage 1: per-rank partials
+// ------------------------------------------------------------------------------------------
+
+__device__ __forceinline__ void fold_row(float (&acc)[8], float wj, const u32x4 &v)
+{
+    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        acc[2 * k] = __builtin_fmaf(wj, bf16_lo(wd[k]), acc[2 * k]);
+        acc[2 * k + 1] = __builtin_fmaf(wj, bf16_hi(wd[k]), acc[2 * k + 1]);
+    }
+}
+
+__device__ __forceinline__ u32x4 pack_bf16(const float (&acc)[8])
+{
+    u32x4 o;
+    o.x = bf16_rne(acc[0]) | (bf16_rne(acc[1]) << 16);
+    o.y = bf16_rne(acc[2]) | (bf16_rne(acc[3]) << 16);
+    o.z = bf16_rne(acc[4]) | (bf16_rne(acc[5]) << 16);
+    o.w = bf16_rne(acc[6]) | (bf16_rne(acc[7]) << 16);
+    return o;
+}
+
+// K <= KG <= 8: every row of the token loaded once, then one fold per rank.
+template <int KG, int U>
+__device__ __forceinline__ void combine_ranks_item(const PairLds &L, const u32x4 *__restrict__ y,
+                                                   u32x4 *__restrict__ part, int tl, int seg,
+                                                   int H8, int K)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    int cidx[U];
+    bool cok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = (seg * U + u) * kWave + lane;
+        cok[u] = c < H8;
+        cidx[u] = cok[u] ? c : H8 - 1;
+    }
+    int rk[KG], pr[KG], yr[KG];
+    float wj[KG];
+    u32x4 v[KG][U];
+#pragma unroll
+    for (int g = 0; g < KG; ++g) {
+        const int k = tl * K + (g < K ? g : K - 1);
+        rk[g] = g < K ? wave_uniform(L.rnk[k]) : -1;
+        pr[g] = wave_uniform(L.src[k]);        // the pair's rank row = its partial's row
+        yr[g] = g < K ? wave_uniform(L.dst[k]) : -1;
+        wj[g] = __int_as_float(wave_uniform(__float_as_int(L.w[k])));
+        const u32x4 *src = y + (size_t)(yr[g] >= 0 ? yr[g] : 0) * H8;
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[g][u] = load16<true>(src + cidx[u]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int g = 0; g < KG; ++g) {
+        if (rk[g] < 0) continue;
+        bool first = true;
+#pragma unroll
+        for (int h = 0; h < g; ++h) first = first && rk[h] != rk[g];
+        if (!first) continue;                  // this rank's partial was written at its first pair
+        float acc[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[u][c] = 0.0f;
+#pragma unroll
+        for (int g2 = g; g2 < KG; ++g2) {
+            if (rk[g2] != rk[g] || yr[g2] < 0) continue;
+#pragma unroll
+            for (int u = 0; u < U; ++u) fold_row(acc[u], wj[g2], v[g2][u]);
+        }
+        u32x4 *dst = part + (size_t)pr[g] * H8;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (cok[u]) store16<true>(dst + cidx[u], pack_bf16(acc[u]));
+    }
+}
+
+// K > 8: pairs in j order; at the first pair of each rank, that rank's pairs are folded one
+// row at a time.
+__device__ __forceinline__ void combine_ranks_item_seq(const PairLds &L,
+                                                       const u32x4 *__restrict__ y,
+                                                       u32x4 *__restrict__ part, int tl, int seg,
+                                                       int H8, int K)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int c = seg * kWave + lane;
+    const bool cok = c < H8;
+    const int ci = cok ? c : H8 - 1;
+    for (int g = 0; g < K; ++g) {
+        const int rg = wave_uniform(L.rnk[tl * K + g]);
+        if (rg < 0) continue;
+        bool first = true;
+        for (int h = 0; h < g && first; ++h) first = wave_uniform(L.rnk[tl * K + h]) != rg;
+        if (!first) continue;
+        float acc[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+        for (int g2 = g; g2 < K; ++g2) {
+            const int k = tl * K + g2;
+            const int yr = wave_uniform(L.dst[k]);
+            if (wave_uniform(L.rnk[k]) != rg || yr < 0) continue;
+            const float wj = __int_as_float(wave_uniform(__float_as_int(L.w[k])));
+            fold_row(acc, wj, load16<true>(y + (size_t)yr * H8 + ci));
+        }
+        if (cok) store16<true>(part + (size_t)wave_uniform(L.src[tl * K + g]) * H8 + ci,
+                               pack_bf16(acc));
+    }
+}
+
+template <int KG, int U, bool SEQ>
+__global__ __launch_bounds__(kThreads) void combine_ranks_kernel(
+    const u32x4 *__restrict__ y, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ slot, const int32_t *__restrict__ rank_slot,
+    const float *__restrict__ w, u32x4 *__restrict__ part, int T, int H8, int E, int C, int K,
+    int R, int tpb, int nseg)
+{
+    __shared__ PairLds L;
+    const int wave = wave_uniform(threadIdx.x / kWave);
+    const int ntg = ceil_div(T, tpb);
+    for (int tg = blockIdx.x; tg < ntg; tg += gridDim.x) {
+        const int t0 = tg * tpb, nt = min(tpb, T - t0);
+        __syncthreads();
+        stage_pairs(L, idx, slot, rank_slot, w, t0, nt, T, E, C, K, R);
+        __syncthreads();
+        for (int item = wave; item < nt * nseg; item += kWaves) {
+            const int tl = item / nseg, seg = item - tl * nseg;
+            if constexpr (SEQ) combine_ranks_item_seq(L, y, part, tl, seg, H8, K);
+            else combine_ranks_item<KG, U>(L, y, part, tl, seg, H8, K);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// combine, stage 2: the token's partials summed in ascending rank
+// ------------------------------------------------------------------------------------------
+
+template <int KG, int U, bool MULTI>
+__global__ __launch_bounds__(kThreads) void combine_reduce_kernel(
+    const u32x4 *__restrict__ part, const int32_t *__restrict__ rank_slot,
+    u32x4 *__restrict__ out, int T, int H8, int R, int Q, int tpb, int nseg)
+{
+    __shared__ int32_t rs[kStage];
+    __shared__ int32_t plist[kStage];     // per token, its partial rows in ascending rank
+    const int wave = wave_uniform(threadIdx.x / kWave);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int ntg = ceil_div(T, tpb);
+    for (int tg = blockIdx.x; tg < ntg; tg += gridDim.x) {
+        const int t0 = tg * tpb, nt = min(tpb, T - t0);
+        __syncthreads();
+        for (int k = threadIdx.x; k < nt * R; k += kThreads) rs[k] = rank_slot[(size_t)t0 * R + k];
+        __syncthreads();
+        if ((int)threadIdx.x < nt) {
+            const int tl = threadIdx.x;
+            int n = 0;
+            for (int r = 0; r < R && n < Q; ++r) {
+                const int p = rs[tl * R + r];
+                if ((unsigned)p < (unsigned)T) plist[tl * Q + n++] = r * T + p;
+            }
+            for (; n < Q; ++n) plist[tl * Q + n] = -1;
+        }
+        __syncthreads();
+        for (int item = wave; item < nt * nseg; item += kWaves) {
+            const int tl = item / nseg, seg = item - tl * nseg;
+            int cidx[U];
+            bool cok[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = (seg * U + u) * kWave + lane;
+                cok[u] = c < H8;
+                cidx[u] = cok[u] ? c : H8 - 1;
+            }
+            float acc[U][8];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[u][c] = 0.0f;
+            const int first_row = wave_uniform(plist[tl * Q]);
+            const int npg = MULTI ? ceil_div(Q, KG) : 1;
+            for (int pg = 0; pg < npg; ++pg) {
+                int pr[KG];
+                u32x4 v[KG][U];
+#pragma unroll
+                for (int g = 0; g < KG; ++g) {
+                    const int n = pg * KG + g;
+                    pr[g] = n < Q ? wave_uniform(plist[tl * Q + n]) : -1;
+                    // absent entries reload the first row (a cache hit), or row 0 if none
+                    const int rr = pr[g] >= 0 ? pr[g] : (first_row >= 0 ? first_row : 0);
+                    const u32x4 *src = part + (size_t)rr * H8;
+#pragma unroll
+                    for (int u = 0; u < U; ++u) v[g][u] = load16<true>(src + cidx[u]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int g = 0; g < KG; ++g) {
+                    const bool keep = pr[g] >= 0;
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const uint32_t wd[4] = {v[g][u].x, v[g][u].y, v[g][u].z, v[g][u].w};
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const float lo = acc[u][2 * c] + bf16_lo(wd[c]);
+                            const float hi = acc[u][2 * c + 1] + bf16_hi(wd[c]);
+                            acc[u][2 * c] = keep ? lo : acc[u][2 * c];
+                            acc[u][2 * c + 1] = keep ? hi : acc[u][2 * c + 1];
+                        }
+                    }
+                }
+            }
+            u32x4 *dst = out + (size_t)(t0 + tl) * H8;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (cok[u]) store16<true>(dst + cidx[u], pack_bf16(acc[u]));
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// launch shapes
+// ------------------------------------------------------------------------------------------
+
+// Chunks per lane: four on batches of at least ~4096 items, fewer on small ones.
+int pick_u(int T, int H8)
+{
+    if (EP_TWO_STAGE_U) return EP_TWO_STAGE_U;
+    for (int u : {4, 2})
+        if ((long)T * ceil_div(H8, u * kWave) >= 4096) return u;
+    return 1;
+}
+
+// Tokens per group: up to 4 at prefill size, with every staged table within kStage entries.
+int pick_tpb(int T, int per_token_a, int per_token_b)
+{
+    int tpb = T >= 2048 ? 4 : 1;
+    while (tpb > 1 && (tpb * per_token_a > kStage || tpb * per_token_b > kStage)) --tpb;
+    return tpb;
+}
+
+// Tokens per group for the staging copy: as the one-stage dispatch, about one item per
+// wavefront (two tokens per group at prefill size, four if a row is a single item).
+int pick_tpb_copy(int T, int R, int nseg)
+{
+    int tpb = (T >= 2048 ? 2 : 1) * (nseg == 1 ? 2 : 1);
+    while (tpb > 1 && tpb * R > kStage) --tpb;
+    return tpb;
+}
+
+dim3 grid_for(int T, int tpb) { return dim3(ceil_div(T, tpb)); }
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------------
+// launchers
+// ------------------------------------------------------------------------------------------
+
+hipError_t launch_rank_layout(const ep_shape_t &s, const int32_t *idx, int32_t *rank_slot,
+                              int32_t *rank_tokens, hipStream_t stream)
+{
+    const dim3 grid(s.T > 0 ? ceil_div(s.T, kRankTile) : 1), block(kRankTile);
+#define EP_LAUNCH_RL(KV)                                                                        \
+    return launch(rank_layout_kernel<KV>, grid, block, 0, stream, idx, s.T, s.K, s.E, s.R,      \
+                  rank_slot, rank_tokens)
+    if (s.K == 4) EP_LAUNCH_RL(1);
+    if (s.K == 8) EP_LAUNCH_RL(2);
+    if (s.K == 12) EP_LAUNCH_RL(3);
+    if (s.K == 16) EP_LAUNCH_RL(4);
+    EP_LAUNCH_RL(0);
+#undef EP_LAUNCH_RL
+}
+
+hipError_t launch_dispatch_ranks_bf16(const ep_shape_t &s, const uint16_t *x,
+                                      const int32_t *rank_slot, uint16_t *stage,
+                                      hipStream_t stream)
+{
+    const int H8 = s.H / 8, U = pick_u(s.T, H8), nseg = ceil_div(H8, U * kWave);
+    const int tpb = pick_tpb_copy(s.T, s.R, nseg);
+    const dim3 grid = grid_for(s.T, tpb), block(kThreads);
+    const u32x4 *xv = reinterpret_cast<const u32x4 *>(x);
+    u32x4 *sv = reinterpret_cast<u32x4 *>(stage);
+#define EP_LAUNCH_DR(KG, MULTI)                                                                \
+    do {                                                                                       \
+        if (U >= 4)                                                                            \
+            return launch(dispatch_ranks_bf16_kernel<KG, 4, MULTI>, grid, block, 0, stream, xv, \
+                          rank_slot, sv, s.T, H8, s.R, tpb, nseg);                             \
+        if (U == 2)                                                                            \
+            return launch(dispatch_ranks_bf16_kernel<KG, 2, MULTI>, grid, block, 0, stream, xv, \
+                          rank_slot, sv, s.T, H8, s.R, tpb, nseg);                             \
+        return launch(dispatch_ranks_bf16_kernel<KG, 1, MULTI>, grid, block, 0, stream, xv,     \
+                      rank_slot, sv, s.T, H8, s.R, tpb, nseg);                                 \
+    } while (0)
+    EP_BY_K(s.R, EP_LAUNCH_DR);
+#undef EP_LAUNCH_DR
+}
+
+hipError_t launch_dispatch_ranks_fp8(const ep_shape_t &s, const uint16_t *x,
+                                     const int32_t *rank_slot, uint8_t *stage_q,
+                                     float *stage_scale, hipStream_t stream)
+{
+    const int nseg = ceil_div(s.H, 16 * kWave);
+    const int tpb = pick_tpb_copy(s.T, s.R, nseg);
+    const dim3 grid = grid_for(s.T, tpb), block(kThreads);
+    const u32x4 *xv = reinterpret_cast<const u32x4 *>(x);
+    u32x4 *qv = reinterpret_cast<u32x4 *>(stage_q);
+#define EP_LAUNCH_DRQ(KG, MULTI)                                                                \
+    return launch(dispatch_ranks_fp8_kernel<KG, MULTI>, grid, block, 0, stream, xv, rank_slot, \
+                  qv, stage_scale, s.T, s.H, s.R, tpb, nseg)
+    EP_BY_K(s.R, EP_LAUNCH_DRQ);
+#undef EP_LAUNCH_DRQ
+}
+
+hipError_t launch_dispatch_expand_bf16(const ep_shape_t &s, const uint16_t *stage,
+                                       const int32_t *idx, const int32_t *slot,
+                                       const int32_t *rank_slot, uint16_t *recv,
+                                       hipStream_t stream)
+{
+    const int H8 = s.H / 8, U = pick_u(s.T, H8);
+    const int nseg = ceil_div(H8, U * kWave);
+    const int tpb = pick_tpb(s.T, s.K, s.R);
+    const dim3 grid = grid_for(s.T, tpb), block(kThreads);
+    const u32x4 *sv = reinterpret_cast<const u32x4 *>(stage);
+    u32x4 *rv = reinterpret_cast<u32x4 *>(recv);
+#define EP_LAUNCH_EX(KG, MULTI)                                                                 \
+    do {                                                                                        \
+        if (U >= 4)                                                                             \
+            return launch(expand_bf16_kernel<KG, 4, MULTI>, grid, block, 0, stream, sv, idx,     \
+                          slot, rank_slot, rv, s.T, H8, s.E, s.C, s.K, s.R, tpb, nseg);         \
+        if (U == 2)                                                                             \
+            return launch(expand_bf16_kernel<KG, 2, MULTI>, grid, block, 0, stream, sv, idx,     \
+                          slot, rank_slot, rv, s.T, H8, s.E, s.C, s.K, s.R, tpb, nseg);         \
+        return launch(expand_bf16_kernel<KG, 1, MULTI>, grid, block, 0, stream, sv, idx, slot,   \
+                      rank_slot, rv, s.T, H8, s.E, s.C, s.K, s.R, tpb, nseg);                   \
+    } while (0)
+    EP_BY_K(s.K, EP_LAUNCH_EX);
+#undef EP_LAUNCH_EX
+}
+
+hipError_t launch_dispatch_expand_fp8(const ep_shape_t &s, const uint8_t *stage_q,
+                                      const float *stage_scale, const int32_t *idx,
+                                      const int32_t *slot, const int32_t *rank_slot,
+                                      uint8_t *recv_q, float *recv_scale, hipStream_t stream)
+{
+    const int nseg = ceil_div(s.H, 16 * kWave);
+    const int tpb = pick_tpb(s.T, s.K, s.R);
+    const dim3 grid = grid_for(s.T, tpb), block(kThreads);
+    const u32x4 *sq = reinterpret_cast<const u32x4 *>(stage_q);
+    u32x4 *rq = reinterpret_cast<u32x4 *>(recv_q);
+#define EP_LAUNCH_EXQ(KG, MULTI)                                                                 \
+    return launch(expand_fp8_kernel<KG, MULTI>, grid, block, 0, stream, sq, stage_scale, idx,    \
+                  slot, rank_slot, rq, recv_scale, s.T, s.H, s.E, s.C, s.K, s.R, tpb, nseg)
+    EP_BY_K(s.K, EP_LAUNCH_EXQ);
+#undef EP_LAUNCH_EXQ
+}
+
+hipError_t launch_combine_ranks(const ep_shape_t &s, const uint16_t *y, const int32_t *idx,
+                                const int32_t *slot, const int32_t *rank_slot, const float *w,
+                                uint16_t *part, hipStream_t stream)
+{
+    const int H8 = s.H / 8;
+    const bool seq = s.K > 8;
+    const int U = seq ? 1 : pick_u(s.T, H8);
+    const int nseg = ceil_div(H8, U * kWave);
+    const int tpb = pick_tpb(s.T, s.K, s.R);
+    const dim3 grid = grid_for(s.T, tpb), block(kThreads);
+    const u32x4 *yv = reinterpret_cast<const u32x4 *>(y);
+    u32x4 *pv = reinterpret_cast<u32x4 *>(part);
+    if (seq)
+        return launch(combine_ranks_kernel<1, 1, true>, grid, block, 0, stream, yv, idx, slot,
+                      rank_slot, w, pv, s.T, H8, s.E, s.C, s.K, s.R, tpb, nseg);
+#define EP_LAUNCH_CR(KG)                                                                        \
+    do {                                                                                        \
+        if (U >= 4)                                                                             \
+            return launch(combine_ranks_kernel<KG, 4, false>, grid, block, 0, stream, yv, idx,   \
+                          slot, rank_slot, w, pv, s.T, H8, s.E, s.C, s.K, s.R, tpb, nseg);      \
+        if (U == 2)                                                                             \
+            return launch(combine_ranks_kernel<KG, 2, false>, grid, block, 0, stream, yv, idx,   \
+                          slot, rank_slot, w, pv, s.T, H8, s.E, s.C, s.K, s.R, tpb, nseg);      \
+        return launch(combine_ranks_kernel<KG, 1, false>, grid, block, 0, stream, yv, idx, slot, \
+                      rank_slot, w, pv, s.T, H8, s.E, s.C, s.K, s.R, tpb, nseg);                \
+    } while (0)
+    if (s.K > 4) EP_LAUNCH_CR(8);
+    if (s.K > 2) EP_LAUNCH_CR(4);
+    if (s.K > 1) EP_LAUNCH_CR(2);
+    EP_LAUNCH_CR(1);
+#undef EP_LAUNCH_CR
+}
+
+hipError_t launch_combine_reduce(const ep_shape_t &s, const uint16_t *part,
+                                 const int32_t *rank_slot, uint16_t *out, hipStream_t stream)
+{
+    const int H8 = s.H / 8, U = pick_u(s.T, H8);
+    const int nseg = ceil_div(H8, U * kWave);
+    const int Q = s.K < s.R ? s.K : s.R;           // a token reaches at most min(K, R) ranks
+    const int tpb = pick_tpb(s.T, s.R, Q);
+    const dim3 grid = grid_for(s.T, tpb), block(kThreads);
+    const u32x4 *pv = reinterpret_cast<const u32x4 *>(part);
+    u32x4 *ov = reinterpret_cast<u32x4 *>(out);
+#define EP_LAUNCH_RD(KG, MULTI)                                                                 \
+    do {                                                                                        \
+        if (U >= 4)                                                                             \
+            return launch(combine_reduce_kernel<KG, 4, MULTI>, grid, block, 0, stream, pv,       \
+                          rank_slot, ov, s.T, H8, s.R, Q, tpb, nseg);                           \
+        if (U == 2)                                                                             \
+            return launch(combine_reduce_kernel<KG, 2, MULTI>, grid, block, 0, stream, pv,       \
+                          rank_slot, ov, s.T, H8, s.R, Q, tpb, nseg);                           \
+        return launch(combine_reduce_kernel<KG, 1, MULTI>, grid, block, 0, stream, pv,           \
+                      rank_slot, ov, s.T, H8, s.R, Q, tpb, nseg);                               \
+    } while (0)
+    EP_BY_K(Q, EP_LAUNCH_RD);
+#undef EP_LAUNCH_RD
+}
+
+}  // namespace ep

@@ -56,6 +56,7 @@ enum {
 #define EP_MAX_EXPERTS 1024    /* largest E the layout kernel supports */
 #define EP_MAX_TOPK 256        /* largest K dispatch and combine support */
 #define EP_FP8_BLOCK 128       /* channels per FP8 scale */
+#define EP_MAX_RANKS 64        /* largest R the two-stage (per-rank) calls support */
 
 /*
  * ep_layout -- routing layout: per-expert counts, exclusive offsets and stable in-order slots
@@ -174,6 +175,94 @@ int ep_layout_dispatch_fp8(const ep_shape_t *shape, const uint16_t *x, const int
  */
 int ep_combine(const ep_shape_t *shape, const uint16_t *y, const int32_t *topk_idx,
                const int32_t *slot, const float *topk_w, uint16_t *out, hipStream_t stream);
+
+/*
+ * Two-stage, rank-deduplicated path.
+ *
+ * The pages' kernel chain moves a token to each virtual rank once (dispatch_impl), and the
+ * rank expands it into its experts' rows (dispatch_copy_epilogue); on the way back each rank
+ * reduces its experts' outputs per token (combine_impl) before the final top-k reduction on the
+ * token's side (combine_reduce_epilogue) (afdEP-comm validation record, kernel_timelines). Here
+ * the "transport" is a staging buffer in the same HBM, rank-major: stage[R][T][row], where row
+ * p of rank r holds the p-th token (in token order) sent to r. Composed, the calls give the
+ * one-stage results: ep_dispatch_ranks + ep_dispatch_expand leave recv exactly as ep_dispatch
+ * does (likewise for FP8); ep_combine_ranks + ep_combine_reduce compute the combine with the
+ * per-rank partial rounded to bf16 (the precision a rank would send back) and the partials
+ * summed in fp32 in ascending rank, which is bit-identical to ep_combine when R = 1.
+ *
+ * Common requirements (else EP_ERR_UNSUPPORTED): R <= EP_MAX_RANKS, R*T <= INT32_MAX; the
+ * row-buffer alignment and H rules of the one-stage calls.
+ */
+
+/*
+ * ep_rank_layout -- which virtual ranks each token goes to, and where.
+ *
+ * Token t is sent to rank r if any of its ids is a valid expert (0 <= id < E) of rank r,
+ * whatever the capacity decides later (the sender sees only the routing).
+ *   topk_idx    [T*K] int32 in   16-byte aligned
+ *   rank_slot   [T*R] int32 out  #{t' < t : t' sent to r} if t is sent to r, else -1;
+ *                                 16-byte aligned
+ *   rank_tokens [R]   int32 out  number of tokens sent to each rank
+ * T = 0 writes rank_tokens as zeros. Bit-exact and deterministic.
+ */
+int ep_rank_layout(const ep_shape_t *shape, const int32_t *topk_idx, int32_t *rank_slot,
+                   int32_t *rank_tokens, hipStream_t stream);
+
+/*
+ * ep_dispatch_ranks -- stage 1 of dispatch: each token row copied once to every rank it is
+ * sent to. stage [R*T*H] uint16 (bf16) out, 16-byte aligned: stage[r][rank_slot[t][r]][:] =
+ * x[t][:]; rows of tokens a rank does not receive are untouched. H % 8 == 0.
+ */
+int ep_dispatch_ranks(const ep_shape_t *shape, const uint16_t *x, const int32_t *rank_slot,
+                      uint16_t *stage, hipStream_t stream);
+
+/*
+ * ep_dispatch_ranks_fp8 -- stage 1 with the FP8 cast: each token quantised once (exactly as in
+ * ep_dispatch_fp8) and its codes / scales written to stage_q [R*T*H] uint8 (16-byte aligned)
+ * and stage_scale [R*T*(H/128)] float (4-byte aligned) at row rank_slot[t][r] of each rank.
+ * H % 128 == 0.
+ */
+int ep_dispatch_ranks_fp8(const ep_shape_t *shape, const uint16_t *x, const int32_t *rank_slot,
+                          uint8_t *stage_q, float *stage_scale, hipStream_t stream);
+
+/*
+ * ep_dispatch_expand -- stage 2 of dispatch, each rank's own expansion: for every pair i = t*K
+ * + j with 0 <= e < E and 0 <= slot[i] < C, recv[e][slot[i]][:] = stage[e / (E/R)]
+ * [rank_slot[t][e / (E/R)]][:]. Other rows of recv are untouched. K <= EP_MAX_TOPK, H % 8 == 0.
+ */
+int ep_dispatch_expand(const ep_shape_t *shape, const uint16_t *stage, const int32_t *topk_idx,
+                       const int32_t *slot, const int32_t *rank_slot, uint16_t *recv,
+                       hipStream_t stream);
+
+/*
+ * ep_dispatch_expand_fp8 -- stage 2 for FP8: codes and scales of the staged row copied to every
+ * kept pair's row of recv_q / recv_scale. H % 128 == 0.
+ */
+int ep_dispatch_expand_fp8(const ep_shape_t *shape, const uint8_t *stage_q,
+                           const float *stage_scale, const int32_t *topk_idx,
+                           const int32_t *slot, const int32_t *rank_slot, uint8_t *recv_q,
+                           float *recv_scale, hipStream_t stream);
+
+/*
+ * ep_combine_ranks -- stage 1 of combine, on each rank: one partial row per token the rank
+ * received,
+ *   part[r][rank_slot[t][r]][h] = bf16_rne(acc), acc = +0.0f, then for j = 0 .. K-1 ascending,
+ *   for each kept pair of t whose expert is in rank r: acc = fmaf(topk_w[i], y[e][slot][h], acc)
+ * (+0 if all of t's pairs in r were dropped). part [R*T*H] uint16 (bf16), 16-byte aligned; rows
+ * of tokens a rank did not receive are untouched. K <= EP_MAX_TOPK, H % 8 == 0.
+ */
+int ep_combine_ranks(const ep_shape_t *shape, const uint16_t *y, const int32_t *topk_idx,
+                     const int32_t *slot, const int32_t *rank_slot, const float *topk_w,
+                     uint16_t *part, hipStream_t stream);
+
+/*
+ * ep_combine_reduce -- stage 2 of combine, on the token's side:
+ *   out[t][h] = bf16_rne(acc), acc = +0.0f, then for r = 0 .. R-1 ascending with t sent to r:
+ *   acc = acc + float(part[r][rank_slot[t][r]][h])   (one IEEE fp32 addition each)
+ * A token sent nowhere gives +0. out [T*H] uint16 (bf16), 16-byte aligned. H % 8 == 0.
+ */
+int ep_combine_reduce(const ep_shape_t *shape, const uint16_t *part, const int32_t *rank_slot,
+                      uint16_t *out, hipStream_t stream);
 
 /* Static text for an EP_* code. */
 const char *ep_error_string(int code);

@@ -74,6 +74,9 @@ def lib():
         L.oracle_combine_ranks.restype = None
         L.oracle_combine_reduce.argtypes = [_c_int] * 3 + [_u16p, _i32p, _u16p]
         L.oracle_combine_reduce.restype = None
+        L.oracle_combine_two_stage_tokens.argtypes = ([_c_int, _i32p] + [_c_int] * 5
+                                                      + [_u16p, _i32p, _i32p, _i32p, _f32p, _u16p])
+        L.oracle_combine_two_stage_tokens.restype = None
         L.oracle_bf16_rne_array.argtypes = [_f32p, _u16p, _c_long]
         L.oracle_bf16_rne_array.restype = None
         L.oracle_e4m3_rne_sat_array.argtypes = [_f32p, _u8p, _c_long]
@@ -265,5 +268,20 @@ def combine_reduce(part: np.ndarray, rank_slot: np.ndarray) -> np.ndarray:
     R, T, H = part.shape
     out = np.empty((T, H), dtype=np.uint16)
     lib().oracle_combine_reduce(T, H, R, _c(part), _c(rank_slot), out)
+    return out
+
+
+def combine_two_stage_tokens(tokens: np.ndarray, y: np.ndarray, topk_idx: np.ndarray,
+                             slot: np.ndarray, rank_slot: np.ndarray,
+                             topk_w: np.ndarray) -> np.ndarray:
+    """The two-stage combine for a subset of tokens; row n of the result is token tokens[n]."""
+    E, C, H = y.shape
+    T, K = topk_idx.shape
+    R = rank_slot.shape[1]
+    tok = _c(tokens, np.int32)
+    assert tok.size == 0 or (tok.min() >= 0 and tok.max() < T)
+    out = np.empty((tok.size, H), dtype=np.uint16)
+    lib().oracle_combine_two_stage_tokens(tok.size, tok, H, E, K, C, R, _c(y), _c(topk_idx),
+                                          _c(slot), _c(rank_slot), _c(topk_w, np.float32), out)
     return out
 

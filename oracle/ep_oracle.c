@@ -440,6 +440,35 @@ void oracle_combine_reduce(int T, int H, int R, const uint16_t *part, const int3
         }
 }
 
+/* The two-stage combine for a subset of tokens: out row n is token tokens[n]. The token's
+ * per-rank partials are formed as in oracle_combine_ranks (rounded to bf16) and summed as in
+ * oracle_combine_reduce. */
+void oracle_combine_two_stage_tokens(int n_tokens, const int32_t *tokens, int H, int E, int K,
+                                     int C, int R, const uint16_t *y, const int32_t *topk_idx,
+                                     const int32_t *slot, const int32_t *rank_slot,
+                                     const float *topk_w, uint16_t *out)
+{
+    int EL = E / R;
+    for (int n = 0; n < n_tokens; ++n) {
+        int t = tokens[n];
+        for (int h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int r = 0; r < R; ++r) {
+                if (rank_slot[(long)t * R + r] < 0) continue;
+                float part = 0.0f;
+                for (int j = 0; j < K; ++j) {
+                    long i = (long)t * K + j;
+                    int32_t e = topk_idx[i], s = slot[i];
+                    if (!pair_kept(e, s, E, C) || e / EL != r) continue;
+                    part = fmaf(topk_w[i], oracle_bf16_to_f32(y[((long)e * C + s) * H + h]), part);
+                }
+                acc = acc + oracle_bf16_to_f32(oracle_bf16_rne(part));
+            }
+            out[(long)n * H + h] = oracle_bf16_rne(acc);
+        }
+    }
+}
+
 /* Same as oracle_combine for a subset of tokens: out row n is token tokens[n]. */
 void oracle_combine_tokens(int n_tokens, const int32_t *tokens, int H, int E, int K, int C,
                            const uint16_t *y, const int32_t *topk_idx, const int32_t *slot,

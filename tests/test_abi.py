@@ -43,6 +43,7 @@ def test_header_constants_match_binding():
     assert int(consts["EP_MAX_EXPERTS"]) == B.EP_MAX_EXPERTS
     assert int(consts["EP_MAX_TOPK"]) == B.EP_MAX_TOPK
     assert int(consts["EP_FP8_BLOCK"]) == B.EP_FP8_BLOCK
+    assert int(consts["EP_MAX_RANKS"]) == B.EP_MAX_RANKS
     codes = dict(re.findall(r"(EP_OK|EP_ERR_[A-Z]+)\s*=\s*(-?\d+)", text))
     assert {k: int(v) for k, v in codes.items()} == {
         "EP_OK": B.EP_OK, "EP_ERR_INVALID": B.EP_ERR_INVALID, "EP_ERR_ALIGN": B.EP_ERR_ALIGN,
@@ -101,3 +102,29 @@ def test_dispatch_and_combine_reject_bad_arguments(lib):
     assert lib.ep_dispatch_fp8(shape(**big_k), A16, A16, A16, A16, A16, None) == B.EP_ERR_UNSUPPORTED
     assert lib.ep_combine(shape(**big_k), A16, A16, A16, A16, A16, None) == B.EP_ERR_UNSUPPORTED
     assert "EP_MAX_TOPK" in lib.ep_last_error().decode()
+
+
+def test_two_stage_calls_reject_bad_arguments(lib):
+    many_ranks = dict(E=128, R=128)                     # R above EP_MAX_RANKS
+    assert lib.ep_rank_layout(shape(**many_ranks), A16, A16, A16, None) == B.EP_ERR_UNSUPPORTED
+    assert "EP_MAX_RANKS" in lib.ep_last_error().decode()
+    assert lib.ep_rank_layout(shape(), A16 + 4, A16, A16, None) == B.EP_ERR_ALIGN
+    assert lib.ep_rank_layout(shape(), A16, A16 + 4, A16, None) == B.EP_ERR_ALIGN
+    assert lib.ep_rank_layout(shape(), A16, A16, None, None) == B.EP_ERR_INVALID
+    assert lib.ep_rank_layout(shape(T=1 << 28, K=1, R=16), A16, A16, A16, None) == B.EP_ERR_UNSUPPORTED
+    assert "R*T" in lib.ep_last_error().decode()
+    assert lib.ep_dispatch_ranks(shape(**many_ranks), A16, A16, A16, None) == B.EP_ERR_UNSUPPORTED
+    assert lib.ep_dispatch_ranks(shape(), A16, A16, A16 + 2, None) == B.EP_ERR_ALIGN
+    assert lib.ep_dispatch_ranks(shape(H=12), A16, A16, A16, None) == B.EP_ERR_UNSUPPORTED
+    assert lib.ep_dispatch_ranks_fp8(shape(H=1000), A16, A16, A16, A16, None) == B.EP_ERR_UNSUPPORTED
+    assert lib.ep_dispatch_ranks_fp8(shape(), A16, A16, A16, A16 + 2, None) == B.EP_ERR_ALIGN
+    assert lib.ep_dispatch_expand(shape(), A16, A16, A16, None, A16, None) == B.EP_ERR_INVALID
+    assert lib.ep_dispatch_expand(shape(), A16, A16, A16, A16, A16 + 8, None) == B.EP_ERR_ALIGN
+    assert lib.ep_dispatch_expand_fp8(shape(), A16, A16 + 2, A16, A16, A16, A16, A16,
+                                      None) == B.EP_ERR_ALIGN
+    assert lib.ep_combine_ranks(shape(), A16, A16, A16, A16, A16, A16 + 4, None) == B.EP_ERR_ALIGN
+    assert lib.ep_combine_ranks(shape(K=300, E=512, R=1), A16, A16, A16, A16, A16, A16,
+                                None) == B.EP_ERR_UNSUPPORTED
+    assert lib.ep_combine_reduce(shape(), A16, None, A16, None) == B.EP_ERR_INVALID
+    assert lib.ep_combine_reduce(shape(**many_ranks), A16, A16, A16, None) == B.EP_ERR_UNSUPPORTED
+

@@ -39,3 +39,21 @@ def test_algorithmic_bytes_prefill_bf16():
     assert b == 8 * T * K + (2 * T * H + 2 * H * T * K + 8 * T * K) + (2 * H * T * K + 12 * T * K + 2 * T * H)
     assert round(b / 1e6, 1) == 302.9
     assert round(A.step_bytes(T, K, H, T * K, fp8=True) / 1e6, 1) == 237.9
+
+
+def test_two_stage_bytes_reduce_to_one_stage_when_nothing_is_shared():
+    """With one expert per rank and distinct experts per token every (token, rank) carries
+    exactly one pair (N_tr = N_kept): the expansion and the reduction then only move rows the
+    one-stage kernels move directly, so the two stages together cost exactly one extra write and
+    read of every row on each side."""
+    T, K, H = 4096, 8, 2048
+    R = E = 128
+    n = T * K
+    one_dispatch = A.dispatch_bytes(T, K, H, n, False)
+    two_dispatch = (A.dispatch_ranks_bytes(T, R, H, n, False)
+                    + A.dispatch_expand_bytes(T, K, R, H, n, n, False))
+    assert two_dispatch - one_dispatch == 2 * (2 * H * n) + 2 * 4 * T * R
+    one_combine = A.combine_bytes(T, K, H, n)
+    two_combine = A.combine_ranks_bytes(T, K, R, H, n, n) + A.combine_reduce_bytes(T, R, H, n)
+    assert two_combine - one_combine == 2 * (2 * H * n) + 2 * 4 * T * R
+

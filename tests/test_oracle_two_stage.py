@@ -277,3 +277,17 @@ def test_final_reduction_is_in_ascending_rank_order():
     assert (part[:, 0] == y[:, 0]).all()
     assert (got == 0).all()
     assert (oracle.combine(y, idx, lay["slot"], w) == 0x3F80).all()     # j order: 1
+
+
+@pytest.mark.parametrize("T,H,E,K,C,R,seed", TWO_STAGE_CASES)
+def test_two_stage_tokens_subset_matches_full(T, H, E, K, C, R, seed):
+    """The token-subset form (used at sizes where the full oracle is slow) gives the full
+    result's rows."""
+    idx, _, w = random_case(T, H, E, K, C, R, seed)
+    lay = oracle.layout(idx, E, C, R)
+    y = y_for(lay, E, C, H, seed)
+    full, _, rl = two_stage_combine(y, idx, lay["slot"], w, E, R)
+    tokens = np.array([T - 1, 0, T // 2, 3, T // 3], np.int32)
+    sub = oracle.combine_two_stage_tokens(tokens, y, idx, lay["slot"], rl["rank_slot"], w)
+    assert np.array_equal(sub, full[tokens])
+
