@@ -41,7 +41,9 @@ class EpConfig:
     The E experts are laid out as R virtual ranks of E/R experts each (rank-major).
     ``route`` is one of ``uniform`` (K distinct experts per token, uniformly at random),
     ``zipf`` (K distinct experts sampled without replacement from a Zipf(s) law over a seeded
-    expert permutation) or ``balanced`` (the closed-form stride route; see ``balanced_route``).
+    expert permutation), ``balanced`` (the closed-form stride route; see ``balanced_route``) or
+    ``unbalanced`` (K distinct experts without replacement, where a seeded eighth of the experts
+    is ``unbalanced_ratio`` times as likely as the others).
     ``fp8`` selects the FP8 dispatch for the benchmark step; combine is bf16 in every config.
     """
     name: str
@@ -55,6 +57,7 @@ class EpConfig:
     fp8: bool = False
     outliers: bool = False
     zipf_s: float = 1.2
+    unbalanced_ratio: float = 1.0
     seed: int = 0
     note: str = ""
 
@@ -86,6 +89,15 @@ CONFIGS: dict[str, EpConfig] = {c.name: c for c in [
              note="Prefill-like FP8 dispatch on 96 experts, 3 virtual ranks x 32 experts"),
     EpConfig("balanced_stride", T=1024, H=2048, E=128, K=8, C=4096, R=16, route="balanced",
              note="Closed-form stride route: every expert receives exactly T*K/E pairs"),
+    # The second family: the pages' balanced stride route above and a skew with a named
+    # unbalanced ratio (the benchmark's --unbalanced-ratio axis, which the pages name but did not
+    # run). A seeded 16 of the 128 experts are 4 times as likely as the rest.
+    EpConfig("unbalanced_r4", T=4096, H=2048, E=128, K=8, C=4096, R=16, route="unbalanced",
+             unbalanced_ratio=4.0,
+             note="Prefill-like, hot eighth of the experts 4x as likely; no drops (C = T)"),
+    EpConfig("unbalanced_r4_c512", T=4096, H=2048, E=128, K=8, C=512, R=16,
+             route="unbalanced", unbalanced_ratio=4.0,
+             note="The same with capacity 512: the hot experts drop in token order"),
 ]}
 
 
@@ -140,6 +152,16 @@ def _route(cfg: EpConfig, rng: np.random.Generator) -> np.ndarray:
         return np.argsort(-keys, axis=1, kind="stable")[:, :K].astype(np.int32)
     if cfg.route == "balanced":
         return balanced_route(T, K, E, cfg.seed)
+    if cfg.route == "unbalanced":
+        # a seeded eighth of the experts (at least one) has weight `unbalanced_ratio`, the
+        # rest weight 1; K distinct experts per token by the Gumbel-top-K construction
+        perm = rng.permutation(E)
+        p = np.ones(E, dtype=np.float64)
+        p[perm[:max(1, E // 8)]] = cfg.unbalanced_ratio
+        p /= p.sum()
+        g = rng.gumbel(size=(T, E))
+        keys = np.log(p)[None, :] + g
+        return np.argsort(-keys, axis=1, kind="stable")[:, :K].astype(np.int32)
     raise ValueError(f"unknown route {cfg.route!r}")
 
 

@@ -77,6 +77,15 @@ def lib():
         L.oracle_combine_two_stage_tokens.argtypes = ([_c_int, _i32p] + [_c_int] * 5
                                                       + [_u16p, _i32p, _i32p, _i32p, _f32p, _u16p])
         L.oracle_combine_two_stage_tokens.restype = None
+        L.oracle_packed_offsets.argtypes = [_c_int, _c_int, _i32p, _i32p]
+        L.oracle_packed_offsets.restype = None
+        L.oracle_dispatch_packed.argtypes = [_c_int] * 6 + [_u16p, _i32p, _i32p, _i32p, _u16p]
+        L.oracle_dispatch_packed.restype = None
+        L.oracle_dispatch_packed_fp8.argtypes = ([_c_int] * 6
+                                                 + [_u16p, _i32p, _i32p, _i32p, _u8p, _f32p])
+        L.oracle_dispatch_packed_fp8.restype = None
+        L.oracle_combine_packed.argtypes = [_c_int] * 6 + [_u16p, _i32p, _i32p, _i32p, _f32p, _u16p]
+        L.oracle_combine_packed.restype = None
         L.oracle_bf16_rne_array.argtypes = [_f32p, _u16p, _c_long]
         L.oracle_bf16_rne_array.restype = None
         L.oracle_e4m3_rne_sat_array.argtypes = [_f32p, _u8p, _c_long]
@@ -283,5 +292,50 @@ def combine_two_stage_tokens(tokens: np.ndarray, y: np.ndarray, topk_idx: np.nda
     out = np.empty((tok.size, H), dtype=np.uint16)
     lib().oracle_combine_two_stage_tokens(tok.size, tok, H, E, K, C, R, _c(y), _c(topk_idx),
                                           _c(slot), _c(rank_slot), _c(topk_w, np.float32), out)
+    return out
+
+
+# ------------------------------------------------------------------------------------------
+# packed, aligned receive layout
+# ------------------------------------------------------------------------------------------
+
+def packed_offsets(count: np.ndarray, align: int) -> np.ndarray:
+    """offset [E+1]: exclusive scan of the kept counts rounded up to multiples of ``align``;
+    offset[E] is the number of rows of the packed buffer."""
+    cnt = _c(count, np.int32)
+    off = np.empty(cnt.size + 1, dtype=np.int32)
+    lib().oracle_packed_offsets(cnt.size, int(align), cnt, off)
+    return off
+
+
+def dispatch_packed(x, topk_idx, slot, offset, E, C, recv):
+    """bf16 dispatch into the packed ``recv`` (uint16 [rows, H]), in place."""
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    rows = recv.shape[0]
+    assert recv.shape == (rows, H) and recv.dtype == np.uint16 and recv.flags.c_contiguous
+    lib().oracle_dispatch_packed(T, H, E, K, C, rows, _c(x), _c(topk_idx), _c(slot), _c(offset),
+                                 recv)
+    return recv
+
+
+def dispatch_packed_fp8(x, topk_idx, slot, offset, E, C, recv_q, recv_scale):
+    """FP8 dispatch into the packed ``recv_q`` [rows, H] and ``recv_scale`` [rows, H/128]."""
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    rows = recv_q.shape[0]
+    assert recv_q.shape == (rows, H) and recv_scale.shape == (rows, H // 128)
+    lib().oracle_dispatch_packed_fp8(T, H, E, K, C, rows, _c(x), _c(topk_idx), _c(slot),
+                                     _c(offset), recv_q, recv_scale)
+    return recv_q, recv_scale
+
+
+def combine_packed(y, topk_idx, slot, offset, topk_w, E, C):
+    """Combine from the packed ``y`` (uint16 [rows, H]) -> out (uint16 [T, H])."""
+    rows, H = y.shape
+    T, K = topk_idx.shape
+    out = np.empty((T, H), dtype=np.uint16)
+    lib().oracle_combine_packed(T, H, E, K, C, rows, _c(y), _c(topk_idx), _c(slot), _c(offset),
+                                _c(topk_w, np.float32), out)
     return out
 

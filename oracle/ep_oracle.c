@@ -34,7 +34,10 @@
  *    applied to the experts' rows on the receiving side); a rank's tokens keep token order; the
  *    per-rank partial is the same fmaf fold over the token's kept pairs of that rank, rounded
  *    once to bf16 (the combine payload is bf16); the final row is the fp32 sum of the
- *    partials in ascending rank, rounded once to bf16.
+ *    partials in ascending rank, rounded once to bf16. Packed layout (the expert_alignment
+ *    parameter the pages pin to 1 for their runs): each expert's kept count rounded up to a
+ *    multiple of the alignment, offsets the exclusive scan of those, pair (t, j) at row
+ *    offset[e] + slot of a [rows][H] buffer; padding rows are left as they are.
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fPIC -shared (no -ffast-math, no
  * FMA contraction: every fp32 operation below is one IEEE operation).
@@ -467,6 +470,81 @@ void oracle_combine_two_stage_tokens(int n_tokens, const int32_t *tokens, int H,
             out[(long)n * H + h] = oracle_bf16_rne(acc);
         }
     }
+}
+
+/* ----------------------------------------------------------------------------------------- */
+/* Packed, aligned receive layout                                                             */
+/* ----------------------------------------------------------------------------------------- */
+
+/* offset[0] = 0, offset[e + 1] = offset[e] + (count[e] rounded up to a multiple of align);
+ * offset[E] is the number of rows the packed buffer needs. */
+void oracle_packed_offsets(int E, int align, const int32_t *count, int32_t *offset)
+{
+    offset[0] = 0;
+    for (int e = 0; e < E; ++e) {
+        int32_t padded = (count[e] + align - 1) / align * align;
+        offset[e + 1] = offset[e] + padded;
+    }
+}
+
+/* Row of a kept pair in a packed buffer of `rows` rows, or -1. */
+static long packed_row(int32_t e, int32_t s, int E, int C, const int32_t *offset, int rows)
+{
+    if (!pair_kept(e, s, E, C)) return -1;
+    long r = (long)offset[e] + s;
+    return (r >= 0 && r < rows) ? r : -1;
+}
+
+/* recv[offset[e] + slot[i]][:] = x[i / K][:] for every kept pair i; other rows as they are. */
+void oracle_dispatch_packed(int T, int H, int E, int K, int C, int rows, const uint16_t *x,
+                            const int32_t *topk_idx, const int32_t *slot, const int32_t *offset,
+                            uint16_t *recv)
+{
+    for (int t = 0; t < T; ++t)
+        for (int j = 0; j < K; ++j) {
+            long i = (long)t * K + j;
+            long r = packed_row(topk_idx[i], slot[i], E, C, offset, rows);
+            if (r < 0) continue;
+            memcpy(recv + r * H, x + (long)t * H, (size_t)H * sizeof(uint16_t));
+        }
+}
+
+/* FP8 into the packed layout: token t quantised once, codes and scales to every kept row. */
+void oracle_dispatch_packed_fp8(int T, int H, int E, int K, int C, int rows, const uint16_t *x,
+                                const int32_t *topk_idx, const int32_t *slot,
+                                const int32_t *offset, uint8_t *recv_q, float *recv_scale)
+{
+    int NB = H / 128;
+    uint8_t q[H > 0 ? H : 1];
+    float sc[NB > 0 ? NB : 1];
+    for (int t = 0; t < T; ++t) {
+        quantise_token(H, x + (long)t * H, q, sc);
+        for (int j = 0; j < K; ++j) {
+            long i = (long)t * K + j;
+            long r = packed_row(topk_idx[i], slot[i], E, C, offset, rows);
+            if (r < 0) continue;
+            memcpy(recv_q + r * H, q, (size_t)H);
+            memcpy(recv_scale + r * NB, sc, (size_t)NB * sizeof(float));
+        }
+    }
+}
+
+/* Combine from the packed layout: as oracle_combine with y[e][slot] at row offset[e] + slot. */
+void oracle_combine_packed(int T, int H, int E, int K, int C, int rows, const uint16_t *y,
+                           const int32_t *topk_idx, const int32_t *slot, const int32_t *offset,
+                           const float *topk_w, uint16_t *out)
+{
+    for (int t = 0; t < T; ++t)
+        for (int h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int j = 0; j < K; ++j) {
+                long i = (long)t * K + j;
+                long r = packed_row(topk_idx[i], slot[i], E, C, offset, rows);
+                if (r < 0) continue;
+                acc = fmaf(topk_w[i], oracle_bf16_to_f32(y[r * H + h]), acc);
+            }
+            out[(long)t * H + h] = oracle_bf16_rne(acc);
+        }
 }
 
 /* Same as oracle_combine for a subset of tokens: out row n is token tokens[n]. */
