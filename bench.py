@@ -280,6 +280,60 @@ class Workload:
         self.combine_ranks(s)
         self.combine_reduce(s)
 
+    # the packed, aligned receive layout: layout with padded offsets, dispatch and combine on
+    # [rows][H] buffers
+    def enable_packed(self, align):
+        torch, c = self.torch, self.cfg
+        dev = torch.device("cuda", 0)
+        self.align = align
+        rows = self.B.packed_rows_bound(c.T, c.K, c.E, c.C, align)
+        b = {"rows": rows}
+        if c.fp8:
+            b["precv_q"] = torch.empty((rows, c.H), dtype=torch.uint8, device=dev)
+            b["precv_s"] = torch.empty((rows, c.H // 128), dtype=torch.float32, device=dev)
+        else:
+            b["precv"] = torch.empty((rows, c.H), dtype=torch.int16, device=dev)
+        g = torch.Generator(device=dev)
+        g.manual_seed(2000 + c.seed)
+        b["py"] = torch.randn((rows, c.H), generator=g, device=dev).to(torch.bfloat16).view(torch.int16)
+        for s in self.sets:
+            s.update(b)
+            s["play"] = dict(slot=torch.empty((c.T, c.K), dtype=torch.int32, device=dev),
+                             expert_count=torch.empty(c.E, dtype=torch.int32, device=dev),
+                             packed_offset=torch.empty(c.E + 1, dtype=torch.int32, device=dev),
+                             rank_count=torch.empty(c.R, dtype=torch.int32, device=dev),
+                             rank_offset=torch.empty(c.R, dtype=torch.int32, device=dev),
+                             stats=torch.empty(4, dtype=torch.int32, device=dev))
+        for k in range(len(self.sets)):
+            self.step_packed(k)
+        torch.cuda.synchronize()
+        return [int(s["play"]["packed_offset"][-1]) for s in self.sets]
+
+    def layout_packed(self, s):
+        c = self.cfg
+        self.B.ep_layout_packed(s["idx"], c.E, c.C, c.R, self.align, **s["play"])
+
+    def dispatch_packed(self, s):
+        c, p = self.cfg, s["play"]
+        if c.fp8:
+            self.B.ep_dispatch_packed_fp8(s["x"], s["idx"], p["slot"], p["packed_offset"],
+                                          s["precv_q"], s["precv_s"], c.E, c.C)
+        else:
+            self.B.ep_dispatch_packed(s["x"], s["idx"], p["slot"], p["packed_offset"], s["precv"],
+                                      c.E, c.C)
+
+    def combine_packed(self, s):
+        c, p = self.cfg, s["play"]
+        self.B.ep_combine_packed(s["py"], s["idx"], p["slot"], p["packed_offset"], s["w"], c.E,
+                                 c.C, out=s["out"])
+
+    def step_packed(self, k):
+        """One pass in the packed layout: three launches."""
+        s = self.sets[k % len(self.sets)]
+        self.layout_packed(s)
+        self.dispatch_packed(s)
+        self.combine_packed(s)
+
     def kernel_avg_us(self, flush, runs=25, per_run=8, kernels=None):
         """Average duration of each kernel launched back to back: per run, a 2 GiB fill of
         `flush` is enqueued first, and while it executes the host enqueues an event, `per_run`
@@ -407,6 +461,48 @@ def two_stage_report(cfg, flush, args, torch, B, W, A):
     return out
 
 
+def packed_report(cfg, align, flush, args, torch, B, W, A):
+    """The packed, aligned layout on one workload: the three-launch pass pipelined and each
+    kernel back to back. The algorithmic bytes are those of the padded three-call pass: the
+    same rows move, and padding rows are never touched."""
+    wl = Workload(cfg, NSETS, torch, B, W)
+    n_kept = wl.kept()[0]
+    rows_needed = wl.enable_packed(align)[0]
+    ms, _ = wl.timed_loop(args.steps, args.warmup, step=wl.step_packed)
+    kus = wl.kernel_avg_us(flush, kernels=(
+        ("layout_packed", wl.layout_packed), ("dispatch_packed", wl.dispatch_packed),
+        ("combine_packed", wl.combine_packed)))
+    alg = A.step_bytes(cfg.T, cfg.K, cfg.H, n_kept, cfg.fp8)
+    kb = {"layout_packed": A.layout_bytes(cfg.T, cfg.K),
+          "dispatch_packed": A.dispatch_bytes(cfg.T, cfg.K, cfg.H, n_kept, cfg.fp8),
+          "combine_packed": A.combine_bytes(cfg.T, cfg.K, cfg.H, n_kept)}
+    out = {"workload": cfg.name, "alignment": align, "rows": rows_needed,
+           "padding_rows": rows_needed - n_kept, "us_per_pass": round(ms * 1e3, 3),
+           "hbm_frac": round(alg / (ms * 1e-3) / A.HBM_PEAK_BYTES_PER_S, 4),
+           "kernel_avg_us": {k: round(v, 3) for k, v in kus.items()},
+           "kernel_hbm_frac": {k: round(kb[k] / (kus[k] * 1e-6) / A.HBM_PEAK_BYTES_PER_S, 4)
+                               for k in kus}}
+    del wl
+    torch.cuda.empty_cache()
+    return out
+
+
+def family_report(names, args, torch, B, W, A):
+    """The fused step (layout + dispatch, then combine) on the balanced and unbalanced routes."""
+    out = {}
+    for name in names:
+        cfg = W.get_config(name)
+        wl = Workload(cfg, NSETS, torch, B, W)
+        n_kept = wl.kept()[0]
+        ms, _ = wl.timed_loop(args.steps, args.warmup)
+        alg = A.step_bytes(cfg.T, cfg.K, cfg.H, n_kept, cfg.fp8)
+        out[name] = {"us_per_step": round(ms * 1e3, 3), "kept_pairs": n_kept,
+                     "hbm_frac": round(alg / (ms * 1e-3) / A.HBM_PEAK_BYTES_PER_S, 4)}
+        del wl
+        torch.cuda.empty_cache()
+    return out
+
+
 def launch_floor(samples, flush, torch, B):
     """The latency floor of the step's structure, measured like the T=128 single-shot: one and
     two back-to-back launches of the library's layout kernel on an empty batch (one workgroup
@@ -522,6 +618,11 @@ def main():
     two_stage = {n: two_stage_report(W.get_config(n), flush, args, torch, B, W, A)
                  for n in (args.workload, "prefill_fp8")}
     log(f"two-stage: {json.dumps(two_stage)}")
+    packed = packed_report(W.get_config(args.workload), 128, flush, args, torch, B, W, A)
+    log(f"packed: {json.dumps(packed)}")
+    family = family_report(("balanced_stride", "unbalanced_r4", "unbalanced_r4_c512"), args,
+                           torch, B, W, A)
+    log(f"route family: {json.dumps(family)}")
     floor = launch_floor(args.latency_samples, flush, torch, B)
     log(f"launch floor: {floor}")
 
@@ -566,6 +667,8 @@ def main():
         "t128_us": {n: brief(n) for n in ("decode_bf16", "decode_fp8") if n in results},
         "launch_floor_us": floor,
         "two_stage": two_stage,
+        "packed_layout": packed,
+        "route_family": family,
         "prefill_fp8": brief("prefill_fp8") if "prefill_fp8" in results else None,
         "roofline": roofline,
         "cpu_baseline": cpu,

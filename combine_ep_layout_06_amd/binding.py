@@ -25,7 +25,8 @@ EP_MAX_RANKS = 64
 EXPORTED = ("ep_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_layout_dispatch",
             "ep_layout_dispatch_fp8", "ep_combine", "ep_rank_layout", "ep_dispatch_ranks",
             "ep_dispatch_ranks_fp8", "ep_dispatch_expand", "ep_dispatch_expand_fp8",
-            "ep_combine_ranks", "ep_combine_reduce", "ep_error_string", "ep_last_error",
+            "ep_combine_ranks", "ep_combine_reduce", "ep_layout_packed", "ep_dispatch_packed",
+            "ep_dispatch_packed_fp8", "ep_combine_packed", "ep_error_string", "ep_last_error",
             "ep_version")
 
 
@@ -70,6 +71,11 @@ def load_library():
         L.ep_dispatch_expand_fp8.argtypes = [sp] + [vp] * 8
         L.ep_combine_ranks.argtypes = [sp] + [vp] * 7
         L.ep_combine_reduce.argtypes = [sp] + [vp] * 4
+        i32 = ctypes.c_int32
+        L.ep_layout_packed.argtypes = [sp, i32] + [vp] * 8
+        L.ep_dispatch_packed.argtypes = [sp, i32] + [vp] * 6
+        L.ep_dispatch_packed_fp8.argtypes = [sp, i32] + [vp] * 7
+        L.ep_combine_packed.argtypes = [sp, i32] + [vp] * 7
         for fn in EXPORTED:
             if fn.startswith("ep_") and fn not in ("ep_error_string", "ep_last_error",
                                                    "ep_version"):
@@ -421,5 +427,110 @@ def ep_combine_reduce(part: torch.Tensor, rank_slot: torch.Tensor, K: int, *, ou
     rc = load_library().ep_combine_reduce(ctypes.byref(sh), _ptr(part), _ptr(rank_slot), _ptr(out),
                                           _stream(stream))
     _check("ep_combine_reduce", rc)
+    return out
+
+
+# ------------------------------------------------------------------------------------------
+# packed, aligned receive layout (buffers are [rows, ...])
+# ------------------------------------------------------------------------------------------
+
+def packed_rows_bound(T: int, K: int, E: int, C: int, alignment: int) -> int:
+    """Rows that always suffice for a packed buffer: every kept pair plus each expert's padding."""
+    return min(T * K, E * C) + E * (alignment - 1)
+
+
+def ep_layout_packed(topk_idx: torch.Tensor, E: int, C: int, R: int, alignment: int, *,
+                     slot=None, expert_count=None, packed_offset=None, rank_count=None,
+                     rank_offset=None, stats=None, stream=None):
+    """Layout with packed offsets: returns ``slot``, ``expert_count``, ``packed_offset``
+    [E + 1] (offset of each expert's rows, then the rows needed), ``rank_count``,
+    ``rank_offset`` (padded rows per rank) and ``stats``."""
+    dev = topk_idx.device
+    T, K = topk_idx.shape
+    mk = lambda n: torch.empty(n, dtype=torch.int32, device=dev)
+    slot = mk((T, K)) if slot is None else slot
+    expert_count = mk(E) if expert_count is None else expert_count
+    packed_offset = mk(E + 1) if packed_offset is None else packed_offset
+    rank_count = mk(R) if rank_count is None else rank_count
+    rank_offset = mk(R) if rank_offset is None else rank_offset
+    stats = mk(EP_STATS_LEN) if stats is None else stats
+    _need(topk_idx, "topk_idx", torch.int32, T * K, dev)
+    _need(slot, "slot", torch.int32, T * K, dev)
+    for name, t, n in (("expert_count", expert_count, E), ("packed_offset", packed_offset, E + 1),
+                       ("rank_count", rank_count, R), ("rank_offset", rank_offset, R),
+                       ("stats", stats, EP_STATS_LEN)):
+        _need(t, name, torch.int32, n, dev)
+    sh = _shape(T, 1, E, K, C, R)
+    rc = load_library().ep_layout_packed(ctypes.byref(sh), int(alignment), _ptr(topk_idx),
+                                         _ptr(slot), _ptr(expert_count), _ptr(packed_offset),
+                                         _ptr(rank_count), _ptr(rank_offset), _ptr(stats),
+                                         _stream(stream))
+    _check("ep_layout_packed", rc)
+    return dict(slot=slot, expert_count=expert_count, packed_offset=packed_offset,
+                rank_count=rank_count, rank_offset=rank_offset, stats=stats)
+
+
+def ep_dispatch_packed(x: torch.Tensor, topk_idx: torch.Tensor, slot: torch.Tensor,
+                       packed_offset: torch.Tensor, recv: torch.Tensor, E: int, C: int, *,
+                       stream=None):
+    """bf16 dispatch into the packed ``recv`` [rows, H] (in place)."""
+    dev = x.device
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    rows = recv.shape[0]
+    _need(x, "x", _bf16(x), T * H, dev)
+    _need(topk_idx, "topk_idx", torch.int32, T * K, dev)
+    _need(slot, "slot", torch.int32, T * K, dev)
+    _need(packed_offset, "packed_offset", torch.int32, E + 1, dev)
+    _need(recv, "recv", _bf16(recv), rows * H, dev)
+    sh = _shape(T, H, E, K, C, 1)
+    rc = load_library().ep_dispatch_packed(ctypes.byref(sh), int(rows), _ptr(x), _ptr(topk_idx),
+                                           _ptr(slot), _ptr(packed_offset), _ptr(recv),
+                                           _stream(stream))
+    _check("ep_dispatch_packed", rc)
+    return recv
+
+
+def ep_dispatch_packed_fp8(x: torch.Tensor, topk_idx: torch.Tensor, slot: torch.Tensor,
+                           packed_offset: torch.Tensor, recv_q: torch.Tensor,
+                           recv_scale: torch.Tensor, E: int, C: int, *, stream=None):
+    """FP8 dispatch into the packed ``recv_q`` [rows, H] and ``recv_scale`` [rows, H/128]."""
+    dev = x.device
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    rows = recv_q.shape[0]
+    _need(x, "x", _bf16(x), T * H, dev)
+    _need(topk_idx, "topk_idx", torch.int32, T * K, dev)
+    _need(slot, "slot", torch.int32, T * K, dev)
+    _need(packed_offset, "packed_offset", torch.int32, E + 1, dev)
+    _need(recv_q, "recv_q", torch.uint8, rows * H, dev)
+    _need(recv_scale, "recv_scale", torch.float32, rows * (H // EP_FP8_BLOCK), dev)
+    sh = _shape(T, H, E, K, C, 1)
+    rc = load_library().ep_dispatch_packed_fp8(ctypes.byref(sh), int(rows), _ptr(x),
+                                               _ptr(topk_idx), _ptr(slot), _ptr(packed_offset),
+                                               _ptr(recv_q), _ptr(recv_scale), _stream(stream))
+    _check("ep_dispatch_packed_fp8", rc)
+    return recv_q, recv_scale
+
+
+def ep_combine_packed(y: torch.Tensor, topk_idx: torch.Tensor, slot: torch.Tensor,
+                      packed_offset: torch.Tensor, topk_w: torch.Tensor, E: int, C: int, *,
+                      out=None, stream=None):
+    """Combine from the packed ``y`` [rows, H] -> ``out`` [T, H] bf16."""
+    dev = y.device
+    T, K = topk_idx.shape
+    rows, H = y.shape
+    out = torch.empty((T, H), dtype=_bf16(y), device=dev) if out is None else out
+    _need(y, "y", _bf16(y), rows * H, dev)
+    _need(topk_idx, "topk_idx", torch.int32, T * K, dev)
+    _need(slot, "slot", torch.int32, T * K, dev)
+    _need(packed_offset, "packed_offset", torch.int32, E + 1, dev)
+    _need(topk_w, "topk_w", torch.float32, T * K, dev)
+    _need(out, "out", _bf16(out), T * H, dev)
+    sh = _shape(T, H, E, K, C, 1)
+    rc = load_library().ep_combine_packed(ctypes.byref(sh), int(rows), _ptr(y), _ptr(topk_idx),
+                                          _ptr(slot), _ptr(packed_offset), _ptr(topk_w), _ptr(out),
+                                          _stream(stream))
+    _check("ep_combine_packed", rc)
     return out
 

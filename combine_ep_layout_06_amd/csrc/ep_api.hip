@@ -95,9 +95,8 @@ int ep_layout(const ep_shape_t *shape, const int32_t *topk_idx, int32_t *slot,
     if (int rc = check_layout_args(shape, topk_idx, slot, expert_count, expert_offset, stats,
                                    "ep_layout"))
         return rc;
-    return hip_status(ep::launch_layout(*shape, topk_idx, slot, expert_count, expert_offset,
-                                        rank_count, rank_offset, stats, stream),
-                      "ep_layout");
+    const ep::LayoutOut o{slot, expert_count, expert_offset, rank_count, rank_offset, stats};
+    return hip_status(ep::launch_layout(*shape, topk_idx, o, stream), "ep_layout");
 }
 
 int ep_layout_dispatch(const ep_shape_t *shape, const uint16_t *x, const int32_t *topk_idx,
@@ -298,6 +297,87 @@ int ep_combine_reduce(const ep_shape_t *shape, const uint16_t *part, const int32
     if (!aligned(part, 16) || !aligned(out, 16))
         return fail(EP_ERR_ALIGN, "ep_combine_reduce: part and out must be 16-byte aligned");
     return hip_status(ep::launch_combine_reduce(*shape, part, rank_slot, out, stream), fn);
+}
+
+int ep_layout_packed(const ep_shape_t *shape, int32_t alignment, const int32_t *topk_idx,
+                     int32_t *slot, int32_t *expert_count, int32_t *packed_offset,
+                     int32_t *rank_count, int32_t *rank_offset, int32_t *stats,
+                     hipStream_t stream)
+{
+    const char *fn = "ep_layout_packed";
+    if (int rc = check_layout_args(shape, topk_idx, slot, expert_count, packed_offset, stats, fn))
+        return rc;
+    if (alignment < 1) return fail(EP_ERR_INVALID, "ep_layout_packed: alignment must be >= 1");
+    if ((int64_t)shape->E * ((int64_t)shape->C + alignment - 1) > INT32_MAX)
+        return fail(EP_ERR_UNSUPPORTED, "ep_layout_packed: E*(C + alignment - 1) exceeds INT32_MAX");
+    ep::LayoutOut o{slot, expert_count, packed_offset, rank_count, rank_offset, stats};
+    o.offset_end = packed_offset + shape->E;
+    o.align = alignment;
+    return hip_status(ep::launch_layout(*shape, topk_idx, o, stream), fn);
+}
+
+namespace {
+
+int check_packed(const ep_shape_t *shape, int32_t rows, const int32_t *packed_offset,
+                 const char *fn, int h_multiple)
+{
+    if (int rc = check_shape(shape, fn)) return rc;
+    if (int rc = check_rows(shape, fn, h_multiple)) return rc;
+    if (rows < 0) return fail(EP_ERR_INVALID, std::string(fn) + ": rows must be >= 0");
+    if (shape->T > 0 && !packed_offset)
+        return fail(EP_ERR_INVALID, std::string(fn) + ": NULL required pointer");
+    return EP_OK;
+}
+
+}  // namespace
+
+int ep_dispatch_packed(const ep_shape_t *shape, int32_t rows, const uint16_t *x,
+                       const int32_t *topk_idx, const int32_t *slot,
+                       const int32_t *packed_offset, uint16_t *recv, hipStream_t stream)
+{
+    const char *fn = "ep_dispatch_packed";
+    if (int rc = check_packed(shape, rows, packed_offset, fn, 8)) return rc;
+    if (shape->T == 0) return hip_status(hipSuccess, fn);
+    if (!x || !topk_idx || !slot || !recv) return fail(EP_ERR_INVALID, "ep_dispatch_packed: NULL required pointer");
+    if (!aligned(x, 16) || !aligned(recv, 16))
+        return fail(EP_ERR_ALIGN, "ep_dispatch_packed: x and recv must be 16-byte aligned");
+    return hip_status(ep::launch_dispatch_bf16(*shape, x, topk_idx, slot, recv, stream,
+                                               ep::RowMap{packed_offset, rows}),
+                      fn);
+}
+
+int ep_dispatch_packed_fp8(const ep_shape_t *shape, int32_t rows, const uint16_t *x,
+                           const int32_t *topk_idx, const int32_t *slot,
+                           const int32_t *packed_offset, uint8_t *recv_q, float *recv_scale,
+                           hipStream_t stream)
+{
+    const char *fn = "ep_dispatch_packed_fp8";
+    if (int rc = check_packed(shape, rows, packed_offset, fn, EP_FP8_BLOCK)) return rc;
+    if (shape->T == 0) return hip_status(hipSuccess, fn);
+    if (!x || !topk_idx || !slot || !recv_q || !recv_scale)
+        return fail(EP_ERR_INVALID, "ep_dispatch_packed_fp8: NULL required pointer");
+    if (!aligned(x, 16) || !aligned(recv_q, 16) || !aligned(recv_scale, 4))
+        return fail(EP_ERR_ALIGN, "ep_dispatch_packed_fp8: x and recv_q must be 16-byte aligned, "
+                                  "recv_scale 4-byte aligned");
+    return hip_status(ep::launch_dispatch_fp8(*shape, x, topk_idx, slot, recv_q, recv_scale,
+                                              stream, ep::RowMap{packed_offset, rows}),
+                      fn);
+}
+
+int ep_combine_packed(const ep_shape_t *shape, int32_t rows, const uint16_t *y,
+                      const int32_t *topk_idx, const int32_t *slot, const int32_t *packed_offset,
+                      const float *topk_w, uint16_t *out, hipStream_t stream)
+{
+    const char *fn = "ep_combine_packed";
+    if (int rc = check_packed(shape, rows, packed_offset, fn, 8)) return rc;
+    if (shape->T == 0) return hip_status(hipSuccess, fn);
+    if (!y || !topk_idx || !slot || !topk_w || !out)
+        return fail(EP_ERR_INVALID, "ep_combine_packed: NULL required pointer");
+    if (!aligned(y, 16) || !aligned(out, 16))
+        return fail(EP_ERR_ALIGN, "ep_combine_packed: y and out must be 16-byte aligned");
+    return hip_status(ep::launch_combine(*shape, y, topk_idx, slot, topk_w, out, stream,
+                                         ep::RowMap{packed_offset, rows}),
+                      fn);
 }
 
 const char *ep_error_string(int code)

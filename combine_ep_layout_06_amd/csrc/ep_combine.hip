@@ -59,7 +59,8 @@ template <int KG, int U, bool MULTI>
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     const u32x4 *__restrict__ y, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ slot, const float *__restrict__ topk_w,
-    u32x4 *__restrict__ out, int T, int H8, int E, int C, int K, int tpb, int nseg)
+    u32x4 *__restrict__ out, int T, int H8, int E, int C, int K, int tpb, int nseg,
+    const int32_t *__restrict__ poff, int prows)
 {
     __shared__ int32_t rows[kStage];
     __shared__ float wts[kStage];
@@ -72,8 +73,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
         __syncthreads();                     // the previous group is done with rows[] / wts[]
         for (int k = threadIdx.x; k < nt * K; k += kThreads) {
             const size_t i = (size_t)t0 * K + k;
-            const int e = idx[i], s = slot[i];
-            rows[k] = ((unsigned)e < (unsigned)E && (unsigned)s < (unsigned)C) ? e * C + s : -1;
+            rows[k] = pair_row(idx[i], slot[i], E, C, poff, prows);
             wts[k] = topk_w[i];
         }
         __syncthreads();
@@ -167,14 +167,15 @@ int pick_tpb(int T, int K)
 
 template <int U>
 hipError_t launch_u(const ep_shape_t &s, const u32x4 *y, const int32_t *idx, const int32_t *slot,
-                    const float *w, u32x4 *out, int H8, int tpb, int nseg, hipStream_t stream)
+                    const float *w, u32x4 *out, int H8, int tpb, int nseg, hipStream_t stream,
+                    RowMap map)
 {
     const int groups = ceil_div(s.T, tpb);
     const dim3 grid(EP_COMBINE_MAX_BLOCKS ? min(groups, EP_COMBINE_MAX_BLOCKS) : groups);
     const dim3 block(kThreads);
 #define EP_COMBINE_LAUNCH(KG, MULTI)                                                            \
     return launch(combine_kernel<KG, U, MULTI>, grid, block, 0, stream, y, idx, slot, w, out,   \
-                  s.T, H8, s.E, s.C, s.K, tpb, nseg)
+                  s.T, H8, s.E, s.C, s.K, tpb, nseg, map.offset, map.rows)
     if (s.K > 8) EP_COMBINE_LAUNCH(8, true);
     if (s.K > 4) EP_COMBINE_LAUNCH(8, false);
     if (s.K > 2) EP_COMBINE_LAUNCH(4, false);
@@ -186,7 +187,8 @@ hipError_t launch_u(const ep_shape_t &s, const u32x4 *y, const int32_t *idx, con
 }  // namespace
 
 hipError_t launch_combine(const ep_shape_t &s, const uint16_t *y, const int32_t *idx,
-                          const int32_t *slot, const float *w, uint16_t *out, hipStream_t stream)
+                          const int32_t *slot, const float *w, uint16_t *out, hipStream_t stream,
+                          RowMap map)
 {
     if (s.T == 0) return hipSuccess;
     const int H8 = s.H / 8;
@@ -195,9 +197,9 @@ hipError_t launch_combine(const ep_shape_t &s, const uint16_t *y, const int32_t 
     const int tpb = pick_tpb(s.T, s.K);
     const u32x4 *yv = reinterpret_cast<const u32x4 *>(y);
     u32x4 *ov = reinterpret_cast<u32x4 *>(out);
-    if (U >= 4) return launch_u<4>(s, yv, idx, slot, w, ov, H8, tpb, nseg, stream);
-    if (U == 2) return launch_u<2>(s, yv, idx, slot, w, ov, H8, tpb, nseg, stream);
-    return launch_u<1>(s, yv, idx, slot, w, ov, H8, tpb, nseg, stream);
+    if (U >= 4) return launch_u<4>(s, yv, idx, slot, w, ov, H8, tpb, nseg, stream, map);
+    if (U == 2) return launch_u<2>(s, yv, idx, slot, w, ov, H8, tpb, nseg, stream, map);
+    return launch_u<1>(s, yv, idx, slot, w, ov, H8, tpb, nseg, stream, map);
 }
 
 }  // namespace ep

@@ -67,6 +67,17 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float v)
     return sign | code;
 }
 
+// Row of pair (e, s) in the receive buffer, or -1 if it is not kept: e*C + s in the padded
+// [E][C] layout, offset[e] + s (below `rows`) in a packed one.
+__device__ __forceinline__ int pair_row(int e, int s, int E, int C, const int32_t *offset,
+                                        int rows)
+{
+    if ((unsigned)e >= (unsigned)E || (unsigned)s >= (unsigned)C) return -1;
+    if (!offset) return e * C + s;
+    const int r = offset[e] + s;
+    return (unsigned)r < (unsigned)rows ? r : -1;
+}
+
 // Number of set bits of `mask` in lanes below this one (v_mbcnt).
 __device__ __forceinline__ int count_below(uint64_t mask)
 {

@@ -4,7 +4,8 @@
 //
 // Work split. Tokens are cut into groups of `tpb`; a workgroup of 4 wavefronts takes groups in
 // a grid-stride loop. For each group it first stages the receive-row numbers (e*C + slot, or
-// -1 for a pair that is not kept) of the group's tpb*K pairs in LDS with one coalesced pass, so
+// offset[e] + slot in a packed buffer, or -1 for a pair that is not kept) of the group's tpb*K
+// pairs in LDS with one coalesced pass, so
 // no wavefront waits on a dependent global load before its row copy. A wavefront item is one
 // token and one segment of its row. HBM traffic: 2*H per token read plus 2*H (bf16) or
 // H + 4*H/128 (FP8) per kept pair written.
@@ -32,11 +33,11 @@ constexpr int kStage = 256;        // staged pairs per group (tpb * K <= kStage)
 // Stage the receive rows of tokens [t0, t0 + nt) into rows[] (one coalesced pass).
 __device__ __forceinline__ void stage_rows(int32_t *rows, const int32_t *__restrict__ idx,
                                            const int32_t *__restrict__ slot, int t0, int nt,
-                                           int K, int E, int C)
+                                           int K, int E, int C, const int32_t *poff, int prows)
 {
     for (int k = threadIdx.x; k < nt * K; k += kThreads) {
         const size_t i = (size_t)t0 * K + k;
-        rows[k] = recv_row(idx[i], slot[i], E, C);
+        rows[k] = pair_row(idx[i], slot[i], E, C, poff, prows);
     }
 }
 
@@ -44,7 +45,7 @@ template <int KG, int U, bool MULTI>
 __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
     const u32x4 *__restrict__ x, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ slot, u32x4 *__restrict__ recv, int T, int H8, int E, int C,
-    int K, int tpb, int nseg)
+    int K, int tpb, int nseg, const int32_t *__restrict__ poff, int prows)
 {
     __shared__ int32_t rows[kStage];
     const int wave = wave_uniform(threadIdx.x / kWave);
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
         const int t0 = tg * tpb;
         const int nt = min(tpb, T - t0);
         __syncthreads();                     // the previous group is done with rows[]
-        stage_rows(rows, idx, slot, t0, nt, K, E, C);
+        stage_rows(rows, idx, slot, t0, nt, K, E, C, poff, prows);
         __syncthreads();
         for (int item = wave; item < nt * nseg; item += kWaves) {
             const int tl = item / nseg;
@@ -67,7 +68,8 @@ template <int KG, bool MULTI>
 __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
     const u32x4 *__restrict__ x, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ slot, u32x4 *__restrict__ recv_q,
-    float *__restrict__ recv_scale, int T, int H, int E, int C, int K, int tpb, int nseg)
+    float *__restrict__ recv_scale, int T, int H, int E, int C, int K, int tpb, int nseg,
+    const int32_t *__restrict__ poff, int prows)
 {
     __shared__ int32_t rows[kStage];
     const int wave = wave_uniform(threadIdx.x / kWave);
@@ -76,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
         const int t0 = tg * tpb;
         const int nt = min(tpb, T - t0);
         __syncthreads();
-        stage_rows(rows, idx, slot, t0, nt, K, E, C);
+        stage_rows(rows, idx, slot, t0, nt, K, E, C, poff, prows);
         __syncthreads();
         for (int item = wave; item < nt * nseg; item += kWaves) {
             const int tl = item / nseg;
@@ -114,12 +116,12 @@ dim3 grid_for(int T, int tpb)
 template <int U>
 hipError_t launch_bf16_u(const ep_shape_t &s, const u32x4 *x, const int32_t *idx,
                          const int32_t *slot, u32x4 *recv, int H8, int tpb, int nseg,
-                         hipStream_t stream)
+                         hipStream_t stream, RowMap map)
 {
     const dim3 grid = grid_for(s.T, tpb), block(kThreads);
 #define EP_LAUNCH_BF16(KG, MULTI)                                                            \
     return launch(dispatch_bf16_kernel<KG, U, MULTI>, grid, block, 0, stream, x, idx, slot,  \
-                  recv, s.T, H8, s.E, s.C, s.K, tpb, nseg)
+                  recv, s.T, H8, s.E, s.C, s.K, tpb, nseg, map.offset, map.rows)
     EP_BY_K(s.K, EP_LAUNCH_BF16);
 #undef EP_LAUNCH_BF16
 }
@@ -127,7 +129,8 @@ hipError_t launch_bf16_u(const ep_shape_t &s, const u32x4 *x, const int32_t *idx
 }  // namespace
 
 hipError_t launch_dispatch_bf16(const ep_shape_t &s, const uint16_t *x, const int32_t *idx,
-                                const int32_t *slot, uint16_t *recv, hipStream_t stream)
+                                const int32_t *slot, uint16_t *recv, hipStream_t stream,
+                                RowMap map)
 {
     if (s.T == 0) return hipSuccess;
     const int H8 = s.H / 8;
@@ -136,14 +139,14 @@ hipError_t launch_dispatch_bf16(const ep_shape_t &s, const uint16_t *x, const in
     const int tpb = pick_tpb(s.T, s.K, nseg);
     const u32x4 *xv = reinterpret_cast<const u32x4 *>(x);
     u32x4 *rv = reinterpret_cast<u32x4 *>(recv);
-    if (U >= 4) return launch_bf16_u<4>(s, xv, idx, slot, rv, H8, tpb, nseg, stream);
-    if (U == 2) return launch_bf16_u<2>(s, xv, idx, slot, rv, H8, tpb, nseg, stream);
-    return launch_bf16_u<1>(s, xv, idx, slot, rv, H8, tpb, nseg, stream);
+    if (U >= 4) return launch_bf16_u<4>(s, xv, idx, slot, rv, H8, tpb, nseg, stream, map);
+    if (U == 2) return launch_bf16_u<2>(s, xv, idx, slot, rv, H8, tpb, nseg, stream, map);
+    return launch_bf16_u<1>(s, xv, idx, slot, rv, H8, tpb, nseg, stream, map);
 }
 
 hipError_t launch_dispatch_fp8(const ep_shape_t &s, const uint16_t *x, const int32_t *idx,
                                const int32_t *slot, uint8_t *recv_q, float *recv_scale,
-                               hipStream_t stream)
+                               hipStream_t stream, RowMap map)
 {
     if (s.T == 0) return hipSuccess;
     const int nseg = ceil_div(s.H, 16 * kWave);
@@ -153,7 +156,7 @@ hipError_t launch_dispatch_fp8(const ep_shape_t &s, const uint16_t *x, const int
     u32x4 *qv = reinterpret_cast<u32x4 *>(recv_q);
 #define EP_LAUNCH_FP8(KG, MULTI)                                                             \
     return launch(dispatch_fp8_kernel<KG, MULTI>, grid, block, 0, stream, xv, idx, slot, qv, \
-                  recv_scale, s.T, s.H, s.E, s.C, s.K, tpb, nseg)
+                  recv_scale, s.T, s.H, s.E, s.C, s.K, tpb, nseg, map.offset, map.rows)
     EP_BY_K(s.K, EP_LAUNCH_FP8);
 #undef EP_LAUNCH_FP8
 }

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kTileThreads) void layout_dispatch_bf16_kernel(
         const int tl = item / nseg;
         dispatch_item_bf16<KG, U, MULTI>(x, recv, rows, t0 + tl, tl, item - tl * nseg, H8, K);
     }
-    if (last) layout_finish(TK, E, C, R, lds, m, o);
+    if (last) layout_finish<false>(TK, E, C, R, lds, m, o);
 }
 
 template <int KG, bool MULTI>
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kTileThreads) void layout_dispatch_fp8_kernel(
         dispatch_item_fp8<KG, MULTI>(x, recv_q, recv_scale, rows, t0 + tl, tl, item - tl * nseg,
                                      H, K);
     }
-    if (last) layout_finish(TK, E, C, R, lds, m, o);
+    if (last) layout_finish<false>(TK, E, C, R, lds, m, o);
 }
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }

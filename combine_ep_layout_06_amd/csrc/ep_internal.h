@@ -32,21 +32,32 @@ inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t
                            stream);
 }
 
-// Outputs of the layout (see ep_layout in ep.h); rank_count / rank_offset may be null.
+// Outputs of the layout (see ep_layout in ep.h); rank_count / rank_offset may be null. A
+// non-null offset_end asks for the packed layout: the offsets and rank sums are over the counts
+// rounded up to multiples of align (>= 1), and offset_end receives the total number of rows.
 struct LayoutOut {
     int32_t *slot, *count, *offset, *rank_count, *rank_offset, *stats;
+    int32_t *offset_end = nullptr;
+    int align = 1;
 };
 
-hipError_t launch_layout(const ep_shape_t &s, const int32_t *idx, int32_t *slot, int32_t *count,
-                         int32_t *offset, int32_t *rank_count, int32_t *rank_offset,
-                         int32_t *stats, hipStream_t stream);
+// Where a kept pair's row is: e*C + slot in the padded [E][C] buffer (offset null), or
+// offset[e] + slot in a packed buffer of `rows` rows.
+struct RowMap {
+    const int32_t *offset = nullptr;
+    int rows = 0;
+};
+
+hipError_t launch_layout(const ep_shape_t &s, const int32_t *idx, const LayoutOut &o,
+                         hipStream_t stream);
 
 hipError_t launch_dispatch_bf16(const ep_shape_t &s, const uint16_t *x, const int32_t *idx,
-                                const int32_t *slot, uint16_t *recv, hipStream_t stream);
+                                const int32_t *slot, uint16_t *recv, hipStream_t stream,
+                                RowMap map = RowMap());
 
 hipError_t launch_dispatch_fp8(const ep_shape_t &s, const uint16_t *x, const int32_t *idx,
                                const int32_t *slot, uint8_t *recv_q, float *recv_scale,
-                               hipStream_t stream);
+                               hipStream_t stream, RowMap map = RowMap());
 
 hipError_t launch_layout_dispatch_bf16(const ep_shape_t &s, const uint16_t *x,
                                        const int32_t *idx, const LayoutOut &o, uint16_t *recv,
@@ -58,7 +69,7 @@ hipError_t launch_layout_dispatch_fp8(const ep_shape_t &s, const uint16_t *x, co
 
 hipError_t launch_combine(const ep_shape_t &s, const uint16_t *y, const int32_t *idx,
                           const int32_t *slot, const float *w, uint16_t *out,
-                          hipStream_t stream);
+                          hipStream_t stream, RowMap map = RowMap());
 
 // two-stage, rank-deduplicated path
 hipError_t launch_rank_layout(const ep_shape_t &s, const int32_t *idx, int32_t *rank_slot,

@@ -8,6 +8,7 @@ namespace ep {
 
 namespace {
 
+template <bool PACKED>
 __global__ __launch_bounds__(kTileThreads) void layout_kernel(const int32_t *__restrict__ idx,
                                                                int TK, int E, int C, int R,
                                                                int nbits, int lg_nc,
@@ -20,21 +21,23 @@ __global__ __launch_bounds__(kTileThreads) void layout_kernel(const int32_t *__r
     const TileIds ids = layout_tile_loads(idx, TK, tile_begin, kTileThreads);
     layout_tile(ids, idx, TK, E, C, nbits, tile_begin, kTileThreads, last, lds, m, o.slot,
                 nullptr);
-    if (last) layout_finish(TK, E, C, R, lds, m, o);
+    if (last) layout_finish<PACKED>(TK, E, C, R, lds, m, o);
 }
 
 }  // namespace
 
-hipError_t launch_layout(const ep_shape_t &s, const int32_t *idx, int32_t *slot, int32_t *count,
-                         int32_t *offset, int32_t *rank_count, int32_t *rank_offset,
-                         int32_t *stats, hipStream_t stream)
+hipError_t launch_layout(const ep_shape_t &s, const int32_t *idx, const LayoutOut &o,
+                         hipStream_t stream)
 {
     const int TK = s.T * s.K;
     const int tiles = TK > 0 ? (TK + kTileThreads - 1) / kTileThreads : 1;
-    const LayoutOut o{slot, count, offset, rank_count, rank_offset, stats};
     const int lg_nc = layout_lg_nc(s.E);
-    return launch(layout_kernel, dim3(tiles), dim3(kTileThreads), layout_lds_bytes(s.E, lg_nc),
-                  stream, idx, TK, s.E, s.C, s.R, expert_bits(s.E), lg_nc, o);
+    const size_t lds = layout_lds_bytes(s.E, lg_nc);
+    if (o.offset_end)           // packed: counts rounded up to o.align, total rows written
+        return launch(layout_kernel<true>, dim3(tiles), dim3(kTileThreads), lds, stream, idx,
+                      TK, s.E, s.C, s.R, expert_bits(s.E), lg_nc, o);
+    return launch(layout_kernel<false>, dim3(tiles), dim3(kTileThreads), lds, stream, idx, TK,
+                  s.E, s.C, s.R, expert_bits(s.E), lg_nc, o);
 }
 
 }  // namespace ep

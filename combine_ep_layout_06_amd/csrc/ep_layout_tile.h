@@ -24,7 +24,9 @@
 //     slot = base + rank, or -1 past C.
 // The workgroup of the last tile then holds the total of every bin and finishes the layout:
 //  4. count = min(total, C), its exclusive scan in expert order (DPP wave scans plus wave
-//     totals), the per-rank sums and the stats; dropped = routed - kept.
+//     totals), the per-rank sums and the stats; dropped = routed - kept. For a packed layout the
+//     scan and the rank sums are over the counts rounded up to the alignment, and the total
+//     number of rows follows the offsets.
 // No workgroup waits on another and no result depends on scheduling: the outputs are
 // deterministic and need no workspace. The cost is the pass over all earlier ids, one memory
 // round trip plus ~tile_begin/1024 conflict-free LDS atomics per lane.
@@ -60,6 +62,7 @@ struct LayoutLdsMap {
     int base;     // [B]: running totals (earlier tiles + this tile) of the experts
     int scan;     // [E + 1]: exclusive scan of count, then the total kept
     int wsum;     // [kTileWaves], then the invalid and unrouted totals
+    int ksum;     // [kTileWaves]: kept counts per wavefront (differ from wsum when padded)
     int words;    // total
 };
 
@@ -83,7 +86,8 @@ __host__ __device__ inline LayoutLdsMap layout_lds_map(int E, int lg_nc)
     m.base = m.hist + (m.B << m.lg_nc);
     m.scan = m.base + ((m.B + 3) & ~3);
     m.wsum = m.scan + ((E + 1 + 3) & ~3);
-    m.words = m.wsum + kTileWaves + 2;
+    m.ksum = m.wsum + kTileWaves + 2;
+    m.words = m.ksum + kTileWaves;
     return m;
 }
 
@@ -253,7 +257,10 @@ __device__ __forceinline__ void layout_tile(const TileIds &ids, const int32_t *_
 }
 
 // Step 4, by the workgroup of the last tile after layout_tile: base[e] is the total of expert
-// e; the histogram copies of bins E and E+1 hold the invalid and unrouted totals.
+// e; the histogram copies of bins E and E+1 hold the invalid and unrouted totals. PACKED scans
+// the counts rounded up to o.align instead (and writes the total rows to o.offset_end); the
+// plain form is kept apart so the fused kernels carry none of that code.
+template <bool PACKED>
 __device__ __forceinline__ void layout_finish(int TK, int E, int C, int R, int32_t *lds,
                                               const LayoutLdsMap &m, const LayoutOut &o)
 {
@@ -261,10 +268,16 @@ __device__ __forceinline__ void layout_finish(int TK, int E, int C, int R, int32
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const int32_t *base = lds + m.base, *hist = lds + m.hist;
-    int32_t *scan = lds + m.scan, *wsum = lds + m.wsum;
+    int32_t *scan = lds + m.scan, *wsum = lds + m.wsum, *ksum = lds + m.ksum;
     const int cnt = tid < E ? min(base[tid], C) : 0;     // E <= kTileThreads
-    const int incl = wave_inclusive_sum(cnt);
-    if (lane == kWave - 1) wsum[wave] = incl;
+    // rows the expert takes: its count, rounded up to a multiple of the alignment if packed
+    const int rows = PACKED ? (cnt + o.align - 1) / o.align * o.align : cnt;
+    const int incl = wave_inclusive_sum(rows);
+    const int kept_incl = PACKED ? wave_inclusive_sum(cnt) : incl;
+    if (lane == kWave - 1) {
+        wsum[wave] = incl;
+        if (PACKED) ksum[wave] = kept_incl;
+    }
     if (wave == 0) {          // invalid (bin E) and unrouted (bin E+1) totals: sum of the copies
         const int NC = 1 << m.lg_nc;
         const int inv = wave_inclusive_sum(lane < NC ? hist[(E << m.lg_nc) + lane] : 0);
@@ -277,13 +290,16 @@ __device__ __forceinline__ void layout_finish(int TK, int E, int C, int R, int32
     __syncthreads();
     int wbase = 0;
     for (int w = 0; w < wave; ++w) wbase += wsum[w];
-    const int excl = wbase + incl - cnt;
+    const int excl = wbase + incl - rows;
     if (tid < E) {
         o.count[tid] = cnt;
         o.offset[tid] = excl;
         scan[tid] = excl;
     }
-    if (tid == E - 1) scan[E] = excl + cnt;             // total kept
+    if (tid == E - 1) {
+        scan[E] = excl + rows;                           // total rows (= kept if not packed)
+        if (PACKED) *o.offset_end = excl + rows;
+    }
     __syncthreads();
     const int EL = E / R;
     for (int r = tid; r < R; r += kTileThreads) {
@@ -292,7 +308,12 @@ __device__ __forceinline__ void layout_finish(int TK, int E, int C, int R, int32
         if (o.rank_offset) o.rank_offset[r] = lo;
     }
     if (tid == 0) {
-        const int kept = scan[E], invalid = wsum[kTileWaves], unrouted = wsum[kTileWaves + 1];
+        int kept = scan[E];
+        if (PACKED) {
+            kept = 0;
+            for (int w = 0; w < kTileWaves; ++w) kept += ksum[w];
+        }
+        const int invalid = wsum[kTileWaves], unrouted = wsum[kTileWaves + 1];
         o.stats[0] = kept;
         o.stats[1] = TK - unrouted - invalid - kept;
         o.stats[2] = unrouted;

@@ -177,6 +177,56 @@ int ep_combine(const ep_shape_t *shape, const uint16_t *y, const int32_t *topk_i
                const int32_t *slot, const float *topk_w, uint16_t *out, hipStream_t stream);
 
 /*
+ * Packed, aligned receive layout (for grouped-GEMM consumers).
+ *
+ * The pages run with DeepEP's expert_alignment = 1 (DeepEP-V2 on AWS EFA, the test_ep.py
+ * cross-check); alignment A > 1 lets a grouped GEMM take each expert's rows in whole tiles.
+ * Here each expert e takes align_up(expert_count[e], A) consecutive rows of a packed buffer
+ * [rows][H] starting at packed_offset[e], the exclusive scan of those padded counts
+ * (packed_offset[E] = the rows the buffer needs; at most min(T*K, E*C) + E*(A-1)). A kept pair
+ * (t, j) of expert e lives in row packed_offset[e] + slot. Padding rows are never written or
+ * read. The offsets need every tile's counts, so this layout is a call of its own (there is
+ * no fused variant).
+ */
+
+/*
+ * ep_layout_packed -- ep_layout with the packed offsets.
+ *   alignment     >= 1 (1 gives the plain exclusive scan of expert_count)
+ *   packed_offset [E+1] int32 out  as above
+ *   rank_count / rank_offset (may be NULL): padded rows per rank and their exclusive scan, so a
+ *                 rank's experts occupy rows [rank_offset[r], rank_offset[r] + rank_count[r])
+ * slot, expert_count and stats are those of ep_layout. Requires E*(C + A - 1) <= INT32_MAX.
+ */
+int ep_layout_packed(const ep_shape_t *shape, int32_t alignment, const int32_t *topk_idx,
+                     int32_t *slot, int32_t *expert_count, int32_t *packed_offset,
+                     int32_t *rank_count, int32_t *rank_offset, int32_t *stats,
+                     hipStream_t stream);
+
+/*
+ * ep_dispatch_packed / ep_dispatch_packed_fp8 -- ep_dispatch / ep_dispatch_fp8 into a packed
+ * buffer of `rows` rows (recv [rows*H]; recv_q [rows*H], recv_scale [rows*(H/128)]): row
+ * packed_offset[e] + slot for every kept pair, skipped if that is not below `rows`. Other rows
+ * untouched. The rules of the padded calls apply otherwise.
+ */
+int ep_dispatch_packed(const ep_shape_t *shape, int32_t rows, const uint16_t *x,
+                       const int32_t *topk_idx, const int32_t *slot,
+                       const int32_t *packed_offset, uint16_t *recv, hipStream_t stream);
+
+int ep_dispatch_packed_fp8(const ep_shape_t *shape, int32_t rows, const uint16_t *x,
+                           const int32_t *topk_idx, const int32_t *slot,
+                           const int32_t *packed_offset, uint8_t *recv_q, float *recv_scale,
+                           hipStream_t stream);
+
+/*
+ * ep_combine_packed -- ep_combine reading y from a packed buffer of `rows` rows: the expert row
+ * of a kept pair is y[packed_offset[e] + slot] (a pair whose row is not below `rows` counts as
+ * dropped). Same arithmetic, bit for bit, as ep_combine on the padded buffer.
+ */
+int ep_combine_packed(const ep_shape_t *shape, int32_t rows, const uint16_t *y,
+                      const int32_t *topk_idx, const int32_t *slot, const int32_t *packed_offset,
+                      const float *topk_w, uint16_t *out, hipStream_t stream);
+
+/*
  * Two-stage, rank-deduplicated path.
  *
  * The pages' kernel chain moves a token to each virtual rank once (dispatch_impl), and the

@@ -128,3 +128,18 @@ def test_two_stage_calls_reject_bad_arguments(lib):
     assert lib.ep_combine_reduce(shape(), A16, None, A16, None) == B.EP_ERR_INVALID
     assert lib.ep_combine_reduce(shape(**many_ranks), A16, A16, A16, None) == B.EP_ERR_UNSUPPORTED
 
+
+def test_packed_calls_reject_bad_arguments(lib):
+    assert lib.ep_layout_packed(shape(), 0, A16, A16, A16, A16, None, None, A16, None) == B.EP_ERR_INVALID
+    assert lib.ep_layout_packed(shape(E=1024, R=1, C=(1 << 21) - 1), 1 << 12, A16, A16, A16, A16, None,
+                                None, A16, None) == B.EP_ERR_UNSUPPORTED
+    assert lib.ep_layout_packed(shape(), 16, A16 + 4, A16, A16, A16, None, None, A16, None) == B.EP_ERR_ALIGN
+    assert lib.ep_layout_packed(shape(), 16, A16, A16, A16, None, None, None, A16, None) == B.EP_ERR_INVALID
+    assert lib.ep_dispatch_packed(shape(), -1, A16, A16, A16, A16, A16, None) == B.EP_ERR_INVALID
+    assert lib.ep_dispatch_packed(shape(), 10, A16, A16, A16, None, A16, None) == B.EP_ERR_INVALID
+    assert lib.ep_dispatch_packed(shape(), 10, A16, A16, A16, A16, A16 + 2, None) == B.EP_ERR_ALIGN
+    assert lib.ep_dispatch_packed_fp8(shape(H=1000), 10, A16, A16, A16, A16, A16, A16,
+                                      None) == B.EP_ERR_UNSUPPORTED
+    assert lib.ep_combine_packed(shape(), 10, A16, A16, A16, A16, A16, A16 + 8, None) == B.EP_ERR_ALIGN
+    assert lib.ep_combine_packed(shape(H=12), 10, A16, A16, A16, A16, A16, A16, None) == B.EP_ERR_UNSUPPORTED
+

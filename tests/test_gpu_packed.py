@@ -1,0 +1,139 @@
+"""GPU parity of the packed, aligned receive layout (ep_layout_packed, ep_dispatch_packed[_fp8],
+ep_combine_packed) against the oracle, bit for bit.
+
+Small shapes compare whole packed buffers, with a sentinel in every row nobody may write and NaN
+in every packed y row nobody may read; the full workloads compare sampled rows and tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_ep_layout_06_amd import binding as B
+from combine_ep_layout_06_amd import workloads as W
+import gpu_cases as G
+
+pytestmark = pytest.mark.gpu
+
+S16, S8, SF = G.SENTINEL16, G.SENTINEL8, G.SENTINEL_F32
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.load_library()
+
+
+def run_case(idx, x, w, E, C, R, align, full, rows=None, fp8=True, seed=0):
+    T, K = idx.shape
+    H = x.shape[1]
+    idx_d, x_d, w_d = G.to_dev(idx.astype(np.int32)), G.u16_dev(x), G.to_dev(w.astype(np.float32))
+    g = B.ep_layout_packed(idx_d, E, C, R, align)
+    torch.cuda.synchronize()
+    lay = oracle.layout(idx, E, C, R)
+    off = oracle.packed_offsets(lay["count"], align)
+    assert np.array_equal(G.to_np(g["slot"]), lay["slot"]), "slot"
+    assert np.array_equal(G.to_np(g["expert_count"]), lay["count"]), "count"
+    assert np.array_equal(G.to_np(g["stats"]), lay["stats_array"]), "stats"
+    assert np.array_equal(G.to_np(g["packed_offset"]), off), "packed_offset"
+    EL = E // R
+    assert np.array_equal(G.to_np(g["rank_offset"]), off[:-1:EL][:R]), "rank_offset"
+    assert np.array_equal(G.to_np(g["rank_count"]), off[EL::EL] - off[:-1:EL][:R]), "rank_count"
+    rows = int(off[-1]) if rows is None else rows
+    slot = lay["slot"]
+
+    # bf16 dispatch
+    recv = torch.full((rows + 4, H), S16, dtype=torch.int16, device=G.dev())
+    B.ep_dispatch_packed(x_d, idx_d, g["slot"], g["packed_offset"], recv[:rows], E, C)
+    torch.cuda.synchronize()
+    want = np.full((rows + 4, H), S16, np.uint16)
+    oracle.dispatch_packed(x, idx, slot, off, E, C, want[:rows])
+    got = G.to_np(recv).view(np.uint16)
+    if full:
+        assert np.array_equal(got, want), "packed recv"
+    else:
+        pick = np.linspace(0, rows - 1, 509).astype(int)
+        assert np.array_equal(got[pick], want[pick]), "packed recv rows"
+        assert (got[rows:] == np.uint16(S16)).all()
+    del recv
+    # FP8 dispatch
+    if fp8 and H % 128 == 0:
+        NB = H // 128
+        q = torch.full((rows, H), S8, dtype=torch.uint8, device=G.dev())
+        sc = torch.full((rows, NB), SF, dtype=torch.float32, device=G.dev())
+        B.ep_dispatch_packed_fp8(x_d, idx_d, g["slot"], g["packed_offset"], q, sc, E, C)
+        torch.cuda.synchronize()
+        wq = np.full((rows, H), S8, np.uint8)
+        ws = np.full((rows, NB), SF, np.float32)
+        oracle.dispatch_packed_fp8(x, idx, slot, off, E, C, wq, ws)
+        if full:
+            assert np.array_equal(G.to_np(q), wq), "packed codes"
+            assert np.array_equal(G.to_np(sc).view(np.uint32), ws.view(np.uint32)), "packed scales"
+        else:
+            pick = np.linspace(0, rows - 1, 509).astype(int)
+            assert np.array_equal(G.to_np(q)[pick], wq[pick])
+            assert np.array_equal(G.to_np(sc)[pick].view(np.uint32), ws[pick].view(np.uint32))
+        del q, sc
+    # combine from a packed y: kept rows from the expert-output stream, every other row NaN
+    e_f, s_f = idx.reshape(-1), slot.reshape(-1)
+    keep = (e_f >= 0) & (e_f < E) & (s_f >= 0) & (s_f < C)
+    r_f = np.where(keep, off[np.clip(e_f, 0, E - 1)] + s_f, -1)
+    live = keep & (r_f < rows)
+    y_host = np.full((rows, H), W.BF16_NAN, np.uint16)
+    y_host[r_f[live]] = W.y_rows(int(live.sum()), H, seed)
+    y = G.u16_dev(y_host)
+    out = B.ep_combine_packed(y, idx_d, g["slot"], g["packed_offset"], w_d, E, C)
+    torch.cuda.synchronize()
+    got = G.to_np(out).view(np.uint16)
+    if full:
+        assert np.array_equal(got, oracle.combine_packed(y_host, idx, slot, off, w, E, C))
+    else:
+        tokens = np.unique(np.concatenate([[0, T - 1], np.linspace(0, T - 1, 61).astype(int)]))
+        sub = oracle.combine_packed(y_host, idx[tokens], slot[tokens], off, w[tokens], E, C)
+        assert np.array_equal(got[tokens], sub)
+    assert not np.isnan(W.bf16_bits_to_f32(got)).any(), "a padding or NaN row of y was read"
+
+
+SMALL = [
+    # T, H, E, K, C, R
+    (37, 256, 6, 3, 5, 3),
+    (100, 520, 16, 4, 9, 4),
+    (257, 1024, 32, 8, 40, 8),
+    (300, 384, 128, 16, 24, 16),
+]
+
+
+@pytest.mark.parametrize("align", [1, 16, 128])
+@pytest.mark.parametrize("T,H,E,K,C,R", SMALL)
+def test_packed_small(T, H, E, K, C, R, align):
+    _need_gpu()
+    print(f"[packed] small T={T} H={H} E={E} K={K} C={C} R={R} align={align}", flush=True)
+    rng = np.random.default_rng(T + H + align)
+    idx = rng.integers(-2, E + 1, size=(T, K)).astype(np.int32)
+    x = W.f32_to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    w = rng.random((T, K)).astype(np.float32)
+    run_case(idx, x, w, E, C, R, align, full=True, seed=T)
+
+
+def test_packed_truncated_buffer():
+    """A buffer shorter than the offsets need: pairs past its end are not written and count as
+    dropped in combine, exactly as the oracle says."""
+    _need_gpu()
+    rng = np.random.default_rng(5)
+    T, H, E, K, C, R = 200, 256, 16, 4, 60, 4
+    idx = rng.integers(0, E, size=(T, K)).astype(np.int32)
+    x = W.f32_to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    w = rng.random((T, K)).astype(np.float32)
+    off = oracle.packed_offsets(oracle.layout(idx, E, C, R)["count"], 8)
+    run_case(idx, x, w, E, C, R, 8, full=True, rows=int(off[-1]) - 37)
+
+
+@pytest.mark.parametrize("name,align", [("unbalanced_r4", 128), ("unbalanced_r4_c512", 64),
+                                        ("decode_bf16", 16), ("prefill_bf16", 128)])
+def test_packed_workloads(name, align):
+    _need_gpu()
+    cfg = W.get_config(name)
+    print(f"[packed] {name} align={align}", flush=True)
+    inp = W.make_inputs(cfg)
+    run_case(inp["topk_idx"], inp["x"], inp["topk_w"], cfg.E, cfg.C, cfg.R, align,
+             full=cfg.T <= 256, seed=cfg.seed)
