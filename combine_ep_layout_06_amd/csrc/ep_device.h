@@ -67,6 +67,31 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float v)
     return sign | code;
 }
 
+// OCP E4M3 codes of four fp32 values, packed little-endian (v0 in the low byte), by gfx950's
+// conversion instruction (round to nearest even). Checked over all 2^32 fp32 inputs on MI355X:
+// equal to e4m3_rne_sat for every finite |v| <= 464, including e4m3 subnormals and fp32
+// denormals; it differs only for NaN (always 0xFF) and |v| > 464 (NaN instead of saturating),
+// which its callers never pass.
+__device__ __forceinline__ uint32_t e4m3_pack4(float v0, float v1, float v2, float v3)
+{
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, lo, true);
+}
+
+// RN(x / d) for d > 0 given y = RN(1 / d), without a division: q = x*y, then two remainder
+// corrections q += (x - d*q)*y, each remainder exact by FMA. After the first, q is within one
+// ulp of x/d; then, with y the correctly rounded reciprocal, the second gives the correctly
+// rounded quotient (Markstein's theorem on division by FMA). It needs the remainders not to
+// underflow: true when |x / d| >= 2^-11 and d >= 2^-60 / 448; below that the result is still
+// within a denormal step of x/d. The sign is x's (a zero sum in a correction rounds to +0).
+__device__ __forceinline__ float div_by_rcp(float x, float d, float y)
+{
+    float q = __fmul_rn(x, y);
+    q = __builtin_fmaf(__builtin_fmaf(-d, q, x), y, q);
+    q = __builtin_fmaf(__builtin_fmaf(-d, q, x), y, q);
+    return __builtin_copysignf(q, x);
+}
+
 // Row of pair (e, s) in the receive buffer, or -1 if it is not kept: e*C + s in the padded
 // [E][C] layout, offset[e] + s (below `rows`) in a packed one.
 __device__ __forceinline__ int pair_row(int e, int s, int E, int C, const int32_t *offset,

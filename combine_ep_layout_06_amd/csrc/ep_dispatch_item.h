@@ -12,10 +12,13 @@
 // non-temporal ones for this one-row-to-K-rows scatter on MI355X.
 //
 // FP8: a lane owns 16 consecutive channels (two 16-byte loads, one 16-byte store of codes), so
-// a 128-channel block is 8 lanes; the block amax is a DPP max over those 8 lanes. The scale and
-// the codes use IEEE fp32 divisions (HIP's default, correctly rounded) exactly as the
-// definition states: scale = amax / 448, q = e4m3(x / scale); amax = 0 gives scale 0 and the
-// signed zero of x.
+// a 128-channel block is 8 lanes; the block amax is a DPP max over those 8 lanes. The codes are
+// exactly those of the definition, scale = amax / 448 and q = e4m3(x / scale) with IEEE fp32
+// divisions (amax = 0: scale 0 and the signed zero of x). The scale is one division; the 16
+// quotients of a lane come from one reciprocal and FMA corrections (div_by_rcp, equal to the
+// IEEE quotient wherever the code depends on it), and the hardware conversion encodes them. A
+// wavefront with a block whose amax is 0, below 2^-60 or not finite takes the plain path: one
+// IEEE division per element and the software encoder.
 #pragma once
 
 #include "ep_device.h"
@@ -152,11 +155,26 @@ __device__ __forceinline__ QuantPiece cast_item_fp8(const RawPieceFp8 &r)
     p.act = r.act;
     p.scale = amax / 448.0f;
     uint32_t q[4] = {0u, 0u, 0u, 0u};
+    // 2^-60 <= amax < inf in every lane with channels: |x / scale| <= 448 (1 + 2^-22), inside
+    // the range where the hardware conversion is exact, and div_by_rcp's remainders do not
+    // underflow (lanes past H hold zeros and store nothing)
+    const uint32_t ab = __float_as_uint(amax);
+    const bool fast = !r.act || (ab >= 0x21800000u && ab < 0x7F800000u);
+    if (__builtin_expect(__ballot(!fast) == 0, 1)) {
+        const float y = 1.0f / p.scale;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const uint32_t code = (amax == 0.0f) ? ((__float_as_uint(f[k]) >> 24) & 0x80u)
-                                             : e4m3_rne_sat(f[k] / p.scale);
-        q[k / 4] |= code << (8 * (k % 4));
+        for (int i = 0; i < 4; ++i)
+            q[i] = e4m3_pack4(div_by_rcp(f[4 * i], p.scale, y),
+                              div_by_rcp(f[4 * i + 1], p.scale, y),
+                              div_by_rcp(f[4 * i + 2], p.scale, y),
+                              div_by_rcp(f[4 * i + 3], p.scale, y));
+    } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const uint32_t code = (amax == 0.0f) ? ((__float_as_uint(f[k]) >> 24) & 0x80u)
+                                                 : e4m3_rne_sat(f[k] / p.scale);
+            q[k / 4] |= code << (8 * (k % 4));
+        }
     }
     p.q = u32x4{q[0], q[1], q[2], q[3]};
     return p;

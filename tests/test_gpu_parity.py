@@ -185,6 +185,67 @@ def test_fp8_every_bf16_value_through_the_quantiser():
         case.check_fused(fp8=True, full=True)
 
 
+def _fp8_blocks_case(blocks, H=2048):
+    """Run [n][128] bf16 blocks (each block's amax in its own channels) through both FP8
+    dispatch paths, against the oracle, one token row per H // 128 blocks."""
+    nb = H // 128
+    T = -(-blocks.shape[0] // nb)
+    x = np.zeros((T * nb, 128), dtype=np.uint16)
+    x[:blocks.shape[0]] = blocks
+    x[blocks.shape[0]:, 0] = blocks[0, 0]                # no all-zero padding blocks
+    x = x.reshape(T, H)
+    idx = (np.arange(T, dtype=np.int32) % 4)[:, None]
+    case = G.Case(T, H, 4, 1, T, 1, x, idx, np.ones((T, 1), np.float32))
+    case.check_dispatch_fp8(full=True)
+    case.check_fused(fp8=True, full=True)
+
+
+def test_fp8_quotients_where_a_reciprocal_product_rounds_differently():
+    """Inputs where RN(x * RN(1/scale)) and the IEEE quotient RN(x / scale) give different e4m3
+    codes (found here by search on the CPU): the kernel must produce the codes of the IEEE
+    quotient, as the definition and the oracle do."""
+    rng = np.random.default_rng(7)
+    pos = np.arange(1, 0x7F80, dtype=np.uint32)
+    xf = (pos << 16).view(np.float32)
+    blocks = []
+    for ab in rng.integers(0x2180, 0x7F00, size=1500):
+        amax = (np.uint32(ab) << 16).view(np.float32)
+        s = np.float32(amax / np.float32(448.0))
+        y = np.float32(np.float32(1.0) / s)
+        xs = xf[xf <= amax]
+        exact = torch.from_numpy((xs / s).astype(np.float32)).to(torch.float8_e4m3fn)
+        recip = torch.from_numpy((xs * y).astype(np.float32)).to(torch.float8_e4m3fn)
+        diff = np.nonzero((exact.view(torch.uint8) != recip.view(torch.uint8)).numpy())[0]
+        if diff.size:
+            v = (xs[diff].view(np.uint32) >> 16).astype(np.uint16)[:63]
+            b = np.zeros(128, np.uint16)
+            b[0] = ab
+            b[1:1 + v.size] = v
+            b[64:64 + v.size] = v | 0x8000
+            blocks.append(b)
+    assert len(blocks) > 100, len(blocks)
+    _fp8_blocks_case(np.stack(blocks))
+
+
+def test_fp8_small_amax_every_smaller_value():
+    """Blocks whose amax is just above 2^-60 (the smallest amax of the reciprocal path) or a
+    little larger, holding every bf16 value below it of both signs, subnormals included: the
+    FMA remainders come closest to underflow here."""
+    for ab in (0x2180, 0x21C1, 0x2300, 0x2F7F):
+        amax = (np.uint32(ab) << 16).view(np.float32)
+        vals = np.arange(0, 0x7F80, dtype=np.uint32)
+        vals = vals[(vals << 16).view(np.float32) <= amax].astype(np.uint16)
+        vals = np.concatenate([vals, vals | 0x8000])
+        per = 127
+        n = -(-vals.size // per)
+        flat = np.zeros(n * per, np.uint16)
+        flat[:vals.size] = vals
+        blocks = np.zeros((n, 128), np.uint16)
+        blocks[:, 0] = ab
+        blocks[:, 1:] = flat.reshape(n, per)
+        _fp8_blocks_case(blocks)
+
+
 def test_fp8_degenerate_blocks():
     """All-zero blocks (scale 0, signed-zero codes), bf16 subnormals, a tiny amax."""
     H = 512
