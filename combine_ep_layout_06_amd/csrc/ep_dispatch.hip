@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
     }
 }
 
-template <int KG, bool MULTI>
+template <int KG, int U, bool MULTI>
 __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
     const u32x4 *__restrict__ x, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ slot, u32x4 *__restrict__ recv_q,
@@ -82,8 +82,8 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
         __syncthreads();
         for (int item = wave; item < nt * nseg; item += kWaves) {
             const int tl = item / nseg;
-            dispatch_item_fp8<KG, MULTI>(x, recv_q, recv_scale, rows, t0 + tl, tl,
-                                         item - tl * nseg, H, K);
+            dispatch_item_fp8<KG, U, MULTI>(x, recv_q, recv_scale, rows, t0 + tl, tl,
+                                            item - tl * nseg, H, K);
         }
     }
 }
@@ -126,6 +126,21 @@ hipError_t launch_bf16_u(const ep_shape_t &s, const u32x4 *x, const int32_t *idx
 #undef EP_LAUNCH_BF16
 }
 
+template <int U>
+hipError_t launch_fp8_u(const ep_shape_t &s, const u32x4 *x, const int32_t *idx,
+                        const int32_t *slot, u32x4 *recv_q, float *recv_scale, hipStream_t stream,
+                        RowMap map)
+{
+    const int nseg = ceil_div(s.H, U * 16 * kWave);
+    const int tpb = pick_tpb(s.T, s.K, nseg);
+    const dim3 grid = grid_for(s.T, tpb), block(kThreads);
+#define EP_LAUNCH_FP8(KG, MULTI)                                                              \
+    return launch(dispatch_fp8_kernel<KG, U, MULTI>, grid, block, 0, stream, x, idx, slot,    \
+                  recv_q, recv_scale, s.T, s.H, s.E, s.C, s.K, tpb, nseg, map.offset, map.rows)
+    EP_BY_K(s.K, EP_LAUNCH_FP8);
+#undef EP_LAUNCH_FP8
+}
+
 }  // namespace
 
 hipError_t launch_dispatch_bf16(const ep_shape_t &s, const uint16_t *x, const int32_t *idx,
@@ -149,16 +164,11 @@ hipError_t launch_dispatch_fp8(const ep_shape_t &s, const uint16_t *x, const int
                                hipStream_t stream, RowMap map)
 {
     if (s.T == 0) return hipSuccess;
-    const int nseg = ceil_div(s.H, 16 * kWave);
-    const int tpb = pick_tpb(s.T, s.K, nseg);
-    const dim3 grid = grid_for(s.T, tpb), block(kThreads);
     const u32x4 *xv = reinterpret_cast<const u32x4 *>(x);
     u32x4 *qv = reinterpret_cast<u32x4 *>(recv_q);
-#define EP_LAUNCH_FP8(KG, MULTI)                                                             \
-    return launch(dispatch_fp8_kernel<KG, MULTI>, grid, block, 0, stream, xv, idx, slot, qv, \
-                  recv_scale, s.T, s.H, s.E, s.C, s.K, tpb, nseg, map.offset, map.rows)
-    EP_BY_K(s.K, EP_LAUNCH_FP8);
-#undef EP_LAUNCH_FP8
+    if (pick_u_fp8(s.T, s.H) == 2)
+        return launch_fp8_u<2>(s, xv, idx, slot, qv, recv_scale, stream, map);
+    return launch_fp8_u<1>(s, xv, idx, slot, qv, recv_scale, stream, map);
 }
 
 }  // namespace ep

@@ -108,114 +108,172 @@ __device__ __forceinline__ void dispatch_item_bf16(const u32x4 *__restrict__ x,
 }
 
 // FP8 item, split in three: the row load, the cast (which needs only the row) and the stores
-// (which need the slots). Segment `seg` (1024 channels) of token t; H % 128 == 0.
+// (which need the slots). A lane takes U pieces of 16 channels, 1024 channels apart, so every
+// load and store instruction covers 1 KiB of one row; segment `seg` is channels
+// [seg*U*1024, (seg+1)*U*1024). H % 128 == 0, so a piece's 8-lane groups are whole blocks.
+template <int U>
 struct RawPieceFp8 {
-    u32x4 a, b;       // this lane's 16 channels, zero where it has none
-    bool act;         // this lane's channels exist (whole 8-lane groups)
+    u32x4 a[U], b[U];     // each piece's 16 channels, zero where it has none
+    bool act[U];          // the piece's channels exist
 };
 
+template <int U>
 struct QuantPiece {
-    u32x4 q;          // 16 codes of this lane's channels
-    float scale;      // scale of this lane's 128-channel block
-    bool act;
+    u32x4 q[U];           // 16 codes per piece
+    float scale[U];       // scale of each piece's 128-channel block
+    bool act[U];
 };
 
-__device__ __forceinline__ RawPieceFp8 load_item_fp8(const u32x4 *__restrict__ x, int t, int seg,
-                                                     int H)
+// First channel of piece u of segment seg for this lane.
+__device__ __forceinline__ int fp8_channel(int seg, int u, int U, int lane)
+{
+    return (seg * U + u) * (16 * kWave) + lane * 16;
+}
+
+template <int U>
+__device__ __forceinline__ RawPieceFp8<U> load_item_fp8(const u32x4 *__restrict__ x, int t,
+                                                        int seg, int H)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int h0 = seg * (16 * kWave) + lane * 16;   // first channel of this lane
-    RawPieceFp8 r;
-    r.act = h0 < H;
-    r.a = u32x4{0u, 0u, 0u, 0u};
-    r.b = r.a;
-    if (r.act) {
-        const u32x4 *src = x + (size_t)t * (H / 8) + h0 / 8;
-        r.a = load16<EP_DISPATCH_NT_LOAD>(src);
-        r.b = load16<EP_DISPATCH_NT_LOAD>(src + 1);
+    RawPieceFp8<U> r;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int h0 = fp8_channel(seg, u, U, lane);
+        r.act[u] = h0 < H;
+        r.a[u] = u32x4{0u, 0u, 0u, 0u};
+        r.b[u] = r.a[u];
+        if (r.act[u]) {
+            const u32x4 *src = x + (size_t)t * (H / 8) + h0 / 8;
+            r.a[u] = load16<EP_DISPATCH_NT_LOAD>(src);
+            r.b[u] = load16<EP_DISPATCH_NT_LOAD>(src + 1);
+        }
     }
     return r;
 }
 
-// All 64 lanes take part (the block amax is a DPP max over 8 lanes).
-__device__ __forceinline__ QuantPiece cast_item_fp8(const RawPieceFp8 &r)
+// All 64 lanes take part (a block amax is a DPP max over 8 lanes).
+template <int U>
+__device__ __forceinline__ QuantPiece<U> cast_item_fp8(const RawPieceFp8<U> &r)
 {
-    const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
-    float f[16];
-    uint32_t m = 0;
+    QuantPiece<U> p;
+    float amax[U];
+    bool fast = true;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        f[2 * k] = bf16_lo(w[k]);
-        f[2 * k + 1] = bf16_hi(w[k]);
-        m = max(m, (w[k] << 16) & 0x7FFFFFFFu);
-        m = max(m, w[k] & 0x7FFF0000u);
-    }
-    const float amax = group8_max(__uint_as_float(m));   // |x| bits: integer order
-    QuantPiece p;
-    p.act = r.act;
-    p.scale = amax / 448.0f;
-    uint32_t q[4] = {0u, 0u, 0u, 0u};
-    // 2^-60 <= amax < inf in every lane with channels: |x / scale| <= 448 (1 + 2^-22), inside
-    // the range where the hardware conversion is exact, and div_by_rcp's remainders do not
-    // underflow (lanes past H hold zeros and store nothing)
-    const uint32_t ab = __float_as_uint(amax);
-    const bool fast = !r.act || (ab >= 0x21800000u && ab < 0x7F800000u);
-    if (__builtin_expect(__ballot(!fast) == 0, 1)) {
-        const float y = 1.0f / p.scale;
+    for (int u = 0; u < U; ++u) {
+        const uint32_t w[8] = {r.a[u].x, r.a[u].y, r.a[u].z, r.a[u].w,
+                               r.b[u].x, r.b[u].y, r.b[u].z, r.b[u].w};
+        uint32_t m = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            q[i] = e4m3_pack4(div_by_rcp(f[4 * i], p.scale, y),
-                              div_by_rcp(f[4 * i + 1], p.scale, y),
-                              div_by_rcp(f[4 * i + 2], p.scale, y),
-                              div_by_rcp(f[4 * i + 3], p.scale, y));
-    } else {
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const uint32_t code = (amax == 0.0f) ? ((__float_as_uint(f[k]) >> 24) & 0x80u)
-                                                 : e4m3_rne_sat(f[k] / p.scale);
-            q[k / 4] |= code << (8 * (k % 4));
+        for (int k = 0; k < 8; ++k) {
+            m = max(m, (w[k] << 16) & 0x7FFFFFFFu);
+            m = max(m, w[k] & 0x7FFF0000u);
         }
+        amax[u] = group8_max(__uint_as_float(m));   // |x| bits: integer order
+        p.act[u] = r.act[u];
+        p.scale[u] = amax[u] / 448.0f;
+        // 2^-60 <= amax < inf in every piece with channels: |x / scale| <= 448 (1 + 2^-22),
+        // inside the range where the hardware conversion is exact, and div_by_rcp's
+        // remainders do not underflow (pieces past H hold zeros and store nothing)
+        const uint32_t ab = __float_as_uint(amax[u]);
+        fast = fast && (!r.act[u] || (ab >= 0x21800000u && ab < 0x7F800000u));
     }
-    p.q = u32x4{q[0], q[1], q[2], q[3]};
+    const bool all_fast = __ballot(!fast) == 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t w[8] = {r.a[u].x, r.a[u].y, r.a[u].z, r.a[u].w,
+                               r.b[u].x, r.b[u].y, r.b[u].z, r.b[u].w};
+        float f[16];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            f[2 * k] = bf16_lo(w[k]);
+            f[2 * k + 1] = bf16_hi(w[k]);
+        }
+        uint32_t q[4] = {0u, 0u, 0u, 0u};
+        if (__builtin_expect(all_fast, 1)) {
+            const float y = 1.0f / p.scale[u];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                q[i] = e4m3_pack4(div_by_rcp(f[4 * i], p.scale[u], y),
+                                  div_by_rcp(f[4 * i + 1], p.scale[u], y),
+                                  div_by_rcp(f[4 * i + 2], p.scale[u], y),
+                                  div_by_rcp(f[4 * i + 3], p.scale[u], y));
+        } else {
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const uint32_t code = (amax[u] == 0.0f)
+                                          ? ((__float_as_uint(f[k]) >> 24) & 0x80u)
+                                          : e4m3_rne_sat(f[k] / p.scale[u]);
+                q[k / 4] |= code << (8 * (k % 4));
+            }
+        }
+        p.q[u] = u32x4{q[0], q[1], q[2], q[3]};
+    }
     return p;
 }
 
-__device__ __forceinline__ QuantPiece quant_item_fp8(const u32x4 *__restrict__ x, int t, int seg,
-                                                     int H)
+template <int U>
+__device__ __forceinline__ QuantPiece<U> quant_item_fp8(const u32x4 *__restrict__ x, int t,
+                                                        int seg, int H)
 {
-    return cast_item_fp8(load_item_fp8(x, t, seg, H));
+    return cast_item_fp8<U>(load_item_fp8<U>(x, t, seg, H));
 }
 
-template <int KG, bool MULTI>
-__device__ __forceinline__ void store_item_fp8(const QuantPiece &p, u32x4 *__restrict__ recv_q,
+// Codes: one 16-byte store per piece and row. Scales: the segment's U*8 blocks of a row in one
+// store instruction; lane 8i + u (u < U) holds the scale of block i of piece u (every lane of
+// that 8-lane group does) and stores it.
+template <int KG, int U, bool MULTI>
+__device__ __forceinline__ void store_item_fp8(const QuantPiece<U> &p, u32x4 *__restrict__ recv_q,
                                                float *__restrict__ recv_scale,
                                                const int32_t *rows, int tl, int seg, int H, int K)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int H16 = H / 16, NB = H / 128;
-    const int h0 = seg * (16 * kWave) + lane * 16;
+    const int su = lane & 7;
+    const int sblk = (seg * U + su) * 8 + (lane >> 3);
+    float sval = p.scale[0];
+#pragma unroll
+    for (int u = 1; u < U; ++u)
+        if (su == u) sval = p.scale[u];
+    const bool sact = su < U && sblk < NB;
     const int npg = MULTI ? (K + KG - 1) / KG : 1;
     for (int pg = 0; pg < npg; ++pg) {
         int r[KG];
         token_rows<KG>(rows, tl, pg * KG, K, r);
 #pragma unroll
         for (int g = 0; g < KG; ++g) {
-            if (r[g] < 0 || !p.act) continue;
-            store16<EP_DISPATCH_NT_STORE>(recv_q + (size_t)r[g] * H16 + h0 / 16, p.q);
-            if ((lane & 7) == 0) recv_scale[(size_t)r[g] * NB + h0 / 128] = p.scale;
+            if (r[g] < 0) continue;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (p.act[u])
+                    store16<EP_DISPATCH_NT_STORE>(
+                        recv_q + (size_t)r[g] * H16 + fp8_channel(seg, u, U, lane) / 16, p.q[u]);
+            if (sact) recv_scale[(size_t)r[g] * NB + sblk] = sval;
         }
     }
 }
 
-template <int KG, bool MULTI>
+template <int KG, int U, bool MULTI>
 __device__ __forceinline__ void dispatch_item_fp8(const u32x4 *__restrict__ x,
                                                   u32x4 *__restrict__ recv_q,
                                                   float *__restrict__ recv_scale,
                                                   const int32_t *rows, int t, int tl, int seg,
                                                   int H, int K)
 {
-    store_item_fp8<KG, MULTI>(quant_item_fp8(x, t, seg, H), recv_q, recv_scale, rows, tl, seg, H,
-                              K);
+    store_item_fp8<KG, U, MULTI>(quant_item_fp8<U>(x, t, seg, H), recv_q, recv_scale, rows, tl,
+                                 seg, H, K);
+}
+
+// Pieces per lane for an FP8 dispatch of T tokens of H channels: two when each token still
+// fills them and the batch keeps at least 4096 wavefront items, else one (measured on MI355X:
+// wide items win on prefill-sized batches, as for bf16 rows).
+#ifndef EP_FP8_U
+#define EP_FP8_U 0
+#endif
+inline int pick_u_fp8(int T, int H)
+{
+    if (EP_FP8_U) return EP_FP8_U;
+    const int nseg2 = (H + 2 * 16 * kWave - 1) / (2 * 16 * kWave);
+    return (H >= 2 * 16 * kWave && (long)T * nseg2 >= 4096) ? 2 : 1;
 }
 
 // Instantiate LAUNCH(KG, MULTI) for the pair-group size that fits K.

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kTileThreads) void layout_dispatch_bf16_kernel(
     if (last) layout_finish<false>(TK, E, C, R, lds, m, o);
 }
 
-template <int KG, bool MULTI>
+template <int KG, int U, bool MULTI>
 __global__ __launch_bounds__(kTileThreads) void layout_dispatch_fp8_kernel(
     const u32x4 *__restrict__ x, const int32_t *__restrict__ idx, LayoutOut o,
     u32x4 *__restrict__ recv_q, float *__restrict__ recv_scale, int T, int H, int E, int C,
@@ -76,8 +76,8 @@ __global__ __launch_bounds__(kTileThreads) void layout_dispatch_fp8_kernel(
     layout_tile(ids, idx, TK, E, C, nbits, t0 * K, TT * K, last, lds, m, o.slot, rows);
     for (int item = wave; item < nitems; item += kTileWaves) {
         const int tl = item / nseg;
-        dispatch_item_fp8<KG, MULTI>(x, recv_q, recv_scale, rows, t0 + tl, tl, item - tl * nseg,
-                                     H, K);
+        dispatch_item_fp8<KG, U, MULTI>(x, recv_q, recv_scale, rows, t0 + tl, tl,
+                                        item - tl * nseg, H, K);
     }
     if (last) layout_finish<false>(TK, E, C, R, lds, m, o);
 }
@@ -118,6 +118,22 @@ hipError_t launch_bf16_u(const ep_shape_t &s, const u32x4 *x, const int32_t *idx
 #undef EP_LAUNCH_FUSED_BF16
 }
 
+template <int U>
+hipError_t launch_fp8_u(const ep_shape_t &s, const u32x4 *x, const int32_t *idx,
+                        const LayoutOut &o, u32x4 *recv_q, float *recv_scale, hipStream_t stream)
+{
+    const int TT = pick_tt(s.T, s.K, true);
+    const int nseg = ceil_div(s.H, U * 16 * kWave);
+    const dim3 grid(s.T > 0 ? ceil_div(s.T, TT) : 1), block(kTileThreads);
+    const int nbits = expert_bits(s.E), lg_nc = layout_lg_nc(s.E);
+    const size_t lds = layout_lds_bytes(s.E, lg_nc);
+#define EP_LAUNCH_FUSED_FP8(KG, MULTI)                                                          \
+    return launch(layout_dispatch_fp8_kernel<KG, U, MULTI>, grid, block, lds, stream, x, idx,  \
+                  o, recv_q, recv_scale, s.T, s.H, s.E, s.C, s.K, s.R, nbits, lg_nc, TT, nseg)
+    EP_BY_K(s.K, EP_LAUNCH_FUSED_FP8);
+#undef EP_LAUNCH_FUSED_FP8
+}
+
 }  // namespace
 
 hipError_t launch_layout_dispatch_bf16(const ep_shape_t &s, const uint16_t *x,
@@ -139,18 +155,10 @@ hipError_t launch_layout_dispatch_fp8(const ep_shape_t &s, const uint16_t *x, co
                                       const LayoutOut &o, uint8_t *recv_q, float *recv_scale,
                                       hipStream_t stream)
 {
-    const int TT = pick_tt(s.T, s.K, true);
-    const int nseg = ceil_div(s.H, 16 * kWave);
-    const dim3 grid(s.T > 0 ? ceil_div(s.T, TT) : 1), block(kTileThreads);
-    const int nbits = expert_bits(s.E), lg_nc = layout_lg_nc(s.E);
-    const size_t lds = layout_lds_bytes(s.E, lg_nc);
     const u32x4 *xv = reinterpret_cast<const u32x4 *>(x);
     u32x4 *qv = reinterpret_cast<u32x4 *>(recv_q);
-#define EP_LAUNCH_FUSED_FP8(KG, MULTI)                                                          \
-    return launch(layout_dispatch_fp8_kernel<KG, MULTI>, grid, block, lds, stream, xv, idx, o, \
-                  qv, recv_scale, s.T, s.H, s.E, s.C, s.K, s.R, nbits, lg_nc, TT, nseg)
-    EP_BY_K(s.K, EP_LAUNCH_FUSED_FP8);
-#undef EP_LAUNCH_FUSED_FP8
+    if (pick_u_fp8(s.T, s.H) == 2) return launch_fp8_u<2>(s, xv, idx, o, qv, recv_scale, stream);
+    return launch_fp8_u<1>(s, xv, idx, o, qv, recv_scale, stream);
 }
 
 }  // namespace ep

@@ -251,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_ranks_bf16_kernel(
     }
 }
 
-template <int KG, bool MULTI>
+template <int KG, int U, bool MULTI>
 __global__ __launch_bounds__(kThreads) void dispatch_ranks_fp8_kernel(
     const u32x4 *__restrict__ x, const int32_t *__restrict__ rank_slot,
     u32x4 *__restrict__ stage_q, float *__restrict__ stage_scale, int T, int H, int R, int tpb,
@@ -267,8 +267,8 @@ __global__ __launch_bounds__(kThreads) void dispatch_ranks_fp8_kernel(
         __syncthreads();
         for (int item = wave; item < nt * nseg; item += kWaves) {
             const int tl = item / nseg;
-            dispatch_item_fp8<KG, MULTI>(x, stage_q, stage_scale, rows, t0 + tl, tl,
-                                         item - tl * nseg, H, R);
+            dispatch_item_fp8<KG, U, MULTI>(x, stage_q, stage_scale, rows, t0 + tl, tl,
+                                            item - tl * nseg, H, R);
         }
     }
 }
@@ -729,20 +729,33 @@ hipError_t launch_dispatch_ranks_bf16(const ep_shape_t &s, const uint16_t *x,
 #undef EP_LAUNCH_DR
 }
 
+namespace {
+
+template <int U>
+hipError_t launch_ranks_fp8_u(const ep_shape_t &s, const u32x4 *x, const int32_t *rank_slot,
+                              u32x4 *stage_q, float *stage_scale, hipStream_t stream)
+{
+    const int nseg = ceil_div(s.H, U * 16 * kWave);
+    const int tpb = pick_tpb_copy(s.T, s.R, nseg);
+    const dim3 grid = grid_for(s.T, tpb), block(kThreads);
+#define EP_LAUNCH_DRQ(KG, MULTI)                                                                \
+    return launch(dispatch_ranks_fp8_kernel<KG, U, MULTI>, grid, block, 0, stream, x,          \
+                  rank_slot, stage_q, stage_scale, s.T, s.H, s.R, tpb, nseg)
+    EP_BY_K(s.R, EP_LAUNCH_DRQ);
+#undef EP_LAUNCH_DRQ
+}
+
+}  // namespace
+
 hipError_t launch_dispatch_ranks_fp8(const ep_shape_t &s, const uint16_t *x,
                                      const int32_t *rank_slot, uint8_t *stage_q,
                                      float *stage_scale, hipStream_t stream)
 {
-    const int nseg = ceil_div(s.H, 16 * kWave);
-    const int tpb = pick_tpb_copy(s.T, s.R, nseg);
-    const dim3 grid = grid_for(s.T, tpb), block(kThreads);
     const u32x4 *xv = reinterpret_cast<const u32x4 *>(x);
     u32x4 *qv = reinterpret_cast<u32x4 *>(stage_q);
-#define EP_LAUNCH_DRQ(KG, MULTI)                                                                \
-    return launch(dispatch_ranks_fp8_kernel<KG, MULTI>, grid, block, 0, stream, xv, rank_slot, \
-                  qv, stage_scale, s.T, s.H, s.R, tpb, nseg)
-    EP_BY_K(s.R, EP_LAUNCH_DRQ);
-#undef EP_LAUNCH_DRQ
+    if (pick_u_fp8(s.T, s.H) == 2)
+        return launch_ranks_fp8_u<2>(s, xv, rank_slot, qv, stage_scale, stream);
+    return launch_ranks_fp8_u<1>(s, xv, rank_slot, qv, stage_scale, stream);
 }
 
 hipError_t launch_dispatch_expand_bf16(const ep_shape_t &s, const uint16_t *stage,

@@ -80,6 +80,8 @@ SMALL = [
     (1500, 128, 64, 6, 100, 4),       # T*K = 9000: nine layout tiles, a ragged last tile
     (300, 384, 128, 16, 24, 16),      # K = 16: two groups of 8 pairs
     (2049, 256, 8, 1, 300, 2),        # K = 1
+    (2048, 3072, 16, 4, 600, 4),      # FP8 with two 1024-channel pieces per lane: 2 segments,
+                                      # the second one's upper piece past H
 ]
 
 
