@@ -82,6 +82,8 @@ SMALL = [
     (2049, 256, 8, 1, 300, 2),        # K = 1
     (2048, 3072, 16, 4, 600, 4),      # FP8 with two 1024-channel pieces per lane: 2 segments,
                                       # the second one's upper piece past H
+    (2051, 256, 16, 4, 700, 4),       # prefill-sized fused tiles (8 tokens) with a 3-token
+                                      # last tile
 ]
 
 
