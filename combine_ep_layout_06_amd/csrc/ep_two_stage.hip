@@ -587,14 +587,16 @@ __global__ __launch_bounds__(kThreads) void combine_reduce_kernel(
         __syncthreads();
         for (int k = threadIdx.x; k < nt * R; k += kThreads) rs[k] = rank_slot[(size_t)t0 * R + k];
         __syncthreads();
-        if ((int)threadIdx.x < nt) {
-            const int tl = threadIdx.x;
-            int n = 0;
-            for (int r = 0; r < R && n < Q; ++r) {
-                const int p = rs[tl * R + r];
-                if ((unsigned)p < (unsigned)T) plist[tl * Q + n++] = r * T + p;
-            }
-            for (; n < Q; ++n) plist[tl * Q + n] = -1;
+        // one wavefront per token: lane r holds rank r's slot (R <= 64); the ranks the token
+        // reached take the first entries of its list in ascending rank (ballot position), the
+        // rest of its Q entries are -1
+        for (int tl = wave; tl < nt; tl += kWaves) {
+            const int p = lane < R ? rs[tl * R + lane] : -1;
+            const bool ok = lane < R && (unsigned)p < (unsigned)T;
+            const uint64_t m = __ballot(ok);
+            const int n = count_below(m);
+            if (ok && n < Q) plist[tl * Q + n] = lane * T + p;
+            if (lane >= (int)__popcll(m) && lane < Q) plist[tl * Q + lane] = -1;
         }
         __syncthreads();
         for (int item = wave; item < nt * nseg; item += kWaves) {
