@@ -247,6 +247,14 @@ class Workload:
         c = self.cfg
         self.B.ep_rank_layout(s["idx"], c.E, c.R, **s["rl"])
 
+    def rank_layout_dispatch(self, s):
+        c = self.cfg
+        if c.fp8:
+            self.B.ep_rank_layout_dispatch_fp8(s["x"], s["idx"], c.E, c.R, stage_q=s["stage_q"],
+                                               stage_scale=s["stage_s"], **s["rl"])
+        else:
+            self.B.ep_rank_layout_dispatch(s["x"], s["idx"], c.E, c.R, stage=s["stage"], **s["rl"])
+
     def dispatch_ranks(self, s):
         if self.cfg.fp8:
             self.B.ep_dispatch_ranks_fp8(s["x"], s["rl"]["rank_slot"], s["stage_q"], s["stage_s"])
@@ -271,7 +279,16 @@ class Workload:
         self.B.ep_combine_reduce(s["part"], s["rl"]["rank_slot"], self.cfg.K, out=s["out"])
 
     def step2(self, k):
-        """One two-stage pass: six launches."""
+        """One two-stage pass: five launches (the rank layout fused with stage 1)."""
+        s = self.sets[k % len(self.sets)]
+        self.layout(s)
+        self.rank_layout_dispatch(s)
+        self.expand(s)
+        self.combine_ranks(s)
+        self.combine_reduce(s)
+
+    def step2_unfused(self, k):
+        """The same pass with the rank layout and stage 1 as two launches."""
         s = self.sets[k % len(self.sets)]
         self.layout(s)
         self.rank_layout(s)
@@ -432,23 +449,28 @@ def cpu_baseline(cfg, budget_s, W, A):
 
 def two_stage_report(cfg, flush, args, torch, B, W, A):
     """The two-stage, rank-deduplicated pass on one workload: each kernel back to back, the
-    whole six-launch pass pipelined, bytes per kernel, and the rows that would cross ranks."""
+    whole pass pipelined (five launches, and six with the rank layout apart), bytes per kernel,
+    and the rows that would cross ranks."""
     wl = Workload(cfg, NSETS, torch, B, W)
     n_kept = wl.kept()[0]
     n_tr = wl.enable_two_stage()[0]
     ms, _ = wl.timed_loop(args.steps, args.warmup, step=wl.step2)
+    ms6, _ = wl.timed_loop(args.steps, args.warmup, step=wl.step2_unfused)
     kus = wl.kernel_avg_us(flush, kernels=(
-        ("rank_layout", wl.rank_layout), ("dispatch_ranks", wl.dispatch_ranks),
-        ("dispatch_expand", wl.expand), ("combine_ranks", wl.combine_ranks),
-        ("combine_reduce", wl.combine_reduce)))
+        ("rank_layout_dispatch", wl.rank_layout_dispatch), ("rank_layout", wl.rank_layout),
+        ("dispatch_ranks", wl.dispatch_ranks), ("dispatch_expand", wl.expand),
+        ("combine_ranks", wl.combine_ranks), ("combine_reduce", wl.combine_reduce)))
     T, K, H, R = cfg.T, cfg.K, cfg.H, cfg.R
     kb = {"rank_layout": A.rank_layout_bytes(T, K, R),
           "dispatch_ranks": A.dispatch_ranks_bytes(T, R, H, n_tr, cfg.fp8),
           "dispatch_expand": A.dispatch_expand_bytes(T, K, R, H, n_tr, n_kept, cfg.fp8),
           "combine_ranks": A.combine_ranks_bytes(T, K, R, H, n_tr, n_kept),
           "combine_reduce": A.combine_reduce_bytes(T, R, H, n_tr)}
-    alg = A.layout_bytes(T, K) + sum(kb.values())
+    kb["rank_layout_dispatch"] = kb["rank_layout"] + kb["dispatch_ranks"]
+    alg = (A.layout_bytes(T, K) + kb["rank_layout_dispatch"] + kb["dispatch_expand"] +
+           kb["combine_ranks"] + kb["combine_reduce"])
     out = {"workload": cfg.name, "us_per_pass": round(ms * 1e3, 3),
+           "us_per_pass_rank_layout_apart": round(ms6 * 1e3, 3),
            "hbm_frac": round(alg / (ms * 1e-3) / A.HBM_PEAK_BYTES_PER_S, 4),
            "algorithmic_bytes": alg,
            "rows_crossing_ranks": n_tr, "kept_pairs": n_kept,

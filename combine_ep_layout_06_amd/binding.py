@@ -24,7 +24,8 @@ EP_MAX_RANKS = 64
 #: every entry point the header declares
 EXPORTED = ("ep_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_layout_dispatch",
             "ep_layout_dispatch_fp8", "ep_combine", "ep_rank_layout", "ep_dispatch_ranks",
-            "ep_dispatch_ranks_fp8", "ep_dispatch_expand", "ep_dispatch_expand_fp8",
+            "ep_dispatch_ranks_fp8", "ep_rank_layout_dispatch", "ep_rank_layout_dispatch_fp8",
+            "ep_dispatch_expand", "ep_dispatch_expand_fp8",
             "ep_combine_ranks", "ep_combine_reduce", "ep_layout_packed", "ep_dispatch_packed",
             "ep_dispatch_packed_fp8", "ep_combine_packed", "ep_error_string", "ep_last_error",
             "ep_version")
@@ -67,6 +68,8 @@ def load_library():
         L.ep_rank_layout.argtypes = [sp, vp, vp, vp, vp]
         L.ep_dispatch_ranks.argtypes = [sp, vp, vp, vp, vp]
         L.ep_dispatch_ranks_fp8.argtypes = [sp, vp, vp, vp, vp, vp]
+        L.ep_rank_layout_dispatch.argtypes = [sp] + [vp] * 6
+        L.ep_rank_layout_dispatch_fp8.argtypes = [sp] + [vp] * 7
         L.ep_dispatch_expand.argtypes = [sp] + [vp] * 6
         L.ep_dispatch_expand_fp8.argtypes = [sp] + [vp] * 8
         L.ep_combine_ranks.argtypes = [sp] + [vp] * 7
@@ -341,6 +344,62 @@ def ep_dispatch_ranks_fp8(x: torch.Tensor, rank_slot: torch.Tensor, stage_q: tor
                                               _ptr(stage_q), _ptr(stage_scale), _stream(stream))
     _check("ep_dispatch_ranks_fp8", rc)
     return stage_q, stage_scale
+
+
+def ep_rank_layout_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, R: int, *,
+                            stage=None, rank_slot=None, rank_tokens=None, stream=None):
+    """ep_rank_layout and ep_dispatch_ranks in one launch: ``x`` [T, H] bf16 -> ``stage``
+    [R, T, H] bf16 (rows of tokens a rank does not receive untouched), ``rank_slot`` [T, R],
+    ``rank_tokens`` [R]."""
+    dev = x.device
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    stage = torch.empty((R, T, H), dtype=_bf16(x), device=dev) if stage is None else stage
+    rank_slot = torch.empty((T, R), dtype=torch.int32, device=dev) if rank_slot is None else rank_slot
+    rank_tokens = (torch.empty(R, dtype=torch.int32, device=dev) if rank_tokens is None
+                   else rank_tokens)
+    _need(x, "x", _bf16(x), T * H, dev)
+    _need(topk_idx, "topk_idx", torch.int32, T * K, dev)
+    _need(rank_slot, "rank_slot", torch.int32, T * R, dev)
+    _need(rank_tokens, "rank_tokens", torch.int32, R, dev)
+    _need(stage, "stage", _bf16(stage), R * T * H, dev)
+    sh = _shape(T, H, E, K, 1, R)
+    rc = load_library().ep_rank_layout_dispatch(ctypes.byref(sh), _ptr(x), _ptr(topk_idx),
+                                                _ptr(rank_slot), _ptr(rank_tokens), _ptr(stage),
+                                                _stream(stream))
+    _check("ep_rank_layout_dispatch", rc)
+    return dict(stage=stage, rank_slot=rank_slot, rank_tokens=rank_tokens)
+
+
+def ep_rank_layout_dispatch_fp8(x: torch.Tensor, topk_idx: torch.Tensor, E: int, R: int, *,
+                                stage_q=None, stage_scale=None, rank_slot=None,
+                                rank_tokens=None, stream=None):
+    """ep_rank_layout and ep_dispatch_ranks_fp8 in one launch: ``stage_q`` [R, T, H] uint8,
+    ``stage_scale`` [R, T, H/128] float32, ``rank_slot`` [T, R], ``rank_tokens`` [R]."""
+    dev = x.device
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    NB = H // EP_FP8_BLOCK
+    stage_q = torch.empty((R, T, H), dtype=torch.uint8, device=dev) if stage_q is None else stage_q
+    stage_scale = (torch.empty((R, T, NB), dtype=torch.float32, device=dev)
+                   if stage_scale is None else stage_scale)
+    rank_slot = torch.empty((T, R), dtype=torch.int32, device=dev) if rank_slot is None else rank_slot
+    rank_tokens = (torch.empty(R, dtype=torch.int32, device=dev) if rank_tokens is None
+                   else rank_tokens)
+    _need(x, "x", _bf16(x), T * H, dev)
+    _need(topk_idx, "topk_idx", torch.int32, T * K, dev)
+    _need(rank_slot, "rank_slot", torch.int32, T * R, dev)
+    _need(rank_tokens, "rank_tokens", torch.int32, R, dev)
+    _need(stage_q, "stage_q", torch.uint8, R * T * H, dev)
+    _need(stage_scale, "stage_scale", torch.float32, R * T * NB, dev)
+    sh = _shape(T, H, E, K, 1, R)
+    rc = load_library().ep_rank_layout_dispatch_fp8(ctypes.byref(sh), _ptr(x), _ptr(topk_idx),
+                                                    _ptr(rank_slot), _ptr(rank_tokens),
+                                                    _ptr(stage_q), _ptr(stage_scale),
+                                                    _stream(stream))
+    _check("ep_rank_layout_dispatch_fp8", rc)
+    return dict(stage_q=stage_q, stage_scale=stage_scale, rank_slot=rank_slot,
+                rank_tokens=rank_tokens)
 
 
 def ep_dispatch_expand(stage: torch.Tensor, topk_idx: torch.Tensor, slot: torch.Tensor,

@@ -227,6 +227,46 @@ int ep_dispatch_ranks_fp8(const ep_shape_t *shape, const uint16_t *x, const int3
                       fn);
 }
 
+int ep_rank_layout_dispatch(const ep_shape_t *shape, const uint16_t *x, const int32_t *topk_idx,
+                            int32_t *rank_slot, int32_t *rank_tokens, uint16_t *stage,
+                            hipStream_t stream)
+{
+    const char *fn = "ep_rank_layout_dispatch";
+    if (int rc = check_shape(shape, fn)) return rc;
+    if (int rc = check_rows(shape, fn, 8)) return rc;
+    if (int rc = check_ranks(shape, fn)) return rc;
+    if ((shape->T > 0 && (!x || !topk_idx || !rank_slot || !stage)) || !rank_tokens)
+        return fail(EP_ERR_INVALID, "ep_rank_layout_dispatch: NULL required pointer");
+    if (!aligned(topk_idx, 16) || !aligned(x, 16) || !aligned(stage, 16))
+        return fail(EP_ERR_ALIGN, "ep_rank_layout_dispatch: topk_idx, x and stage must be "
+                                  "16-byte aligned");
+    return hip_status(ep::launch_rank_layout_dispatch_bf16(*shape, x, topk_idx, rank_slot,
+                                                           rank_tokens, stage, stream),
+                      fn);
+}
+
+int ep_rank_layout_dispatch_fp8(const ep_shape_t *shape, const uint16_t *x,
+                                const int32_t *topk_idx, int32_t *rank_slot,
+                                int32_t *rank_tokens, uint8_t *stage_q, float *stage_scale,
+                                hipStream_t stream)
+{
+    const char *fn = "ep_rank_layout_dispatch_fp8";
+    if (int rc = check_shape(shape, fn)) return rc;
+    if (int rc = check_rows(shape, fn, EP_FP8_BLOCK)) return rc;
+    if (int rc = check_ranks(shape, fn)) return rc;
+    if ((shape->T > 0 && (!x || !topk_idx || !rank_slot || !stage_q || !stage_scale)) ||
+        !rank_tokens)
+        return fail(EP_ERR_INVALID, "ep_rank_layout_dispatch_fp8: NULL required pointer");
+    if (!aligned(topk_idx, 16) || !aligned(x, 16) || !aligned(stage_q, 16) ||
+        !aligned(stage_scale, 4))
+        return fail(EP_ERR_ALIGN, "ep_rank_layout_dispatch_fp8: topk_idx, x and stage_q must be "
+                                  "16-byte aligned, stage_scale 4-byte aligned");
+    return hip_status(ep::launch_rank_layout_dispatch_fp8(*shape, x, topk_idx, rank_slot,
+                                                          rank_tokens, stage_q, stage_scale,
+                                                          stream),
+                      fn);
+}
+
 int ep_dispatch_expand(const ep_shape_t *shape, const uint16_t *stage, const int32_t *topk_idx,
                        const int32_t *slot, const int32_t *rank_slot, uint16_t *recv,
                        hipStream_t stream)

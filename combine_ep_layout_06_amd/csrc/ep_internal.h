@@ -75,6 +75,14 @@ hipError_t launch_combine(const ep_shape_t &s, const uint16_t *y, const int32_t 
 hipError_t launch_rank_layout(const ep_shape_t &s, const int32_t *idx, int32_t *rank_slot,
                               int32_t *rank_tokens, hipStream_t stream);
 
+hipError_t launch_rank_layout_dispatch_bf16(const ep_shape_t &s, const uint16_t *x,
+                                            const int32_t *idx, int32_t *rank_slot,
+                                            int32_t *rank_tokens, uint16_t *stage,
+                                            hipStream_t stream);
+hipError_t launch_rank_layout_dispatch_fp8(const ep_shape_t &s, const uint16_t *x,
+                                           const int32_t *idx, int32_t *rank_slot,
+                                           int32_t *rank_tokens, uint8_t *stage_q,
+                                           float *stage_scale, hipStream_t stream);
 hipError_t launch_dispatch_ranks_bf16(const ep_shape_t &s, const uint16_t *x,
                                       const int32_t *rank_slot, uint16_t *stage,
                                       hipStream_t stream);

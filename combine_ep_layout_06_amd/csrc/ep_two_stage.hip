@@ -16,6 +16,11 @@
 //    over the wavefronts, like the expert layout.
 //  * dispatch_ranks (bf16 / FP8): the dispatch work items of ep_dispatch_item.h with the R
 //    staging rows of a token in place of its K expert rows.
+//  * rank_layout_dispatch (bf16 / FP8): the two above in one launch. A workgroup of 1024 lanes
+//    takes a tile of at most 64 tokens, counts the earlier tokens per rank as rank_layout does
+//    (every lane, 64 tokens per wavefront step), ranks its own tokens in one wavefront (ballot
+//    + v_mbcnt per rank) and copies them at once, so the layout of later tiles overlaps the
+//    copies of earlier ones.
 //  * expand (bf16 / FP8): per kept pair, the staged row of the pair's rank is copied to the
 //    pair's expert row; all of a token's row loads are issued before its stores (pairs of one
 //    rank load the same row, which the second time comes from the cache).
@@ -29,6 +34,10 @@
 
 #ifndef EP_TWO_STAGE_U
 #define EP_TWO_STAGE_U 0        // 16-byte chunks per lane per item (0 = choose from the shape)
+#endif
+
+#ifndef EP_RANKS_FUSED_TT
+#define EP_RANKS_FUSED_TT 0      // tokens per tile of the fused rank layout + stage 1
 #endif
 
 namespace ep {
@@ -270,6 +279,153 @@ __global__ __launch_bounds__(kThreads) void dispatch_ranks_fp8_kernel(
             dispatch_item_fp8<KG, U, MULTI>(x, stage_q, stage_scale, rows, t0 + tl, tl,
                                             item - tl * nseg, H, R);
         }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// rank layout and stage 1 fused: each workgroup ranks a tile of at most 64 tokens against all
+// earlier tokens, then copies (or quantises and copies) the tile's rows to their staging rows
+// ------------------------------------------------------------------------------------------
+
+// Per-rank counts of the tokens [0, t0) in this wavefront's share (tokens wave*64 + lane +
+// b*kRankTile): kRankBatch tokens per lane are loaded together (16-byte id vectors when
+// KV > 0), then per rank the wavefront adds up one ballot count per batch. Lane r returns rank
+// r's total.
+template <int KV>
+__device__ __forceinline__ int rank_prefix_wave(const int32_t *__restrict__ idx, int t0, int K,
+                                                int E, int EL, int R)
+{
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int q0 = wave * kWave + lane;
+    int acc = 0;
+    for (int b0 = 0; b0 * kRankTile + wave * kWave < t0; b0 += kRankBatch) {
+        uint64_t m[kRankBatch];
+        if constexpr (KV > 0) {
+            int4 v[kRankBatch][KV];
+#pragma unroll
+            for (int b = 0; b < kRankBatch; ++b) {
+#pragma unroll
+                for (int j = 0; j < KV; ++j) v[b][j] = int4{-1, -1, -1, -1};
+                if ((b0 + b) * kRankTile + wave * kWave < t0) {        // wavefront-uniform
+                    const int q = min(q0 + (b0 + b) * kRankTile, t0 - 1);
+#pragma unroll
+                    for (int j = 0; j < KV; ++j)
+                        v[b][j] = reinterpret_cast<const int4 *>(idx + (size_t)q * K)[j];
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < kRankBatch; ++b)
+                m[b] = q0 + (b0 + b) * kRankTile < t0 ? ranks_of(v[b], KV, E, EL) : 0;
+        } else {
+#pragma unroll
+            for (int b = 0; b < kRankBatch; ++b) {
+                const int q = q0 + (b0 + b) * kRankTile;
+                m[b] = q < t0 ? token_ranks_any(idx, q, K, E, EL) : 0;
+            }
+        }
+        // batches holding any of this wavefront's earlier tokens
+        const int nb = min(kRankBatch, ceil_div(t0 - b0 * kRankTile - wave * kWave, kRankTile));
+        for (int r = 0; r < R; ++r) {
+            int c = 0;
+#pragma unroll
+            for (int b = 0; b < kRankBatch; ++b)
+                if (b < nb) c += __popcll(__ballot(((m[b] >> r) & 1u) != 0));
+            acc = lane == r ? acc + c : acc;
+        }
+    }
+    return acc;
+}
+
+// Rank layout of the tile [t0, t0 + nt), nt <= kWave, in a workgroup of kRankTile lanes:
+// rank_slot rows of the tile (coalesced, through LDS), rows[tl*R + r] = r*T + slot or -1 in
+// LDS for the copies, and rank_tokens in the last workgroup. Ends with a barrier.
+template <int KV>
+__device__ __forceinline__ void rank_tile(const int32_t *__restrict__ idx, int t0, int nt, int T,
+                                          int K, int E, int R, bool last,
+                                          int32_t *__restrict__ rank_slot,
+                                          int32_t *__restrict__ rank_tokens, int32_t *rows,
+                                          int32_t *slots, int32_t (*wcnt)[EP_MAX_RANKS])
+{
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int EL = E / R;
+    uint64_t own = 0;                  // wavefront 0, lane tl: the tile's token tl
+    if (wave == 0 && lane < nt) {
+        const int t = t0 + lane;
+        if constexpr (KV > 0) {
+            int4 v[KV];
+#pragma unroll
+            for (int j = 0; j < KV; ++j) v[j] = reinterpret_cast<const int4 *>(idx + (size_t)t * K)[j];
+            own = ranks_of(v, KV, E, EL);
+        } else {
+            own = token_ranks_any(idx, t, K, E, EL);
+        }
+    }
+    const int acc = rank_prefix_wave<KV>(idx, t0, K, E, EL, R);
+    if (lane < R) wcnt[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+        int base = 0;                  // lane r: tokens before t0 sent to rank r
+        if (lane < R)
+            for (int w = 0; w < kRankWaves; ++w) base += wcnt[w][lane];
+        for (int r = 0; r < R; ++r) {
+            const bool sent = (own >> r) & 1u;
+            const uint64_t bal = __ballot(sent);
+            const int b = __builtin_amdgcn_readlane(base, r);
+            const int pos = b + count_below(bal);
+            if (lane < nt) {
+                slots[lane * R + r] = sent ? pos : -1;
+                rows[lane * R + r] = sent ? r * T + pos : -1;
+            }
+            if (last && lane == 0) rank_tokens[r] = b + (int)__popcll(bal);
+        }
+    }
+    __syncthreads();
+    for (int k = threadIdx.x; k < nt * R; k += kRankTile) rank_slot[(size_t)t0 * R + k] = slots[k];
+}
+
+template <int KV, int KG, int U, bool MULTI>
+__global__ __launch_bounds__(kRankTile) void rank_layout_dispatch_bf16_kernel(
+    const u32x4 *__restrict__ x, const int32_t *__restrict__ idx, int32_t *__restrict__ rank_slot,
+    int32_t *__restrict__ rank_tokens, u32x4 *__restrict__ stage, int T, int H8, int K, int E,
+    int R, int TT, int nseg)
+{
+    __shared__ int32_t wcnt[kRankWaves][EP_MAX_RANKS];
+    __shared__ int32_t rows[kRankTile];
+    __shared__ int32_t slots[kRankTile];
+    const int wave = wave_uniform(threadIdx.x / kWave);
+    const int t0 = blockIdx.x * TT, nt = min(TT, T - t0);
+    const int nitems = nt * nseg;
+    // the first item's row loads need no slot: issued before the layout's loads
+    RowPiece<U> first;
+    if (wave < nitems) first = load_item_bf16<U>(x, t0 + wave / nseg, wave % nseg, H8);
+    rank_tile<KV>(idx, t0, nt, T, K, E, R, blockIdx.x == gridDim.x - 1, rank_slot, rank_tokens,
+                  rows, slots, wcnt);
+    if (wave < nitems)
+        store_item_bf16<KG, U, MULTI>(first, stage, rows, wave / nseg, wave % nseg, H8, R);
+    for (int item = wave + kRankWaves; item < nitems; item += kRankWaves) {
+        const int tl = item / nseg;
+        dispatch_item_bf16<KG, U, MULTI>(x, stage, rows, t0 + tl, tl, item - tl * nseg, H8, R);
+    }
+}
+
+template <int KV, int KG, int U, bool MULTI>
+__global__ __launch_bounds__(kRankTile) void rank_layout_dispatch_fp8_kernel(
+    const u32x4 *__restrict__ x, const int32_t *__restrict__ idx, int32_t *__restrict__ rank_slot,
+    int32_t *__restrict__ rank_tokens, u32x4 *__restrict__ stage_q,
+    float *__restrict__ stage_scale, int T, int H, int K, int E, int R, int TT, int nseg)
+{
+    __shared__ int32_t wcnt[kRankWaves][EP_MAX_RANKS];
+    __shared__ int32_t rows[kRankTile];
+    __shared__ int32_t slots[kRankTile];
+    const int wave = wave_uniform(threadIdx.x / kWave);
+    const int t0 = blockIdx.x * TT, nt = min(TT, T - t0);
+    const int nitems = nt * nseg;
+    rank_tile<KV>(idx, t0, nt, T, K, E, R, blockIdx.x == gridDim.x - 1, rank_slot, rank_tokens,
+                  rows, slots, wcnt);
+    for (int item = wave; item < nitems; item += kRankWaves) {
+        const int tl = item / nseg;
+        dispatch_item_fp8<KG, U, MULTI>(x, stage_q, stage_scale, rows, t0 + tl, tl,
+                                        item - tl * nseg, H, R);
     }
 }
 
@@ -758,6 +914,100 @@ hipError_t launch_dispatch_ranks_fp8(const ep_shape_t &s, const uint16_t *x,
     if (pick_u_fp8(s.T, s.H) == 2)
         return launch_ranks_fp8_u<2>(s, xv, rank_slot, qv, stage_scale, stream);
     return launch_ranks_fp8_u<1>(s, xv, rank_slot, qv, stage_scale, stream);
+}
+
+namespace {
+
+// Tokens per fused tile: at most one wavefront's worth (one lane per token ranks the tile),
+// TT*R <= kRankTile staged rows; 16 on prefill-sized batches (one workgroup per CU at
+// T = 4096), 4 on small ones.
+int pick_tt_ranks(int T, int R)
+{
+    int tt = EP_RANKS_FUSED_TT ? EP_RANKS_FUSED_TT : (T >= 2048 ? 16 : 4);
+    tt = min(tt, kWave);
+    while (tt > 1 && tt * R > kRankTile) tt /= 2;
+    return tt;
+}
+
+template <int KV, int U>
+hipError_t launch_rank_dispatch_bf16(const ep_shape_t &s, const u32x4 *x, const int32_t *idx,
+                                     int32_t *rank_slot, int32_t *rank_tokens, u32x4 *stage,
+                                     hipStream_t stream)
+{
+    const int H8 = s.H / 8, nseg = ceil_div(H8, U * kWave), TT = pick_tt_ranks(s.T, s.R);
+    const dim3 grid(s.T > 0 ? ceil_div(s.T, TT) : 1), block(kRankTile);
+#define EP_LAUNCH_RLD(KG, MULTI)                                                                \
+    return launch(rank_layout_dispatch_bf16_kernel<KV, KG, U, MULTI>, grid, block, 0, stream,  \
+                  x, idx, rank_slot, rank_tokens, stage, s.T, H8, s.K, s.E, s.R, TT, nseg)
+    EP_BY_K(s.R, EP_LAUNCH_RLD);
+#undef EP_LAUNCH_RLD
+}
+
+template <int KV, int U>
+hipError_t launch_rank_dispatch_fp8(const ep_shape_t &s, const u32x4 *x, const int32_t *idx,
+                                    int32_t *rank_slot, int32_t *rank_tokens, u32x4 *stage_q,
+                                    float *stage_scale, hipStream_t stream)
+{
+    const int nseg = ceil_div(s.H, U * 16 * kWave), TT = pick_tt_ranks(s.T, s.R);
+    const dim3 grid(s.T > 0 ? ceil_div(s.T, TT) : 1), block(kRankTile);
+#define EP_LAUNCH_RLQ(KG, MULTI)                                                                \
+    return launch(rank_layout_dispatch_fp8_kernel<KV, KG, U, MULTI>, grid, block, 0, stream,   \
+                  x, idx, rank_slot, rank_tokens, stage_q, stage_scale, s.T, s.H, s.K, s.E,     \
+                  s.R, TT, nseg)
+    EP_BY_K(s.R, EP_LAUNCH_RLQ);
+#undef EP_LAUNCH_RLQ
+}
+
+template <int KV>
+hipError_t launch_rank_dispatch_bf16_kv(const ep_shape_t &s, const uint16_t *x,
+                                        const int32_t *idx, int32_t *rank_slot,
+                                        int32_t *rank_tokens, uint16_t *stage, hipStream_t stream)
+{
+    const u32x4 *xv = reinterpret_cast<const u32x4 *>(x);
+    u32x4 *sv = reinterpret_cast<u32x4 *>(stage);
+    const int U = pick_u(s.T, s.H / 8);
+    if (U >= 4) return launch_rank_dispatch_bf16<KV, 4>(s, xv, idx, rank_slot, rank_tokens, sv, stream);
+    if (U == 2) return launch_rank_dispatch_bf16<KV, 2>(s, xv, idx, rank_slot, rank_tokens, sv, stream);
+    return launch_rank_dispatch_bf16<KV, 1>(s, xv, idx, rank_slot, rank_tokens, sv, stream);
+}
+
+template <int KV>
+hipError_t launch_rank_dispatch_fp8_kv(const ep_shape_t &s, const uint16_t *x,
+                                       const int32_t *idx, int32_t *rank_slot,
+                                       int32_t *rank_tokens, uint8_t *stage_q,
+                                       float *stage_scale, hipStream_t stream)
+{
+    const u32x4 *xv = reinterpret_cast<const u32x4 *>(x);
+    u32x4 *qv = reinterpret_cast<u32x4 *>(stage_q);
+    if (pick_u_fp8(s.T, s.H) == 2)
+        return launch_rank_dispatch_fp8<KV, 2>(s, xv, idx, rank_slot, rank_tokens, qv,
+                                               stage_scale, stream);
+    return launch_rank_dispatch_fp8<KV, 1>(s, xv, idx, rank_slot, rank_tokens, qv, stage_scale,
+                                           stream);
+}
+
+}  // namespace
+
+hipError_t launch_rank_layout_dispatch_bf16(const ep_shape_t &s, const uint16_t *x,
+                                            const int32_t *idx, int32_t *rank_slot,
+                                            int32_t *rank_tokens, uint16_t *stage,
+                                            hipStream_t stream)
+{
+    if (s.K == 8)
+        return launch_rank_dispatch_bf16_kv<2>(s, x, idx, rank_slot, rank_tokens, stage, stream);
+    return launch_rank_dispatch_bf16_kv<0>(s, x, idx, rank_slot, rank_tokens, stage, stream);
+}
+
+hipError_t launch_rank_layout_dispatch_fp8(const ep_shape_t &s, const uint16_t *x,
+                                           const int32_t *idx, int32_t *rank_slot,
+                                           int32_t *rank_tokens, uint8_t *stage_q,
+                                           float *stage_scale, hipStream_t stream)
+{
+    if (s.K == 8)
+        return launch_rank_dispatch_fp8_kv<2>(s, x, idx, rank_slot, rank_tokens, stage_q,
+                                              stage_scale, stream);
+    return launch_rank_dispatch_fp8_kv<0>(s, x, idx, rank_slot, rank_tokens, stage_q,
+                                          stage_scale, stream);
 }
 
 hipError_t launch_dispatch_expand_bf16(const ep_shape_t &s, const uint16_t *stage,

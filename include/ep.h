@@ -276,6 +276,24 @@ int ep_dispatch_ranks_fp8(const ep_shape_t *shape, const uint16_t *x, const int3
                           uint8_t *stage_q, float *stage_scale, hipStream_t stream);
 
 /*
+ * ep_rank_layout_dispatch / ep_rank_layout_dispatch_fp8 -- ep_rank_layout and
+ * ep_dispatch_ranks (or ep_dispatch_ranks_fp8) in one launch: each workgroup ranks a tile of
+ * tokens against all earlier ones and copies the tile's rows to their staging rows at once, so
+ * the layout overlaps the copies. Outputs (rank_slot, rank_tokens, stage / stage_q +
+ * stage_scale) are bit-identical to those of the two calls; the argument rules are theirs
+ * combined (topk_idx, x, stage / stage_q 16-byte aligned; rank_slot needs no alignment here).
+ * T = 0 writes rank_tokens as zeros and nothing else.
+ */
+int ep_rank_layout_dispatch(const ep_shape_t *shape, const uint16_t *x, const int32_t *topk_idx,
+                            int32_t *rank_slot, int32_t *rank_tokens, uint16_t *stage,
+                            hipStream_t stream);
+
+int ep_rank_layout_dispatch_fp8(const ep_shape_t *shape, const uint16_t *x,
+                                const int32_t *topk_idx, int32_t *rank_slot,
+                                int32_t *rank_tokens, uint8_t *stage_q, float *stage_scale,
+                                hipStream_t stream);
+
+/*
  * ep_dispatch_expand -- stage 2 of dispatch, each rank's own expansion: for every pair i = t*K
  * + j with 0 <= e < E and 0 <= slot[i] < C, recv[e][slot[i]][:] = stage[e / (E/R)]
  * [rank_slot[t][e / (E/R)]][:]. Other rows of recv are untouched. K <= EP_MAX_TOPK, H % 8 == 0.

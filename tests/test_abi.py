@@ -127,6 +127,20 @@ def test_two_stage_calls_reject_bad_arguments(lib):
                                 None) == B.EP_ERR_UNSUPPORTED
     assert lib.ep_combine_reduce(shape(), A16, None, A16, None) == B.EP_ERR_INVALID
     assert lib.ep_combine_reduce(shape(**many_ranks), A16, A16, A16, None) == B.EP_ERR_UNSUPPORTED
+    # the fused rank layout + stage 1: the rules of both calls
+    rld, rlq = lib.ep_rank_layout_dispatch, lib.ep_rank_layout_dispatch_fp8
+    assert rld(shape(**many_ranks), A16, A16, A16, A16, A16, None) == B.EP_ERR_UNSUPPORTED
+    assert rld(shape(), A16, A16 + 4, A16, A16, A16, None) == B.EP_ERR_ALIGN
+    assert rld(shape(), A16 + 2, A16, A16, A16, A16, None) == B.EP_ERR_ALIGN
+    assert rld(shape(), A16, A16, A16, A16, A16 + 2, None) == B.EP_ERR_ALIGN
+    assert rld(shape(), A16, A16, A16, None, A16, None) == B.EP_ERR_INVALID
+    assert rld(shape(), A16, A16, None, A16, A16, None) == B.EP_ERR_INVALID
+    assert rld(shape(H=12), A16, A16, A16, A16, A16, None) == B.EP_ERR_UNSUPPORTED
+    assert rld(shape(T=1 << 28, K=1, R=16), A16, A16, A16, A16, A16, None) == B.EP_ERR_UNSUPPORTED
+    assert rlq(shape(H=1000), A16, A16, A16, A16, A16, A16, None) == B.EP_ERR_UNSUPPORTED
+    assert rlq(shape(), A16, A16, A16, A16, A16, A16 + 2, None) == B.EP_ERR_ALIGN
+    assert rlq(shape(), A16, A16, A16, A16, A16 + 4, A16, None) == B.EP_ERR_ALIGN
+    assert rlq(shape(), A16, A16, A16, A16, None, A16, None) == B.EP_ERR_INVALID
 
 
 def test_packed_calls_reject_bad_arguments(lib):

@@ -76,6 +76,13 @@ class TwoStage:
         one = np.full((E, C, H), S16, np.uint16)
         oracle.dispatch(self.x, self.idx, self.slot, E, C, one)
         assert np.array_equal(want, one), "two-stage oracle differs from one-stage"
+        # the fused rank layout + stage 1: the same three outputs
+        fused = torch.full((R, T, H), S16, dtype=torch.int16, device=G.dev())
+        f = B.ep_rank_layout_dispatch(self.case.x_d, self.case.idx_d, E, R, stage=fused)
+        torch.cuda.synchronize()
+        assert np.array_equal(G.to_np(f["rank_slot"]), self.rl["rank_slot"]), "fused rank_slot"
+        assert np.array_equal(G.to_np(f["rank_tokens"]), self.rl["rank_tokens"]), "fused rank_tokens"
+        assert np.array_equal(G.to_np(fused).view(np.uint16), want_stage), "fused stage"
 
     def dispatch_fp8_full(self):
         T, H, E, C, R = self.T, self.H, self.E, self.C, self.R
@@ -89,6 +96,16 @@ class TwoStage:
         oracle.dispatch_ranks_fp8(self.x, self.rl["rank_slot"], wq, ws)
         assert np.array_equal(G.to_np(sq), wq), "stage codes"
         assert np.array_equal(G.to_np(ss).view(np.uint32), ws.view(np.uint32)), "stage scales"
+        fq = torch.full((R, T, H), S8, dtype=torch.uint8, device=G.dev())
+        fs = torch.full((R, T, NB), SF, dtype=torch.float32, device=G.dev())
+        f = B.ep_rank_layout_dispatch_fp8(self.case.x_d, self.case.idx_d, self.E, R, stage_q=fq,
+                                          stage_scale=fs)
+        torch.cuda.synchronize()
+        assert np.array_equal(G.to_np(f["rank_slot"]), self.rl["rank_slot"]), "fused rank_slot"
+        assert np.array_equal(G.to_np(f["rank_tokens"]), self.rl["rank_tokens"]), "fused rank_tokens"
+        assert np.array_equal(G.to_np(fq), wq), "fused stage codes"
+        assert np.array_equal(G.to_np(fs).view(np.uint32), ws.view(np.uint32)), "fused stage scales"
+        del fq, fs
         rq = torch.full((E, C, H), S8, dtype=torch.uint8, device=G.dev())
         rs = torch.full((E, C, NB), SF, dtype=torch.float32, device=G.dev())
         B.ep_dispatch_expand_fp8(sq, ss, self.case.idx_d, self.case.g["slot"],
@@ -171,6 +188,17 @@ def test_two_stage_workloads(name):
         sq = torch.empty((R, T, H), dtype=torch.uint8, device=G.dev())
         ss = torch.empty((R, T, NB), dtype=torch.float32, device=G.dev())
         B.ep_dispatch_ranks_fp8(c.x_d, ts.g["rank_slot"], sq, ss)
+        f = B.ep_rank_layout_dispatch_fp8(c.x_d, c.idx_d, E, R)
+        torch.cuda.synchronize()
+        assert torch.equal(f["rank_slot"], ts.g["rank_slot"])
+        assert torch.equal(f["rank_tokens"], ts.g["rank_tokens"])
+        sent = torch.from_numpy(ts.rl["rank_slot"] >= 0).to(G.dev())
+        tt, rr = torch.nonzero(sent, as_tuple=True)
+        rows = rr * T + ts.g["rank_slot"][tt, rr].long()
+        assert torch.equal(f["stage_q"].view(R * T, H)[rows], sq.view(R * T, H)[rows])
+        assert torch.equal(f["stage_scale"].view(R * T, -1)[rows].view(torch.int32),
+                           ss.view(R * T, -1)[rows].view(torch.int32))
+        del f
         q2 = torch.full((E, C, H), S8, dtype=torch.uint8, device=G.dev())
         s2 = torch.full((E, C, NB), SF, dtype=torch.float32, device=G.dev())
         B.ep_dispatch_expand_fp8(sq, ss, c.idx_d, c.g["slot"], ts.g["rank_slot"], q2, s2, C)
@@ -183,6 +211,15 @@ def test_two_stage_workloads(name):
     else:
         stage = torch.empty((R, T, H), dtype=torch.int16, device=G.dev())
         B.ep_dispatch_ranks(c.x_d, ts.g["rank_slot"], stage)
+        f = B.ep_rank_layout_dispatch(c.x_d, c.idx_d, E, R)
+        torch.cuda.synchronize()
+        assert torch.equal(f["rank_slot"], ts.g["rank_slot"])
+        assert torch.equal(f["rank_tokens"], ts.g["rank_tokens"])
+        sent = torch.from_numpy(ts.rl["rank_slot"] >= 0).to(G.dev())
+        tt, rr = torch.nonzero(sent, as_tuple=True)
+        rows = rr * T + ts.g["rank_slot"][tt, rr].long()
+        assert torch.equal(f["stage"].view(R * T, H)[rows], stage.view(R * T, H)[rows])
+        del f
         r2 = torch.full((E, C, H), S16, dtype=torch.int16, device=G.dev())
         B.ep_dispatch_expand(stage, c.idx_d, c.g["slot"], ts.g["rank_slot"], r2, C)
         r1 = torch.full((E, C, H), S16, dtype=torch.int16, device=G.dev())
@@ -236,6 +273,12 @@ def test_two_stage_empty_and_unrouted():
     g = B.ep_rank_layout(idx, 8, 4)
     torch.cuda.synchronize()
     assert G.to_np(g["rank_tokens"]).tolist() == [0, 0, 0, 0]
+    x0 = torch.zeros((0, 256), dtype=torch.int16, device="cuda")
+    for fn in (B.ep_rank_layout_dispatch, B.ep_rank_layout_dispatch_fp8):
+        rt = torch.full((4,), 7, dtype=torch.int32, device="cuda")
+        fn(x0, idx, 8, 4, rank_tokens=rt)
+        torch.cuda.synchronize()
+        assert G.to_np(rt).tolist() == [0, 0, 0, 0]
     # every id unrouted or invalid: nothing is sent anywhere, the output is +0
     ts = TwoStage(16, 64, 8, 4, 4, 4, np.where(np.arange(64).reshape(16, 4) % 2, -1, 9)
                   .astype(np.int32), W.f32_to_bf16_bits(np.ones((16, 64), np.float32)),
