@@ -27,8 +27,8 @@ EXPORTED = ("ep_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_layout_dispatch",
             "ep_dispatch_ranks_fp8", "ep_rank_layout_dispatch", "ep_rank_layout_dispatch_fp8",
             "ep_dispatch_expand", "ep_dispatch_expand_fp8",
             "ep_combine_ranks", "ep_combine_reduce", "ep_layout_packed", "ep_dispatch_packed",
-            "ep_dispatch_packed_fp8", "ep_combine_packed", "ep_error_string", "ep_last_error",
-            "ep_version")
+            "ep_dispatch_packed_fp8", "ep_layout_dispatch_packed", "ep_layout_dispatch_packed_fp8",
+            "ep_combine_packed", "ep_error_string", "ep_last_error", "ep_version")
 
 
 class EpShape(ctypes.Structure):
@@ -79,6 +79,8 @@ def load_library():
         L.ep_dispatch_packed.argtypes = [sp, i32] + [vp] * 6
         L.ep_dispatch_packed_fp8.argtypes = [sp, i32] + [vp] * 7
         L.ep_combine_packed.argtypes = [sp, i32] + [vp] * 7
+        L.ep_layout_dispatch_packed.argtypes = [sp, i32, i32] + [vp] * 10
+        L.ep_layout_dispatch_packed_fp8.argtypes = [sp, i32, i32] + [vp] * 11
         for fn in EXPORTED:
             if fn.startswith("ep_") and fn not in ("ep_error_string", "ep_last_error",
                                                    "ep_version"):
@@ -570,6 +572,73 @@ def ep_dispatch_packed_fp8(x: torch.Tensor, topk_idx: torch.Tensor, slot: torch.
                                                _ptr(recv_q), _ptr(recv_scale), _stream(stream))
     _check("ep_dispatch_packed_fp8", rc)
     return recv_q, recv_scale
+
+
+def _packed_layout_outputs(dev, T, K, E, R, slot, expert_count, packed_offset, rank_count,
+                           rank_offset, stats):
+    mk = lambda n: torch.empty(n, dtype=torch.int32, device=dev)
+    out = dict(slot=mk((T, K)) if slot is None else slot,
+               expert_count=mk(E) if expert_count is None else expert_count,
+               packed_offset=mk(E + 1) if packed_offset is None else packed_offset,
+               rank_count=mk(R) if rank_count is None else rank_count,
+               rank_offset=mk(R) if rank_offset is None else rank_offset,
+               stats=mk(EP_STATS_LEN) if stats is None else stats)
+    _need(out["slot"], "slot", torch.int32, T * K, dev)
+    for name, n in (("expert_count", E), ("packed_offset", E + 1), ("rank_count", R),
+                    ("rank_offset", R), ("stats", EP_STATS_LEN)):
+        _need(out[name], name, torch.int32, n, dev)
+    return out
+
+
+def ep_layout_dispatch_packed(x: torch.Tensor, topk_idx: torch.Tensor, recv: torch.Tensor, E: int,
+                              C: int, R: int, alignment: int, *, slot=None, expert_count=None,
+                              packed_offset=None, rank_count=None, rank_offset=None, stats=None,
+                              stream=None):
+    """ep_layout_packed and ep_dispatch_packed in one launch: the packed layout's outputs (a
+    dict as ep_layout_packed returns) and ``recv`` [rows, H] bf16 filled in place."""
+    dev = x.device
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    rows = recv.shape[0]
+    o = _packed_layout_outputs(dev, T, K, E, R, slot, expert_count, packed_offset, rank_count,
+                               rank_offset, stats)
+    _need(x, "x", _bf16(x), T * H, dev)
+    _need(topk_idx, "topk_idx", torch.int32, T * K, dev)
+    _need(recv, "recv", _bf16(recv), rows * H, dev)
+    sh = _shape(T, H, E, K, C, R)
+    rc = load_library().ep_layout_dispatch_packed(
+        ctypes.byref(sh), int(alignment), int(rows), _ptr(x), _ptr(topk_idx), _ptr(o["slot"]),
+        _ptr(o["expert_count"]), _ptr(o["packed_offset"]), _ptr(o["rank_count"]),
+        _ptr(o["rank_offset"]), _ptr(o["stats"]), _ptr(recv), _stream(stream))
+    _check("ep_layout_dispatch_packed", rc)
+    return o
+
+
+def ep_layout_dispatch_packed_fp8(x: torch.Tensor, topk_idx: torch.Tensor, recv_q: torch.Tensor,
+                                  recv_scale: torch.Tensor, E: int, C: int, R: int,
+                                  alignment: int, *, slot=None, expert_count=None,
+                                  packed_offset=None, rank_count=None, rank_offset=None,
+                                  stats=None, stream=None):
+    """ep_layout_packed and ep_dispatch_packed_fp8 in one launch: the packed layout's outputs,
+    ``recv_q`` [rows, H] and ``recv_scale`` [rows, H/128] filled in place."""
+    dev = x.device
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    rows = recv_q.shape[0]
+    o = _packed_layout_outputs(dev, T, K, E, R, slot, expert_count, packed_offset, rank_count,
+                               rank_offset, stats)
+    _need(x, "x", _bf16(x), T * H, dev)
+    _need(topk_idx, "topk_idx", torch.int32, T * K, dev)
+    _need(recv_q, "recv_q", torch.uint8, rows * H, dev)
+    _need(recv_scale, "recv_scale", torch.float32, rows * (H // EP_FP8_BLOCK), dev)
+    sh = _shape(T, H, E, K, C, R)
+    rc = load_library().ep_layout_dispatch_packed_fp8(
+        ctypes.byref(sh), int(alignment), int(rows), _ptr(x), _ptr(topk_idx), _ptr(o["slot"]),
+        _ptr(o["expert_count"]), _ptr(o["packed_offset"]), _ptr(o["rank_count"]),
+        _ptr(o["rank_offset"]), _ptr(o["stats"]), _ptr(recv_q), _ptr(recv_scale),
+        _stream(stream))
+    _check("ep_layout_dispatch_packed_fp8", rc)
+    return o
 
 
 def ep_combine_packed(y: torch.Tensor, topk_idx: torch.Tensor, slot: torch.Tensor,

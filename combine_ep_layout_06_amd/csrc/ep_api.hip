@@ -371,6 +371,74 @@ int check_packed(const ep_shape_t *shape, int32_t rows, const int32_t *packed_of
 
 }  // namespace
 
+namespace {
+
+// ep_layout_dispatch_packed[_fp8]: the checks of ep_layout_packed and ep_dispatch_packed[_fp8].
+int check_layout_dispatch_packed(const ep_shape_t *shape, int32_t alignment, int32_t rows,
+                                 const uint16_t *x, const int32_t *topk_idx, const int32_t *slot,
+                                 const int32_t *expert_count, const int32_t *packed_offset,
+                                 const int32_t *stats, const char *fn, int h_multiple)
+{
+    const std::string f(fn);
+    if (int rc = check_layout_args(shape, topk_idx, slot, expert_count, packed_offset, stats, fn))
+        return rc;
+    if (int rc = check_rows(shape, fn, h_multiple)) return rc;
+    if (alignment < 1) return fail(EP_ERR_INVALID, f + ": alignment must be >= 1");
+    if ((int64_t)shape->E * ((int64_t)shape->C + alignment - 1) > INT32_MAX)
+        return fail(EP_ERR_UNSUPPORTED, f + ": E*(C + alignment - 1) exceeds INT32_MAX");
+    if (rows < 0) return fail(EP_ERR_INVALID, f + ": rows must be >= 0");
+    if (shape->T > 0 && !x) return fail(EP_ERR_INVALID, f + ": NULL required pointer");
+    if (!aligned(x, 16)) return fail(EP_ERR_ALIGN, f + ": x must be 16-byte aligned");
+    return EP_OK;
+}
+
+}  // namespace
+
+int ep_layout_dispatch_packed(const ep_shape_t *shape, int32_t alignment, int32_t rows,
+                              const uint16_t *x, const int32_t *topk_idx, int32_t *slot,
+                              int32_t *expert_count, int32_t *packed_offset, int32_t *rank_count,
+                              int32_t *rank_offset, int32_t *stats, uint16_t *recv,
+                              hipStream_t stream)
+{
+    const char *fn = "ep_layout_dispatch_packed";
+    if (int rc = check_layout_dispatch_packed(shape, alignment, rows, x, topk_idx, slot,
+                                              expert_count, packed_offset, stats, fn, 8))
+        return rc;
+    if (shape->T > 0 && !recv) return fail(EP_ERR_INVALID, "ep_layout_dispatch_packed: NULL required pointer");
+    if (!aligned(recv, 16))
+        return fail(EP_ERR_ALIGN, "ep_layout_dispatch_packed: recv must be 16-byte aligned");
+    ep::LayoutOut o{slot, expert_count, packed_offset, rank_count, rank_offset, stats};
+    o.offset_end = packed_offset + shape->E;
+    o.align = alignment;
+    return hip_status(ep::launch_layout_dispatch_packed_bf16(*shape, x, topk_idx, o, rows, recv,
+                                                             stream),
+                      fn);
+}
+
+int ep_layout_dispatch_packed_fp8(const ep_shape_t *shape, int32_t alignment, int32_t rows,
+                                  const uint16_t *x, const int32_t *topk_idx, int32_t *slot,
+                                  int32_t *expert_count, int32_t *packed_offset,
+                                  int32_t *rank_count, int32_t *rank_offset, int32_t *stats,
+                                  uint8_t *recv_q, float *recv_scale, hipStream_t stream)
+{
+    const char *fn = "ep_layout_dispatch_packed_fp8";
+    if (int rc = check_layout_dispatch_packed(shape, alignment, rows, x, topk_idx, slot,
+                                              expert_count, packed_offset, stats, fn,
+                                              EP_FP8_BLOCK))
+        return rc;
+    if (shape->T > 0 && (!recv_q || !recv_scale))
+        return fail(EP_ERR_INVALID, "ep_layout_dispatch_packed_fp8: NULL required pointer");
+    if (!aligned(recv_q, 16) || !aligned(recv_scale, 4))
+        return fail(EP_ERR_ALIGN, "ep_layout_dispatch_packed_fp8: recv_q must be 16-byte aligned, "
+                                  "recv_scale 4-byte aligned");
+    ep::LayoutOut o{slot, expert_count, packed_offset, rank_count, rank_offset, stats};
+    o.offset_end = packed_offset + shape->E;
+    o.align = alignment;
+    return hip_status(ep::launch_layout_dispatch_packed_fp8(*shape, x, topk_idx, o, rows, recv_q,
+                                                            recv_scale, stream),
+                      fn);
+}
+
 int ep_dispatch_packed(const ep_shape_t *shape, int32_t rows, const uint16_t *x,
                        const int32_t *topk_idx, const int32_t *slot,
                        const int32_t *packed_offset, uint16_t *recv, hipStream_t stream)

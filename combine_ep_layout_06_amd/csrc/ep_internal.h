@@ -75,6 +75,13 @@ hipError_t launch_combine(const ep_shape_t &s, const uint16_t *y, const int32_t 
 hipError_t launch_rank_layout(const ep_shape_t &s, const int32_t *idx, int32_t *rank_slot,
                               int32_t *rank_tokens, hipStream_t stream);
 
+hipError_t launch_layout_dispatch_packed_bf16(const ep_shape_t &s, const uint16_t *x,
+                                              const int32_t *idx, const LayoutOut &o,
+                                              int rows_cap, uint16_t *recv, hipStream_t stream);
+hipError_t launch_layout_dispatch_packed_fp8(const ep_shape_t &s, const uint16_t *x,
+                                             const int32_t *idx, const LayoutOut &o,
+                                             int rows_cap, uint8_t *recv_q, float *recv_scale,
+                                             hipStream_t stream);
 hipError_t launch_rank_layout_dispatch_bf16(const ep_shape_t &s, const uint16_t *x,
                                             const int32_t *idx, int32_t *rank_slot,
                                             int32_t *rank_tokens, uint16_t *stage,

@@ -31,6 +31,11 @@
 // deterministic and need no workspace. The cost is the pass over all earlier ids, one memory
 // round trip plus ~tile_begin/1024 conflict-free LDS atomics per lane.
 //
+// ALL (packed layout fused with dispatch): a pair's packed row offset[e] + slot needs every
+// expert's total, so the tile also counts the ids AFTER it, into a second replicated histogram
+// (each id of the batch still costs one atomic). Step 3 then yields each expert's total, and
+// every workgroup scans the counts rounded up to the alignment into the packed offsets itself.
+//
 // LDS is the launch's dynamic shared memory, carved by layout_lds_map(E, lg_nc); its size grows
 // with E (17 KB at E = 128, 140 KB at E = 1024).
 #pragma once
@@ -63,6 +68,9 @@ struct LayoutLdsMap {
     int scan;     // [E + 1]: exclusive scan of count, then the total kept
     int wsum;     // [kTileWaves], then the invalid and unrouted totals
     int ksum;     // [kTileWaves]: kept counts per wavefront (differ from wsum when padded)
+    int hist2;    // ALL: [B][NC] replicated histogram of the later tiles (before base)
+    int tot;      // ALL: [E] totals of the experts
+    int off;      // ALL: [E] packed offsets
     int words;    // total
 };
 
@@ -75,7 +83,7 @@ inline int layout_lg_nc(int E)
     return lg;
 }
 
-__host__ __device__ inline LayoutLdsMap layout_lds_map(int E, int lg_nc)
+__host__ __device__ inline LayoutLdsMap layout_lds_map(int E, int lg_nc, bool all = false)
 {
     LayoutLdsMap m;
     m.B = E + 2;
@@ -83,17 +91,20 @@ __host__ __device__ inline LayoutLdsMap layout_lds_map(int E, int lg_nc)
     const int wcnt_words = (kTileWaves * m.B + 3) & ~3;   // keep hist 16-byte aligned
     m.wcnt = 0;
     m.hist = wcnt_words;
-    m.base = m.hist + (m.B << m.lg_nc);
+    m.hist2 = m.hist + (m.B << m.lg_nc);                  // cleared together with hist
+    m.base = m.hist2 + (all ? (m.B << m.lg_nc) : 0);
     m.scan = m.base + ((m.B + 3) & ~3);
     m.wsum = m.scan + ((E + 1 + 3) & ~3);
     m.ksum = m.wsum + kTileWaves + 2;
-    m.words = m.ksum + kTileWaves;
+    m.tot = m.ksum + kTileWaves;
+    m.off = m.tot + (all ? E : 0);
+    m.words = m.off + (all ? E : 0);
     return m;
 }
 
-inline size_t layout_lds_bytes(int E, int lg_nc)
+inline size_t layout_lds_bytes(int E, int lg_nc, bool all = false)
 {
-    return (size_t)layout_lds_map(E, lg_nc).words * 4;
+    return (size_t)layout_lds_map(E, lg_nc, all).words * 4;
 }
 
 // Bin of an id: itself for an expert, E for an invalid id, E+1 for -1 (unrouted).
@@ -117,8 +128,28 @@ __device__ __forceinline__ int row16_total(int v)
 struct TileIds {
     int4 v[kPrefixVec];   // earlier-tile id vectors tid + u*1024 (clamped; see layout_tile)
     int own;              // this lane's pair, -1 past the tile or the batch
+    int tail;             // ALL: one of the last TK % 4 ids if they come after the tile
 };
 
+// ALL: the vectors other than the tile's own, numbered 0 .. nb + (se - sb): the nb earlier
+// ones, then vectors sb .. se of the later ones (se = TK / 4 whole vectors; the TK % 4 ids past
+// them are the tails).
+struct OtherVecs {
+    int nb, sb, se;
+    __device__ int count() const { return nb + (se - sb); }
+    __device__ int phys(int v) const { return v < nb ? v : sb + (v - nb); }
+};
+
+__device__ __forceinline__ OtherVecs other_vecs(int TK, int tile_begin, int P)
+{
+    OtherVecs o;
+    o.nb = tile_begin / 4;
+    o.se = TK / 4;
+    o.sb = min((tile_begin + P) / 4, o.se);     // P is a multiple of 4
+    return o;
+}
+
+template <bool ALL = false>
 __device__ __forceinline__ TileIds layout_tile_loads(const int32_t *__restrict__ idx, int TK,
                                                      int tile_begin, int P)
 {
@@ -126,17 +157,35 @@ __device__ __forceinline__ TileIds layout_tile_loads(const int32_t *__restrict__
     const int tid = threadIdx.x;
     const int p = tile_begin + tid;
     t.own = (tid < P && p < TK) ? idx[p] : -1;
-    const int nvec = tile_begin / 4;      // tile_begin is a multiple of 4: whole vectors
+    t.tail = -1;
     // a batch is issued only if some lane of the wavefront needs it: the load pipe of a CU
     // moves ~64 bytes per clock, so clamped duplicates would still cost issue time
-    const int wave_q0 = __builtin_amdgcn_readfirstlane(tid & ~(kWave - 1));
-    const int4 *idx4 = reinterpret_cast<const int4 *>(idx);
+    if constexpr (ALL) {
+        const int tp = (TK / 4) * 4 + tid;      // a tail id past the tile
+        if (tid < TK % 4 && tp >= tile_begin + P) t.tail = idx[tp];
+        const OtherVecs ov = other_vecs(TK, tile_begin, P);
+        const int nvec = ov.count();
+        const int wave_q0 = __builtin_amdgcn_readfirstlane(tid & ~(kWave - 1));
+        const int4 *idx4 = reinterpret_cast<const int4 *>(idx);
 #pragma unroll
-    for (int u = 0; u < kPrefixVec; ++u) {
-        t.v[u] = int4{0, 0, 0, 0};
-        if (wave_q0 + u * kTileThreads < nvec) {
-            const int q = tid + u * kTileThreads;
-            t.v[u] = idx4[q < nvec ? q : nvec - 1];
+        for (int u = 0; u < kPrefixVec; ++u) {
+            t.v[u] = int4{0, 0, 0, 0};
+            if (wave_q0 + u * kTileThreads < nvec) {
+                const int q = tid + u * kTileThreads;
+                t.v[u] = idx4[ov.phys(q < nvec ? q : nvec - 1)];
+            }
+        }
+    } else {
+        const int nvec = tile_begin / 4;      // tile_begin is a multiple of 4: whole vectors
+        const int wave_q0 = __builtin_amdgcn_readfirstlane(tid & ~(kWave - 1));
+        const int4 *idx4 = reinterpret_cast<const int4 *>(idx);
+#pragma unroll
+        for (int u = 0; u < kPrefixVec; ++u) {
+            t.v[u] = int4{0, 0, 0, 0};
+            if (wave_q0 + u * kTileThreads < nvec) {
+                const int q = tid + u * kTileThreads;
+                t.v[u] = idx4[q < nvec ? q : nvec - 1];
+            }
         }
     }
     return t;
@@ -146,11 +195,16 @@ __device__ __forceinline__ TileIds layout_tile_loads(const int32_t *__restrict__
 // layout_tile_loads. Writes slot[] for the tile's pairs and, if rows is not null,
 // rows[k] = e*C + slot (or -1 for a pair that is not kept) for local pair k. `last` marks the
 // workgroup that will call layout_finish. Ends with a barrier.
+// ALL: also counts the later tiles, and rows[k] = off[e] + slot, the pair's row in a packed
+// buffer of rows_cap rows with each expert's count rounded up to `align` (-1 if not kept or
+// past the buffer); the packed offsets are left in LDS at m.off.
+template <bool ALL = false>
 __device__ __forceinline__ void layout_tile(const TileIds &ids, const int32_t *__restrict__ idx,
                                             int TK, int E, int C, int nbits, int tile_begin,
                                             int P, bool last, int32_t *lds,
                                             const LayoutLdsMap &m,
-                                            int32_t *__restrict__ slot, int32_t *rows)
+                                            int32_t *__restrict__ slot, int32_t *rows,
+                                            int align = 1, int rows_cap = 0)
 {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -168,34 +222,75 @@ __device__ __forceinline__ void layout_tile(const TileIds &ids, const int32_t *_
 
     // 1. earlier tiles into the replicated histogram. Vectors past the prefix were clamped to
     //    its last one; their counts are skipped.
-    const int nvec = tile_begin / 4;
     const int copy = lane & (NC - 1);
-    if (nvec > 0) {
-#pragma unroll
-        for (int u = 0; u < kPrefixVec; ++u) {
-            const bool ok = tid + u * kTileThreads < nvec;
-            const int e4[4] = {ids.v[u].x, ids.v[u].y, ids.v[u].z, ids.v[u].w};
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-                if (ok) atomicAdd(&hist[(layout_bin(e4[c], E) << m.lg_nc) + copy], 1);
-        }
-        // prefixes longer than kPrefixVec*4096 ids: the rest in further batches
-        const int4 *idx4 = reinterpret_cast<const int4 *>(idx);
-        for (int q0 = tid + kPrefixVec * kTileThreads; q0 < nvec;
-             q0 += kPrefixVec * kTileThreads) {
-            int4 v[kPrefixVec];
+    if constexpr (ALL) {
+        // every other vector: the earlier ones into hist, the later ones into the second
+        // histogram, then the last TK % 4 ids if they come after the tile
+        const OtherVecs ov = other_vecs(TK, tile_begin, P);
+        const int nvec = ov.count();
+        int32_t *hist2 = lds + m.hist2;
+        if (nvec > 0) {
 #pragma unroll
             for (int u = 0; u < kPrefixVec; ++u) {
-                const int q = q0 + u * kTileThreads;
-                v[u] = idx4[q < nvec ? q : nvec - 1];
+                const int q = tid + u * kTileThreads;
+                int32_t *h = q < ov.nb ? hist : hist2;
+                const int e4[4] = {ids.v[u].x, ids.v[u].y, ids.v[u].z, ids.v[u].w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (q < nvec) atomicAdd(&h[(layout_bin(e4[c], E) << m.lg_nc) + copy], 1);
             }
+            // more than kPrefixVec*4096 other ids: the rest in further batches
+            const int4 *idx4 = reinterpret_cast<const int4 *>(idx);
+            for (int q0 = tid + kPrefixVec * kTileThreads; q0 < nvec;
+                 q0 += kPrefixVec * kTileThreads) {
+                int4 v[kPrefixVec];
+#pragma unroll
+                for (int u = 0; u < kPrefixVec; ++u) {
+                    const int q = q0 + u * kTileThreads;
+                    v[u] = idx4[ov.phys(q < nvec ? q : nvec - 1)];
+                }
+#pragma unroll
+                for (int u = 0; u < kPrefixVec; ++u) {
+                    const int q = q0 + u * kTileThreads;
+                    int32_t *h = q < ov.nb ? hist : hist2;
+                    const int e4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        if (q < nvec) atomicAdd(&h[(layout_bin(e4[c], E) << m.lg_nc) + copy], 1);
+                }
+            }
+        }
+        if (tid < TK % 4 && (TK / 4) * 4 + tid >= tile_begin + P)
+            atomicAdd(&hist2[(layout_bin(ids.tail, E) << m.lg_nc) + copy], 1);
+    } else {
+        const int nvec = tile_begin / 4;
+        if (nvec > 0) {
 #pragma unroll
             for (int u = 0; u < kPrefixVec; ++u) {
-                const bool ok = q0 + u * kTileThreads < nvec;
-                const int e4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+                const bool ok = tid + u * kTileThreads < nvec;
+                const int e4[4] = {ids.v[u].x, ids.v[u].y, ids.v[u].z, ids.v[u].w};
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
                     if (ok) atomicAdd(&hist[(layout_bin(e4[c], E) << m.lg_nc) + copy], 1);
+            }
+            // prefixes longer than kPrefixVec*4096 ids: the rest in further batches
+            const int4 *idx4 = reinterpret_cast<const int4 *>(idx);
+            for (int q0 = tid + kPrefixVec * kTileThreads; q0 < nvec;
+                 q0 += kPrefixVec * kTileThreads) {
+                int4 v[kPrefixVec];
+#pragma unroll
+                for (int u = 0; u < kPrefixVec; ++u) {
+                    const int q = q0 + u * kTileThreads;
+                    v[u] = idx4[q < nvec ? q : nvec - 1];
+                }
+#pragma unroll
+                for (int u = 0; u < kPrefixVec; ++u) {
+                    const bool ok = q0 + u * kTileThreads < nvec;
+                    const int e4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        if (ok) atomicAdd(&hist[(layout_bin(e4[c], E) << m.lg_nc) + copy], 1);
+                }
             }
         }
     }
@@ -242,8 +337,36 @@ __device__ __forceinline__ void layout_tile(const TileIds &ids, const int32_t *_
         const int incl = row16_inclusive_sum(c);
         wcnt[w * B + e] = b0 + incl - c;
         if (w == kTileWaves - 1) base[e] = b0 + incl;
+        if constexpr (ALL) {            // the later tiles' count: the expert's total
+            const int32_t *h2 = lds + m.hist2 + (e << m.lg_nc) + (w << (m.lg_nc - 4));
+            int part2;
+            if (m.lg_nc == 6) {
+                const int4 q = *reinterpret_cast<const int4 *>(h2);
+                part2 = (q.x + q.y) + (q.z + q.w);
+            } else if (m.lg_nc == 5) {
+                const int2 q = *reinterpret_cast<const int2 *>(h2);
+                part2 = q.x + q.y;
+            } else {
+                part2 = h2[0];
+            }
+            const int a0 = row16_total(part2);
+            if (w == kTileWaves - 1) lds[m.tot + e] = b0 + incl + a0;
+        }
     }
     __syncthreads();
+    if constexpr (ALL) {
+        // packed offsets: exclusive scan of align_up(min(total, C), align) in expert order
+        int32_t *wsum = lds + m.wsum;
+        const int cnt = tid < E ? min(lds[m.tot + tid], C) : 0;   // E <= kTileThreads
+        const int prow = (cnt + align - 1) / align * align;
+        const int incl = wave_inclusive_sum(prow);
+        if (lane == kWave - 1) wsum[wave] = incl;
+        __syncthreads();
+        int wb = 0;
+        for (int w = 0; w < wave; ++w) wb += wsum[w];
+        if (tid < E) lds[m.off + tid] = wb + incl - prow;
+        __syncthreads();
+    }
     if (in) {
         int s = -1;
         if (routed) {
@@ -251,7 +374,12 @@ __device__ __forceinline__ void layout_tile(const TileIds &ids, const int32_t *_
             s = pos < C ? pos : -1;
         }
         slot[p] = s;
-        if (rows) rows[tid] = s >= 0 ? own * C + s : -1;
+        if constexpr (ALL) {
+            const int r = s >= 0 ? lds[m.off + own] + s : -1;
+            rows[tid] = (unsigned)r < (unsigned)rows_cap ? r : -1;
+        } else {
+            if (rows) rows[tid] = s >= 0 ? own * C + s : -1;
+        }
     }
     __syncthreads();
 }

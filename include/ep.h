@@ -185,8 +185,8 @@ int ep_combine(const ep_shape_t *shape, const uint16_t *y, const int32_t *topk_i
  * [rows][H] starting at packed_offset[e], the exclusive scan of those padded counts
  * (packed_offset[E] = the rows the buffer needs; at most min(T*K, E*C) + E*(A-1)). A kept pair
  * (t, j) of expert e lives in row packed_offset[e] + slot. Padding rows are never written or
- * read. The offsets need every tile's counts, so this layout is a call of its own (there is
- * no fused variant).
+ * read. The offsets need every expert's total: ep_layout_packed computes them as a call of its
+ * own, and ep_layout_dispatch_packed has every workgroup count all pairs to fuse the two.
  */
 
 /*
@@ -216,6 +216,27 @@ int ep_dispatch_packed_fp8(const ep_shape_t *shape, int32_t rows, const uint16_t
                            const int32_t *topk_idx, const int32_t *slot,
                            const int32_t *packed_offset, uint8_t *recv_q, float *recv_scale,
                            hipStream_t stream);
+
+/*
+ * ep_layout_dispatch_packed / ep_layout_dispatch_packed_fp8 -- ep_layout_packed followed by
+ * ep_dispatch_packed / ep_dispatch_packed_fp8 into a buffer of `rows` rows, in one launch:
+ * every workgroup counts all pairs, so it knows the packed offsets without waiting for the
+ * others. Outputs are bit-identical to the two calls and the rules of both apply (alignment
+ * >= 1, rows >= 0, topk_idx / x / recv / recv_q 16-byte aligned, recv_scale 4-byte aligned).
+ * For large E (the layout's two histograms beyond 64 KB of LDS, E above ~320) the call runs
+ * the two steps as two launches.
+ */
+int ep_layout_dispatch_packed(const ep_shape_t *shape, int32_t alignment, int32_t rows,
+                              const uint16_t *x, const int32_t *topk_idx, int32_t *slot,
+                              int32_t *expert_count, int32_t *packed_offset, int32_t *rank_count,
+                              int32_t *rank_offset, int32_t *stats, uint16_t *recv,
+                              hipStream_t stream);
+
+int ep_layout_dispatch_packed_fp8(const ep_shape_t *shape, int32_t alignment, int32_t rows,
+                                  const uint16_t *x, const int32_t *topk_idx, int32_t *slot,
+                                  int32_t *expert_count, int32_t *packed_offset,
+                                  int32_t *rank_count, int32_t *rank_offset, int32_t *stats,
+                                  uint8_t *recv_q, float *recv_scale, hipStream_t stream);
 
 /*
  * ep_combine_packed -- ep_combine reading y from a packed buffer of `rows` rows: the expert row

@@ -143,6 +143,26 @@ def test_two_stage_calls_reject_bad_arguments(lib):
     assert rlq(shape(), A16, A16, A16, A16, None, A16, None) == B.EP_ERR_INVALID
 
 
+def test_fused_packed_calls_reject_bad_arguments(lib):
+    ldp, ldq = lib.ep_layout_dispatch_packed, lib.ep_layout_dispatch_packed_fp8
+    ok = (A16,) * 8                                # x, topk_idx, slot, count, offset, rc, ro, stats
+    assert ldp(shape(), 0, 10, *ok, A16, None) == B.EP_ERR_INVALID           # alignment < 1
+    assert ldp(shape(), 16, -1, *ok, A16, None) == B.EP_ERR_INVALID          # rows < 0
+    assert ldp(shape(), 16, 10, A16 + 2, *ok[1:], A16, None) == B.EP_ERR_ALIGN   # x
+    assert ldp(shape(), 16, 10, A16, A16 + 4, *ok[2:], A16, None) == B.EP_ERR_ALIGN  # topk_idx
+    assert ldp(shape(), 16, 10, *ok, A16 + 8, None) == B.EP_ERR_ALIGN        # recv
+    assert ldp(shape(), 16, 10, *ok, None, None) == B.EP_ERR_INVALID         # recv NULL
+    assert ldp(shape(), 16, 10, A16, A16, A16, A16, None, A16, A16, A16, A16,
+               None) == B.EP_ERR_INVALID                                     # packed_offset
+    assert ldp(shape(H=12), 16, 10, *ok, A16, None) == B.EP_ERR_UNSUPPORTED
+    assert ldp(shape(E=2048, R=1), 16, 10, *ok, A16, None) == B.EP_ERR_UNSUPPORTED
+    assert ldp(shape(E=1024, R=1, C=(1 << 21) - 1), 1 << 12, 10, *ok, A16,
+               None) == B.EP_ERR_UNSUPPORTED                                 # E*(C+A-1)
+    assert ldq(shape(H=1000), 16, 10, *ok, A16, A16, None) == B.EP_ERR_UNSUPPORTED
+    assert ldq(shape(), 16, 10, *ok, A16, A16 + 2, None) == B.EP_ERR_ALIGN   # recv_scale
+    assert ldq(shape(), 16, 10, *ok, None, A16, None) == B.EP_ERR_INVALID
+
+
 def test_packed_calls_reject_bad_arguments(lib):
     assert lib.ep_layout_packed(shape(), 0, A16, A16, A16, A16, None, None, A16, None) == B.EP_ERR_INVALID
     assert lib.ep_layout_packed(shape(E=1024, R=1, C=(1 << 21) - 1), 1 << 12, A16, A16, A16, A16, None,

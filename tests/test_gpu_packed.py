@@ -74,6 +74,42 @@ def run_case(idx, x, w, E, C, R, align, full, rows=None, fp8=True, seed=0):
             assert np.array_equal(G.to_np(q)[pick], wq[pick])
             assert np.array_equal(G.to_np(sc)[pick].view(np.uint32), ws[pick].view(np.uint32))
         del q, sc
+    # the packed layout and dispatch in one launch: the same outputs
+    lay_want = dict(slot=lay["slot"], expert_count=lay["count"], stats=lay["stats_array"],
+                    packed_offset=off, rank_offset=off[:-1:EL][:R],
+                    rank_count=off[EL::EL] - off[:-1:EL][:R])
+    recv = torch.full((rows + 4, H), S16, dtype=torch.int16, device=G.dev())
+    f = B.ep_layout_dispatch_packed(x_d, idx_d, recv[:rows], E, C, R, align)
+    torch.cuda.synchronize()
+    for k, v in lay_want.items():
+        assert np.array_equal(G.to_np(f[k]), v), f"fused {k}"
+    got = G.to_np(recv).view(np.uint16)
+    if full:
+        assert np.array_equal(got, want), "fused packed recv"
+    else:
+        pick = np.linspace(0, rows - 1, 509).astype(int)
+        assert np.array_equal(got[pick], want[pick]), "fused packed recv rows"
+        assert (got[rows:] == np.uint16(S16)).all()
+    del recv
+    if fp8 and H % 128 == 0:
+        NB = H // 128
+        q = torch.full((rows, H), S8, dtype=torch.uint8, device=G.dev())
+        sc = torch.full((rows, NB), SF, dtype=torch.float32, device=G.dev())
+        f = B.ep_layout_dispatch_packed_fp8(x_d, idx_d, q, sc, E, C, R, align)
+        torch.cuda.synchronize()
+        for k, v in lay_want.items():
+            assert np.array_equal(G.to_np(f[k]), v), f"fused fp8 {k}"
+        wq = np.full((rows, H), S8, np.uint8)
+        ws = np.full((rows, NB), SF, np.float32)
+        oracle.dispatch_packed_fp8(x, idx, slot, off, E, C, wq, ws)
+        if full:
+            assert np.array_equal(G.to_np(q), wq), "fused packed codes"
+            assert np.array_equal(G.to_np(sc).view(np.uint32), ws.view(np.uint32))
+        else:
+            pick = np.linspace(0, rows - 1, 509).astype(int)
+            assert np.array_equal(G.to_np(q)[pick], wq[pick])
+            assert np.array_equal(G.to_np(sc)[pick].view(np.uint32), ws[pick].view(np.uint32))
+        del q, sc
     # combine from a packed y: kept rows from the expert-output stream, every other row NaN
     e_f, s_f = idx.reshape(-1), slot.reshape(-1)
     keep = (e_f >= 0) & (e_f < E) & (s_f >= 0) & (s_f < C)
@@ -100,6 +136,9 @@ SMALL = [
     (100, 520, 16, 4, 9, 4),
     (257, 1024, 32, 8, 40, 8),
     (300, 384, 128, 16, 24, 16),
+    (2051, 256, 256, 8, 80, 8),       # prefill-sized tiles, E = 256: the fused layout+dispatch
+    (700, 128, 512, 4, 9, 4),         # E = 512: its histograms exceed the fused kernel's LDS,
+                                      # the call runs as two launches
 ]
 
 
