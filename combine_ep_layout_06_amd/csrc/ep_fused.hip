@@ -14,6 +14,11 @@
 // slots are known, so the layout of later tiles overlaps the copies of earlier ones; and in the
 // bf16 kernel each wavefront issues its first row piece's loads together with the layout's own
 // loads, since only the stores need the slots.
+//
+// The packed variants (layout_dispatch_packed_*) write each pair to its row of a packed,
+// aligned buffer, offset[e] + slot. Those offsets need every expert's total, so each of their
+// tiles counts all pairs, the later ones too (layout_tile<true>), and scans the offsets itself.
+// The results are identical to ep_layout_packed followed by ep_dispatch_packed[_fp8].
 #include "ep_dispatch_item.h"
 #include "ep_internal.h"
 #include "ep_layout_tile.h"
