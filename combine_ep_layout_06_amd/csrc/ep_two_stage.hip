@@ -83,6 +83,55 @@ __device__ __forceinline__ uint64_t token_ranks_any(const int32_t *__restrict__ 
     return m;
 }
 
+// Per-rank counts of the tokens [0, t0) in this wavefront's share (tokens wave*64 + lane +
+// b*kRankTile): kRankBatch tokens per lane are loaded together (16-byte id vectors when
+// KV > 0), then per rank the wavefront adds up one ballot count per batch. Lane r returns rank
+// r's total.
+template <int KV>
+__device__ __forceinline__ int rank_prefix_wave(const int32_t *__restrict__ idx, int t0, int K,
+                                                int E, int EL, int R)
+{
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int q0 = wave * kWave + lane;
+    int acc = 0;
+    for (int b0 = 0; b0 * kRankTile + wave * kWave < t0; b0 += kRankBatch) {
+        uint64_t m[kRankBatch];
+        if constexpr (KV > 0) {
+            int4 v[kRankBatch][KV];
+#pragma unroll
+            for (int b = 0; b < kRankBatch; ++b) {
+#pragma unroll
+                for (int j = 0; j < KV; ++j) v[b][j] = int4{-1, -1, -1, -1};
+                if ((b0 + b) * kRankTile + wave * kWave < t0) {        // wavefront-uniform
+                    const int q = min(q0 + (b0 + b) * kRankTile, t0 - 1);
+#pragma unroll
+                    for (int j = 0; j < KV; ++j)
+                        v[b][j] = reinterpret_cast<const int4 *>(idx + (size_t)q * K)[j];
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < kRankBatch; ++b)
+                m[b] = q0 + (b0 + b) * kRankTile < t0 ? ranks_of(v[b], KV, E, EL) : 0;
+        } else {
+#pragma unroll
+            for (int b = 0; b < kRankBatch; ++b) {
+                const int q = q0 + (b0 + b) * kRankTile;
+                m[b] = q < t0 ? token_ranks_any(idx, q, K, E, EL) : 0;
+            }
+        }
+        // batches holding any of this wavefront's earlier tokens
+        const int nb = min(kRankBatch, ceil_div(t0 - b0 * kRankTile - wave * kWave, kRankTile));
+        for (int r = 0; r < R; ++r) {
+            int c = 0;
+#pragma unroll
+            for (int b = 0; b < kRankBatch; ++b)
+                if (b < nb) c += __popcll(__ballot(((m[b] >> r) & 1u) != 0));
+            acc = lane == r ? acc + c : acc;
+        }
+    }
+    return acc;
+}
+
 // KV > 0: K = 4*KV ids per token, read as KV 16-byte vectors; KV = 0: any K.
 template <int KV>
 __global__ __launch_bounds__(kRankTile) void rank_layout_kernel(
@@ -96,76 +145,20 @@ __global__ __launch_bounds__(kRankTile) void rank_layout_kernel(
     const int EL = E / R;
     const int t0 = blockIdx.x * kRankTile;
     const int t = t0 + tid;
-    const int q_first = wave * kWave + lane;     // this lane's token in each earlier tile
 
-    // 1. the lane's own token and the earlier tiles, 64 tokens per wavefront step (t0 is a
-    //    multiple of 1024, so a step is whole or absent). The first kRankBatch tiles and the
-    //    own token are loaded straight-line, all in flight together; per rank, the wavefront
-    //    sums the ballot counts of its tokens (scalar adds) and lane r keeps rank r's total.
+    // 1. the lane's own token and the earlier tiles (rank_prefix_wave): the own ids are loaded
+    //    first and used after the prefix count, so all loads are in flight together
     uint64_t own = 0;
-    uint64_t m[kRankBatch];
+    int4 vo[KV > 0 ? KV : 1];
     if constexpr (KV > 0) {
-        int4 vo[KV], v[kRankBatch][KV];
         if (t < T) {
 #pragma unroll
             for (int j = 0; j < KV; ++j) vo[j] = reinterpret_cast<const int4 *>(idx + (size_t)t * K)[j];
         }
-#pragma unroll
-        for (int b = 0; b < kRankBatch; ++b)
-            if (b * kRankTile < t0) {
-#pragma unroll
-                for (int j = 0; j < KV; ++j)
-                    v[b][j] = reinterpret_cast<const int4 *>(
-                        idx + (size_t)(q_first + b * kRankTile) * K)[j];
-            }
-        own = t < T ? ranks_of(vo, KV, E, EL) : 0;
-#pragma unroll
-        for (int b = 0; b < kRankBatch; ++b) m[b] = b * kRankTile < t0 ? ranks_of(v[b], KV, E, EL) : 0;
-    } else {
-        own = t < T ? token_ranks_any(idx, t, K, E, EL) : 0;
-#pragma unroll
-        for (int b = 0; b < kRankBatch; ++b)
-            m[b] = b * kRankTile < t0 ? token_ranks_any(idx, q_first + b * kRankTile, K, E, EL) : 0;
     }
-    int acc = 0;
-    for (int b0 = 0;; b0 += kRankBatch) {
-        const int nb = min(kRankBatch, t0 / kRankTile - b0);     // tiles in this batch
-        uint32_t lo[kRankBatch], hi[kRankBatch];
-#pragma unroll
-        for (int b = 0; b < kRankBatch; ++b) {
-            lo[b] = (uint32_t)m[b];
-            hi[b] = (uint32_t)(m[b] >> 32);
-        }
-        for (int r = 0; r < R && nb > 0; ++r) {
-            int c = 0;
-#pragma unroll
-            for (int b = 0; b < kRankBatch; ++b)
-                if (b < nb) c += __popcll(__ballot((((r < 32 ? lo[b] : hi[b]) >> (r & 31)) & 1u) != 0));
-            acc = lane == r ? acc + c : acc;
-        }
-        if ((b0 + kRankBatch) * kRankTile >= t0) break;
-        // prefixes longer than kRankBatch tiles (T > 5*1024): further batches
-        const int bn = b0 + kRankBatch;
-        if constexpr (KV > 0) {
-            int4 v[kRankBatch][KV];
-#pragma unroll
-            for (int b = 0; b < kRankBatch; ++b)
-                if ((bn + b) * kRankTile < t0) {
-#pragma unroll
-                    for (int j = 0; j < KV; ++j)
-                        v[b][j] = reinterpret_cast<const int4 *>(
-                            idx + (size_t)(q_first + (bn + b) * kRankTile) * K)[j];
-                }
-#pragma unroll
-            for (int b = 0; b < kRankBatch; ++b)
-                m[b] = (bn + b) * kRankTile < t0 ? ranks_of(v[b], KV, E, EL) : 0;
-        } else {
-#pragma unroll
-            for (int b = 0; b < kRankBatch; ++b)
-                m[b] = (bn + b) * kRankTile < t0
-                           ? token_ranks_any(idx, q_first + (bn + b) * kRankTile, K, E, EL) : 0;
-        }
-    }
+    const int acc = rank_prefix_wave<KV>(idx, t0, K, E, EL, R);
+    if constexpr (KV > 0) own = t < T ? ranks_of(vo, KV, E, EL) : 0;
+    else own = t < T ? token_ranks_any(idx, t, K, E, EL) : 0;
     if (lane < R) wcnt[wave][lane] = acc;
     __syncthreads();
     if (tid < R) {
@@ -286,55 +279,6 @@ __global__ __launch_bounds__(kThreads) void dispatch_ranks_fp8_kernel(
 // rank layout and stage 1 fused: each workgroup ranks a tile of at most 64 tokens against all
 // earlier tokens, then copies (or quantises and copies) the tile's rows to their staging rows
 // ------------------------------------------------------------------------------------------
-
-// Per-rank counts of the tokens [0, t0) in this wavefront's share (tokens wave*64 + lane +
-// b*kRankTile): kRankBatch tokens per lane are loaded together (16-byte id vectors when
-// KV > 0), then per rank the wavefront adds up one ballot count per batch. Lane r returns rank
-// r's total.
-template <int KV>
-__device__ __forceinline__ int rank_prefix_wave(const int32_t *__restrict__ idx, int t0, int K,
-                                                int E, int EL, int R)
-{
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const int q0 = wave * kWave + lane;
-    int acc = 0;
-    for (int b0 = 0; b0 * kRankTile + wave * kWave < t0; b0 += kRankBatch) {
-        uint64_t m[kRankBatch];
-        if constexpr (KV > 0) {
-            int4 v[kRankBatch][KV];
-#pragma unroll
-            for (int b = 0; b < kRankBatch; ++b) {
-#pragma unroll
-                for (int j = 0; j < KV; ++j) v[b][j] = int4{-1, -1, -1, -1};
-                if ((b0 + b) * kRankTile + wave * kWave < t0) {        // wavefront-uniform
-                    const int q = min(q0 + (b0 + b) * kRankTile, t0 - 1);
-#pragma unroll
-                    for (int j = 0; j < KV; ++j)
-                        v[b][j] = reinterpret_cast<const int4 *>(idx + (size_t)q * K)[j];
-                }
-            }
-#pragma unroll
-            for (int b = 0; b < kRankBatch; ++b)
-                m[b] = q0 + (b0 + b) * kRankTile < t0 ? ranks_of(v[b], KV, E, EL) : 0;
-        } else {
-#pragma unroll
-            for (int b = 0; b < kRankBatch; ++b) {
-                const int q = q0 + (b0 + b) * kRankTile;
-                m[b] = q < t0 ? token_ranks_any(idx, q, K, E, EL) : 0;
-            }
-        }
-        // batches holding any of this wavefront's earlier tokens
-        const int nb = min(kRankBatch, ceil_div(t0 - b0 * kRankTile - wave * kWave, kRankTile));
-        for (int r = 0; r < R; ++r) {
-            int c = 0;
-#pragma unroll
-            for (int b = 0; b < kRankBatch; ++b)
-                if (b < nb) c += __popcll(__ballot(((m[b] >> r) & 1u) != 0));
-            acc = lane == r ? acc + c : acc;
-        }
-    }
-    return acc;
-}
 
 // Rank layout of the tile [t0, t0 + nt), nt <= kWave, in a workgroup of kRankTile lanes:
 // rank_slot rows of the tile (coalesced, through LDS), rows[tl*R + r] = r*T + slot or -1 in
