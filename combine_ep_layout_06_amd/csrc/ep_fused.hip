@@ -79,7 +79,9 @@ __global__ __launch_bounds__(kTileThreads) void layout_dispatch_fp8_kernel(
     const int nt = min(TT, T - t0);
     const int wave = wave_uniform(threadIdx.x / kWave);
     const int nitems = nt * nseg;
-    // (loading the first row before the layout, as the bf16 kernel does, measured slower here)
+    // (loading the first row before the layout, as the bf16 kernel does, measured slower here,
+    // with the division-based cast and again with the reciprocal one: 18.6 -> 19.2 us at
+    // T = 4096)
     const TileIds ids = layout_tile_loads(idx, TK, t0 * K, TT * K);
     layout_tile(ids, idx, TK, E, C, nbits, t0 * K, TT * K, last, lds, m, o.slot, rows);
     for (int item = wave; item < nitems; item += kTileWaves) {
