@@ -139,6 +139,7 @@ SMALL = [
     (2051, 256, 256, 8, 80, 8),       # prefill-sized tiles, E = 256: the fused layout+dispatch
     (700, 128, 512, 4, 9, 4),         # E = 512: its histograms exceed the fused kernel's LDS,
                                       # the call runs as two launches
+    (40, 256, 300, 256, 20, 3),       # K = EP_MAX_TOPK
 ]
 
 

@@ -84,6 +84,7 @@ SMALL = [
                                       # the second one's upper piece past H
     (2051, 256, 16, 4, 700, 4),       # prefill-sized fused tiles (8 tokens) with a 3-token
                                       # last tile
+    (40, 256, 300, 256, 20, 3),       # K = EP_MAX_TOPK: 32 pair groups per token, full tiles
 ]
 
 
