@@ -177,3 +177,31 @@ def test_packed_workloads(name, align):
     inp = W.make_inputs(cfg)
     run_case(inp["topk_idx"], inp["x"], inp["topk_w"], cfg.E, cfg.C, cfg.R, align,
              full=cfg.T <= 256, seed=cfg.seed)
+
+
+def test_packed_empty_tokens():
+    """T = 0: zero offsets (the packed buffer needs no rows), zero counts and stats, nothing
+    written."""
+    _need_gpu()
+    E, C, R, H = 16, 4, 4, 256
+    idx = torch.zeros((0, 8), dtype=torch.int32, device="cuda")
+    x = torch.zeros((0, H), dtype=torch.int16, device="cuda")
+    i32 = lambda n, v: torch.full((n,), v, dtype=torch.int32, device="cuda")
+    g = B.ep_layout_packed(idx, E, C, R, 16, packed_offset=i32(E + 1, 7))
+    torch.cuda.synchronize()
+    assert G.to_np(g["packed_offset"]).tolist() == [0] * (E + 1)
+    assert G.to_np(g["expert_count"]).tolist() == [0] * E
+    assert G.to_np(g["stats"]).tolist() == [0, 0, 0, 0]
+    recv = torch.full((8, H), S16, dtype=torch.int16, device="cuda")
+    f = B.ep_layout_dispatch_packed(x, idx, recv, E, C, R, 16, packed_offset=i32(E + 1, 7),
+                                    stats=i32(4, 7))
+    q = torch.full((8, H), S8, dtype=torch.uint8, device="cuda")
+    sc = torch.full((8, H // 128), SF, dtype=torch.float32, device="cuda")
+    f8 = B.ep_layout_dispatch_packed_fp8(x, idx, q, sc, E, C, R, 16, stats=i32(4, 7))
+    out = B.ep_combine_packed(recv, idx, g["slot"], g["packed_offset"],
+                              torch.zeros((0, 8), device="cuda"), E, C)
+    torch.cuda.synchronize()
+    assert G.to_np(f["packed_offset"]).tolist() == [0] * (E + 1)
+    assert G.to_np(f["stats"]).tolist() == [0, 0, 0, 0] == G.to_np(f8["stats"]).tolist()
+    assert int((recv != S16).sum()) == 0 and int((q != S8).sum()) == 0
+    assert out.shape == (0, H)
