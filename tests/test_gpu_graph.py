@@ -1,5 +1,6 @@
-"""The decode-size step (fused layout + dispatch, then combine) captured in a HIP graph and
-replayed: every replay must leave exactly the outputs of the eager calls.
+"""Passes captured in a HIP graph and replayed: the decode-size step (fused layout + dispatch,
+then combine), the two-stage pass and the packed pass. Every replay must leave exactly the
+outputs of the eager calls.
 
 The library's kernels issue no memset and no allocation, so the captured graph holds only
 their launches; the replays are separated by unrelated eager work and synchronisations, and
@@ -93,3 +94,114 @@ def test_graph_replay_matches_eager(name):
     # the eager result itself against the oracle's layout
     G.check_layout(inp["topk_idx"], cfg.E, cfg.C, cfg.R, lay)
     del g
+
+
+def _capture_and_replay(step, outputs, partial, tag):
+    """Run `step` eagerly, capture it in a graph, then replay it four times, each replay after
+    eager work that overwrites every output; each replay must reproduce the eager outputs.
+
+    ``outputs`` are written whole by `step` and get scribbled over before each replay;
+    ``partial`` buffers (receive rows of unused slots stay as they were) are zeroed instead, as
+    they were before the eager call."""
+    step()
+    torch.cuda.synchronize()
+    want = {k: v.clone() for k, v in list(outputs.items()) + list(partial.items())}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for v in outputs.values():
+            v.view(torch.uint8).fill_(0xA5)
+        for v in partial.values():
+            v.zero_()
+        junk = torch.randn(1 << 20, device=G.dev()).sum()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in list(outputs.items()) + list(partial.items()):
+            assert torch.equal(v, want[k]), f"{tag} replay {rep}: {k}"
+    del g
+    return want
+
+
+def _small_inputs(T=512, H=512, E=64, K=8, C=256, R=8):
+    cfg = W.EpConfig("graph_small", T=T, H=H, E=E, K=K, C=C, R=R)
+    inp = W.make_inputs(cfg)
+    dev = G.dev()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    return cfg, inp, G.u16_dev(inp["x"]), G.to_dev(inp["topk_idx"]), G.to_dev(inp["topk_w"]), gen
+
+
+def test_graph_replay_two_stage_pass():
+    """The two-stage pass (layout, fused rank layout + staging copy, expansion, partial
+    combine, reduce) replayed from a graph, with the FP8 staging copy and expansion too."""
+    _need_gpu()
+    print("[graph] two-stage pass", flush=True)
+    cfg, inp, x, idx, w, gen = _small_inputs()
+    dev = G.dev()
+    T, H, E, K, C, R = cfg.T, cfg.H, cfg.E, cfg.K, cfg.C, cfg.R
+    mk = lambda *n: torch.empty(n, dtype=torch.int32, device=dev)
+    lay = dict(slot=mk(T, K), expert_count=mk(E), expert_offset=mk(E), rank_count=mk(R),
+               rank_offset=mk(R), stats=mk(4))
+    rl = dict(rank_slot=mk(T, R), rank_tokens=mk(R))
+    stage = torch.empty((R, T, H), dtype=torch.int16, device=dev)
+    recv = torch.zeros((E, C, H), dtype=torch.int16, device=dev)
+    y = torch.randn((E, C, H), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
+    part = torch.empty((R, T, H), dtype=torch.int16, device=dev)
+    out = torch.empty((T, H), dtype=torch.int16, device=dev)
+    stage_q = torch.empty((R, T, H), dtype=torch.uint8, device=dev)
+    stage_s = torch.empty((R, T, H // 128), dtype=torch.float32, device=dev)
+    recv_q = torch.zeros((E, C, H), dtype=torch.uint8, device=dev)
+    recv_s = torch.zeros((E, C, H // 128), dtype=torch.float32, device=dev)
+
+    def step():
+        B.ep_layout(idx, E, C, R, **lay)
+        B.ep_rank_layout_dispatch(x, idx, E, R, stage=stage, **rl)
+        B.ep_dispatch_expand(stage, idx, lay["slot"], rl["rank_slot"], recv, C)
+        B.ep_rank_layout_dispatch_fp8(x, idx, E, R, stage_q=stage_q, stage_scale=stage_s, **rl)
+        B.ep_dispatch_expand_fp8(stage_q, stage_s, idx, lay["slot"], rl["rank_slot"], recv_q,
+                                 recv_s, C)
+        B.ep_combine_ranks(y, idx, lay["slot"], rl["rank_slot"], w, C, part=part)
+        B.ep_combine_reduce(part, rl["rank_slot"], K, out=out)
+
+    # stage and part are intermediates (rows of unsent (token, rank) pairs are never written);
+    # what the pass hands on is compared
+    _capture_and_replay(step, dict(lay, **rl, out=out),
+                        dict(recv=recv, recv_q=recv_q, recv_s=recv_s), "two-stage")
+    G.check_layout(inp["topk_idx"], E, C, R, lay)
+
+
+def test_graph_replay_packed_pass():
+    """The packed pass (fused packed layout + dispatch, then packed combine) replayed from a
+    graph, bf16 and FP8."""
+    _need_gpu()
+    print("[graph] packed pass", flush=True)
+    cfg, inp, x, idx, w, gen = _small_inputs()
+    dev = G.dev()
+    T, H, E, K, C, R = cfg.T, cfg.H, cfg.E, cfg.K, cfg.C, cfg.R
+    A = 16
+    rows = B.packed_rows_bound(T, K, E, C, A)
+    mk = lambda *n: torch.empty(n, dtype=torch.int32, device=dev)
+    play = dict(slot=mk(T, K), expert_count=mk(E), packed_offset=mk(E + 1), rank_count=mk(R),
+                rank_offset=mk(R), stats=mk(4))
+    recv = torch.zeros((rows, H), dtype=torch.int16, device=dev)
+    q = torch.zeros((rows, H), dtype=torch.uint8, device=dev)
+    sc = torch.zeros((rows, H // 128), dtype=torch.float32, device=dev)
+    y = torch.randn((rows, H), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
+    out = torch.empty((T, H), dtype=torch.int16, device=dev)
+
+    def step():
+        B.ep_layout_dispatch_packed(x, idx, recv, E, C, R, A, **play)
+        B.ep_layout_dispatch_packed_fp8(x, idx, q, sc, E, C, R, A, **play)
+        B.ep_combine_packed(y, idx, play["slot"], play["packed_offset"], w, E, C, out=out)
+
+    _capture_and_replay(step, dict(play, out=out), dict(recv=recv, q=q, sc=sc), "packed")
