@@ -2,13 +2,17 @@
 
 Argument marshalling only: each function checks dtypes, devices, sizes and contiguity, then
 passes ``data_ptr()`` values and torch's current HIP stream to the C entry point of the same
-name. Every step of the computation runs in the library's gfx950 kernels; there is no other
-code path. If the library is missing the functions raise instead of computing anything.
+name. Under ``record()`` the C calls are captured into a CallList instead, whose ``replay()``
+re-issues them without the Python-side checks (for loops that refill the same buffers). Every
+step of the computation runs in the library's gfx950 kernels; there is no other code path. If
+the library is missing the functions raise instead of computing anything.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
+import threading
 
 import torch
 
@@ -118,8 +122,56 @@ def _stream(stream) -> int:
     return stream.cuda_stream
 
 
-def _ptr(t: torch.Tensor | None):
-    return None if t is None else t.data_ptr()
+class CallList:
+    """Entry-point calls captured by `record`: the same C calls with the same device pointers,
+    re-issued by `replay` with none of the wrappers' checks or allocations. It holds references
+    to every tensor the calls use, so the buffers live as long as the list."""
+
+    def __init__(self):
+        self.calls = []      # (C function, name, shape, pointer and int arguments, stream)
+        self._tensors = []
+
+    def __len__(self):
+        return len(self.calls)
+
+    def replay(self, stream=None):
+        """Issue the recorded calls in order, each on the stream it was recorded with if one was
+        given then, else on ``stream`` (default: torch's current stream)."""
+        s = _stream(stream)
+        for fn, name, sh, args, st in self.calls:
+            rc = fn(ctypes.byref(sh), *args, s if st is None else st)
+            if rc != EP_OK:
+                _check(name, rc)
+
+
+_recording = threading.local()
+
+
+@contextlib.contextmanager
+def record():
+    """Inside the block, the entry-point functions validate their arguments and allocate any
+    missing outputs as usual, but the C calls are captured instead of issued. Yields the
+    CallList; its ``replay()`` then launches the same kernels on the same buffers, which is
+    all a serving loop needs when each step refills the same input tensors."""
+    prev = getattr(_recording, "calls", None)
+    cl = CallList()
+    _recording.calls = cl
+    try:
+        yield cl
+    finally:
+        _recording.calls = prev
+
+
+def _call(name: str, sh: EpShape, *args, stream=None):
+    """Issue (or record) one C call; tensor arguments are passed as their data pointers."""
+    fn = getattr(load_library(), name)
+    cargs = tuple(a.data_ptr() if isinstance(a, torch.Tensor) else a for a in args)
+    cl = getattr(_recording, "calls", None)
+    if cl is not None:
+        cl._tensors.extend(a for a in args if isinstance(a, torch.Tensor))
+        cl.calls.append((fn, name, sh, cargs, None if stream is None else stream.cuda_stream))
+        return
+    _check(name, fn(ctypes.byref(sh), *cargs, _stream(stream)))
 
 
 def _need(t: torch.Tensor, name: str, dtype: torch.dtype, numel: int, device):
@@ -160,10 +212,8 @@ def ep_layout(topk_idx: torch.Tensor, E: int, C: int, R: int, *, slot=None, expe
                        ("stats", stats, EP_STATS_LEN)):
         _need(t, name, torch.int32, n, dev)
     sh = _shape(T, 1, E, K, C, R)
-    rc = load_library().ep_layout(ctypes.byref(sh), _ptr(topk_idx), _ptr(slot),
-                                  _ptr(expert_count), _ptr(expert_offset), _ptr(rank_count),
-                                  _ptr(rank_offset), _ptr(stats), _stream(stream))
-    _check("ep_layout", rc)
+    _call("ep_layout", sh, topk_idx, slot, expert_count, expert_offset, rank_count, rank_offset,
+          stats, stream=stream)
     return dict(slot=slot, expert_count=expert_count, expert_offset=expert_offset,
                 rank_count=rank_count, rank_offset=rank_offset, stats=stats)
 
@@ -184,9 +234,9 @@ def _layout_outputs(dev, T, K, E, R, slot, expert_count, expert_offset, rank_cou
     return out
 
 
-def _layout_ptrs(lay):
-    return [_ptr(lay[k]) for k in ("slot", "expert_count", "expert_offset", "rank_count",
-                                    "rank_offset", "stats")]
+def _layout_ts(lay):
+    return [lay[k] for k in ("slot", "expert_count", "expert_offset", "rank_count",
+                             "rank_offset", "stats")]
 
 
 def ep_layout_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, recv: torch.Tensor, E: int,
@@ -203,9 +253,7 @@ def ep_layout_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, recv: torch.Tens
     _need(topk_idx, "topk_idx", torch.int32, T * K, dev)
     _need(recv, "recv", _bf16(recv), E * C * H, dev)
     sh = _shape(T, H, E, K, C, R)
-    rc = load_library().ep_layout_dispatch(ctypes.byref(sh), _ptr(x), _ptr(topk_idx),
-                                           *_layout_ptrs(lay), _ptr(recv), _stream(stream))
-    _check("ep_layout_dispatch", rc)
+    _call("ep_layout_dispatch", sh, x, topk_idx, *_layout_ts(lay), recv, stream=stream)
     return lay
 
 
@@ -226,10 +274,8 @@ def ep_layout_dispatch_fp8(x: torch.Tensor, topk_idx: torch.Tensor, recv_q: torc
           else torch.uint8, E * C * H, dev)
     _need(recv_scale, "recv_scale", torch.float32, E * C * (H // EP_FP8_BLOCK), dev)
     sh = _shape(T, H, E, K, C, R)
-    rc = load_library().ep_layout_dispatch_fp8(ctypes.byref(sh), _ptr(x), _ptr(topk_idx),
-                                               *_layout_ptrs(lay), _ptr(recv_q),
-                                               _ptr(recv_scale), _stream(stream))
-    _check("ep_layout_dispatch_fp8", rc)
+    _call("ep_layout_dispatch_fp8", sh, x, topk_idx, *_layout_ts(lay), recv_q, recv_scale,
+          stream=stream)
     return lay
 
 
@@ -245,9 +291,7 @@ def ep_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, slot: torch.Tensor, rec
     _need(slot, "slot", torch.int32, T * K, dev)
     _need(recv, "recv", _bf16(recv), E * C * H, dev)
     sh = _shape(T, H, E, K, C, 1)
-    rc = load_library().ep_dispatch(ctypes.byref(sh), _ptr(x), _ptr(topk_idx), _ptr(slot),
-                                    _ptr(recv), _stream(stream))
-    _check("ep_dispatch", rc)
+    _call("ep_dispatch", sh, x, topk_idx, slot, recv, stream=stream)
     return recv
 
 
@@ -266,9 +310,7 @@ def ep_dispatch_fp8(x: torch.Tensor, topk_idx: torch.Tensor, slot: torch.Tensor,
           else torch.uint8, E * C * H, dev)
     _need(recv_scale, "recv_scale", torch.float32, E * C * (H // EP_FP8_BLOCK), dev)
     sh = _shape(T, H, E, K, C, 1)
-    rc = load_library().ep_dispatch_fp8(ctypes.byref(sh), _ptr(x), _ptr(topk_idx), _ptr(slot),
-                                        _ptr(recv_q), _ptr(recv_scale), _stream(stream))
-    _check("ep_dispatch_fp8", rc)
+    _call("ep_dispatch_fp8", sh, x, topk_idx, slot, recv_q, recv_scale, stream=stream)
     return recv_q, recv_scale
 
 
@@ -286,9 +328,7 @@ def ep_combine(y: torch.Tensor, topk_idx: torch.Tensor, slot: torch.Tensor,
     _need(topk_w, "topk_w", torch.float32, T * K, dev)
     _need(out, "out", _bf16(out), T * H, dev)
     sh = _shape(T, H, E, K, C, 1)
-    rc = load_library().ep_combine(ctypes.byref(sh), _ptr(y), _ptr(topk_idx), _ptr(slot),
-                                   _ptr(topk_w), _ptr(out), _stream(stream))
-    _check("ep_combine", rc)
+    _call("ep_combine", sh, y, topk_idx, slot, topk_w, out, stream=stream)
     return out
 
 
@@ -309,9 +349,7 @@ def ep_rank_layout(topk_idx: torch.Tensor, E: int, R: int, *, rank_slot=None, ra
     _need(rank_slot, "rank_slot", torch.int32, T * R, dev)
     _need(rank_tokens, "rank_tokens", torch.int32, R, dev)
     sh = _shape(T, 1, E, K, 1, R)
-    rc = load_library().ep_rank_layout(ctypes.byref(sh), _ptr(topk_idx), _ptr(rank_slot),
-                                       _ptr(rank_tokens), _stream(stream))
-    _check("ep_rank_layout", rc)
+    _call("ep_rank_layout", sh, topk_idx, rank_slot, rank_tokens, stream=stream)
     return dict(rank_slot=rank_slot, rank_tokens=rank_tokens)
 
 
@@ -325,9 +363,7 @@ def ep_dispatch_ranks(x: torch.Tensor, rank_slot: torch.Tensor, stage: torch.Ten
     _need(rank_slot, "rank_slot", torch.int32, T * R, dev)
     _need(stage, "stage", _bf16(stage), R * T * H, dev)
     sh = _shape(T, H, R, 1, 1, R)
-    rc = load_library().ep_dispatch_ranks(ctypes.byref(sh), _ptr(x), _ptr(rank_slot), _ptr(stage),
-                                          _stream(stream))
-    _check("ep_dispatch_ranks", rc)
+    _call("ep_dispatch_ranks", sh, x, rank_slot, stage, stream=stream)
     return stage
 
 
@@ -342,9 +378,7 @@ def ep_dispatch_ranks_fp8(x: torch.Tensor, rank_slot: torch.Tensor, stage_q: tor
     _need(stage_q, "stage_q", torch.uint8, R * T * H, dev)
     _need(stage_scale, "stage_scale", torch.float32, R * T * (H // EP_FP8_BLOCK), dev)
     sh = _shape(T, H, R, 1, 1, R)
-    rc = load_library().ep_dispatch_ranks_fp8(ctypes.byref(sh), _ptr(x), _ptr(rank_slot),
-                                              _ptr(stage_q), _ptr(stage_scale), _stream(stream))
-    _check("ep_dispatch_ranks_fp8", rc)
+    _call("ep_dispatch_ranks_fp8", sh, x, rank_slot, stage_q, stage_scale, stream=stream)
     return stage_q, stage_scale
 
 
@@ -366,10 +400,7 @@ def ep_rank_layout_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, R: 
     _need(rank_tokens, "rank_tokens", torch.int32, R, dev)
     _need(stage, "stage", _bf16(stage), R * T * H, dev)
     sh = _shape(T, H, E, K, 1, R)
-    rc = load_library().ep_rank_layout_dispatch(ctypes.byref(sh), _ptr(x), _ptr(topk_idx),
-                                                _ptr(rank_slot), _ptr(rank_tokens), _ptr(stage),
-                                                _stream(stream))
-    _check("ep_rank_layout_dispatch", rc)
+    _call("ep_rank_layout_dispatch", sh, x, topk_idx, rank_slot, rank_tokens, stage, stream=stream)
     return dict(stage=stage, rank_slot=rank_slot, rank_tokens=rank_tokens)
 
 
@@ -395,11 +426,8 @@ def ep_rank_layout_dispatch_fp8(x: torch.Tensor, topk_idx: torch.Tensor, E: int,
     _need(stage_q, "stage_q", torch.uint8, R * T * H, dev)
     _need(stage_scale, "stage_scale", torch.float32, R * T * NB, dev)
     sh = _shape(T, H, E, K, 1, R)
-    rc = load_library().ep_rank_layout_dispatch_fp8(ctypes.byref(sh), _ptr(x), _ptr(topk_idx),
-                                                    _ptr(rank_slot), _ptr(rank_tokens),
-                                                    _ptr(stage_q), _ptr(stage_scale),
-                                                    _stream(stream))
-    _check("ep_rank_layout_dispatch_fp8", rc)
+    _call("ep_rank_layout_dispatch_fp8", sh, x, topk_idx, rank_slot, rank_tokens, stage_q,
+          stage_scale, stream=stream)
     return dict(stage_q=stage_q, stage_scale=stage_scale, rank_slot=rank_slot,
                 rank_tokens=rank_tokens)
 
@@ -417,10 +445,7 @@ def ep_dispatch_expand(stage: torch.Tensor, topk_idx: torch.Tensor, slot: torch.
     _need(rank_slot, "rank_slot", torch.int32, T * R, dev)
     _need(recv, "recv", _bf16(recv), E * C * H, dev)
     sh = _shape(T, H, E, K, C, R)
-    rc = load_library().ep_dispatch_expand(ctypes.byref(sh), _ptr(stage), _ptr(topk_idx),
-                                           _ptr(slot), _ptr(rank_slot), _ptr(recv),
-                                           _stream(stream))
-    _check("ep_dispatch_expand", rc)
+    _call("ep_dispatch_expand", sh, stage, topk_idx, slot, rank_slot, recv, stream=stream)
     return recv
 
 
@@ -443,10 +468,8 @@ def ep_dispatch_expand_fp8(stage_q: torch.Tensor, stage_scale: torch.Tensor,
     _need(recv_q, "recv_q", torch.uint8, E * C * H, dev)
     _need(recv_scale, "recv_scale", torch.float32, E * C * NB, dev)
     sh = _shape(T, H, E, K, C, R)
-    rc = load_library().ep_dispatch_expand_fp8(ctypes.byref(sh), _ptr(stage_q), _ptr(stage_scale),
-                                               _ptr(topk_idx), _ptr(slot), _ptr(rank_slot),
-                                               _ptr(recv_q), _ptr(recv_scale), _stream(stream))
-    _check("ep_dispatch_expand_fp8", rc)
+    _call("ep_dispatch_expand_fp8", sh, stage_q, stage_scale, topk_idx, slot, rank_slot, recv_q,
+          recv_scale, stream=stream)
     return recv_q, recv_scale
 
 
@@ -467,10 +490,7 @@ def ep_combine_ranks(y: torch.Tensor, topk_idx: torch.Tensor, slot: torch.Tensor
     _need(topk_w, "topk_w", torch.float32, T * K, dev)
     _need(part, "part", _bf16(part), R * T * H, dev)
     sh = _shape(T, H, E, K, C, R)
-    rc = load_library().ep_combine_ranks(ctypes.byref(sh), _ptr(y), _ptr(topk_idx), _ptr(slot),
-                                         _ptr(rank_slot), _ptr(topk_w), _ptr(part),
-                                         _stream(stream))
-    _check("ep_combine_ranks", rc)
+    _call("ep_combine_ranks", sh, y, topk_idx, slot, rank_slot, topk_w, part, stream=stream)
     return part
 
 
@@ -485,9 +505,7 @@ def ep_combine_reduce(part: torch.Tensor, rank_slot: torch.Tensor, K: int, *, ou
     _need(rank_slot, "rank_slot", torch.int32, T * R, dev)
     _need(out, "out", _bf16(out), T * H, dev)
     sh = _shape(T, H, R, K, 1, R)
-    rc = load_library().ep_combine_reduce(ctypes.byref(sh), _ptr(part), _ptr(rank_slot), _ptr(out),
-                                          _stream(stream))
-    _check("ep_combine_reduce", rc)
+    _call("ep_combine_reduce", sh, part, rank_slot, out, stream=stream)
     return out
 
 
@@ -522,11 +540,8 @@ def ep_layout_packed(topk_idx: torch.Tensor, E: int, C: int, R: int, alignment: 
                        ("stats", stats, EP_STATS_LEN)):
         _need(t, name, torch.int32, n, dev)
     sh = _shape(T, 1, E, K, C, R)
-    rc = load_library().ep_layout_packed(ctypes.byref(sh), int(alignment), _ptr(topk_idx),
-                                         _ptr(slot), _ptr(expert_count), _ptr(packed_offset),
-                                         _ptr(rank_count), _ptr(rank_offset), _ptr(stats),
-                                         _stream(stream))
-    _check("ep_layout_packed", rc)
+    _call("ep_layout_packed", sh, int(alignment), topk_idx, slot, expert_count, packed_offset,
+          rank_count, rank_offset, stats, stream=stream)
     return dict(slot=slot, expert_count=expert_count, packed_offset=packed_offset,
                 rank_count=rank_count, rank_offset=rank_offset, stats=stats)
 
@@ -545,10 +560,8 @@ def ep_dispatch_packed(x: torch.Tensor, topk_idx: torch.Tensor, slot: torch.Tens
     _need(packed_offset, "packed_offset", torch.int32, E + 1, dev)
     _need(recv, "recv", _bf16(recv), rows * H, dev)
     sh = _shape(T, H, E, K, C, 1)
-    rc = load_library().ep_dispatch_packed(ctypes.byref(sh), int(rows), _ptr(x), _ptr(topk_idx),
-                                           _ptr(slot), _ptr(packed_offset), _ptr(recv),
-                                           _stream(stream))
-    _check("ep_dispatch_packed", rc)
+    _call("ep_dispatch_packed", sh, int(rows), x, topk_idx, slot, packed_offset, recv,
+          stream=stream)
     return recv
 
 
@@ -567,10 +580,8 @@ def ep_dispatch_packed_fp8(x: torch.Tensor, topk_idx: torch.Tensor, slot: torch.
     _need(recv_q, "recv_q", torch.uint8, rows * H, dev)
     _need(recv_scale, "recv_scale", torch.float32, rows * (H // EP_FP8_BLOCK), dev)
     sh = _shape(T, H, E, K, C, 1)
-    rc = load_library().ep_dispatch_packed_fp8(ctypes.byref(sh), int(rows), _ptr(x),
-                                               _ptr(topk_idx), _ptr(slot), _ptr(packed_offset),
-                                               _ptr(recv_q), _ptr(recv_scale), _stream(stream))
-    _check("ep_dispatch_packed_fp8", rc)
+    _call("ep_dispatch_packed_fp8", sh, int(rows), x, topk_idx, slot, packed_offset, recv_q,
+          recv_scale, stream=stream)
     return recv_q, recv_scale
 
 
@@ -606,11 +617,9 @@ def ep_layout_dispatch_packed(x: torch.Tensor, topk_idx: torch.Tensor, recv: tor
     _need(topk_idx, "topk_idx", torch.int32, T * K, dev)
     _need(recv, "recv", _bf16(recv), rows * H, dev)
     sh = _shape(T, H, E, K, C, R)
-    rc = load_library().ep_layout_dispatch_packed(
-        ctypes.byref(sh), int(alignment), int(rows), _ptr(x), _ptr(topk_idx), _ptr(o["slot"]),
-        _ptr(o["expert_count"]), _ptr(o["packed_offset"]), _ptr(o["rank_count"]),
-        _ptr(o["rank_offset"]), _ptr(o["stats"]), _ptr(recv), _stream(stream))
-    _check("ep_layout_dispatch_packed", rc)
+    _call("ep_layout_dispatch_packed", sh, int(alignment), int(rows), x, topk_idx, o["slot"],
+          o["expert_count"], o["packed_offset"], o["rank_count"], o["rank_offset"], o["stats"],
+          recv, stream=stream)
     return o
 
 
@@ -632,12 +641,9 @@ def ep_layout_dispatch_packed_fp8(x: torch.Tensor, topk_idx: torch.Tensor, recv_
     _need(recv_q, "recv_q", torch.uint8, rows * H, dev)
     _need(recv_scale, "recv_scale", torch.float32, rows * (H // EP_FP8_BLOCK), dev)
     sh = _shape(T, H, E, K, C, R)
-    rc = load_library().ep_layout_dispatch_packed_fp8(
-        ctypes.byref(sh), int(alignment), int(rows), _ptr(x), _ptr(topk_idx), _ptr(o["slot"]),
-        _ptr(o["expert_count"]), _ptr(o["packed_offset"]), _ptr(o["rank_count"]),
-        _ptr(o["rank_offset"]), _ptr(o["stats"]), _ptr(recv_q), _ptr(recv_scale),
-        _stream(stream))
-    _check("ep_layout_dispatch_packed_fp8", rc)
+    _call("ep_layout_dispatch_packed_fp8", sh, int(alignment), int(rows), x, topk_idx, o["slot"],
+          o["expert_count"], o["packed_offset"], o["rank_count"], o["rank_offset"], o["stats"],
+          recv_q, recv_scale, stream=stream)
     return o
 
 
@@ -656,9 +662,7 @@ def ep_combine_packed(y: torch.Tensor, topk_idx: torch.Tensor, slot: torch.Tenso
     _need(topk_w, "topk_w", torch.float32, T * K, dev)
     _need(out, "out", _bf16(out), T * H, dev)
     sh = _shape(T, H, E, K, C, 1)
-    rc = load_library().ep_combine_packed(ctypes.byref(sh), int(rows), _ptr(y), _ptr(topk_idx),
-                                          _ptr(slot), _ptr(packed_offset), _ptr(topk_w), _ptr(out),
-                                          _stream(stream))
-    _check("ep_combine_packed", rc)
+    _call("ep_combine_packed", sh, int(rows), y, topk_idx, slot, packed_offset, topk_w, out,
+          stream=stream)
     return out
 

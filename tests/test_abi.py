@@ -177,3 +177,39 @@ def test_packed_calls_reject_bad_arguments(lib):
     assert lib.ep_combine_packed(shape(), 10, A16, A16, A16, A16, A16, A16 + 8, None) == B.EP_ERR_ALIGN
     assert lib.ep_combine_packed(shape(H=12), 10, A16, A16, A16, A16, A16, A16, None) == B.EP_ERR_UNSUPPORTED
 
+
+
+def test_record_captures_calls_without_issuing(lib):
+    """binding.record(): the wrappers validate and allocate as usual, but the C calls are only
+    captured (CPU tensors pass the wrappers' checks; nothing reaches the library). The captured
+    pointers are the tensors' data pointers, in the header's argument order."""
+    import torch
+    T, H, E, K, C, R = 4, 256, 8, 2, 4, 2
+    idx = torch.zeros((T, K), dtype=torch.int32)
+    x = torch.zeros((T, H), dtype=torch.int16)
+    w = torch.ones((T, K), dtype=torch.float32)
+    recv = torch.zeros((E, C, H), dtype=torch.int16)
+    with B.record() as outer:
+        lay = B.ep_layout_dispatch(x, idx, recv, E, C, R)
+        with B.record() as inner:
+            out = B.ep_combine(recv, idx, lay["slot"], w, C)
+        B.ep_combine(recv, idx, lay["slot"], w, C, out=out)
+    assert [c[1] for c in outer.calls] == ["ep_layout_dispatch", "ep_combine"]
+    assert [c[1] for c in inner.calls] == ["ep_combine"]
+    fn, name, sh, args, st = outer.calls[0]
+    assert fn is lib.ep_layout_dispatch and st is None
+    assert (sh.T, sh.H, sh.E, sh.K, sh.C, sh.R) == (T, H, E, K, C, R)
+    assert args == (x.data_ptr(), idx.data_ptr(), lay["slot"].data_ptr(),
+                    lay["expert_count"].data_ptr(), lay["expert_offset"].data_ptr(),
+                    lay["rank_count"].data_ptr(), lay["rank_offset"].data_ptr(),
+                    lay["stats"].data_ptr(), recv.data_ptr())
+    assert outer.calls[1][3] == (recv.data_ptr(), idx.data_ptr(), lay["slot"].data_ptr(),
+                                 w.data_ptr(), out.data_ptr())
+    # every tensor a call uses stays referenced by the list
+    kept = {t.data_ptr() for t in outer._tensors}
+    assert all(a in kept for _, _, _, a, _ in outer.calls for a in a)
+    # outside the block the wrappers issue again: R = 3 does not divide E = 8, which only the
+    # library checks (the null stream object only carries a handle; nothing is launched)
+    import types
+    with pytest.raises(B.EpError):
+        B.ep_layout(idx, E, C, 3, stream=types.SimpleNamespace(cuda_stream=0))

@@ -205,3 +205,66 @@ def test_graph_replay_packed_pass():
         B.ep_combine_packed(y, idx, play["slot"], play["packed_offset"], w, E, C, out=out)
 
     _capture_and_replay(step, dict(play, out=out), dict(recv=recv, q=q, sc=sc), "packed")
+
+
+@pytest.mark.parametrize("name", ["decode_bf16", "decode_fp8"])
+def test_recorded_calls_replay_matches_eager(name):
+    """binding.record(): the decode step's calls recorded once on batch 0's buffers, then
+    replayed after each new batch is copied into those buffers (on the current stream, and on
+    a side stream), equal to the checked wrappers on fresh buffers, and the layout to the
+    oracle's."""
+    _need_gpu()
+    cfg = W.get_config(name)
+    print(f"[replay] {name}", flush=True)
+    dev = G.dev()
+    batches = [W.make_inputs(cfg, seed=cfg.seed + k) for k in range(3)]
+    x = G.u16_dev(batches[0]["x"])
+    idx = G.to_dev(batches[0]["topk_idx"])
+    w = G.to_dev(batches[0]["topk_w"])
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    y = torch.randn((cfg.E, cfg.C, cfg.H), generator=gen, device=dev).to(torch.bfloat16)
+    y = y.view(torch.int16)
+
+    def recv_bufs():
+        if cfg.fp8:
+            return (torch.zeros((cfg.E, cfg.C, cfg.H), dtype=torch.uint8, device=dev),
+                    torch.zeros((cfg.E, cfg.C, cfg.H // 128), dtype=torch.float32, device=dev))
+        return (torch.zeros((cfg.E, cfg.C, cfg.H), dtype=torch.int16, device=dev),)
+
+    def step(recv):
+        if cfg.fp8:
+            lay = B.ep_layout_dispatch_fp8(x, idx, recv[0], recv[1], cfg.E, cfg.C, cfg.R)
+        else:
+            lay = B.ep_layout_dispatch(x, idx, recv[0], cfg.E, cfg.C, cfg.R)
+        return lay, B.ep_combine(y, idx, lay["slot"], w, cfg.C)
+
+    recv = recv_bufs()
+    with B.record() as cl:
+        lay, out = step(recv)
+    assert [c[1] for c in cl.calls] == [
+        "ep_layout_dispatch_fp8" if cfg.fp8 else "ep_layout_dispatch", "ep_combine"]
+    side = torch.cuda.Stream()
+    for k, b in enumerate(batches + batches[:1]):
+        x.copy_(G.u16_dev(b["x"]))
+        idx.copy_(G.to_dev(b["topk_idx"]))
+        w.copy_(G.to_dev(b["topk_w"]))
+        for t in recv:
+            t.zero_()
+        out.fill_(0x1234)
+        if k % 2:
+            side.wait_stream(torch.cuda.current_stream())
+            cl.replay(stream=side)
+            torch.cuda.current_stream().wait_stream(side)
+        else:
+            cl.replay()
+        torch.cuda.synchronize()
+        fresh = recv_bufs()
+        lay2, out2 = step(fresh)
+        torch.cuda.synchronize()
+        for key in lay:
+            assert torch.equal(lay[key], lay2[key]), f"batch {k}: {key}"
+        assert torch.equal(out, out2), f"batch {k}: out"
+        for a, b2 in zip(recv, fresh):
+            assert torch.equal(a, b2), f"batch {k}: recv"
+        G.check_layout(b["topk_idx"], cfg.E, cfg.C, cfg.R, lay)
