@@ -140,6 +140,7 @@ SMALL = [
     (700, 128, 512, 4, 9, 4),         # E = 512: its histograms exceed the fused kernel's LDS,
                                       # the call runs as two launches
     (40, 256, 300, 256, 20, 3),       # K = EP_MAX_TOPK
+    (600, 256, 32, 6, 40, 4),         # 512 <= T < 1024: fused tiles of two tokens
 ]
 
 

@@ -85,6 +85,8 @@ SMALL = [
     (2051, 256, 16, 4, 700, 4),       # prefill-sized fused tiles (8 tokens) with a 3-token
                                       # last tile
     (40, 256, 300, 256, 20, 3),       # K = EP_MAX_TOPK: 32 pair groups per token, full tiles
+    (700, 256, 64, 6, 60, 8),         # 512 <= T < 1024: fused tiles of two tokens
+    (600, 256, 32, 5, 90, 4),         # two tokens would make 10 pairs: tiles of four tokens
 ]
 
 
