@@ -213,3 +213,13 @@ def test_record_captures_calls_without_issuing(lib):
     import types
     with pytest.raises(B.EpError):
         B.ep_layout(idx, E, C, 3, stream=types.SimpleNamespace(cuda_stream=0))
+
+
+def test_c_client_links_against_the_library():
+    """The plain C client (tests/c_abi) is built against include/ep.h alone and resolves every
+    symbol it uses from libep_mi355x.so and the HIP runtime (loading it calls nothing)."""
+    client = os.path.join(ROOT, "tests", "c_abi", "ep_c_client.so")
+    if not os.path.exists(client):
+        pytest.skip("tests/c_abi/ep_c_client.so not built (build() compiles it)")
+    lib = ctypes.CDLL(client)
+    assert hasattr(lib, "ep_c_client_check")
