@@ -112,14 +112,30 @@ def _check(fn: str, rc: int):
         raise EpError(fn, rc, load_library().ep_last_error().decode())
 
 
+_shapes: dict = {}
+
+
 def _shape(T, H, E, K, C, R) -> EpShape:
-    return EpShape(int(T), int(H), int(E), int(K), int(C), int(R))
+    # one EpShape per distinct shape (the C calls only read it)
+    key = (T, H, E, K, C, R)
+    sh = _shapes.get(key)
+    if sh is None:
+        if len(_shapes) >= 4096:
+            _shapes.clear()
+        sh = _shapes[key] = EpShape(*(int(v) for v in key))
+    return sh
+
+
+# torch's current HIP stream of the current device as a raw handle, without building a Stream
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(stream) -> int:
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return stream.cuda_stream
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None:
+        return _raw_stream(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 class CallList:
@@ -165,24 +181,31 @@ def record():
 def _call(name: str, sh: EpShape, *args, stream=None):
     """Issue (or record) one C call; tensor arguments are passed as their data pointers."""
     fn = getattr(load_library(), name)
-    cargs = tuple(a.data_ptr() if isinstance(a, torch.Tensor) else a for a in args)
+    cargs = [a.data_ptr() if isinstance(a, torch.Tensor) else a for a in args]
     cl = getattr(_recording, "calls", None)
     if cl is not None:
-        cl._tensors.extend(a for a in args if isinstance(a, torch.Tensor))
-        cl.calls.append((fn, name, sh, cargs, None if stream is None else stream.cuda_stream))
+        cl._tensors.extend([a for a in args if isinstance(a, torch.Tensor)])
+        cl.calls.append((fn, name, sh, tuple(cargs),
+                         None if stream is None else stream.cuda_stream))
         return
-    _check(name, fn(ctypes.byref(sh), *cargs, _stream(stream)))
+    rc = fn(ctypes.byref(sh), *cargs, _stream(stream))
+    if rc != EP_OK:
+        _check(name, rc)
 
 
 def _need(t: torch.Tensor, name: str, dtype: torch.dtype, numel: int, device):
+    if t.dtype != dtype or t.device != device or not t.is_contiguous() or t.numel() != numel:
+        _reject(t, name, dtype, numel, device)
+
+
+def _reject(t: torch.Tensor, name: str, dtype: torch.dtype, numel: int, device):
     if t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
     if t.device != device:
         raise ValueError(f"{name}: expected device {device}, got {t.device}")
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous")
-    if t.numel() != numel:
-        raise ValueError(f"{name}: expected {numel} elements, got {t.numel()}")
+    raise ValueError(f"{name}: expected {numel} elements, got {t.numel()}")
 
 
 def _bf16(t: torch.Tensor) -> torch.dtype:
