@@ -13,9 +13,9 @@
 // instruction covers 1 KiB of a row).
 //
 // Memory-level parallelism. For a group of KG pairs (KG = K rounded up to a power of two, at
-// most 8) the wavefront issues every row load first, as straight-line code with clamped
-// addresses (a pair that is not kept loads row 0 and its result is discarded by a select), and
-// only then folds the rows in j order with fmaf. The K row fetches of a token are therefore
+// most 8) the wavefront issues every row load first, as straight-line code (a pair that is not
+// kept reads a row of zeros with weight -0, which the fold adds as an exact -0, so no
+// per-element select is needed), and only then folds the rows in j order with fmaf. The K row fetches of a token are therefore
 // in flight together; a branch around any load would make the compiler wait for earlier
 // loads before issuing the next one. Loads of y and stores of out are non-temporal: each byte
 // is touched once (non-temporal loads measured ~25% faster here).
@@ -54,8 +54,16 @@ constexpr int kStage = 256;        // staged pairs per group (tpb * K <= kStage)
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// KG: pairs per group (K <= KG unless MULTI); U: chunks per lane per item.
-template <int KG, int U, bool MULTI>
+// A row of zeros that pairs which are not kept read instead of an expert row, with weight -0:
+// fmaf(-0, +0, acc) adds an exact -0, which leaves every acc unchanged (+0 and -0 included), so
+// the fold needs no per-element select. Never written (zero-initialised at load); rows of up
+// to kZeroChunks 16-byte chunks (H <= 32768) use it, longer ones fall back to the select.
+constexpr int kZeroChunks = 4096;
+__device__ u32x4 g_zero_row[kZeroChunks];
+
+// KG: pairs per group (K <= KG unless MULTI); U: chunks per lane per item; ZROW: H8 <=
+// kZeroChunks (pairs that are not kept read the zero row; otherwise a select drops them).
+template <int KG, int U, bool MULTI, bool ZROW>
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     const u32x4 *__restrict__ y, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ slot, const float *__restrict__ topk_w,
@@ -107,7 +115,13 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
                     const int rr = uniform(rows[k]);
                     r[g] = j < K ? rr : -1;
                     wj[g] = __int_as_float(uniform(__float_as_int(wts[k])));
-                    const u32x4 *src = y + (size_t)(r[g] >= 0 ? r[g] : 0) * H8;
+                    const u32x4 *src;
+                    if constexpr (ZROW) {
+                        src = r[g] >= 0 ? y + (size_t)r[g] * H8 : g_zero_row;
+                        wj[g] = r[g] >= 0 ? wj[g] : -0.0f;
+                    } else {
+                        src = y + (size_t)(r[g] >= 0 ? r[g] : 0) * H8;
+                    }
 #pragma unroll
                     for (int u = 0; u < U; ++u)
                         v[g][u] = load16<EP_COMBINE_NT_LOAD>(src + cidx[u]);
@@ -116,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int g = 0; g < KG; ++g) {
-                    const bool keep = r[g] >= 0;
+                    const bool keep = ZROW || r[g] >= 0;
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         const uint32_t wd[4] = {v[g][u].x, v[g][u].y, v[g][u].z, v[g][u].w};
@@ -174,8 +188,11 @@ hipError_t launch_u(const ep_shape_t &s, const u32x4 *y, const int32_t *idx, con
     const dim3 grid(EP_COMBINE_MAX_BLOCKS ? min(groups, EP_COMBINE_MAX_BLOCKS) : groups);
     const dim3 block(kThreads);
 #define EP_COMBINE_LAUNCH(KG, MULTI)                                                            \
-    return launch(combine_kernel<KG, U, MULTI>, grid, block, 0, stream, y, idx, slot, w, out,   \
-                  s.T, H8, s.E, s.C, s.K, tpb, nseg, map.offset, map.rows)
+    return H8 <= kZeroChunks                                                                    \
+               ? launch(combine_kernel<KG, U, MULTI, true>, grid, block, 0, stream, y, idx,     \
+                        slot, w, out, s.T, H8, s.E, s.C, s.K, tpb, nseg, map.offset, map.rows) \
+               : launch(combine_kernel<KG, U, MULTI, false>, grid, block, 0, stream, y, idx,    \
+                        slot, w, out, s.T, H8, s.E, s.C, s.K, tpb, nseg, map.offset, map.rows)
     if (s.K > 8) EP_COMBINE_LAUNCH(8, true);
     if (s.K > 4) EP_COMBINE_LAUNCH(8, false);
     if (s.K > 2) EP_COMBINE_LAUNCH(4, false);

@@ -283,6 +283,38 @@ def test_combine_identity_law_on_gpu():
     assert np.array_equal(G.to_np(out).view(np.uint16), want)
 
 
+def test_combine_dropped_pairs_leave_signed_zero_and_inf():
+    """A pair that is not kept must leave the running sum exactly as it is, -0 and +-Inf
+    included (the oracle skips it). Token 1's only kept product underflows to -0 and a dropped
+    pair follows; token 0 sums +Inf and a finite row, then a dropped pair; token 2 has an
+    invalid and an unrouted id around a kept pair that gives -0 again; token 3 has nothing
+    kept (+0). Every output row is compared bit for bit with the oracle."""
+    print("[parity] combine: dropped pairs after -0 and Inf sums", flush=True)
+    T, H, E, K, C = 4, 256, 4, 3, 1
+    idx = np.array([[0, 1, 1], [2, 1, 0], [-1, 3, 7], [1, 2, 0]], dtype=np.int32)
+    lay = oracle.layout(idx, E, C, 1)
+    slot = lay["slot"]
+    # kept: (0,0) e0 s0, (0,1) e1 s0, (1,0) e2 s0, (2,1) e3 s0; every other pair dropped or
+    # not routed
+    assert [tuple(p) for p in np.argwhere(slot >= 0)] == [(0, 0), (0, 1), (1, 0), (2, 1)]
+    f = np.zeros((E, C, H), dtype=np.float32)
+    f[0, 0] = np.inf
+    f[1, 0] = 1.0
+    f[2, 0] = -1.0e-20
+    f[3, 0] = 2.0e-20
+    y = W.f32_to_bf16_bits(f)
+    w = np.full((T, K), 1.0, dtype=np.float32)
+    w[1, 0] = 1.0e-30          # -1e-50 underflows: fmaf gives -0
+    w[2, 1] = -1.0e-30         # -2e-50: -0 again
+    want = oracle.combine(y, idx, slot, w)
+    assert (want[1] == 0x8000).all() and (want[2] == 0x8000).all()
+    assert (want[0] == 0x7F80).all() and (want[3] == 0x0000).all()
+    y_d = torch.from_numpy(y.view(np.int16)).to(G.dev())
+    out = B.ep_combine(y_d, G.to_dev(idx), G.to_dev(slot), G.to_dev(w), C)
+    torch.cuda.synchronize()
+    assert np.array_equal(G.to_np(out).view(np.uint16), want)
+
+
 def test_deterministic_repeat():
     cfg = W.get_config("skew_zipf_c256")
     case = G.Case.from_config(cfg)
