@@ -146,6 +146,7 @@ class CallList:
     def __init__(self):
         self.calls = []      # (C function, name, shape, pointer and int arguments, stream)
         self._tensors = []
+        self.device = None   # the device of the recorded tensors
 
     def __len__(self):
         return len(self.calls)
@@ -153,6 +154,9 @@ class CallList:
     def replay(self, stream=None):
         """Issue the recorded calls in order, each on the stream it was recorded with if one was
         given then, else on ``stream`` (default: torch's current stream)."""
+        if not self.calls:
+            return
+        _require_current("replay", self.device)
         s = _stream(stream)
         for fn, name, sh, args, st in self.calls:
             rc = fn(ctypes.byref(sh), *args, s if st is None else st)
@@ -178,16 +182,35 @@ def record():
         _recording.calls = prev
 
 
+def _require_current(name: str, dev):
+    """The library launches on the current HIP device, so the tensors must live there (device
+    pointers of another GPU, or host pointers, would be read by the kernels)."""
+    if dev is not None and dev.type == "cuda" and dev.index == torch.cuda.current_device():
+        return
+    try:
+        cur = f"cuda:{torch.cuda.current_device()}"
+    except RuntimeError:
+        cur = "none (no GPU)"
+    raise ValueError(f"{name}: the tensors are on {dev}, but the library launches on the current "
+                     f"HIP device ({cur}); move them there or call under torch.cuda.device()")
+
+
 def _call(name: str, sh: EpShape, *args, stream=None):
     """Issue (or record) one C call; tensor arguments are passed as their data pointers."""
     fn = getattr(load_library(), name)
     cargs = [a.data_ptr() if isinstance(a, torch.Tensor) else a for a in args]
+    dev = next((a.device for a in args if isinstance(a, torch.Tensor)), None)
     cl = getattr(_recording, "calls", None)
     if cl is not None:
+        if cl.calls and dev != cl.device:
+            raise ValueError(f"{name}: a recorded list holds calls on one device only "
+                             f"({cl.device}, not {dev})")
+        cl.device = dev
         cl._tensors.extend([a for a in args if isinstance(a, torch.Tensor)])
         cl.calls.append((fn, name, sh, tuple(cargs),
                          None if stream is None else stream.cuda_stream))
         return
+    _require_current(name, dev)
     rc = fn(ctypes.byref(sh), *cargs, _stream(stream))
     if rc != EP_OK:
         _check(name, rc)

@@ -208,11 +208,12 @@ def test_record_captures_calls_without_issuing(lib):
     # every tensor a call uses stays referenced by the list
     kept = {t.data_ptr() for t in outer._tensors}
     assert all(a in kept for _, _, _, a, _ in outer.calls for a in a)
-    # outside the block the wrappers issue again: R = 3 does not divide E = 8, which only the
-    # library checks (the null stream object only carries a handle; nothing is launched)
-    import types
-    with pytest.raises(B.EpError):
-        B.ep_layout(idx, E, C, 3, stream=types.SimpleNamespace(cuda_stream=0))
+    # outside the block the wrappers issue again, and refuse host tensors before the library
+    # could launch on their pointers; a recorded list of host tensors will not replay either
+    with pytest.raises(ValueError, match="current HIP device"):
+        B.ep_layout(idx, E, C, R)
+    with pytest.raises(ValueError, match="current HIP device"):
+        outer.replay()
 
 
 def test_c_client_links_against_the_library():
