@@ -672,7 +672,14 @@ __global__ __launch_bounds__(kThreads) void combine_ranks_kernel(
 // combine, stage 2: the token's partials summed in ascending rank
 // ------------------------------------------------------------------------------------------
 
-template <int KG, int U, bool MULTI>
+// A row of zeros that absent list entries read with weight -0: fmaf(-0, +0, acc) adds an exact
+// -0 and leaves every acc as it is, and fmaf(1, v, acc) is exactly acc + v, so the fold needs no
+// per-element select. Never written (zero-initialised at load); rows of up to kZeroChunks
+// 16-byte chunks use it, longer ones keep the select.
+constexpr int kZeroChunks = 4096;
+__device__ u32x4 g_zero_row[kZeroChunks];
+
+template <int KG, int U, bool MULTI, bool ZROW>
 __global__ __launch_bounds__(kThreads) void combine_reduce_kernel(
     const u32x4 *__restrict__ part, const int32_t *__restrict__ rank_slot,
     u32x4 *__restrict__ out, int T, int H8, int R, int Q, int tpb, int nseg)
@@ -718,28 +725,37 @@ __global__ __launch_bounds__(kThreads) void combine_reduce_kernel(
             const int npg = MULTI ? ceil_div(Q, KG) : 1;
             for (int pg = 0; pg < npg; ++pg) {
                 int pr[KG];
+                float wg[KG];
                 u32x4 v[KG][U];
 #pragma unroll
                 for (int g = 0; g < KG; ++g) {
                     const int n = pg * KG + g;
                     pr[g] = n < Q ? wave_uniform(plist[tl * Q + n]) : -1;
-                    // absent entries reload the first row (a cache hit), or row 0 if none
-                    const int rr = pr[g] >= 0 ? pr[g] : (first_row >= 0 ? first_row : 0);
-                    const u32x4 *src = part + (size_t)rr * H8;
+                    const u32x4 *src;
+                    if constexpr (ZROW) {
+                        src = pr[g] >= 0 ? part + (size_t)pr[g] * H8 : g_zero_row;
+                        wg[g] = pr[g] >= 0 ? 1.0f : -0.0f;
+                    } else {
+                        // absent entries reload the first row (a cache hit), or row 0 if none
+                        const int rr = pr[g] >= 0 ? pr[g] : (first_row >= 0 ? first_row : 0);
+                        src = part + (size_t)rr * H8;
+                        wg[g] = 1.0f;
+                    }
 #pragma unroll
                     for (int u = 0; u < U; ++u) v[g][u] = load16<true>(src + cidx[u]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int g = 0; g < KG; ++g) {
-                    const bool keep = pr[g] >= 0;
+                    const bool keep = ZROW || pr[g] >= 0;
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         const uint32_t wd[4] = {v[g][u].x, v[g][u].y, v[g][u].z, v[g][u].w};
 #pragma unroll
                         for (int c = 0; c < 4; ++c) {
-                            const float lo = acc[u][2 * c] + bf16_lo(wd[c]);
-                            const float hi = acc[u][2 * c + 1] + bf16_hi(wd[c]);
+                            const float lo = __builtin_fmaf(wg[g], bf16_lo(wd[c]), acc[u][2 * c]);
+                            const float hi =
+                                __builtin_fmaf(wg[g], bf16_hi(wd[c]), acc[u][2 * c + 1]);
                             acc[u][2 * c] = keep ? lo : acc[u][2 * c];
                             acc[u][2 * c + 1] = keep ? hi : acc[u][2 * c + 1];
                         }
@@ -1042,19 +1058,25 @@ hipError_t launch_combine_reduce(const ep_shape_t &s, const uint16_t *part,
     const dim3 grid = grid_for(s.T, tpb), block(kThreads);
     const u32x4 *pv = reinterpret_cast<const u32x4 *>(part);
     u32x4 *ov = reinterpret_cast<u32x4 *>(out);
-#define EP_LAUNCH_RD(KG, MULTI)                                                                 \
+#define EP_LAUNCH_RD_Z(KG, MULTI, Z)                                                            \
     do {                                                                                        \
         if (U >= 4)                                                                             \
-            return launch(combine_reduce_kernel<KG, 4, MULTI>, grid, block, 0, stream, pv,       \
+            return launch(combine_reduce_kernel<KG, 4, MULTI, Z>, grid, block, 0, stream, pv,    \
                           rank_slot, ov, s.T, H8, s.R, Q, tpb, nseg);                           \
         if (U == 2)                                                                             \
-            return launch(combine_reduce_kernel<KG, 2, MULTI>, grid, block, 0, stream, pv,       \
+            return launch(combine_reduce_kernel<KG, 2, MULTI, Z>, grid, block, 0, stream, pv,    \
                           rank_slot, ov, s.T, H8, s.R, Q, tpb, nseg);                           \
-        return launch(combine_reduce_kernel<KG, 1, MULTI>, grid, block, 0, stream, pv,           \
+        return launch(combine_reduce_kernel<KG, 1, MULTI, Z>, grid, block, 0, stream, pv,        \
                       rank_slot, ov, s.T, H8, s.R, Q, tpb, nseg);                               \
+    } while (0)
+#define EP_LAUNCH_RD(KG, MULTI)                                                                 \
+    do {                                                                                        \
+        if (H8 <= kZeroChunks) EP_LAUNCH_RD_Z(KG, MULTI, true);                                 \
+        EP_LAUNCH_RD_Z(KG, MULTI, false);                                                       \
     } while (0)
     EP_BY_K(Q, EP_LAUNCH_RD);
 #undef EP_LAUNCH_RD
+#undef EP_LAUNCH_RD_Z
 }
 
 }  // namespace ep

@@ -13,8 +13,9 @@
  *  - All array arguments are DEVICE pointers owned by the caller (for example the storage of
  *    torch tensors). The library never allocates, frees or synchronises: each call checks its
  *    arguments on the host, enqueues its kernels on `stream` (0 = the null stream) and returns.
- *    Its only device memory of its own is static, in the loaded code object: a 64 KiB row of
- *    zeros that combine reads, and never writes, for pairs that are not kept.
+ *    Its only device memory of its own is static, in the loaded code object: two 64 KiB rows of
+ *    zeros that combine and the two-stage reduce read, and never write, in place of pairs or
+ *    partial rows that are not there.
  *  - bf16 values are passed as their 16-bit patterns (uint16_t); FP8 values as OCP E4M3 codes
  *    (uint8_t, OFP8 specification rev. 1.0: bias 7, 3 mantissa bits, max 448, S.1111.111 NaN).
  *  - Pair index i = t*K + j names choice j of token t ("token order").
