@@ -163,11 +163,12 @@ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // and CUs share the copies (measured on MI355X at T = 128: one token per tile 12.5 us per
 // single-shot bf16 step against 13.3 us with four); on large ones (T = 4096) bf16 rows do best
 // at 8 tokens per tile (two workgroups per CU, one copying while the other is in its layout),
-// FP8 rows at 16.
+// FP8 rows at 16; at T = 2048 bf16 takes 4 (30.5 against 30.9 us per step with 8).
 int pick_tt(int T, int K, bool fp8)
 {
     int tt = EP_FUSED_TT ? EP_FUSED_TT
-                         : (T >= 2048 ? (fp8 ? 16 : 8) : T >= 1024 ? 4 : T >= 512 ? 2 : 1);
+                         : fp8 ? (T >= 2048 ? 16 : T >= 1024 ? 4 : T >= 512 ? 2 : 1)
+                               : (T >= 4096 ? 8 : T >= 1024 ? 4 : T >= 512 ? 2 : 1);
     while ((tt * K) % 4 != 0) tt *= 2;
     while (tt > 4 && tt * K > kTileThreads) tt -= 4;
     return tt;
