@@ -328,6 +328,37 @@ def test_deterministic_repeat():
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
 
+def test_concurrent_streams_on_separate_buffers():
+    """The library is stateless: two streams, each running fused layout + dispatch and combine
+    on its own batch and buffers with no synchronisation between them, give each batch's
+    oracle result."""
+    print("[parity] two concurrent streams", flush=True)
+    cases = [G.Case.random(700, 512, 32, 4, 60, 4, seed=s) for s in (21, 22)]
+    work = []
+    for c in cases:
+        y_host, y = c.make_y()
+        recv = torch.full((c.E, c.C, c.H), G.SENTINEL16, dtype=torch.int16, device=G.dev())
+        work.append((c, y_host, y, recv, torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    results = []
+    for rep in range(3):
+        outs = []
+        for c, y_host, y, recv, st in work:
+            with torch.cuda.stream(st):
+                lay = B.ep_layout_dispatch(c.x_d, c.idx_d, recv, c.E, c.C, c.R)
+                outs.append((lay, B.ep_combine(y, c.idx_d, lay["slot"], c.w_d, c.C)))
+        torch.cuda.synchronize()
+        results.append(outs)
+    for outs in results:
+        for (c, y_host, y, recv, st), (lay, out) in zip(work, outs):
+            assert np.array_equal(G.to_np(lay["slot"]), c.lay["slot"])
+            want = oracle.combine(y_host, c.idx, c.lay["slot"], c.w)
+            assert np.array_equal(G.to_np(out).view(np.uint16), want)
+            d = np.full((c.E, c.C, c.H), G.SENTINEL16, dtype=np.uint16)
+            oracle.dispatch(c.x, c.idx, c.lay["slot"], c.E, c.C, d)
+            assert np.array_equal(G.to_np(recv).view(np.uint16), d)
+
+
 def test_non_default_stream():
     cfg = W.get_config("decode_bf16")
     case = G.Case.from_config(cfg)
