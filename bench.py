@@ -24,8 +24,8 @@ outputs, as an MoE layer does. A variant where every batch also has its own buff
 reported beside it. Decode-like latency is single-shot: each sample first overwrites 2 GiB
 (beyond every cache) outside the event pair, then times one step (median of the samples).
 
-``--gpus N`` with N > 1 is refused: this build measures one GPU; inter-GPU transport is not
-part of it.
+``--gpus N`` with N > 1 is refused: the benchmark measures one GPU; the library has no
+inter-GPU transport.
 """
 from __future__ import annotations
 
