@@ -287,3 +287,52 @@ def test_two_stage_empty_and_unrouted():
     assert (ts.rl["rank_slot"] == -1).all()
     got, _ = ts.combine_full()
     assert (got == 0).all()
+
+
+def test_two_stage_pass_with_layout_on_a_second_stream():
+    """The expert layout on a second stream, beside the fused rank layout + staging copy on the
+    first (both read only the batch), the expansion and the combines after the first waits for
+    the second: the same outputs as the five launches in one stream, and the oracle's layouts."""
+    _need_gpu()
+    print("[two-stage] layout on a second stream", flush=True)
+    T, H, E, K, C, R = 700, 512, 64, 8, 80, 16
+    case = G.Case.random(T, H, E, K, C, R, seed=31, lo=0, hi=E)
+    y_host, y = case.make_y()
+    dev = G.dev()
+
+    def run(overlap):
+        mk = lambda *n: torch.empty(n, dtype=torch.int32, device=dev)
+        lay = dict(slot=mk(T, K), expert_count=mk(E), expert_offset=mk(E), rank_count=mk(R),
+                   rank_offset=mk(R), stats=mk(4))
+        stage = torch.empty((R, T, H), dtype=torch.int16, device=dev)
+        recv = torch.full((E, C, H), S16, dtype=torch.int16, device=dev)
+        part = torch.empty((R, T, H), dtype=torch.int16, device=dev)
+        torch.cuda.synchronize()
+        main = torch.cuda.current_stream()
+        side = torch.cuda.Stream()
+        if overlap:
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                B.ep_layout(case.idx_d, E, C, R, **lay)
+        else:
+            B.ep_layout(case.idx_d, E, C, R, **lay)
+        rl = B.ep_rank_layout_dispatch(case.x_d, case.idx_d, E, R, stage=stage)
+        if overlap:
+            main.wait_stream(side)
+        B.ep_dispatch_expand(stage, case.idx_d, lay["slot"], rl["rank_slot"], recv, C)
+        B.ep_combine_ranks(y, case.idx_d, lay["slot"], rl["rank_slot"], case.w_d, C, part=part)
+        out = B.ep_combine_reduce(part, rl["rank_slot"], K)
+        torch.cuda.synchronize()
+        return lay, rl, recv, out
+
+    lay0, rl0, recv0, out0 = run(False)
+    for rep in range(3):
+        lay1, rl1, recv1, out1 = run(True)
+        for k in lay0:
+            assert torch.equal(lay0[k], lay1[k]), f"rep {rep}: {k}"
+        assert torch.equal(rl0["rank_slot"], rl1["rank_slot"]), f"rep {rep}: rank_slot"
+        assert torch.equal(recv0, recv1), f"rep {rep}: recv"
+        assert torch.equal(out0, out1), f"rep {rep}: out"
+    G.check_layout(case.idx, E, C, R, lay1)
+    want = oracle.rank_layout(case.idx, E, R)
+    assert np.array_equal(G.to_np(rl1["rank_slot"]), want["rank_slot"])
