@@ -13,7 +13,7 @@
 // instruction covers 1 KiB of a row).
 //
 // Memory-level parallelism. For a group of KG pairs (KG = K rounded up to a power of two, at
-// most 8; whole-row items take groups of 4) the wavefront issues every row load first, as straight-line code (a pair that is not
+// most 8; whole-row items take groups of 2) the wavefront issues every row load first, as straight-line code (a pair that is not
 // kept reads a row of zeros with weight -0, which the fold adds as an exact -0, so no
 // per-element select is needed), and only then folds the rows in j order with fmaf. The K row fetches of a token are therefore
 // in flight together; a branch around any load would make the compiler wait for earlier
@@ -195,11 +195,12 @@ hipError_t launch_u(const ep_shape_t &s, const u32x4 *y, const int32_t *idx, con
                         slot, w, out, s.T, H8, s.E, s.C, s.K, tpb, nseg, map.offset, map.rows)
     if (s.K > 8) EP_COMBINE_LAUNCH(8, true);
     if (s.K > 4) {
-        // whole-row items (U = 4) fold two groups of four rows: that build holds 114 VGPRs, so
-        // 4 wavefronts per SIMD fit and a 4096-token batch runs as one round (26.7 against
-        // 27.1 us at T = 4096); narrower items keep one group of eight rows in flight, which
-        // is faster at decode size (4.0 against 4.4 us at T = 128)
-        if constexpr (U >= 4) EP_COMBINE_LAUNCH(4, true);
+        // whole-row items (U = 4) fold their rows in groups of two: that build holds 82 VGPRs,
+        // so 5 wavefronts per SIMD fit (at T = 4096: 26.5 us, against 26.8 with groups of four
+        // at 114 VGPRs, 26.6 with single rows and 27.1 with one group of eight at 162);
+        // narrower items keep one group of eight rows in flight, which is faster at decode
+        // size (4.0 against 4.4 us at T = 128 with groups of four)
+        if constexpr (U >= 4) EP_COMBINE_LAUNCH(2, true);
         else EP_COMBINE_LAUNCH(8, false);
     }
     if (s.K > 2) EP_COMBINE_LAUNCH(4, false);

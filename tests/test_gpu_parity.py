@@ -85,8 +85,8 @@ SMALL = [
     (2051, 256, 16, 4, 700, 4),       # fused tiles of 4 tokens (bf16) and 16 (FP8) with a
                                       # 3-token last tile
     (4099, 256, 16, 4, 1100, 4),      # bf16 fused tiles of 8 tokens, a 3-token last tile
-    (4100, 512, 64, 8, 200, 8),       # whole-row combine items folding two groups of four
-                                      # rows, with drops, unrouted and invalid ids
+    (4100, 512, 64, 8, 200, 8),       # whole-row combine items folding rows in groups of two
+                                      # with drops, unrouted and invalid ids
     (40, 256, 300, 256, 20, 3),       # K = EP_MAX_TOPK: 32 pair groups per token, full tiles
     (700, 256, 64, 6, 60, 8),         # 512 <= T < 1024: fused tiles of two tokens
     (600, 256, 32, 5, 90, 4),         # two tokens would make 10 pairs: tiles of four tokens
