@@ -24,6 +24,10 @@ outputs, as an MoE layer does. A variant where every batch also has its own buff
 reported beside it. Decode-like latency is single-shot: each sample first overwrites 2 GiB
 (beyond every cache) outside the event pair, then times one step (median of the samples).
 
+``--starts N`` repeats all of this in N fresh processes, the order of the four step configs
+rotated by one place per start, and reports the median start with each figure's per-start
+median, min, max and coefficient of variation.
+
 ``--gpus N`` with N > 1 is refused: the benchmark measures one GPU; the library has no
 inter-GPU transport.
 """
@@ -56,11 +60,81 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget for the oracle's CPU baseline")
+    ap.add_argument("--starts", type=int, default=1,
+                    help="run the benchmark in this many fresh processes, one after another, "
+                         "each with the config order rotated by one more place, and report the "
+                         "median over the starts (with min, max and CV per config)")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="rotate the order of the four step configs by this many places")
     ap.add_argument("--only", default=None,
                     help="run only this workload's timed loop (for profiling); 'copy_probe' "
                          "runs a plain 256 MiB device copy instead, the reference kernel for "
                          "scaling HBM byte counters")
     return ap.parse_args()
+
+
+# per-start figures summarised by --starts: (name, path into the JSON line)
+START_FIGURES = (
+    ("prefill_bf16 us_per_step", ("us_per_step",)),
+    ("prefill_bf16 cold us_median", ("cold_single_shot", "us_median")),
+    ("prefill_fp8 us_per_step", ("prefill_fp8", "us_per_step")),
+    ("prefill_fp8 cold us_median", ("prefill_fp8", "cold_single_shot", "us_median")),
+    ("decode_bf16 us_single_shot_median", ("t128_us", "decode_bf16", "us_single_shot_median")),
+    ("decode_fp8 us_single_shot_median", ("t128_us", "decode_fp8", "us_single_shot_median")),
+)
+
+
+def aggregate_starts(lines):
+    """Combine the JSON lines of several process starts into one: the start whose headline
+    value is the (low) median keeps its line, and "starts" gets, per figure, the median of the
+    per-start values, their min, max and coefficient of variation (sample standard deviation
+    over the mean). The first start's CPU baseline is kept when the chosen one has none."""
+    if not lines:
+        raise ValueError("no start produced a result line")
+    vals = [ln["value"] for ln in lines]
+    pick = vals.index(statistics.median_low(vals))
+    out = dict(lines[pick])
+    summary = {"n": len(lines), "picked_start": pick, "value_per_start": vals}
+    for name, path in START_FIGURES:
+        xs = []
+        for ln in lines:
+            v = ln
+            for k in path:
+                v = v.get(k) if isinstance(v, dict) else None
+            if v is not None:
+                xs.append(float(v))
+        if xs:
+            mean = statistics.fmean(xs)
+            cv = statistics.stdev(xs) / mean if len(xs) > 1 and mean else 0.0
+            summary[name] = {"median": round(statistics.median(xs), 3), "min": min(xs),
+                             "max": max(xs), "cv": round(cv, 4), "per_start": xs}
+    out["starts"] = summary
+    if out.get("cpu_baseline") is None:
+        out["cpu_baseline"] = next((ln["cpu_baseline"] for ln in lines
+                                    if ln.get("cpu_baseline")), None)
+    return out
+
+
+def run_starts(args):
+    """--starts N: each start is a fresh child process (started before this process touches
+    the GPU) running the default benchmark with the config order rotated by its index; only
+    the first one times the CPU oracle. Their progress goes to stderr as they run."""
+    import subprocess
+    lines = []
+    for k in range(args.starts):
+        cmd = [sys.executable, os.path.abspath(__file__), "--steps", str(args.steps),
+               "--warmup", str(args.warmup), "--workload", args.workload,
+               "--latency-samples", str(args.latency_samples),
+               "--cpu-seconds", str(args.cpu_seconds), "--rotate", str(k)]
+        if k > 0 or args.no_cpu_baseline:
+            cmd.append("--no-cpu-baseline")
+        log(f"start {k + 1} of {args.starts}: config order rotated by {k}")
+        res = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
+        if res.returncode != 0:
+            log(f"start {k + 1} failed with exit status {res.returncode}")
+            sys.exit(res.returncode if res.returncode > 0 else 1)
+        lines.append(json.loads(res.stdout.strip().splitlines()[-1]))
+    print(json.dumps(aggregate_starts(lines)), flush=True)
 
 
 def log(msg):
@@ -623,6 +697,12 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path has no "
               "inter-GPU transport).", file=sys.stderr)
         sys.exit(2)
+    if args.starts > 1:
+        if args.only:
+            print("--starts and --only do not combine", file=sys.stderr)
+            sys.exit(2)
+        run_starts(args)
+        return
     import torch
     from combine_ep_layout_06_amd import accounting as A
     from combine_ep_layout_06_amd import binding as B
@@ -653,7 +733,9 @@ def main():
     head_cfg = W.get_config(args.workload)
     flush = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")   # beyond every cache
     results = {}
-    for name in dict.fromkeys([args.workload, "prefill_fp8", "decode_bf16", "decode_fp8"]):
+    order = list(dict.fromkeys([args.workload, "prefill_fp8", "decode_bf16", "decode_fp8"]))
+    rot = args.rotate % len(order)
+    for name in order[rot:] + order[:rot]:
         cfg = W.get_config(name)
         wl = Workload(cfg, NSETS, torch, B, W)
         ms, wall_ms = wl.timed_loop(args.steps, args.warmup)
