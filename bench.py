@@ -558,13 +558,18 @@ def cpu_baseline(cfg, budget_s, W, A):
     y = np.empty((cfg.E, cfg.C, cfg.H), dtype=np.uint16)
     y[e, s] = W.y_rows(len(kept_i), cfg.H, cfg.seed)
     recv = np.empty((cfg.E, cfg.C, cfg.H), dtype=np.uint16)
-    times, t_start = [], time.perf_counter()
+    times, parts, t_start = [], {"layout": [], "dispatch": [], "combine": []}, time.perf_counter()
     while time.perf_counter() - t_start < budget_s or not times:
         t0 = time.perf_counter()
         lay = oracle.layout(idx, cfg.E, cfg.C, cfg.R)
+        t1 = time.perf_counter()
         oracle.dispatch(x, idx, lay["slot"], cfg.E, cfg.C, recv)
+        t2 = time.perf_counter()
         oracle.combine(y, idx, lay["slot"], w)
-        times.append(time.perf_counter() - t0)
+        t3 = time.perf_counter()
+        times.append(t3 - t0)
+        for k, dt in (("layout", t1 - t0), ("dispatch", t2 - t1), ("combine", t3 - t2)):
+            parts[k].append(dt)
     med = statistics.median(times)
     payload = A.logical_payload_bytes(cfg.T, cfg.K, cfg.H, False)
     cpu = "unknown"
@@ -577,7 +582,8 @@ def cpu_baseline(cfg, budget_s, W, A):
             "kind": "oracle",
             "sample": f"{len(times)} whole steps (layout + bf16 dispatch + combine) of "
                       f"{cfg.name}, median {med * 1e3:.1f} ms/step, single thread pinned to one "
-                      f"core of {os.cpu_count()} ({cpu})"}
+                      f"core of {os.cpu_count()} ({cpu})",
+            "parts_ms_median": {k: round(statistics.median(v) * 1e3, 3) for k, v in parts.items()}}
 
 
 def two_stage_report(cfg, flush, args, torch, B, W, A):
