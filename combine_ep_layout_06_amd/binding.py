@@ -29,7 +29,7 @@ EP_MAX_RANKS = 64
 EXPORTED = ("ep_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_layout_dispatch",
             "ep_layout_dispatch_fp8", "ep_combine", "ep_rank_layout", "ep_dispatch_ranks",
             "ep_dispatch_ranks_fp8", "ep_rank_layout_dispatch", "ep_rank_layout_dispatch_fp8",
-            "ep_dispatch_expand", "ep_dispatch_expand_fp8",
+            "ep_dispatch_expand", "ep_dispatch_expand_fp8", "ep_layout_dispatch_expand",
             "ep_combine_ranks", "ep_combine_reduce", "ep_layout_packed", "ep_dispatch_packed",
             "ep_dispatch_packed_fp8", "ep_layout_dispatch_packed", "ep_layout_dispatch_packed_fp8",
             "ep_combine_packed", "ep_error_string", "ep_last_error", "ep_version")
@@ -76,6 +76,7 @@ def load_library():
         L.ep_rank_layout_dispatch_fp8.argtypes = [sp] + [vp] * 7
         L.ep_dispatch_expand.argtypes = [sp] + [vp] * 6
         L.ep_dispatch_expand_fp8.argtypes = [sp] + [vp] * 8
+        L.ep_layout_dispatch_expand.argtypes = [sp] + [vp] * 11
         L.ep_combine_ranks.argtypes = [sp] + [vp] * 7
         L.ep_combine_reduce.argtypes = [sp] + [vp] * 4
         i32 = ctypes.c_int32
@@ -493,6 +494,27 @@ def ep_dispatch_expand(stage: torch.Tensor, topk_idx: torch.Tensor, slot: torch.
     sh = _shape(T, H, E, K, C, R)
     _call("ep_dispatch_expand", sh, stage, topk_idx, slot, rank_slot, recv, stream=stream)
     return recv
+
+
+def ep_layout_dispatch_expand(stage: torch.Tensor, topk_idx: torch.Tensor,
+                              rank_slot: torch.Tensor, recv: torch.Tensor, E: int, C: int, *,
+                              slot=None, expert_count=None, expert_offset=None, rank_count=None,
+                              rank_offset=None, stats=None, stream=None):
+    """ep_layout + stage 2 of dispatch in one launch: ``stage`` [R, T, H] -> ``recv`` [E, C, H]
+    bf16 (in place). Returns the layout dict (as ep_layout)."""
+    dev = stage.device
+    R, T, H = stage.shape
+    K = topk_idx.shape[1]
+    lay = _layout_outputs(dev, T, K, E, R, slot, expert_count, expert_offset, rank_count,
+                          rank_offset, stats)
+    _need(stage, "stage", _bf16(stage), R * T * H, dev)
+    _need(topk_idx, "topk_idx", torch.int32, T * K, dev)
+    _need(rank_slot, "rank_slot", torch.int32, T * R, dev)
+    _need(recv, "recv", _bf16(recv), E * C * H, dev)
+    sh = _shape(T, H, E, K, C, R)
+    _call("ep_layout_dispatch_expand", sh, stage, topk_idx, rank_slot, *_layout_ts(lay), recv,
+          stream=stream)
+    return lay
 
 
 def ep_dispatch_expand_fp8(stage_q: torch.Tensor, stage_scale: torch.Tensor,

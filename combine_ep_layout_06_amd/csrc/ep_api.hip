@@ -285,6 +285,27 @@ int ep_dispatch_expand(const ep_shape_t *shape, const uint16_t *stage, const int
                       fn);
 }
 
+int ep_layout_dispatch_expand(const ep_shape_t *shape, const uint16_t *stage,
+                              const int32_t *topk_idx, const int32_t *rank_slot, int32_t *slot,
+                              int32_t *expert_count, int32_t *expert_offset, int32_t *rank_count,
+                              int32_t *rank_offset, int32_t *stats, uint16_t *recv,
+                              hipStream_t stream)
+{
+    const char *fn = "ep_layout_dispatch_expand";
+    if (int rc = check_layout_args(shape, topk_idx, slot, expert_count, expert_offset, stats, fn))
+        return rc;
+    if (int rc = check_rows(shape, fn, 8)) return rc;
+    if (int rc = check_ranks(shape, fn)) return rc;
+    if (shape->T > 0 && (!stage || !rank_slot || !recv))
+        return fail(EP_ERR_INVALID, "ep_layout_dispatch_expand: NULL required pointer");
+    if (!aligned(stage, 16) || !aligned(recv, 16))
+        return fail(EP_ERR_ALIGN,
+                    "ep_layout_dispatch_expand: stage and recv must be 16-byte aligned");
+    const ep::LayoutOut o{slot, expert_count, expert_offset, rank_count, rank_offset, stats};
+    return hip_status(
+        ep::launch_layout_expand_bf16(*shape, stage, topk_idx, rank_slot, o, recv, stream), fn);
+}
+
 int ep_dispatch_expand_fp8(const ep_shape_t *shape, const uint8_t *stage_q,
                            const float *stage_scale, const int32_t *topk_idx,
                            const int32_t *slot, const int32_t *rank_slot, uint8_t *recv_q,

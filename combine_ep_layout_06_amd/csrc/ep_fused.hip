@@ -99,6 +99,74 @@ __global__ __launch_bounds__(kTileThreads) void layout_dispatch_fp8_kernel(
     if (last) layout_finish<false>(TK, E, C, R, lds, m, o);
 }
 
+// The expert layout fused into the two-stage expansion: layout_tile gives the tile's receive
+// rows as in layout_dispatch_bf16_kernel, and each kept pair then copies its rank's staging row
+// (row rank_slot[t][r] of rank r = e / (E/R) in the [R][T] staging buffer, e = row / C) instead
+// of the token's row of x; a pair whose rank_slot entry is outside [0, T) is not copied. Pairs of one rank
+// read the same staging row, so these loads keep the caches (the second read hits).
+// A lane takes one 16-byte chunk per pair (U = 1) and the kernel is held to 8 wavefronts per
+// SIMD (47 VGPRs, 78 SGPRs: two 1024-lane workgroups per CU). Prefill bf16 (T = 4096, R = 16):
+// 48.6 us against 6.7 + 44.8 us for the layout and the expansion apart; half rows per item
+// spill under that bound (60.1 us), and without it one workgroup fits per CU (49.6 us).
+template <int KG, int U, bool MULTI>
+__global__ __launch_bounds__(kTileThreads, 8) void layout_expand_bf16_kernel(
+    const u32x4 *__restrict__ stage, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ rank_slot, LayoutOut o, u32x4 *__restrict__ recv, int T, int H8,
+    int E, int C, int K, int R, int nbits, int lg_nc, int TT, int nseg)
+{
+    extern __shared__ __align__(16) int32_t lds[];
+    __shared__ int32_t rows[kTileThreads];
+    const LayoutLdsMap m = layout_lds_map(E, lg_nc);
+    const int TK = T * K;
+    const bool last = blockIdx.x == gridDim.x - 1;
+    const int t0 = blockIdx.x * TT;
+    const int nt = min(TT, T - t0);
+    const int wave = wave_uniform(threadIdx.x / kWave);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int nitems = nt * nseg;
+    const int EL = E / R;
+    const TileIds ids = layout_tile_loads(idx, TK, t0 * K, TT * K);
+    layout_tile(ids, idx, TK, E, C, nbits, t0 * K, TT * K, last, lds, m, o.slot, rows);
+    for (int item = wave; item < nitems; item += kTileWaves) {
+        const int tl = item / nseg, seg = item - tl * nseg;
+        const int32_t *rs = rank_slot + (size_t)(t0 + tl) * R;
+        const int npg = MULTI ? (K + KG - 1) / KG : 1;
+        for (int pg = 0; pg < npg; ++pg) {
+            int r[KG];
+            token_rows<KG>(rows, tl, pg * KG, K, r);
+            u32x4 v[KG][U];
+#pragma unroll
+            for (int g = 0; g < KG; ++g) {
+                int sr = -1;
+                if (r[g] >= 0) {
+                    const int rk = (r[g] / C) / EL;
+                    const int p = wave_uniform(rs[rk]);
+                    sr = (unsigned)p < (unsigned)T ? rk * T + p : -1;
+                }
+                if (sr < 0) r[g] = -1;     // no staged row: the pair is not copied
+                const u32x4 *src = stage + (size_t)(sr >= 0 ? sr : 0) * H8;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = (seg * U + u) * kWave + lane;
+                    v[g][u] = load16<false>(src + (c < H8 ? c : H8 - 1));
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int g = 0; g < KG; ++g) {
+                if (r[g] < 0) continue;
+                u32x4 *dst = recv + (size_t)r[g] * H8;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = (seg * U + u) * kWave + lane;
+                    if (c < H8) store16<EP_DISPATCH_NT_STORE>(dst + c, v[g][u]);
+                }
+            }
+        }
+    }
+    if (last) layout_finish<false>(TK, E, C, R, lds, m, o);
+}
+
 // The packed layout and dispatch fused: every tile counts all pairs (ALL in layout_tile), so
 // each workgroup knows the packed offsets and copies its tokens to offset[e] + slot at once.
 template <int KG, int U, bool MULTI>
@@ -239,6 +307,36 @@ hipError_t launch_layout_dispatch_bf16(const ep_shape_t &s, const uint16_t *x,
     if (U >= 4) return launch_bf16_u<4>(s, xv, idx, o, rv, H8, TT, nseg, stream);
     if (U == 2) return launch_bf16_u<2>(s, xv, idx, o, rv, H8, TT, nseg, stream);
     return launch_bf16_u<1>(s, xv, idx, o, rv, H8, TT, nseg, stream);
+}
+
+namespace {
+
+template <int U>
+hipError_t launch_expand_u(const ep_shape_t &s, const u32x4 *stage, const int32_t *idx,
+                           const int32_t *rank_slot, const LayoutOut &o, u32x4 *recv, int H8,
+                           int TT, int nseg, hipStream_t stream)
+{
+    const dim3 grid(s.T > 0 ? ceil_div(s.T, TT) : 1), block(kTileThreads);
+    const int nbits = expert_bits(s.E), lg_nc = layout_lg_nc(s.E);
+    const size_t lds = layout_lds_bytes(s.E, lg_nc);
+#define EP_LAUNCH_LX(KG, MULTI)                                                                 \
+    return launch(layout_expand_bf16_kernel<KG, U, MULTI>, grid, block, lds, stream, stage, idx, \
+                  rank_slot, o, recv, s.T, H8, s.E, s.C, s.K, s.R, nbits, lg_nc, TT, nseg)
+    EP_BY_K(s.K, EP_LAUNCH_LX);
+#undef EP_LAUNCH_LX
+}
+
+}  // namespace
+
+hipError_t launch_layout_expand_bf16(const ep_shape_t &s, const uint16_t *stage,
+                                     const int32_t *idx, const int32_t *rank_slot,
+                                     const LayoutOut &o, uint16_t *recv, hipStream_t stream)
+{
+    const int H8 = s.H / 8;
+    const int TT = pick_tt(s.T, s.K, false);
+    const int nseg = ceil_div(H8, kWave);
+    return launch_expand_u<1>(s, reinterpret_cast<const u32x4 *>(stage), idx, rank_slot, o,
+                              reinterpret_cast<u32x4 *>(recv), H8, TT, nseg, stream);
 }
 
 hipError_t launch_layout_dispatch_fp8(const ep_shape_t &s, const uint16_t *x, const int32_t *idx,

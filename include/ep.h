@@ -327,6 +327,20 @@ int ep_dispatch_expand(const ep_shape_t *shape, const uint16_t *stage, const int
                        hipStream_t stream);
 
 /*
+ * ep_layout_dispatch_expand -- ep_layout and ep_dispatch_expand in one launch: each workgroup
+ * lays out a tile of tokens against all earlier ones (as ep_layout_dispatch does) and copies
+ * the tile's kept pairs from their ranks' staging rows at once. Outputs (slot, expert_count,
+ * expert_offset, rank_count, rank_offset, stats, recv) are bit-identical to those of the two
+ * calls, and so are the argument rules (stage and recv 16-byte aligned; rank_count and
+ * rank_offset may be NULL). rank_slot is read, not written. bf16 only; H % 8 == 0.
+ */
+int ep_layout_dispatch_expand(const ep_shape_t *shape, const uint16_t *stage,
+                              const int32_t *topk_idx, const int32_t *rank_slot, int32_t *slot,
+                              int32_t *expert_count, int32_t *expert_offset, int32_t *rank_count,
+                              int32_t *rank_offset, int32_t *stats, uint16_t *recv,
+                              hipStream_t stream);
+
+/*
  * ep_dispatch_expand_fp8 -- stage 2 for FP8: codes and scales of the staged row copied to every
  * kept pair's row of recv_q / recv_scale. H % 128 == 0.
  */

@@ -1,5 +1,6 @@
 """GPU parity of the two-stage, rank-deduplicated path (ep_rank_layout, ep_dispatch_ranks[_fp8],
-ep_dispatch_expand[_fp8], ep_combine_ranks, ep_combine_reduce) against the oracle.
+ep_dispatch_expand[_fp8], ep_layout_dispatch_expand, ep_combine_ranks, ep_combine_reduce) against
+the oracle.
 
 Small shapes compare whole buffers bit for bit, with sentinels in every row a call must not
 touch. The full workloads compare the rank layout in full, the composed dispatch with the
@@ -20,6 +21,9 @@ pytestmark = pytest.mark.gpu
 S16 = G.SENTINEL16
 S8 = G.SENTINEL8
 SF = G.SENTINEL_F32
+
+
+LAYOUT_KEYS = ("slot", "expert_count", "expert_offset", "rank_count", "rank_offset", "stats")
 
 
 def _need_gpu():
@@ -76,6 +80,14 @@ class TwoStage:
         one = np.full((E, C, H), S16, np.uint16)
         oracle.dispatch(self.x, self.idx, self.slot, E, C, one)
         assert np.array_equal(want, one), "two-stage oracle differs from one-stage"
+        # the expert layout fused with the expansion: the layout's outputs and the same recv
+        lx_recv = torch.full((E, C, H), S16, dtype=torch.int16, device=G.dev())
+        lx = B.ep_layout_dispatch_expand(stage, self.case.idx_d, self.g["rank_slot"], lx_recv,
+                                         E, C)
+        torch.cuda.synchronize()
+        for k in LAYOUT_KEYS:
+            assert torch.equal(lx[k], self.case.g[k]), f"fused layout+expand {k}"
+        assert np.array_equal(G.to_np(lx_recv).view(np.uint16), want), "fused layout+expand recv"
         # the fused rank layout + stage 1: the same three outputs
         fused = torch.full((R, T, H), S16, dtype=torch.int16, device=G.dev())
         f = B.ep_rank_layout_dispatch(self.case.x_d, self.case.idx_d, E, R, stage=fused)
@@ -227,6 +239,14 @@ def test_two_stage_workloads(name):
         B.ep_dispatch(c.x_d, c.idx_d, c.g["slot"], r1, C)
         torch.cuda.synchronize()
         assert torch.equal(r1, r2)
+        del r2
+        r3 = torch.full((E, C, H), S16, dtype=torch.int16, device=G.dev())
+        lx = B.ep_layout_dispatch_expand(stage, c.idx_d, ts.g["rank_slot"], r3, E, C)
+        torch.cuda.synchronize()
+        assert torch.equal(r1, r3), "fused layout+expand recv"
+        for k in LAYOUT_KEYS:
+            assert torch.equal(lx[k], c.g[k]), f"fused layout+expand {k}"
+        del r3
         # sampled staging rows are the token rows
         t_i, r_i = np.nonzero(ts.rl["rank_slot"] >= 0)
         pick = np.linspace(0, len(t_i) - 1, 257).astype(int)
@@ -234,7 +254,7 @@ def test_two_stage_workloads(name):
                                 .astype(np.int64)).to(G.dev())
         got = G.to_np(stage.view(R * T, H).index_select(0, rows)).view(np.uint16)
         assert np.array_equal(got, ts.x[t_i[pick]])
-        del stage, r1, r2
+        del stage, r1
     torch.cuda.empty_cache()
     y_host, y = c.make_y()
     part = B.ep_combine_ranks(y, c.idx_d, c.g["slot"], ts.g["rank_slot"], c.w_d, C)
@@ -280,6 +300,14 @@ def test_two_stage_empty_and_unrouted():
         fn(x0, idx, 8, 4, rank_tokens=rt)
         torch.cuda.synchronize()
         assert G.to_np(rt).tolist() == [0, 0, 0, 0]
+    # T = 0 through the fused layout + expansion: zero counts, nothing copied
+    recv = torch.full((8, 2, 256), S16, dtype=torch.int16, device="cuda")
+    lx = B.ep_layout_dispatch_expand(torch.zeros((4, 0, 256), dtype=torch.int16, device="cuda"),
+                                     idx, torch.zeros((0, 4), dtype=torch.int32, device="cuda"),
+                                     recv, 8, 2)
+    torch.cuda.synchronize()
+    assert G.to_np(lx["expert_count"]).tolist() == [0] * 8
+    assert (G.to_np(recv).view(np.uint16) == np.uint16(S16)).all()
     # every id unrouted or invalid: nothing is sent anywhere, the output is +0
     ts = TwoStage(16, 64, 8, 4, 4, 4, np.where(np.arange(64).reshape(16, 4) % 2, -1, 9)
                   .astype(np.int32), W.f32_to_bf16_bits(np.ones((16, 64), np.float32)),
