@@ -397,20 +397,20 @@ class Workload:
 
     def layout_expand(self, s):
         c = self.cfg
-        self.B.ep_layout_dispatch_expand(s["stage"], s["idx"], s["rl"]["rank_slot"], s["recv"],
-                                         c.E, c.C, **s["lay"])
+        if c.fp8:
+            self.B.ep_layout_dispatch_expand_fp8(s["stage_q"], s["stage_s"], s["idx"],
+                                                 s["rl"]["rank_slot"], s["recv_q"], s["recv_s"],
+                                                 c.E, c.C, **s["lay"])
+        else:
+            self.B.ep_layout_dispatch_expand(s["stage"], s["idx"], s["rl"]["rank_slot"],
+                                             s["recv"], c.E, c.C, **s["lay"])
 
     def step2(self, k):
-        """One two-stage pass: the rank layout fused with stage 1 and, for bf16, the expert
-        layout fused with the expansion (four launches; FP8 keeps the expert layout apart)."""
+        """One two-stage pass in four launches: the rank layout fused with stage 1, the expert
+        layout fused with the expansion, the partial combine and the reduce."""
         s = self.sets[k % len(self.sets)]
-        if self.cfg.fp8:
-            self.layout(s)
-            self.rank_layout_dispatch(s)
-            self.expand(s)
-        else:
-            self.rank_layout_dispatch(s)
-            self.layout_expand(s)
+        self.rank_layout_dispatch(s)
+        self.layout_expand(s)
         self.combine_ranks(s)
         self.combine_reduce(s)
 
@@ -618,8 +618,7 @@ def two_stage_report(cfg, flush, args, torch, B, W, A):
     kernels = (("rank_layout_dispatch", wl.rank_layout_dispatch), ("rank_layout", wl.rank_layout),
                ("dispatch_ranks", wl.dispatch_ranks), ("dispatch_expand", wl.expand),
                ("combine_ranks", wl.combine_ranks), ("combine_reduce", wl.combine_reduce))
-    if not cfg.fp8:
-        kernels += (("layout_dispatch_expand", wl.layout_expand),)
+    kernels += (("layout_dispatch_expand", wl.layout_expand),)
     kus = wl.kernel_avg_us(flush, kernels=kernels)
     T, K, H, R = cfg.T, cfg.K, cfg.H, cfg.R
     kb = {"rank_layout": A.rank_layout_bytes(T, K, R),
@@ -632,7 +631,7 @@ def two_stage_report(cfg, flush, args, torch, B, W, A):
     alg = (A.layout_bytes(T, K) + kb["rank_layout_dispatch"] + kb["dispatch_expand"] +
            kb["combine_ranks"] + kb["combine_reduce"])
     out = {"workload": cfg.name, "us_per_pass": round(ms * 1e3, 3),
-           "launches_per_pass": 5 if cfg.fp8 else 4,
+           "launches_per_pass": 4,
            "us_per_pass_five_launches": round(ms5 * 1e3, 3),
            "us_per_pass_rank_layout_apart": round(ms6 * 1e3, 3),
            "hbm_frac": round(alg / (ms * 1e-3) / A.HBM_PEAK_BYTES_PER_S, 4),

@@ -30,6 +30,7 @@ EXPORTED = ("ep_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_layout_dispatch",
             "ep_layout_dispatch_fp8", "ep_combine", "ep_rank_layout", "ep_dispatch_ranks",
             "ep_dispatch_ranks_fp8", "ep_rank_layout_dispatch", "ep_rank_layout_dispatch_fp8",
             "ep_dispatch_expand", "ep_dispatch_expand_fp8", "ep_layout_dispatch_expand",
+            "ep_layout_dispatch_expand_fp8",
             "ep_combine_ranks", "ep_combine_reduce", "ep_layout_packed", "ep_dispatch_packed",
             "ep_dispatch_packed_fp8", "ep_layout_dispatch_packed", "ep_layout_dispatch_packed_fp8",
             "ep_combine_packed", "ep_error_string", "ep_last_error", "ep_version")
@@ -77,6 +78,7 @@ def load_library():
         L.ep_dispatch_expand.argtypes = [sp] + [vp] * 6
         L.ep_dispatch_expand_fp8.argtypes = [sp] + [vp] * 8
         L.ep_layout_dispatch_expand.argtypes = [sp] + [vp] * 11
+        L.ep_layout_dispatch_expand_fp8.argtypes = [sp] + [vp] * 13
         L.ep_combine_ranks.argtypes = [sp] + [vp] * 7
         L.ep_combine_reduce.argtypes = [sp] + [vp] * 4
         i32 = ctypes.c_int32
@@ -514,6 +516,32 @@ def ep_layout_dispatch_expand(stage: torch.Tensor, topk_idx: torch.Tensor,
     sh = _shape(T, H, E, K, C, R)
     _call("ep_layout_dispatch_expand", sh, stage, topk_idx, rank_slot, *_layout_ts(lay), recv,
           stream=stream)
+    return lay
+
+
+def ep_layout_dispatch_expand_fp8(stage_q: torch.Tensor, stage_scale: torch.Tensor,
+                                  topk_idx: torch.Tensor, rank_slot: torch.Tensor,
+                                  recv_q: torch.Tensor, recv_scale: torch.Tensor, E: int, C: int,
+                                  *, slot=None, expert_count=None, expert_offset=None,
+                                  rank_count=None, rank_offset=None, stats=None, stream=None):
+    """ep_layout + FP8 stage 2 in one launch: codes and scales of the staged rows -> ``recv_q``
+    [E, C, H] and ``recv_scale`` [E, C, H/128] (in place). Returns the layout dict."""
+    dev = stage_q.device
+    R, T, H = stage_q.shape
+    K = topk_idx.shape[1]
+    lay = _layout_outputs(dev, T, K, E, R, slot, expert_count, expert_offset, rank_count,
+                          rank_offset, stats)
+    _need(stage_q, "stage_q", stage_q.dtype if stage_q.dtype in (torch.uint8, torch.float8_e4m3fn)
+          else torch.uint8, R * T * H, dev)
+    _need(stage_scale, "stage_scale", torch.float32, R * T * (H // EP_FP8_BLOCK), dev)
+    _need(topk_idx, "topk_idx", torch.int32, T * K, dev)
+    _need(rank_slot, "rank_slot", torch.int32, T * R, dev)
+    _need(recv_q, "recv_q", recv_q.dtype if recv_q.dtype in (torch.uint8, torch.float8_e4m3fn)
+          else torch.uint8, E * C * H, dev)
+    _need(recv_scale, "recv_scale", torch.float32, E * C * (H // EP_FP8_BLOCK), dev)
+    sh = _shape(T, H, E, K, C, R)
+    _call("ep_layout_dispatch_expand_fp8", sh, stage_q, stage_scale, topk_idx, rank_slot,
+          *_layout_ts(lay), recv_q, recv_scale, stream=stream)
     return lay
 
 

@@ -306,6 +306,30 @@ int ep_layout_dispatch_expand(const ep_shape_t *shape, const uint16_t *stage,
         ep::launch_layout_expand_bf16(*shape, stage, topk_idx, rank_slot, o, recv, stream), fn);
 }
 
+int ep_layout_dispatch_expand_fp8(const ep_shape_t *shape, const uint8_t *stage_q,
+                                  const float *stage_scale, const int32_t *topk_idx,
+                                  const int32_t *rank_slot, int32_t *slot, int32_t *expert_count,
+                                  int32_t *expert_offset, int32_t *rank_count,
+                                  int32_t *rank_offset, int32_t *stats, uint8_t *recv_q,
+                                  float *recv_scale, hipStream_t stream)
+{
+    const char *fn = "ep_layout_dispatch_expand_fp8";
+    if (int rc = check_layout_args(shape, topk_idx, slot, expert_count, expert_offset, stats, fn))
+        return rc;
+    if (int rc = check_rows(shape, fn, EP_FP8_BLOCK)) return rc;
+    if (int rc = check_ranks(shape, fn)) return rc;
+    if (shape->T > 0 && (!stage_q || !stage_scale || !rank_slot || !recv_q || !recv_scale))
+        return fail(EP_ERR_INVALID, "ep_layout_dispatch_expand_fp8: NULL required pointer");
+    if (!aligned(stage_q, 16) || !aligned(recv_q, 16) || !aligned(stage_scale, 4) ||
+        !aligned(recv_scale, 4))
+        return fail(EP_ERR_ALIGN, "ep_layout_dispatch_expand_fp8: stage_q and recv_q must be "
+                                  "16-byte aligned, the scales 4-byte aligned");
+    const ep::LayoutOut o{slot, expert_count, expert_offset, rank_count, rank_offset, stats};
+    return hip_status(ep::launch_layout_expand_fp8(*shape, stage_q, stage_scale, topk_idx,
+                                                   rank_slot, o, recv_q, recv_scale, stream),
+                      fn);
+}
+
 int ep_dispatch_expand_fp8(const ep_shape_t *shape, const uint8_t *stage_q,
                            const float *stage_scale, const int32_t *topk_idx,
                            const int32_t *slot, const int32_t *rank_slot, uint8_t *recv_q,

@@ -167,6 +167,67 @@ __global__ __launch_bounds__(kTileThreads, 8) void layout_expand_bf16_kernel(
     if (last) layout_finish<false>(TK, E, C, R, lds, m, o);
 }
 
+// The same for FP8: a lane copies one 16-byte chunk of codes per pair (a 1024-channel segment
+// per wavefront item), and the first lane of each 8-lane group (one 128-channel block) also
+// copies the block's scale.
+template <int KG, bool MULTI>
+__global__ __launch_bounds__(kTileThreads, 8) void layout_expand_fp8_kernel(
+    const u32x4 *__restrict__ stage_q, const float *__restrict__ stage_scale,
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ rank_slot, LayoutOut o,
+    u32x4 *__restrict__ recv_q, float *__restrict__ recv_scale, int T, int H, int E, int C,
+    int K, int R, int nbits, int lg_nc, int TT, int nseg)
+{
+    extern __shared__ __align__(16) int32_t lds[];
+    __shared__ int32_t rows[kTileThreads];
+    const LayoutLdsMap m = layout_lds_map(E, lg_nc);
+    const int TK = T * K;
+    const bool last = blockIdx.x == gridDim.x - 1;
+    const int t0 = blockIdx.x * TT;
+    const int nt = min(TT, T - t0);
+    const int wave = wave_uniform(threadIdx.x / kWave);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int nitems = nt * nseg;
+    const int EL = E / R, H16 = H / 16, NB = H / 128;
+    const TileIds ids = layout_tile_loads(idx, TK, t0 * K, TT * K);
+    layout_tile(ids, idx, TK, E, C, nbits, t0 * K, TT * K, last, lds, m, o.slot, rows);
+    for (int item = wave; item < nitems; item += kTileWaves) {
+        const int tl = item / nseg, seg = item - tl * nseg;
+        const int32_t *rs = rank_slot + (size_t)(t0 + tl) * R;
+        const int h0 = seg * (16 * kWave) + lane * 16;
+        const bool act = h0 < H;
+        const bool lead = act && (lane & 7) == 0;
+        const int cq = act ? h0 / 16 : 0, cs = act ? h0 / 128 : 0;
+        const int npg = MULTI ? (K + KG - 1) / KG : 1;
+        for (int pg = 0; pg < npg; ++pg) {
+            int r[KG];
+            token_rows<KG>(rows, tl, pg * KG, K, r);
+            u32x4 q[KG];
+            float sc[KG];
+#pragma unroll
+            for (int g = 0; g < KG; ++g) {
+                int sr = -1;
+                if (r[g] >= 0) {
+                    const int rk = (r[g] / C) / EL;
+                    const int p = wave_uniform(rs[rk]);
+                    sr = (unsigned)p < (unsigned)T ? rk * T + p : -1;
+                }
+                if (sr < 0) r[g] = -1;     // no staged row: the pair is not copied
+                const size_t row = (size_t)(sr >= 0 ? sr : 0);
+                q[g] = stage_q[row * H16 + cq];
+                sc[g] = stage_scale[row * NB + cs];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int g = 0; g < KG; ++g) {
+                if (r[g] < 0) continue;
+                if (act) recv_q[(size_t)r[g] * H16 + cq] = q[g];
+                if (lead) recv_scale[(size_t)r[g] * NB + cs] = sc[g];
+            }
+        }
+    }
+    if (last) layout_finish<false>(TK, E, C, R, lds, m, o);
+}
+
 // The packed layout and dispatch fused: every tile counts all pairs (ALL in layout_tile), so
 // each workgroup knows the packed offsets and copies its tokens to offset[e] + slot at once.
 template <int KG, int U, bool MULTI>
@@ -337,6 +398,26 @@ hipError_t launch_layout_expand_bf16(const ep_shape_t &s, const uint16_t *stage,
     const int nseg = ceil_div(H8, kWave);
     return launch_expand_u<1>(s, reinterpret_cast<const u32x4 *>(stage), idx, rank_slot, o,
                               reinterpret_cast<u32x4 *>(recv), H8, TT, nseg, stream);
+}
+
+hipError_t launch_layout_expand_fp8(const ep_shape_t &s, const uint8_t *stage_q,
+                                    const float *stage_scale, const int32_t *idx,
+                                    const int32_t *rank_slot, const LayoutOut &o, uint8_t *recv_q,
+                                    float *recv_scale, hipStream_t stream)
+{
+    const int TT = pick_tt(s.T, s.K, false);
+    const int nseg = ceil_div(s.H, 16 * kWave);
+    const dim3 grid(s.T > 0 ? ceil_div(s.T, TT) : 1), block(kTileThreads);
+    const int nbits = expert_bits(s.E), lg_nc = layout_lg_nc(s.E);
+    const size_t lds = layout_lds_bytes(s.E, lg_nc);
+    const u32x4 *sq = reinterpret_cast<const u32x4 *>(stage_q);
+    u32x4 *rq = reinterpret_cast<u32x4 *>(recv_q);
+#define EP_LAUNCH_LXQ(KG, MULTI)                                                                \
+    return launch(layout_expand_fp8_kernel<KG, MULTI>, grid, block, lds, stream, sq, stage_scale, \
+                  idx, rank_slot, o, rq, recv_scale, s.T, s.H, s.E, s.C, s.K, s.R, nbits, lg_nc,  \
+                  TT, nseg)
+    EP_BY_K(s.K, EP_LAUNCH_LXQ);
+#undef EP_LAUNCH_LXQ
 }
 
 hipError_t launch_layout_dispatch_fp8(const ep_shape_t &s, const uint16_t *x, const int32_t *idx,

@@ -67,6 +67,11 @@ hipError_t launch_layout_expand_bf16(const ep_shape_t &s, const uint16_t *stage,
                                      const int32_t *idx, const int32_t *rank_slot,
                                      const LayoutOut &o, uint16_t *recv, hipStream_t stream);
 
+hipError_t launch_layout_expand_fp8(const ep_shape_t &s, const uint8_t *stage_q,
+                                    const float *stage_scale, const int32_t *idx,
+                                    const int32_t *rank_slot, const LayoutOut &o, uint8_t *recv_q,
+                                    float *recv_scale, hipStream_t stream);
+
 hipError_t launch_layout_dispatch_fp8(const ep_shape_t &s, const uint16_t *x, const int32_t *idx,
                                       const LayoutOut &o, uint8_t *recv_q, float *recv_scale,
                                       hipStream_t stream);

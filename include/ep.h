@@ -341,6 +341,19 @@ int ep_layout_dispatch_expand(const ep_shape_t *shape, const uint16_t *stage,
                               hipStream_t stream);
 
 /*
+ * ep_layout_dispatch_expand_fp8 -- ep_layout and ep_dispatch_expand_fp8 in one launch, as
+ * ep_layout_dispatch_expand: the layout outputs, recv_q and recv_scale are bit-identical to
+ * those of the two calls, with their argument rules (stage_q and recv_q 16-byte aligned, the
+ * scales 4-byte aligned, H % 128 == 0).
+ */
+int ep_layout_dispatch_expand_fp8(const ep_shape_t *shape, const uint8_t *stage_q,
+                                  const float *stage_scale, const int32_t *topk_idx,
+                                  const int32_t *rank_slot, int32_t *slot, int32_t *expert_count,
+                                  int32_t *expert_offset, int32_t *rank_count,
+                                  int32_t *rank_offset, int32_t *stats, uint8_t *recv_q,
+                                  float *recv_scale, hipStream_t stream);
+
+/*
  * ep_dispatch_expand_fp8 -- stage 2 for FP8: codes and scales of the staged row copied to every
  * kept pair's row of recv_q / recv_scale. H % 128 == 0.
  */

@@ -1,5 +1,5 @@
 """GPU parity of the two-stage, rank-deduplicated path (ep_rank_layout, ep_dispatch_ranks[_fp8],
-ep_dispatch_expand[_fp8], ep_layout_dispatch_expand, ep_combine_ranks, ep_combine_reduce) against
+ep_dispatch_expand[_fp8], ep_layout_dispatch_expand[_fp8], ep_combine_ranks, ep_combine_reduce) against
 the oracle.
 
 Small shapes compare whole buffers bit for bit, with sentinels in every row a call must not
@@ -128,6 +128,16 @@ class TwoStage:
         oracle.dispatch_fp8(self.x, self.idx, self.slot, E, C, oq, os_)
         assert np.array_equal(G.to_np(rq), oq), "recv codes"
         assert np.array_equal(G.to_np(rs).view(np.uint32), os_.view(np.uint32)), "recv scales"
+        # the expert layout fused with the FP8 expansion
+        lq = torch.full((E, C, H), S8, dtype=torch.uint8, device=G.dev())
+        ls = torch.full((E, C, NB), SF, dtype=torch.float32, device=G.dev())
+        lx = B.ep_layout_dispatch_expand_fp8(sq, ss, self.case.idx_d, self.g["rank_slot"], lq, ls,
+                                             E, C)
+        torch.cuda.synchronize()
+        for k in LAYOUT_KEYS:
+            assert torch.equal(lx[k], self.case.g[k]), f"fused FP8 layout+expand {k}"
+        assert np.array_equal(G.to_np(lq), oq), "fused FP8 layout+expand codes"
+        assert np.array_equal(G.to_np(ls).view(np.uint32), os_.view(np.uint32)), "fused scales"
 
     def combine_full(self):
         T, H, R = self.T, self.H, self.R
@@ -220,7 +230,15 @@ def test_two_stage_workloads(name):
         B.ep_dispatch_fp8(c.x_d, c.idx_d, c.g["slot"], q1, s1, C)
         torch.cuda.synchronize()
         assert torch.equal(q1, q2) and torch.equal(s1.view(torch.int32), s2.view(torch.int32))
-        del sq, ss, q1, q2, s1, s2
+        del q2, s2
+        q3 = torch.full((E, C, H), S8, dtype=torch.uint8, device=G.dev())
+        s3 = torch.full((E, C, NB), SF, dtype=torch.float32, device=G.dev())
+        lx = B.ep_layout_dispatch_expand_fp8(sq, ss, c.idx_d, ts.g["rank_slot"], q3, s3, E, C)
+        torch.cuda.synchronize()
+        assert torch.equal(q1, q3) and torch.equal(s1.view(torch.int32), s3.view(torch.int32))
+        for k in LAYOUT_KEYS:
+            assert torch.equal(lx[k], c.g[k]), f"fused FP8 layout+expand {k}"
+        del sq, ss, q1, q3, s1, s3
     else:
         stage = torch.empty((R, T, H), dtype=torch.int16, device=G.dev())
         B.ep_dispatch_ranks(c.x_d, ts.g["rank_slot"], stage)
