@@ -32,13 +32,14 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 // fp32 -> bf16 pattern, round to nearest even. Adding 0x7FFF plus the kept LSB carries into
 // the upper half exactly when the dropped half is above the midpoint, or at it with an odd
-// LSB; overflow past the largest finite value carries into the infinity pattern. NaN is
-// returned quiet with its sign.
+// LSB; overflow past the largest finite value carries into the infinity pattern. Every NaN
+// gives the one quiet NaN 0x7FC0 (the sign and payload of a NaN that an fp32 sum produces are
+// not fixed by IEEE 754, so a NaN result is written as that single pattern).
 __device__ __forceinline__ uint32_t bf16_rne(float f)
 {
     uint32_t u = __float_as_uint(f);
     uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-    return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? ((u >> 16) | 0x40u) : r;
+    return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? 0x7FC0u : r;
 }
 
 // fp32 -> OCP E4M3 code, round to nearest even, saturating at +-448 (NaN -> S.1111.111).

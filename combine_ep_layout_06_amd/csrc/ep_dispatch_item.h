@@ -19,6 +19,12 @@
 // IEEE quotient wherever the code depends on it), and the hardware conversion encodes them. A
 // wavefront with a block whose amax is 0, below 2^-60 or not finite takes the plain path: one
 // IEEE division per element and the software encoder.
+//
+// Non-finite input: a NaN anywhere in a block makes its amax NaN (the integer max of the |x|
+// patterns puts every NaN above +inf and every finite value); a NaN amax gives the quiet NaN
+// 0x7FC00000 as the scale; every code carries x's own sign bit, so a NaN quotient (x / NaN,
+// +-inf / inf) encodes as sign(x) | 0x7F whatever sign the division gave it. An infinite amax
+// gives an infinite scale, and the finite elements of that block encode as signed zeros.
 #pragma once
 
 #include "ep_device.h"
@@ -168,9 +174,10 @@ __device__ __forceinline__ QuantPiece<U> cast_item_fp8(const RawPieceFp8<U> &r)
             m = max(m, (w[k] << 16) & 0x7FFFFFFFu);
             m = max(m, w[k] & 0x7FFF0000u);
         }
-        amax[u] = group8_max(__uint_as_float(m));   // |x| bits: integer order
+        amax[u] = group8_max(__uint_as_float(m));   // |x| bits: integer order, NaN on top
         p.act[u] = r.act[u];
-        p.scale[u] = amax[u] / 448.0f;
+        p.scale[u] = __float_as_uint(amax[u]) > 0x7F800000u ? __uint_as_float(0x7FC00000u)
+                                                            : amax[u] / 448.0f;
         // 2^-60 <= amax < inf in every piece with channels: |x / scale| <= 448 (1 + 2^-22),
         // inside the range where the hardware conversion is exact, and div_by_rcp's
         // remainders do not underflow (pieces past H hold zeros and store nothing)
@@ -200,9 +207,10 @@ __device__ __forceinline__ QuantPiece<U> cast_item_fp8(const RawPieceFp8<U> &r)
         } else {
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
-                const uint32_t code = (amax[u] == 0.0f)
-                                          ? ((__float_as_uint(f[k]) >> 24) & 0x80u)
-                                          : e4m3_rne_sat(f[k] / p.scale[u]);
+                const uint32_t sign = (__float_as_uint(f[k]) >> 24) & 0x80u;
+                const uint32_t code =
+                    (amax[u] == 0.0f) ? sign
+                                      : sign | (e4m3_rne_sat(f[k] / p.scale[u]) & 0x7Fu);
                 q[k / 4] |= code << (8 * (k % 4));
             }
         }

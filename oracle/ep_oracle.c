@@ -66,18 +66,27 @@ static uint32_t f32_bits(float f)
     return u;
 }
 
+static float f32_from_bits(uint32_t u)
+{
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
 /*
  * fp32 -> bf16, round to nearest, ties to even, by definition: take the two bf16 values that
  * bracket f (truncation toward zero, and the next one away from zero), compare the distances
  * in double precision (exact for fp32 operands), keep the nearer, on a tie keep the one whose
  * last mantissa bit is 0. Overflow past the largest finite bf16 rounds to infinity as IEEE
- * round-to-nearest does. NaN stays NaN (quiet, sign kept).
+ * round-to-nearest does. Every NaN gives the one quiet NaN 0x7FC0: the sign and payload of a
+ * NaN that an fp32 sum produces are not fixed by IEEE 754 and differ between processors, so
+ * an output that is NaN is written as that single pattern.
  */
 uint16_t oracle_bf16_rne(float f)
 {
     uint32_t u = f32_bits(f);
     if (isnan(f))
-        return (uint16_t)((u >> 16) | 0x0040u);
+        return 0x7FC0u;
     if (isinf(f))
         return (uint16_t)(u >> 16);
     uint16_t lo = (uint16_t)(u >> 16);            /* toward zero */
@@ -231,6 +240,16 @@ void oracle_dispatch(int T, int H, int E, int K, int C, const uint16_t *x,
  * If amax == 0 every x in the block is +-0 and q is that signed zero (scale = 0).
  * Then the q row and the scale row are written to every kept slot of t:
  *   recv_q[e][s][h] = q[h];  recv_scale[e][s][b] = scale_b.
+ *
+ * Non-finite input (the pages give no rule; this is the library's policy, so that both sides
+ * give the same bits):
+ *   - a NaN anywhere in the block makes amax NaN (NaN propagates through the max);
+ *   - a NaN amax gives the quiet NaN 0x7FC00000 as the scale (not x's payload);
+ *   - every code carries x's sign bit: the sign of a quotient is the exclusive-or of the
+ *     operands' signs, and the scale is never negative. IEEE 754 fixes that rule for every
+ *     result but NaN; it is applied to NaN quotients too, so a NaN quotient (x / NaN, or
+ *     +-inf / inf) encodes as sign(x) | 0x7F. An infinite amax gives an infinite scale, so the
+ *     finite elements of that block encode as signed zeros.
  */
 static void quantise_token(int H, const uint16_t *row, uint8_t *q, float *sc)
 {
@@ -238,14 +257,16 @@ static void quantise_token(int H, const uint16_t *row, uint8_t *q, float *sc)
         float amax = 0.0f;
         for (int h = 128 * b; h < 128 * b + 128; ++h) {
             float a = fabsf(oracle_bf16_to_f32(row[h]));
-            if (a > amax) amax = a;
+            if (isnan(a) || a > amax) amax = a;
+            if (isnan(amax)) break;
         }
-        float scale = amax / 448.0f;
+        float scale = isnan(amax) ? f32_from_bits(0x7FC00000u) : amax / 448.0f;
         sc[b] = scale;
         for (int h = 128 * b; h < 128 * b + 128; ++h) {
             float v = oracle_bf16_to_f32(row[h]);
-            q[h] = (amax == 0.0f) ? (uint8_t)((row[h] & 0x8000u) ? 0x80 : 0x00)
-                                  : oracle_e4m3_rne_sat(v / scale);
+            uint8_t sign = (row[h] & 0x8000u) ? 0x80 : 0x00;
+            q[h] = (amax == 0.0f) ? sign
+                                  : (uint8_t)(sign | (oracle_e4m3_rne_sat(v / scale) & 0x7F));
         }
     }
 }

@@ -372,3 +372,90 @@ def test_non_default_stream():
     s.synchronize()
     want = oracle.combine(y_host, case.idx, case.lay["slot"], case.w)
     assert np.array_equal(G.to_np(out).view(np.uint16), want)
+
+
+def _non_finite_x(T, H, seed):
+    """Token rows with NaN (both signs, with payloads) and +-inf planted in some 128-channel
+    blocks: blocks with a NaN, blocks with infinities only, blocks with both, and clean blocks
+    around them."""
+    rng = np.random.default_rng(seed)
+    x = W.f32_to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    nb = H // 128
+    for t in range(0, T, 3):
+        b = int(rng.integers(0, nb))
+        kind = t % 4
+        h = 128 * b + rng.integers(0, 128, size=3)
+        if kind == 0:
+            x[t, h[0]] = 0xFFC5                      # -NaN with a payload
+        elif kind == 1:
+            x[t, h[0]] = 0x7F80
+            x[t, h[1]] = 0xFF80                      # +inf and -inf, no NaN
+        elif kind == 2:
+            x[t, h[0]] = 0x7F80
+            x[t, h[1]] = 0x7FC1                      # inf and NaN together: the NaN rule
+        else:
+            x[t, 128 * b:128 * b + 128] = 0x7FC0     # a whole block of NaN
+    return x
+
+
+def test_fp8_non_finite_blocks():
+    """The NaN/inf policy (NaN propagates into the block's amax, a NaN amax gives the quiet NaN
+    scale, every code keeps x's sign, a NaN quotient encodes as sign | 0x7F) on every FP8
+    path: the one-stage dispatch, the fused layout + dispatch, the two-stage staging copy (and
+    its fused form) with the expansion, and the packed dispatch, against the oracle."""
+    print("[parity] FP8 non-finite blocks", flush=True)
+    T, H, E, K, C, R = 97, 1024, 12, 4, 40, 3
+    x = _non_finite_x(T, H, seed=41)
+    rng = np.random.default_rng(42)
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, K)).astype(np.float32)
+    case = G.Case(T, H, E, K, C, R, x, idx, w)
+    case.check_dispatch_fp8(full=True)
+    case.check_fused(fp8=True, full=True)
+    import test_gpu_two_stage as TS
+    ts = TS.TwoStage(T, H, E, K, C, R, idx, x, w, 0)
+    ts.dispatch_fp8_full()
+    import test_gpu_packed as PK
+    PK.run_case(idx, x, w, E, C, R, 16, fp8=True, seed=3)
+    # the policy really is exercised: NaN scales and NaN codes of both signs were produced
+    q = np.zeros((E, C, H), np.uint8)
+    sc = np.zeros((E, C, H // 128), np.float32)
+    oracle.dispatch_fp8(x, idx, case.lay["slot"], E, C, q, sc)
+    assert (sc.view(np.uint32) == 0x7FC00000).any() and (sc == np.inf).any()
+    assert (q == 0x7F).any() and (q == 0xFF).any()
+
+
+def test_combine_nan_and_inf_rows():
+    """Kept expert rows holding NaN (both signs, payloads) and +-inf: every output element
+    whose fp32 sum is NaN is the quiet NaN 0x7FC0, the rest as the oracle computes them, bit
+    for bit; also through the two-stage partial combine and reduce."""
+    print("[parity] combine with NaN/inf rows", flush=True)
+    T, H, E, K, C, R = 200, 512, 16, 4, 60, 4
+    case = G.Case.random(T, H, E, K, C, R, seed=43, lo=0, hi=E)
+    y_host, _ = case.make_y()
+    rng = np.random.default_rng(44)
+    i, s = G.kept_pairs(case.lay)
+    e = case.idx.reshape(-1)[i]
+    for k in rng.choice(len(i), size=60, replace=False):
+        h = rng.integers(0, H, size=2)
+        y_host[e[k], s[k], h[0]] = rng.choice([0x7FC0, 0xFFC0, 0x7FA3, 0x7F80, 0xFF80])
+        y_host[e[k], s[k], h[1]] = rng.choice([0x7F80, 0xFF80])
+    y = G.u16_dev(y_host)
+    out = B.ep_combine(y, case.idx_d, case.g["slot"], case.w_d, C)
+    torch.cuda.synchronize()
+    want = oracle.combine(y_host, case.idx, case.lay["slot"], case.w)
+    got = G.to_np(out).view(np.uint16)
+    assert (want == 0x7FC0).sum() > 20 and ((want & 0x7FFF) == 0x7F80).any()
+    assert np.array_equal(got, want)
+    rl = B.ep_rank_layout(case.idx_d, E, R)
+    part = B.ep_combine_ranks(y, case.idx_d, case.g["slot"], rl["rank_slot"], case.w_d, C)
+    out2 = B.ep_combine_reduce(part, rl["rank_slot"], K)
+    torch.cuda.synchronize()
+    orl = oracle.rank_layout(case.idx, E, R)
+    wp = oracle.combine_ranks(y_host, case.idx, case.lay["slot"], orl["rank_slot"], case.w)
+    sent = orl["rank_slot"] >= 0
+    t_i, r_i = np.nonzero(sent)
+    p_i = orl["rank_slot"][t_i, r_i]
+    assert np.array_equal(G.to_np(part).view(np.uint16)[r_i, p_i], wp[r_i, p_i])
+    assert np.array_equal(G.to_np(out2).view(np.uint16),
+                          oracle.combine_reduce(wp, orl["rank_slot"]))

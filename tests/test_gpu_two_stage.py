@@ -3,9 +3,10 @@ ep_dispatch_expand[_fp8], ep_layout_dispatch_expand[_fp8], ep_combine_ranks, ep_
 the oracle.
 
 Small shapes compare whole buffers bit for bit, with sentinels in every row a call must not
-touch. The full workloads compare the rank layout in full, the composed dispatch with the
-one-stage dispatch (itself checked against the oracle), and sampled output rows with the oracle's
-token-subset form of the two-stage combine.
+touch. The full workloads compare the rank layout in full, every staged row (bf16 and FP8) with
+the oracle's staging copy, the composed dispatch with the one-stage dispatch (itself checked
+against the oracle), and every partial row and every output element of the two-stage combine
+with the oracle.
 """
 import numpy as np
 import pytest
@@ -222,6 +223,16 @@ def test_two_stage_workloads(name):
         assert torch.equal(f["stage_scale"].view(R * T, -1)[rows].view(torch.int32),
                            ss.view(R * T, -1)[rows].view(torch.int32))
         del f
+        # every staged row against the oracle's staging copy
+        wq = np.empty((R, T, H), np.uint8)
+        ws = np.empty((R, T, NB), np.float32)
+        oracle.dispatch_ranks_fp8(ts.x, ts.rl["rank_slot"], wq, ws)
+        t_i, r_i = np.nonzero(ts.rl["rank_slot"] >= 0)
+        p_i = ts.rl["rank_slot"][t_i, r_i]
+        assert np.array_equal(G.to_np(sq)[r_i, p_i], wq[r_i, p_i]), "staged codes"
+        assert np.array_equal(G.to_np(ss)[r_i, p_i].view(np.uint32),
+                              ws[r_i, p_i].view(np.uint32)), "staged scales"
+        del wq, ws
         q2 = torch.full((E, C, H), S8, dtype=torch.uint8, device=G.dev())
         s2 = torch.full((E, C, NB), SF, dtype=torch.float32, device=G.dev())
         B.ep_dispatch_expand_fp8(sq, ss, c.idx_d, c.g["slot"], ts.g["rank_slot"], q2, s2, C)
@@ -265,24 +276,30 @@ def test_two_stage_workloads(name):
         for k in LAYOUT_KEYS:
             assert torch.equal(lx[k], c.g[k]), f"fused layout+expand {k}"
         del r3
-        # sampled staging rows are the token rows
+        # every staged row against the oracle's staging copy (and it is the token's row)
+        want_stage = np.empty((R, T, H), np.uint16)
+        oracle.dispatch_ranks(ts.x, ts.rl["rank_slot"], want_stage)
         t_i, r_i = np.nonzero(ts.rl["rank_slot"] >= 0)
-        pick = np.linspace(0, len(t_i) - 1, 257).astype(int)
-        rows = torch.from_numpy((r_i[pick] * T + ts.rl["rank_slot"][t_i[pick], r_i[pick]])
-                                .astype(np.int64)).to(G.dev())
-        got = G.to_np(stage.view(R * T, H).index_select(0, rows)).view(np.uint16)
-        assert np.array_equal(got, ts.x[t_i[pick]])
-        del stage, r1
+        p_i = ts.rl["rank_slot"][t_i, r_i]
+        got = G.to_np(stage).view(np.uint16)[r_i, p_i]
+        assert np.array_equal(got, want_stage[r_i, p_i]), "staged rows"
+        assert np.array_equal(want_stage[r_i, p_i], ts.x[t_i]), "oracle staging round trip"
+        del stage, r1, want_stage, got
     torch.cuda.empty_cache()
     y_host, y = c.make_y()
     part = B.ep_combine_ranks(y, c.idx_d, c.g["slot"], ts.g["rank_slot"], c.w_d, C)
     out = B.ep_combine_reduce(part, ts.g["rank_slot"], K)
     torch.cuda.synchronize()
-    tokens = np.unique(np.concatenate([[0, T - 1], np.linspace(0, T - 1, 61).astype(int)]))
-    want = oracle.combine_two_stage_tokens(tokens, y_host, ts.idx, ts.slot,
-                                           ts.rl["rank_slot"], ts.w)
-    got = G.to_np(out).view(np.uint16)[tokens]
-    assert np.array_equal(got, want)
+    # every partial row and every output element against the oracle
+    want_part = oracle.combine_ranks(y_host, ts.idx, ts.slot, ts.rl["rank_slot"], ts.w)
+    t_i, r_i = np.nonzero(ts.rl["rank_slot"] >= 0)
+    p_i = ts.rl["rank_slot"][t_i, r_i]
+    assert np.array_equal(G.to_np(part).view(np.uint16)[r_i, p_i], want_part[r_i, p_i]), \
+        "partial rows"
+    want = oracle.combine_reduce(want_part, ts.rl["rank_slot"])
+    del want_part
+    got = G.to_np(out).view(np.uint16)
+    assert np.array_equal(got, want), "combine_reduce"
     # against the one-stage combine at every element: the two results differ by the rounding
     # of each partial to bf16 plus the two final roundings, so
     #   |out2 - out1| <= 2^-8 * (sum_r |partial_r| + |out1| + |out2|) + 2^-20 * sum_r |partial_r|

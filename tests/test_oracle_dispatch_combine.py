@@ -62,8 +62,8 @@ def test_dispatch_round_trip_each_kept_pair_once():
 
 
 def test_fp8_dispatch_properties():
-    """Per token and 128-channel block: the scale times 448 is the block amax to within one
-    fp32 rounding; the amax element encodes to +-448; q is torch's e4m3 cast of x / scale;
+    """Per token and 128-channel block: the scale is amax / 448 by one IEEE fp32 division, bit
+    for bit; the amax element encodes to +-448; q is torch's e4m3 cast of x / scale;
     the dequantised row is within the 3-bit-mantissa bound; every kept slot gets the same row."""
     cfg = W.get_config("decode_fp8")
     inp = W.make_inputs(cfg)
@@ -81,8 +81,9 @@ def test_fp8_dispatch_properties():
         for j in range(1, cfg.K):
             e, s = inp["topk_idx"][t, j], lay["slot"][t, j]
             assert np.array_equal(q[e, s], qrow) and np.array_equal(sc[e, s], scale)
-        rel = np.abs(scale.astype(np.float64) * 448 - amax[t]) / amax[t]
-        assert (rel <= 2.0 ** -23).all()
+        # one IEEE fp32 division (numpy's float32 division), bit for bit
+        want_scale = (amax[t].astype(np.float32) / np.float32(448.0)).astype(np.float32)
+        assert np.array_equal(scale.view(np.uint32), want_scale.view(np.uint32))
         blocks = qrow.reshape(H // 128, 128)
         arg = np.abs(xf[t]).argmax(axis=1)
         assert ((blocks[np.arange(H // 128), arg] & 0x7F) == 0x7E).all()
@@ -92,6 +93,113 @@ def test_fp8_dispatch_properties():
         assert np.array_equal(blocks, want)
     # the outlier workload really exercises large block maxima
     assert amax.max() > 100
+
+
+def test_fp8_scale_is_the_ieee_quotient_for_every_bf16_amax():
+    """scale = amax / 448 by one IEEE fp32 division, bit for bit, for every positive finite
+    bf16 value as a block's amax (numpy's float32 division is that operation). A form that
+    multiplies by a rounded 1/448 differs from it on a large share of these values."""
+    amax_bits = np.arange(0x0001, 0x7F80, dtype=np.uint16)         # positive finite bf16
+    nb = 128                                                        # blocks per token
+    T = -(-len(amax_bits) // nb)
+    H = nb * 128
+    rng = np.random.default_rng(11)
+    x = np.zeros((T, nb, 128), dtype=np.uint16)
+    pos = rng.integers(0, 128, size=T * nb)
+    flat = np.zeros(T * nb, dtype=np.uint16)
+    flat[:len(amax_bits)] = amax_bits
+    sign = rng.integers(0, 2, size=T * nb).astype(np.uint16) << 15
+    x.reshape(T * nb, 128)[np.arange(T * nb), pos] = flat | np.where(flat > 0, sign, 0)
+    x = x.reshape(T, H)
+    idx = np.zeros((T, 1), dtype=np.int32)
+    lay = oracle.layout(idx, 1, T, 1)
+    q = np.zeros((1, T, H), dtype=np.uint8)
+    sc = np.zeros((1, T, nb), dtype=np.float32)
+    oracle.dispatch_fp8(x, idx, lay["slot"], 1, T, q, sc)
+    amax = W.bf16_bits_to_f32(flat)
+    want = amax / np.float32(448.0)
+    assert want.dtype == np.float32
+    assert np.array_equal(sc.reshape(-1).view(np.uint32), want.view(np.uint32))
+    # the multiply-by-reciprocal form would differ on many of these blocks
+    rcp = amax * (np.float32(1.0) / np.float32(448.0))
+    assert (rcp.view(np.uint32) != want.view(np.uint32)).sum() > 1000
+    # codes: torch's e4m3 cast of x / scale wherever the quotient is in [-448, 448]
+    xf = W.bf16_bits_to_f32(x).reshape(T * nb, 128)
+    s = sc.reshape(T * nb, 1)
+    ok = (s[:, 0] > 0)
+    v = (xf[ok] / s[ok]).astype(np.float32)
+    inr = np.abs(v) <= 448.0
+    want_q = torch.from_numpy(np.ascontiguousarray(np.where(inr, v, 0))).to(torch.float8_e4m3fn) \
+        .view(torch.uint8).numpy()
+    got_q = q.reshape(T * nb, 128)[ok]
+    assert np.array_equal(got_q[inr], want_q[inr])
+    assert ((got_q[~inr] & 0x7F) == 0x7E).all()
+
+
+def test_fp8_non_finite_policy():
+    """Non-finite input, as the library defines it: a NaN in a block makes the block's scale
+    the quiet NaN 0x7FC00000 and every code sign(x) | 0x7F; an infinite amax gives an infinite
+    scale, signed zeros for the finite elements and sign(x) | 0x7F for the infinite ones; the
+    other blocks of the token are untouched by either."""
+    H = 512
+    rng = np.random.default_rng(12)
+    x = W.f32_to_bf16_bits(rng.standard_normal((2, H), dtype=np.float32))
+    ref = x.copy()
+    x[0, 3] = 0xFFC1                       # -NaN with a payload in block 0
+    x[0, 200] = 0x7F80                     # +inf in block 1
+    x[0, 201] = 0xFF80                     # -inf in block 1
+    x[0, 300] = 0x7F80                     # +inf and a NaN in block 2: the NaN rule wins
+    x[0, 301] = 0x7FC0
+    x[1] = ref[1]
+    idx = np.array([[0], [0]], dtype=np.int32)
+    lay = oracle.layout(idx, 1, 2, 1)
+    q = np.zeros((1, 2, H), dtype=np.uint8)
+    sc = np.zeros((1, 2, H // 128), dtype=np.float32)
+    oracle.dispatch_fp8(x, idx, lay["slot"], 1, 2, q, sc)
+    sign = ((x[0] >> 8) & 0x80).astype(np.uint8)
+    assert sc[0, 0, 0].view(np.uint32) == 0x7FC00000
+    assert np.array_equal(q[0, 0, :128], sign[:128] | 0x7F)
+    assert sc[0, 0, 1] == np.inf
+    b1 = q[0, 0, 128:256]
+    assert b1[200 - 128] == 0x7F and b1[201 - 128] == 0xFF
+    fin = np.ones(128, bool)
+    fin[[200 - 128, 201 - 128]] = False
+    assert np.array_equal(b1[fin], sign[128:256][fin])          # signed zeros
+    assert sc[0, 0, 2].view(np.uint32) == 0x7FC00000
+    assert np.array_equal(q[0, 0, 256:384], sign[256:384] | 0x7F)
+    # block 3 of token 0 and all of token 1 are the finite quantisation of their own values
+    q2 = np.zeros((1, 2, H), dtype=np.uint8)
+    sc2 = np.zeros((1, 2, H // 128), dtype=np.float32)
+    oracle.dispatch_fp8(ref, idx, lay["slot"], 1, 2, q2, sc2)
+    assert np.array_equal(q[0, 0, 384:], q2[0, 0, 384:]) and sc[0, 0, 3] == sc2[0, 0, 3]
+    assert np.array_equal(q[0, 1], q2[0, 1]) and np.array_equal(sc[0, 1], sc2[0, 1])
+
+
+def test_combine_nan_policy():
+    """A NaN term, or +inf and -inf in one sum, makes that output element the quiet NaN 0x7FC0
+    (sign and payload of the inputs' NaN do not carry over); other elements are unchanged."""
+    c = small_case(T=8, H=64, E=4, K=2, C=8, R=2, seed=13)
+    rng = np.random.default_rng(14)
+    y = W.f32_to_bf16_bits(rng.standard_normal((c["E"], c["C"], c["H"]), dtype=np.float32))
+    base = oracle.combine(y, c["idx"], c["slot"], c["w"])
+    kept = np.argwhere(c["slot"] >= 0)
+    (t0, j0), (t1, j1) = kept[0], kept[-1]
+    y2 = y.copy()
+    y2[c["idx"][t0, j0], c["slot"][t0, j0], 5] = 0xFFC3            # -NaN with a payload
+    out = oracle.combine(y2, c["idx"], c["slot"], c["w"])
+    assert out[t0, 5] == 0x7FC0
+    mask = np.ones_like(out, bool)
+    mask[t0, 5] = False
+    assert np.array_equal(out[mask], base[mask])
+    both = [p for p in kept if p[0] == t1]
+    if len(both) >= 2:
+        (ta, ja), (tb, jb) = both[0], both[1]
+        y3 = y.copy()
+        y3[c["idx"][ta, ja], c["slot"][ta, ja], 7] = 0x7F80
+        y3[c["idx"][tb, jb], c["slot"][tb, jb], 7] = 0xFF80
+        w = np.abs(c["w"]) + np.float32(0.5)
+        out3 = oracle.combine(y3, c["idx"], c["slot"], w)
+        assert out3[ta, 7] == 0x7FC0
 
 
 def test_fp8_zero_block_gives_signed_zero():

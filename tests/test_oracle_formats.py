@@ -54,10 +54,8 @@ def test_bf16_random_patterns_and_specials():
     got, want = oracle.bf16_rne(v), torch_bf16(v)
     nan = np.isnan(v)
     assert np.array_equal(got[~nan], want[~nan])
-    # NaN stays NaN with its sign (torch's own NaN payload may differ)
-    g = got[nan]
-    assert ((g & 0x7F80) == 0x7F80).all() and ((g & 0x7F) != 0).all()
-    assert np.array_equal(g >> 15, (bits[nan] >> 31).astype(np.uint16))
+    # every NaN gives the one quiet NaN 0x7FC0 (torch's CPU cast writes its own NaN pattern)
+    assert nan.any() and (got[nan] == 0x7FC0).all()
 
 
 def test_bf16_ties_to_even():
