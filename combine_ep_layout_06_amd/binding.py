@@ -33,12 +33,23 @@ EXPORTED = ("ep_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_layout_dispatch",
             "ep_layout_dispatch_expand_fp8",
             "ep_combine_ranks", "ep_combine_reduce", "ep_layout_packed", "ep_dispatch_packed",
             "ep_dispatch_packed_fp8", "ep_layout_dispatch_packed", "ep_layout_dispatch_packed_fp8",
-            "ep_combine_packed", "ep_error_string", "ep_last_error", "ep_version")
+            "ep_combine_packed", "ep_check_e4m3_conversion", "ep_last_launches",
+            "ep_error_string", "ep_last_error", "ep_version")
 
 
 class EpShape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("K", ctypes.c_int32), ("C", ctypes.c_int32), ("R", ctypes.c_int32)]
+
+
+class EpLaunchRecord(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_char_p),
+                ("grid_x", ctypes.c_uint32), ("grid_y", ctypes.c_uint32),
+                ("grid_z", ctypes.c_uint32), ("block_x", ctypes.c_uint32),
+                ("block_y", ctypes.c_uint32), ("block_z", ctypes.c_uint32),
+                ("dynamic_lds_bytes", ctypes.c_uint32), ("static_lds_bytes", ctypes.c_uint32),
+                ("vgprs", ctypes.c_int32), ("private_bytes", ctypes.c_uint32),
+                ("max_threads_per_block", ctypes.c_int32)]
 
 
 class EpError(RuntimeError):
@@ -88,6 +99,8 @@ def load_library():
         L.ep_combine_packed.argtypes = [sp, i32] + [vp] * 7
         L.ep_layout_dispatch_packed.argtypes = [sp, i32, i32] + [vp] * 10
         L.ep_layout_dispatch_packed_fp8.argtypes = [sp, i32, i32] + [vp] * 11
+        L.ep_check_e4m3_conversion.argtypes = [ctypes.c_uint32, ctypes.c_uint32, vp, vp, vp]
+        L.ep_last_launches.argtypes = [ctypes.POINTER(EpLaunchRecord), ctypes.c_int]
         for fn in EXPORTED:
             if fn.startswith("ep_") and fn not in ("ep_error_string", "ep_last_error",
                                                    "ep_version"):
@@ -762,3 +775,58 @@ def ep_combine_packed(y: torch.Tensor, topk_idx: torch.Tensor, slot: torch.Tenso
           stream=stream)
     return out
 
+
+
+def ep_check_e4m3_conversion(first_pattern: int, count: int, *, device=None, stream=None):
+    """Compare the FP8 cast's two E4M3 encoders (the hardware conversion and the software
+    one) on the fp32 bit patterns [first_pattern, first_pattern + count) on the current
+    device. Returns (mismatches, smallest mismatching pattern or None) after synchronising."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    res = torch.empty(2, dtype=torch.int32, device=dev)
+    _require_current("ep_check_e4m3_conversion", dev)
+    L = load_library()
+    rc = L.ep_check_e4m3_conversion(first_pattern, count, res.data_ptr(), res.data_ptr() + 4,
+                                    _stream(stream))
+    _check("ep_check_e4m3_conversion", rc)
+    torch.cuda.synchronize(dev)
+    n, first = (int(v) & 0xFFFFFFFF for v in res.cpu().tolist())
+    return n, (None if n == 0 else first)
+
+
+_resources = None
+
+
+def kernel_resources() -> dict:
+    """The compiler's resource figures per kernel symbol, written by the build beside the
+    library (empty if that file is missing)."""
+    global _resources
+    if _resources is None:
+        import json
+        path = os.path.join(os.path.dirname(library_path()), "kernel_resources.json")
+        try:
+            with open(path) as f:
+                _resources = json.load(f).get("kernels", {})
+        except (OSError, ValueError):
+            _resources = {}
+    return _resources
+
+
+def last_launches() -> list:
+    """The kernel launches of this thread's most recent library call: per launch the kernel
+    symbol, grid and workgroup sizes, LDS, and the register figures of the runtime and of the
+    compiler's report."""
+    L = load_library()
+    recs = (EpLaunchRecord * 8)()
+    n = L.ep_last_launches(recs, 8)
+    res = kernel_resources()
+    out = []
+    for r in recs[:min(n, 8)]:
+        name = (r.kernel or b"").decode()
+        d = {"kernel": name, "grid": [r.grid_x, r.grid_y, r.grid_z],
+             "block": [r.block_x, r.block_y, r.block_z],
+             "dynamic_lds_bytes": r.dynamic_lds_bytes, "static_lds_bytes": r.static_lds_bytes,
+             "vgprs": r.vgprs, "private_bytes": r.private_bytes}
+        if name in res:
+            d["compiler"] = res[name]
+        out.append(d)
+    return out

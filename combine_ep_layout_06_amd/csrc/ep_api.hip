@@ -12,6 +12,16 @@
 #define EP_VERSION_STRING "0.1.0"
 #endif
 
+namespace ep {
+
+LaunchLog &launch_log()
+{
+    thread_local LaunchLog log;
+    return log;
+}
+
+}  // namespace ep
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -25,8 +35,10 @@ int fail(int code, const std::string &what)
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Shape rules common to every call. On failure returns a negative code and records why.
+// Every entry point that launches kernels starts here, so this also clears the launch log.
 int check_shape(const ep_shape_t *s, const char *fn)
 {
+    ep::launch_log().n = 0;
     std::string f(fn);
     if (!s) return fail(EP_ERR_INVALID, f + ": shape is NULL");
     if (s->T < 0 || s->H < 1 || s->E < 1 || s->K < 1 || s->C < 1 || s->R < 1)
@@ -531,6 +543,54 @@ int ep_combine_packed(const ep_shape_t *shape, int32_t rows, const uint16_t *y,
     return hip_status(ep::launch_combine(*shape, y, topk_idx, slot, topk_w, out, stream,
                                          ep::RowMap{packed_offset, rows}),
                       fn);
+}
+
+int ep_check_e4m3_conversion(uint32_t first_pattern, uint32_t count, uint32_t *mismatches,
+                             uint32_t *first_mismatch, hipStream_t stream)
+{
+    ep::launch_log().n = 0;
+    if (!mismatches || !first_mismatch)
+        return fail(EP_ERR_INVALID, "ep_check_e4m3_conversion: NULL required pointer");
+    if ((uint64_t)first_pattern + count > (1ull << 32))
+        return fail(EP_ERR_INVALID,
+                    "ep_check_e4m3_conversion: first_pattern + count exceeds 2^32");
+    if (!aligned(mismatches, 4) || !aligned(first_mismatch, 4))
+        return fail(EP_ERR_ALIGN, "ep_check_e4m3_conversion: outputs must be 4-byte aligned");
+    return hip_status(ep::launch_check_e4m3(first_pattern, count, mismatches, first_mismatch,
+                                            stream),
+                      "ep_check_e4m3_conversion");
+}
+
+int ep_last_launches(ep_launch_record_t *records, int capacity)
+{
+    const ep::LaunchLog &log = ep::launch_log();
+    const int n = log.n < ep::kLaunchLogCap ? log.n : ep::kLaunchLogCap;
+    for (int k = 0; records && k < n && k < capacity; ++k) {
+        const ep::LaunchEntry &e = log.e[k];
+        ep_launch_record_t &r = records[k];
+        const char *name = hipKernelNameRefByPtr(e.kernel, nullptr);
+        r.kernel = name ? name : "";
+        r.grid_x = e.grid.x;
+        r.grid_y = e.grid.y;
+        r.grid_z = e.grid.z;
+        r.block_x = e.block.x;
+        r.block_y = e.block.y;
+        r.block_z = e.block.z;
+        r.dynamic_lds_bytes = (uint32_t)e.shmem;
+        hipFuncAttributes a{};
+        if (hipFuncGetAttributes(&a, e.kernel) == hipSuccess) {
+            r.static_lds_bytes = (uint32_t)a.sharedSizeBytes;
+            r.vgprs = a.numRegs;
+            r.private_bytes = (uint32_t)a.localSizeBytes;
+            r.max_threads_per_block = a.maxThreadsPerBlock;
+        } else {
+            r.static_lds_bytes = 0;
+            r.vgprs = -1;
+            r.private_bytes = 0;
+            r.max_threads_per_block = -1;
+        }
+    }
+    return log.n;
 }
 
 const char *ep_error_string(int code)

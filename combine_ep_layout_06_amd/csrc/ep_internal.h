@@ -20,11 +20,29 @@ inline void fill_argv(void **argv, std::tuple<KArgs...> &t, std::index_sequence<
     ((argv[I] = static_cast<void *>(&std::get<I>(t))), ...);
 }
 
+// The launches of the calling thread's most recent entry-point call (ep_last_launches): the
+// argument checks of each call clear it, and launch() appends to it.
+struct LaunchEntry {
+    const void *kernel;
+    dim3 grid, block;
+    size_t shmem;
+};
+constexpr int kLaunchLogCap = 8;
+struct LaunchLog {
+    int n = 0;
+    LaunchEntry e[kLaunchLogCap];
+};
+LaunchLog &launch_log();
+
 template <typename... KArgs, typename... Args>
 inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
                          hipStream_t stream, Args... args)
 {
     static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+    LaunchLog &log = launch_log();
+    if (log.n < kLaunchLogCap)
+        log.e[log.n] = LaunchEntry{reinterpret_cast<const void *>(kernel), grid, block, shmem};
+    ++log.n;
     std::tuple<KArgs...> typed(static_cast<KArgs>(args)...);
     void *argv[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
     fill_argv(argv, typed, std::index_sequence_for<KArgs...>{});
@@ -123,5 +141,9 @@ hipError_t launch_combine_ranks(const ep_shape_t &s, const uint16_t *y, const in
 
 hipError_t launch_combine_reduce(const ep_shape_t &s, const uint16_t *part,
                                  const int32_t *rank_slot, uint16_t *out, hipStream_t stream);
+
+// self-check of the E4M3 encoders
+hipError_t launch_check_e4m3(uint32_t first_pattern, uint32_t n, uint32_t *count,
+                             uint32_t *first, hipStream_t stream);
 
 }  // namespace ep

@@ -121,9 +121,14 @@ int ep_dispatch(const ep_shape_t *shape, const uint16_t *x, const int32_t *topk_
  * Then for every pair with 0 <= e < E and 0 <= slot[i] < C:
  *     recv_q[e][slot[i]][:] = q row,  recv_scale[e][slot[i]][:] = the H/128 scales.
  *
- *   x          [T*H]         uint16 (bf16) in, 16-byte aligned; finite values
+ *   x          [T*H]         uint16 (bf16) in, 16-byte aligned
  *   recv_q     [E*C*H]       uint8 out, 16-byte aligned
  *   recv_scale [E*C*(H/128)] float out, 4-byte aligned
+ *
+ * Non-finite x (the library's policy; every FP8 path follows it): a NaN in a block makes its
+ * amax NaN and its scale the quiet NaN 0x7FC00000; every code carries x's own sign bit, so a
+ * quotient that is NaN (x / NaN, +-inf / inf) encodes as sign(x) | 0x7F; an infinite amax gives
+ * an infinite scale, and the block's finite values encode as signed zeros.
  *
  * Requires H % 128 == 0 and K <= EP_MAX_TOPK (else EP_ERR_UNSUPPORTED). Bit-exact.
  */
@@ -172,9 +177,10 @@ int ep_layout_dispatch_fp8(const ep_shape_t *shape, const uint16_t *x, const int
  *     out[t][h] = bf16_rne(acc), acc = +0.0f, then for j = 0 .. K-1 ascending, for each pair
  *     with 0 <= e < E and 0 <= slot < C:  acc = fmaf(topk_w[i], y[e][slot][h], acc)
  * Pairs that were dropped, unrouted or invalid contribute nothing; a token with none gives +0.
+ * An element whose sum is NaN is written as the quiet NaN 0x7FC0 (whatever the sign and payload
+ * of the NaNs that produced it; the same holds for every bf16 result of the library).
  * Requires H % 8 == 0 and K <= EP_MAX_TOPK (else EP_ERR_UNSUPPORTED). Deterministic; every
- * fp32 step is the one
- * written above, so the result is bit-reproducible.
+ * fp32 step is the one written above, so the result is bit-reproducible.
  */
 int ep_combine(const ep_shape_t *shape, const uint16_t *y, const int32_t *topk_idx,
                const int32_t *slot, const float *topk_w, uint16_t *out, hipStream_t stream);
@@ -382,6 +388,49 @@ int ep_combine_ranks(const ep_shape_t *shape, const uint16_t *y, const int32_t *
  */
 int ep_combine_reduce(const ep_shape_t *shape, const uint16_t *part, const int32_t *rank_slot,
                       uint16_t *out, hipStream_t stream);
+
+/*
+ * ep_check_e4m3_conversion -- self-check of the two OCP E4M3 encoders of the FP8 dispatch on
+ * the current device.
+ *
+ * The FP8 cast (ep_dispatch_fp8 and every call that quantises) encodes its quotients x / scale
+ * with gfx950's packed fp32 -> E4M3 conversion instruction whenever every block amax of a
+ * wavefront's rows is finite and at least 2^-60; then every quotient lies in
+ * [-448 (1 + 2^-22), 448 (1 + 2^-22)]. Otherwise it uses a software encoder: round to nearest
+ * even, saturating at +-448, NaN -> S.1111.111 (OFP8 specification rev. 1.0, "satfinite"
+ * conversion). The fast path is right only where the two agree. This call compares them on
+ * every fp32 bit pattern u in [first_pattern, first_pattern + count) (first_pattern + count
+ * <= 2^32, else EP_ERR_INVALID):
+ *   mismatches     [1] uint32 device out  number of patterns whose two codes differ
+ *   first_mismatch [1] uint32 device out  the smallest such pattern (0xFFFFFFFF if none)
+ * Both 4-byte aligned (else EP_ERR_ALIGN). Enqueued on `stream` like every other call; the
+ * results are there once the stream reaches them.
+ */
+int ep_check_e4m3_conversion(uint32_t first_pattern, uint32_t count, uint32_t *mismatches,
+                             uint32_t *first_mismatch, hipStream_t stream);
+
+/*
+ * ep_last_launches -- the kernel launches of the calling thread's most recent call (any entry
+ * point above that computes), for recording launch shapes beside measurements (the grid and
+ * workgroup sizes a benchmark ran with; awsome-distributed-ai PR #1238, review item 4).
+ * Fills up to `capacity` records and returns the number of launches the call made (0 if its
+ * arguments were rejected). `kernel` points to the runtime's static copy of the kernel's
+ * symbol name (its template arguments give the pair-group size and chunks per lane);
+ * vgprs, static_lds_bytes, private_bytes and max_threads_per_block come from
+ * hipFuncGetAttributes (-1 if the runtime did not give them). Host memory; no GPU work.
+ */
+typedef struct ep_launch_record {
+    const char *kernel;
+    uint32_t grid_x, grid_y, grid_z;        /* workgroups */
+    uint32_t block_x, block_y, block_z;     /* lanes per workgroup */
+    uint32_t dynamic_lds_bytes;             /* LDS requested at launch */
+    uint32_t static_lds_bytes;              /* LDS the kernel declares */
+    int32_t vgprs;                          /* vector registers per lane */
+    uint32_t private_bytes;                 /* scratch per lane (0: no spills to memory) */
+    int32_t max_threads_per_block;
+} ep_launch_record_t;
+
+int ep_last_launches(ep_launch_record_t *records, int capacity);
 
 /* Static text for an EP_* code. */
 const char *ep_error_string(int code);

@@ -143,6 +143,62 @@ def test_two_stage_calls_reject_bad_arguments(lib):
     assert rlq(shape(), A16, A16, A16, A16, None, A16, None) == B.EP_ERR_INVALID
 
 
+def test_fused_layout_expand_calls_reject_bad_arguments(lib):
+    """ep_layout_dispatch_expand[_fp8]: the layout's rules, the two-stage rules and the
+    alignment of every row buffer."""
+    lx, lq = lib.ep_layout_dispatch_expand, lib.ep_layout_dispatch_expand_fp8
+    lay = (A16,) * 6                  # slot, count, offset, rank_count, rank_offset, stats
+    # stage, topk_idx, rank_slot, layout outputs, recv
+    assert lx(shape(E=128, R=128), A16, A16, A16, *lay, A16, None) == B.EP_ERR_UNSUPPORTED
+    assert "EP_MAX_RANKS" in lib.ep_last_error().decode()
+    assert lx(shape(), A16 + 2, A16, A16, *lay, A16, None) == B.EP_ERR_ALIGN       # stage
+    assert lx(shape(), A16, A16 + 4, A16, *lay, A16, None) == B.EP_ERR_ALIGN       # topk_idx
+    assert lx(shape(), A16, A16, A16, *lay, A16 + 8, None) == B.EP_ERR_ALIGN       # recv
+    assert lx(shape(), None, A16, A16, *lay, A16, None) == B.EP_ERR_INVALID        # stage
+    assert lx(shape(), A16, A16, None, *lay, A16, None) == B.EP_ERR_INVALID        # rank_slot
+    assert lx(shape(), A16, A16, A16, *lay, None, None) == B.EP_ERR_INVALID        # recv
+    assert lx(shape(), A16, A16, A16, None, *lay[1:], A16, None) == B.EP_ERR_INVALID  # slot
+    assert lx(shape(H=12), A16, A16, A16, *lay, A16, None) == B.EP_ERR_UNSUPPORTED
+    assert lx(shape(E=2048, R=16), A16, A16, A16, *lay, A16, None) == B.EP_ERR_UNSUPPORTED
+    # stage_q, stage_scale, topk_idx, rank_slot, layout outputs, recv_q, recv_scale
+    assert lq(shape(E=128, R=128), A16, A16, A16, A16, *lay, A16, A16,
+              None) == B.EP_ERR_UNSUPPORTED
+    assert lq(shape(H=1000), A16, A16, A16, A16, *lay, A16, A16, None) == B.EP_ERR_UNSUPPORTED
+    assert lq(shape(), A16 + 8, A16, A16, A16, *lay, A16, A16, None) == B.EP_ERR_ALIGN
+    assert lq(shape(), A16, A16 + 2, A16, A16, *lay, A16, A16, None) == B.EP_ERR_ALIGN
+    assert lq(shape(), A16, A16, A16, A16, *lay, A16 + 8, A16, None) == B.EP_ERR_ALIGN
+    assert lq(shape(), A16, A16, A16, A16, *lay, A16, A16 + 2, None) == B.EP_ERR_ALIGN
+    assert lq(shape(), A16, None, A16, A16, *lay, A16, A16, None) == B.EP_ERR_INVALID
+    assert lq(shape(), A16, A16, A16, A16, *lay, A16, None, None) == B.EP_ERR_INVALID
+    assert lq(shape(T=1 << 28, K=1, R=16), A16, A16, A16, A16, *lay, A16, A16,
+              None) == B.EP_ERR_UNSUPPORTED
+
+
+def test_check_e4m3_conversion_rejects_bad_arguments(lib):
+    chk = lib.ep_check_e4m3_conversion
+    assert chk(0, 16, None, A16, None) == B.EP_ERR_INVALID
+    assert chk(0, 16, A16, None, None) == B.EP_ERR_INVALID
+    assert chk(0xFFFFFFF0, 17, A16, A16 + 4, None) == B.EP_ERR_INVALID       # past 2^32
+    assert "2^32" in lib.ep_last_error().decode()
+    assert chk(0, 16, A16 + 2, A16, None) == B.EP_ERR_ALIGN
+
+
+def test_last_launches_empty_after_a_rejected_call(lib):
+    assert lib.ep_layout(shape(T=-1), A16, A16, A16, A16, None, None, A16, None) == B.EP_ERR_INVALID
+    assert lib.ep_last_launches(None, 0) == 0
+    assert B.last_launches() == []
+
+
+def test_kernel_resources_of_the_build():
+    """The build's resource report names the library's kernels with their register counts."""
+    res = B.kernel_resources()
+    if not res:
+        pytest.skip("kernel_resources.json not built (build() writes it)")
+    fused = [k for k in res if "layout_dispatch_fp8_kernel" in k]
+    assert fused and all(res[k]["sgprs"] > 0 and res[k]["vgprs"] > 0 for k in fused)
+    assert all(res[k]["scratch_bytes"] == 0 for k in res), "a kernel spills to scratch memory"
+
+
 def test_fused_packed_calls_reject_bad_arguments(lib):
     ldp, ldq = lib.ep_layout_dispatch_packed, lib.ep_layout_dispatch_packed_fp8
     ok = (A16,) * 8                                # x, topk_idx, slot, count, offset, rc, ro, stats
