@@ -29,6 +29,12 @@
 #ifndef EP_PACKED_TT
 #define EP_PACKED_TT 0       // tokens per tile of the fused packed kernels (0 = as EP_FUSED_TT)
 #endif
+// Wavefronts per SIMD the FP8 fused kernel is compiled to fit. 8 (two 1024-lane workgroups per
+// CU) holds it to 78 scalar registers (22 of them spilled to vector-register lanes) and 63
+// VGPRs; unbounded it takes 102 scalar registers and one workgroup per CU.
+#ifndef EP_FUSED_FP8_WAVES
+#define EP_FUSED_FP8_WAVES 8
+#endif
 
 namespace ep {
 
@@ -65,7 +71,7 @@ __global__ __launch_bounds__(kTileThreads) void layout_dispatch_bf16_kernel(
 }
 
 template <int KG, int U, bool MULTI>
-__global__ __launch_bounds__(kTileThreads) void layout_dispatch_fp8_kernel(
+__global__ __launch_bounds__(kTileThreads, EP_FUSED_FP8_WAVES) void layout_dispatch_fp8_kernel(
     const u32x4 *__restrict__ x, const int32_t *__restrict__ idx, LayoutOut o,
     u32x4 *__restrict__ recv_q, float *__restrict__ recv_scale, int T, int H, int E, int C,
     int K, int R, int nbits, int lg_nc, int TT, int nseg)
@@ -290,13 +296,14 @@ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // Tokens per tile, with TT*K a multiple of 4 (tile starts stay 16-byte aligned in topk_idx)
 // and TT*K <= 1024 pairs. Small batches use small tiles, about 256 of them, so more workgroups
 // and CUs share the copies (measured on MI355X at T = 128: one token per tile 12.5 us per
-// single-shot bf16 step against 13.3 us with four); on large ones (T = 4096) bf16 rows do best
-// at 8 tokens per tile (two workgroups per CU, one copying while the other is in its layout),
-// FP8 rows at 16; at T = 2048 bf16 takes 4 (30.5 against 30.9 us per step with 8).
+// single-shot bf16 step against 13.3 us with four); on large ones (T = 4096) both dtypes do
+// best at 8 tokens per tile, two workgroups per CU (FP8 at T = 4096, E = 96: 18.2 us, against
+// 19.3 us with 16-token tiles at one workgroup per CU, 26.2 us with 4-token tiles); at
+// T = 2048 bf16 takes 4 (30.5 against 30.9 us per step with 8).
 int pick_tt(int T, int K, bool fp8)
 {
     int tt = EP_FUSED_TT ? EP_FUSED_TT
-                         : fp8 ? (T >= 2048 ? 16 : T >= 1024 ? 4 : T >= 512 ? 2 : 1)
+                         : fp8 ? (T >= 4096 ? 8 : T >= 2048 ? 16 : T >= 1024 ? 4 : T >= 512 ? 2 : 1)
                                : (T >= 4096 ? 8 : T >= 1024 ? 4 : T >= 512 ? 2 : 1);
     while ((tt * K) % 4 != 0) tt *= 2;
     while (tt > 4 && tt * K > kTileThreads) tt -= 4;
