@@ -70,6 +70,11 @@ def parse():
                     help="run only this workload's timed loop (for profiling); 'copy_probe' "
                          "runs a plain 256 MiB device copy instead, the reference kernel for "
                          "scaling HBM byte counters")
+    ap.add_argument("--roctx", action="store_true",
+                    help="with --only: mark each call of the step with a roctx range (ROCm's "
+                         "roctx library; rocprofv3 --marker-trace records them)")
+    ap.add_argument("--three-calls", action="store_true",
+                    help="with --only: time the step as three calls (layout, dispatch, combine)")
     return ap.parse_args()
 
 
@@ -137,6 +142,22 @@ def run_starts(args):
     print(json.dumps(aggregate_starts(lines)), flush=True)
 
 
+def roctx_ranges():
+    """(push, pop) of ROCm's roctx range API, or None if the library is not there."""
+    import ctypes
+    for name in ("libroctx64.so", "libroctx64.so.4", "/opt/rocm/lib/libroctx64.so"):
+        try:
+            L = ctypes.CDLL(name)
+        except OSError:
+            continue
+        L.roctxRangePushA.argtypes = [ctypes.c_char_p]
+        L.roctxRangePushA.restype = ctypes.c_int
+        L.roctxRangePop.argtypes = []
+        L.roctxRangePop.restype = ctypes.c_int
+        return L.roctxRangePushA, L.roctxRangePop
+    return None
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -176,9 +197,12 @@ class Workload:
         self.cfg, self.torch, self.B = cfg, torch, B
         dev = torch.device("cuda", 0)
         self.sets = []
+        self.fingerprints = []
         bufs = None
         for k in range(nsets):
             inp = W.make_inputs(cfg, seed=cfg.seed + k)
+            self.fingerprints.append(W.fingerprint(inp["x"], inp["topk_idx"], inp["topk_w"],
+                                                   cfg=cfg))
             s = {}
             s["x"] = torch.from_numpy(inp["x"].view(np.int16)).to(dev)
             s["idx"] = torch.from_numpy(inp["topk_idx"]).to(dev)
@@ -261,6 +285,18 @@ class Workload:
         self.layout(s)
         self.dispatch(s)
         self.combine(s)
+
+    def launch_shapes(self):
+        """The launches of each call of the step on input batch 0 (ep_last_launches): kernel,
+        grid, workgroup, LDS and register counts, for the record beside the timings."""
+        s = self.sets[0]
+        out = {}
+        for name, fn in (("layout_dispatch", self.layout_dispatch), ("combine", self.combine),
+                         ("layout", self.layout), ("dispatch", self.dispatch)):
+            fn(s)
+            out[name] = [brief_launch(r) for r in self.B.last_launches()]
+        self.torch.cuda.synchronize()
+        return out
 
     def kept(self):
         """Kept pairs per input set: run each set's layout and read its stats."""
@@ -533,6 +569,42 @@ class Workload:
         return out
 
 
+_demangled = {}
+
+
+def demangle(name):
+    """C++ symbol -> readable name (binutils' c++filt if present, else the symbol)."""
+    if name not in _demangled:
+        import subprocess
+        try:
+            res = subprocess.run(["c++filt", name], capture_output=True, text=True, timeout=10)
+            txt = res.stdout.strip() if res.returncode == 0 else name
+        except (OSError, subprocess.SubprocessError):
+            txt = name
+        # keep the kernel and its template arguments, not the parameter list
+        txt = txt.replace("ep::(anonymous namespace)::", "")
+        depth, cut = 0, len(txt)
+        for i, ch in enumerate(txt):
+            depth += ch == "<"
+            depth -= ch == ">"
+            if ch == "(" and depth == 0:
+                cut = i
+                break
+        _demangled[name] = txt[:cut]
+    return _demangled[name]
+
+
+def brief_launch(r):
+    """One launch record in the bench line: kernel, grid, block, LDS and registers."""
+    d = {"kernel": demangle(r["kernel"]), "grid": r["grid"][0], "block": r["block"][0],
+         "lds_bytes": r["dynamic_lds_bytes"] + r["static_lds_bytes"], "vgprs": r["vgprs"]}
+    c = r.get("compiler")
+    if c:
+        d.update(sgprs=c.get("sgprs"), sgpr_spill=c.get("sgpr_spill"),
+                 waves_per_simd=c.get("waves_per_simd"), scratch_bytes=c.get("scratch_bytes"))
+    return d
+
+
 def counter_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` on `workload` from the committed counter record
     (profiles/hbm_traffic.json: rocprofv3 FETCH_SIZE and WRITE_SIZE passes, each scaled by what
@@ -756,8 +828,23 @@ def main():
     if args.only:
         cfg = W.get_config(args.only)
         wl = Workload(cfg, NSETS, torch, B, W)
-        ms, _ = wl.timed_loop(args.steps, args.warmup)
-        log(f"{cfg.name}: {ms * 1e3:.2f} us/step")
+        calls = ((("layout", wl.layout), ("dispatch", wl.dispatch), ("combine", wl.combine))
+                 if args.three_calls else
+                 (("layout_dispatch", wl.layout_dispatch), ("combine", wl.combine)))
+        mark = roctx_ranges() if args.roctx else None
+        if args.roctx and mark is None:
+            log("roctx library not found: running without ranges")
+
+        def step(k):
+            s = wl.sets[k % len(wl.sets)]
+            for name, fn in calls:
+                if mark:
+                    mark[0](name.encode())
+                fn(s)
+                if mark:
+                    mark[1]()
+        ms, _ = wl.timed_loop(args.steps, args.warmup, step=step)
+        log(f"{cfg.name}: {ms * 1e3:.2f} us/step ({' -> '.join(n for n, _ in calls)})")
         return
 
     head_cfg = W.get_config(args.workload)
@@ -804,6 +891,8 @@ def main():
             r["us_single_shot_max"] = round(max(ss), 3)
         kus = wl.kernel_avg_us(flush)
         r["kernel_avg_us"] = {k: round(v, 3) for k, v in kus.items()}
+        r["launches"] = wl.launch_shapes()
+        r["fixture_sha256"] = wl.fingerprints
         kb = {"layout": A.layout_bytes(cfg.T, cfg.K),
               "dispatch": A.dispatch_bytes(cfg.T, cfg.K, cfg.H, n_kept, cfg.fp8),
               "combine": A.combine_bytes(cfg.T, cfg.K, cfg.H, n_kept)}
@@ -841,7 +930,13 @@ def main():
                 "peak": A.HBM_PEAK_BYTES_PER_S / 1e9, "unit": "GB/s",
                 "frac": round(achieved / (A.HBM_PEAK_BYTES_PER_S / 1e9), 4),
                 "traffic": counter_traffic(dom, cfg.name), "avg_launch_us": round(kus[dom], 3),
-                "bytes_per_launch": kb[dom]}
+                "bytes_per_launch": kb[dom],
+                "timing": "median over 25 runs of 8 back-to-back launches, each run after a "
+                          "2 GiB fill, HIP events on the launch stream",
+                "traffic_source": "profiles/hbm_traffic.json: rocprofv3 FETCH_SIZE and "
+                                  "WRITE_SIZE passes of this kernel on this workload, each "
+                                  "scaled by the same counter on a 256 MiB device copy; null "
+                                  "when the kernel's sources changed since"}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -852,7 +947,7 @@ def main():
         c, _, rr, _, _ = results[name]
         keys = ("us_per_step", "wall_us_per_step", "replayed_step", "us_single_shot_median",
                 "graph_us_single_shot_median", "logical_GBps", "hbm_frac", "cold_single_shot",
-                "kernel_avg_us", "three_call_step")
+                "kernel_avg_us", "three_call_step", "launches", "fixture_sha256")
         return {k: rr[k] for k in keys if k in rr}
 
     line = {
@@ -865,7 +960,21 @@ def main():
                                f"C={cfg.C} R={cfg.R} ({cfg.route} distinct top-{cfg.K})",
                    "T": cfg.T, "H": cfg.H, "E": cfg.E, "K": cfg.K, "C": cfg.C, "R": cfg.R,
                    "parallelism": "single GPU"},
+        "fixture_sha256": r["fixture_sha256"],
+        "fixture_recipe": "workloads.make_inputs(cfg, seed=k) for the 4 input batches k = 0..3 "
+                          "(x, topk_idx, topk_w; SHA-256 over the config and their bytes); y "
+                          "from torch's device generator seeded 1000 + k",
+        "launches": r["launches"],
+        # fraction of the 8 TB/s HBM roofline (algorithmic bytes / time) under each protocol;
+        # the cold ones are primary: nothing of the step is in any cache when it starts
         "hbm_roofline_frac": r["hbm_frac"],
+        "hbm_roofline_frac_by_protocol": {
+            "primary": "cold_single_shot",
+            "cold_single_shot": (r.get("cold_single_shot") or {}).get("hbm_frac"),
+            "rotating_all_buffers": (r.get("rotating_all_buffers") or {}).get("hbm_frac"),
+            "pipelined_warm": r["hbm_frac"],
+            "pipelined_warm_note": "K steps back to back over persistent layer buffers: part "
+                                   "of y and recv is served by the last-level cache"},
         "us_per_step": r["us_per_step"],
         "kernel_avg_us": r["kernel_avg_us"],
         "kernel_GBps": r["kernel_GBps"],

@@ -1,13 +1,21 @@
 """Build libep_mi355x.so: the gfx950 HIP kernels and their C ABI (include/ep.h).
 
 ``python -m combine_ep_layout_06_amd.build`` (or ``build()``) compiles every source under
-``csrc/`` with hipcc for gfx950 into ``combine_ep_layout_06_amd/libep_mi355x.so``. Extra
-``-D`` definitions (launch-shape overrides) can be passed with ``defines``.
+``csrc/`` with hipcc for gfx950, one process per source in parallel, and links them into
+``combine_ep_layout_06_amd/libep_mi355x.so``. Extra ``-D`` definitions (launch-shape overrides)
+can be passed with ``defines``.
+
+The same compilation writes ``kernel_resources.json`` beside the library: per kernel (mangled
+symbol), the compiler's own resource report (scalar and vector registers, spills, LDS, the
+wavefronts per SIMD it allows), for recording beside measurements.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import glob
+import json
 import os
+import re
 import subprocess
 import sys
 
@@ -17,14 +25,24 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libep_mi355x.so"
 LIB = os.path.join(PKG, LIB_NAME)
+RESOURCES = os.path.join(PKG, "kernel_resources.json")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Wall", "-Wextra", "-Werror", "-Wno-unused-command-line-argument",
     # no packed-fp32 instructions (v_pk_*_f32) in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+
+# the compiler's per-kernel resource remarks
+_REMARK = re.compile(r"remark:\s+(Function Name|TotalSGPRs|VGPRs|AGPRs|ScratchSize \[bytes/lane\]"
+                     r"|Occupancy \[waves/SIMD\]|SGPRs Spill|VGPRs Spill"
+                     r"|LDS Size \[bytes/block\]):\s*(\S+)")
+_KEYS = {"TotalSGPRs": "sgprs", "VGPRs": "vgprs", "AGPRs": "agprs",
+         "ScratchSize [bytes/lane]": "scratch_bytes", "Occupancy [waves/SIMD]": "waves_per_simd",
+         "SGPRs Spill": "sgpr_spill", "VGPRs Spill": "vgpr_spill",
+         "LDS Size [bytes/block]": "static_lds_bytes"}
 
 
 def hipcc() -> str:
@@ -33,19 +51,55 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
+def parse_resources(text: str) -> dict:
+    """Kernel -> resource figures from hipcc's -Rpass-analysis=kernel-resource-usage remarks."""
+    out, cur = {}, None
+    for m in _REMARK.finditer(text):
+        key, val = m.group(1), m.group(2)
+        if key == "Function Name":
+            cur = out.setdefault(val, {})
+        elif cur is not None:
+            cur[_KEYS[key]] = int(val) if val.lstrip("-").isdigit() else val
+    return out
+
+
+def _compile(src: str, obj: str, defines: dict | None, verbose: bool):
+    cmd = [hipcc(), *HIPCC_FLAGS, "-Rpass-analysis=kernel-resource-usage", f"-I{INCLUDE}",
+           f"-I{CSRC}"]
+    cmd += [f"-D{k}={v}" for k, v in (defines or {}).items()]
+    cmd += ["-c", src, "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    return src, res
+
+
 def build(out: str = LIB, defines: dict | None = None, verbose: bool = False) -> str:
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    objdir = os.path.join(os.path.dirname(out), "_build", os.path.basename(out) + ".obj")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.basename(s)[:-4] + ".o") for s in sources]
+    jobs = max(1, min(len(sources), os.cpu_count() or 1, 16))
+    resources = {}
+    with cf.ThreadPoolExecutor(jobs) as pool:
+        for src, res in pool.map(lambda a: _compile(*a, defines, verbose), zip(sources, objs)):
+            if res.returncode != 0:
+                sys.stderr.write(res.stdout + res.stderr)
+                raise RuntimeError(f"hipcc failed ({res.returncode}) on {src}")
+            resources.update(parse_resources(res.stderr))
     tmp = out + f".tmp{os.getpid()}"
-    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}"]
-    cmd += [f"-D{k}={v}" for k, v in (defines or {}).items()]
-    cmd += [*sources, "-o", tmp]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed ({res.returncode}) building {out}")
+        raise RuntimeError(f"hipcc failed ({res.returncode}) linking {out}")
     os.replace(tmp, out)
+    if out == LIB:
+        with open(RESOURCES + ".tmp", "w") as f:
+            json.dump({"arch": ARCH, "kernels": resources}, f, indent=1, sort_keys=True)
+        os.replace(RESOURCES + ".tmp", RESOURCES)
     return out
 
 
