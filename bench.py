@@ -75,6 +75,9 @@ def parse():
                          "roctx library; rocprofv3 --marker-trace records them)")
     ap.add_argument("--three-calls", action="store_true",
                     help="with --only: time the step as three calls (layout, dispatch, combine)")
+    ap.add_argument("--cold", action="store_true",
+                    help="with --only: single-shot steps, each after a 2 GiB fill (the cold "
+                         "protocol), --steps of them, instead of the pipelined loop")
     return ap.parse_args()
 
 
@@ -843,6 +846,14 @@ def main():
                 fn(s)
                 if mark:
                     mark[1]()
+        if args.cold:
+            flush = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+            for k in range(args.warmup):
+                step(k)
+            ts = wl.single_shot(args.steps, flush, step=step)
+            log(f"{cfg.name}: cold single-shot median {statistics.median(ts):.2f} us "
+                f"({' -> '.join(n for n, _ in calls)}, {len(ts)} samples)")
+            return
         ms, _ = wl.timed_loop(args.steps, args.warmup, step=step)
         log(f"{cfg.name}: {ms * 1e3:.2f} us/step ({' -> '.join(n for n, _ in calls)})")
         return

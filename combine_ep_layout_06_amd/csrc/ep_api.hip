@@ -86,11 +86,14 @@ int check_layout_args(const ep_shape_t *shape, const int32_t *topk_idx, const in
     return EP_OK;
 }
 
-// Limits of the two-stage calls: ranks as 64-bit sets, staging rows r*T + p in int32.
+// Limits of the two-stage calls: ranks as 64-bit sets, staging rows r*T + p in int32, expert
+// ids below EP_MAX_EXPERTS (the rank of an id is found by a multiply exact up to there).
 int check_ranks(const ep_shape_t *s, const char *fn)
 {
     if (s->R > EP_MAX_RANKS)
         return fail(EP_ERR_UNSUPPORTED, std::string(fn) + ": R exceeds EP_MAX_RANKS");
+    if (s->E > EP_MAX_EXPERTS)
+        return fail(EP_ERR_UNSUPPORTED, std::string(fn) + ": E exceeds EP_MAX_EXPERTS");
     if ((int64_t)s->R * s->T > INT32_MAX)
         return fail(EP_ERR_UNSUPPORTED, std::string(fn) + ": R*T exceeds INT32_MAX");
     return EP_OK;

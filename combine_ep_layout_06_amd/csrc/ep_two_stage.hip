@@ -57,43 +57,72 @@ __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; 
 // rank layout
 // ------------------------------------------------------------------------------------------
 
-// Bit of id e's rank (e / EL) if e is a valid expert (0 <= e < E), else 0. Branch-free: the
-// division is unsigned and its result is masked before the shift.
-__device__ __forceinline__ uint64_t rank_bit(int e, int E, int EL)
+// The rank of an expert, e / EL, without a division: e * M >> 20 with M = floor(2^20 / EL) + 1
+// (rank_magic) is exact for 0 <= e < E <= EP_MAX_EXPERTS = 1024. (e M / 2^20 exceeds e / EL by
+// less than e / 2^20, which is below 1 / EL since e EL < 2^20, so the floor is unchanged;
+// EL = 1 gives e + (e >> 20) = e.) Both factors fit the 24-bit multiplier.
+__host__ __device__ inline uint32_t rank_magic(int EL) { return (1u << 20) / (uint32_t)EL + 1u; }
+
+// Bit of id e's rank if e is a valid expert (0 <= e < E), else 0. Branch-free: an invalid id's
+// rank is masked before the shift.
+__device__ __forceinline__ uint64_t rank_bit(int e, int E, uint32_t magic)
 {
-    const unsigned r = (unsigned)e / (unsigned)EL;
+    const unsigned r = __umul24((unsigned)e, magic) >> 20;
     return (unsigned)e < (unsigned)E ? (1ull << (r & 63u)) : 0ull;
 }
 
-__device__ __forceinline__ uint64_t ranks_of(const int4 *v, int nv, int E, int EL)
+__device__ __forceinline__ uint64_t ranks_of(const int4 *v, int nv, int E, uint32_t magic)
 {
     uint64_t m = 0;
     for (int j = 0; j < nv; ++j)
-        m |= rank_bit(v[j].x, E, EL) | rank_bit(v[j].y, E, EL) | rank_bit(v[j].z, E, EL) |
-             rank_bit(v[j].w, E, EL);
+        m |= rank_bit(v[j].x, E, magic) | rank_bit(v[j].y, E, magic) |
+             rank_bit(v[j].z, E, magic) | rank_bit(v[j].w, E, magic);
     return m;
 }
 
 // Rank set of token t for any K, one id at a time.
 __device__ __forceinline__ uint64_t token_ranks_any(const int32_t *__restrict__ idx, int t, int K,
-                                                    int E, int EL)
+                                                    int E, uint32_t magic)
 {
     uint64_t m = 0;
-    for (int j = 0; j < K; ++j) m |= rank_bit(idx[(size_t)t * K + j], E, EL);
+    for (int j = 0; j < K; ++j) m |= rank_bit(idx[(size_t)t * K + j], E, magic);
     return m;
 }
 
+// The 4 bits of n (n < 16) moved to the lowest bit of each byte (bit i -> bit 8i): n times
+// 1 + 2^7 + 2^14 + 2^21 places four copies of n that do not overlap, the mask keeps one bit
+// of each.
+__device__ __forceinline__ uint32_t spread4(uint32_t n) { return __umul24(n, 0x204081u) & 0x01010101u; }
+
+// Sum over the 64 lanes, in every lane.
+__device__ __forceinline__ int wave_total(int v)
+{
+    return __builtin_amdgcn_readlane(wave_inclusive_sum(v), kWave - 1);
+}
+
+// Largest T for which the packed counts of rank_prefix_wave cannot overflow: a lane sees at
+// most kRankBatch earlier tokens per pass of kRankBatch * kRankTile tokens, and its 8-bit
+// fields hold up to 255, so 63 passes.
+constexpr int kPackedRankMaxT = 63 * kRankBatch * kRankTile;
+
 // Per-rank counts of the tokens [0, t0) in this wavefront's share (tokens wave*64 + lane +
 // b*kRankTile): kRankBatch tokens per lane are loaded together (16-byte id vectors when
-// KV > 0), then per rank the wavefront adds up one ballot count per batch. Lane r returns rank
-// r's total.
-template <int KV>
+// KV > 0). Lane r returns rank r's total.
+// RQ > 0 (R <= 4 RQ and T <= kPackedRankMaxT): each lane counts its own tokens per rank in
+// packed 8-bit fields, one 24-bit multiply and a mask per 4 ranks and token (spread4); one
+// wave sum per rank at the end. RQ = 0: per rank and batch one ballot and a scalar popcount
+// (any R <= 64).
+template <int KV, int RQ>
 __device__ __forceinline__ int rank_prefix_wave(const int32_t *__restrict__ idx, int t0, int K,
-                                                int E, int EL, int R)
+                                                int E, uint32_t magic, int R)
 {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int q0 = wave * kWave + lane;
     int acc = 0;
+    // RQ > 0: byte k of cnt[q] counts the lane's tokens sent to rank 4q + k
+    uint32_t cnt[RQ > 0 ? RQ : 1];
+#pragma unroll
+    for (int q = 0; q < (RQ > 0 ? RQ : 1); ++q) cnt[q] = 0;
     for (int b0 = 0; b0 * kRankTile + wave * kWave < t0; b0 += kRankBatch) {
         uint64_t m[kRankBatch];
         if constexpr (KV > 0) {
@@ -111,29 +140,50 @@ __device__ __forceinline__ int rank_prefix_wave(const int32_t *__restrict__ idx,
             }
 #pragma unroll
             for (int b = 0; b < kRankBatch; ++b)
-                m[b] = q0 + (b0 + b) * kRankTile < t0 ? ranks_of(v[b], KV, E, EL) : 0;
+                m[b] = q0 + (b0 + b) * kRankTile < t0 ? ranks_of(v[b], KV, E, magic) : 0;
         } else {
 #pragma unroll
             for (int b = 0; b < kRankBatch; ++b) {
                 const int q = q0 + (b0 + b) * kRankTile;
-                m[b] = q < t0 ? token_ranks_any(idx, q, K, E, EL) : 0;
+                m[b] = q < t0 ? token_ranks_any(idx, q, K, E, magic) : 0;
             }
         }
-        // batches holding any of this wavefront's earlier tokens
-        const int nb = min(kRankBatch, ceil_div(t0 - b0 * kRankTile - wave * kWave, kRankTile));
-        for (int r = 0; r < R; ++r) {
-            int c = 0;
+        if constexpr (RQ > 0) {
+            // tokens past t0 have an empty mask, so every batch can be counted
 #pragma unroll
-            for (int b = 0; b < kRankBatch; ++b)
-                if (b < nb) c += __popcll(__ballot(((m[b] >> r) & 1u) != 0));
-            acc = lane == r ? acc + c : acc;
+            for (int q = 0; q < RQ; ++q)
+#pragma unroll
+                for (int b = 0; b < kRankBatch; ++b)
+                    cnt[q] += spread4((uint32_t)(m[b] >> (4 * q)) & 0xFu);
+        } else {
+            // batches holding any of this wavefront's earlier tokens
+            const int nb = min(kRankBatch, ceil_div(t0 - b0 * kRankTile - wave * kWave, kRankTile));
+            for (int r = 0; r < R; ++r) {
+                int c = 0;
+#pragma unroll
+                for (int b = 0; b < kRankBatch; ++b)
+                    if (b < nb) c += __popcll(__ballot(((m[b] >> r) & 1u) != 0));
+                acc = lane == r ? acc + c : acc;
+            }
+        }
+    }
+    if constexpr (RQ > 0) {
+#pragma unroll
+        for (int q = 0; q < RQ; ++q) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if (4 * q + k >= R) continue;       // wavefront-uniform
+                const int tot = wave_total((int)((cnt[q] >> (8 * k)) & 0xFFu));
+                acc = lane == 4 * q + k ? tot : acc;
+            }
         }
     }
     return acc;
 }
 
-// KV > 0: K = 4*KV ids per token, read as KV 16-byte vectors; KV = 0: any K.
-template <int KV>
+// KV > 0: K = 4*KV ids per token, read as KV 16-byte vectors; KV = 0: any K. RQ: the counting
+// form of rank_prefix_wave.
+template <int KV, int RQ>
 __global__ __launch_bounds__(kRankTile) void rank_layout_kernel(
     const int32_t *__restrict__ idx, int T, int K, int E, int R, int32_t *__restrict__ rank_slot,
     int32_t *__restrict__ rank_tokens)
@@ -142,7 +192,7 @@ __global__ __launch_bounds__(kRankTile) void rank_layout_kernel(
     __shared__ int32_t base[EP_MAX_RANKS];               // earlier-tile counts
     __shared__ int4 out16[kRankTile][4];                 // 16 ranks of each token's output row
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int EL = E / R;
+    const uint32_t magic = rank_magic(E / R);
     const int t0 = blockIdx.x * kRankTile;
     const int t = t0 + tid;
 
@@ -156,9 +206,9 @@ __global__ __launch_bounds__(kRankTile) void rank_layout_kernel(
             for (int j = 0; j < KV; ++j) vo[j] = reinterpret_cast<const int4 *>(idx + (size_t)t * K)[j];
         }
     }
-    const int acc = rank_prefix_wave<KV>(idx, t0, K, E, EL, R);
-    if constexpr (KV > 0) own = t < T ? ranks_of(vo, KV, E, EL) : 0;
-    else own = t < T ? token_ranks_any(idx, t, K, E, EL) : 0;
+    const int acc = rank_prefix_wave<KV, RQ>(idx, t0, K, E, magic, R);
+    if constexpr (KV > 0) own = t < T ? ranks_of(vo, KV, E, magic) : 0;
+    else own = t < T ? token_ranks_any(idx, t, K, E, magic) : 0;
     if (lane < R) wcnt[wave][lane] = acc;
     __syncthreads();
     if (tid < R) {
@@ -283,7 +333,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_ranks_fp8_kernel(
 // Rank layout of the tile [t0, t0 + nt), nt <= kWave, in a workgroup of kRankTile lanes:
 // rank_slot rows of the tile (coalesced, through LDS), rows[tl*R + r] = r*T + slot or -1 in
 // LDS for the copies, and rank_tokens in the last workgroup. Ends with a barrier.
-template <int KV>
+template <int KV, int RQ>
 __device__ __forceinline__ void rank_tile(const int32_t *__restrict__ idx, int t0, int nt, int T,
                                           int K, int E, int R, bool last,
                                           int32_t *__restrict__ rank_slot,
@@ -291,7 +341,7 @@ __device__ __forceinline__ void rank_tile(const int32_t *__restrict__ idx, int t
                                           int32_t *slots, int32_t (*wcnt)[EP_MAX_RANKS])
 {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const int EL = E / R;
+    const uint32_t magic = rank_magic(E / R);
     uint64_t own = 0;                  // wavefront 0, lane tl: the tile's token tl
     if (wave == 0 && lane < nt) {
         const int t = t0 + lane;
@@ -299,12 +349,12 @@ __device__ __forceinline__ void rank_tile(const int32_t *__restrict__ idx, int t
             int4 v[KV];
 #pragma unroll
             for (int j = 0; j < KV; ++j) v[j] = reinterpret_cast<const int4 *>(idx + (size_t)t * K)[j];
-            own = ranks_of(v, KV, E, EL);
+            own = ranks_of(v, KV, E, magic);
         } else {
-            own = token_ranks_any(idx, t, K, E, EL);
+            own = token_ranks_any(idx, t, K, E, magic);
         }
     }
-    const int acc = rank_prefix_wave<KV>(idx, t0, K, E, EL, R);
+    const int acc = rank_prefix_wave<KV, RQ>(idx, t0, K, E, magic, R);
     if (lane < R) wcnt[wave][lane] = acc;
     __syncthreads();
     if (wave == 0) {
@@ -327,7 +377,7 @@ __device__ __forceinline__ void rank_tile(const int32_t *__restrict__ idx, int t
     for (int k = threadIdx.x; k < nt * R; k += kRankTile) rank_slot[(size_t)t0 * R + k] = slots[k];
 }
 
-template <int KV, int KG, int U, bool MULTI>
+template <int KV, int RQ, int KG, int U, bool MULTI>
 __global__ __launch_bounds__(kRankTile, 8) void rank_layout_dispatch_bf16_kernel(
     const u32x4 *__restrict__ x, const int32_t *__restrict__ idx, int32_t *__restrict__ rank_slot,
     int32_t *__restrict__ rank_tokens, u32x4 *__restrict__ stage, int T, int H8, int K, int E,
@@ -342,8 +392,8 @@ __global__ __launch_bounds__(kRankTile, 8) void rank_layout_dispatch_bf16_kernel
     // the first item's row loads need no slot: issued before the layout's loads
     RowPiece<U> first;
     if (wave < nitems) first = load_item_bf16<U>(x, t0 + wave / nseg, wave % nseg, H8);
-    rank_tile<KV>(idx, t0, nt, T, K, E, R, blockIdx.x == gridDim.x - 1, rank_slot, rank_tokens,
-                  rows, slots, wcnt);
+    rank_tile<KV, RQ>(idx, t0, nt, T, K, E, R, blockIdx.x == gridDim.x - 1, rank_slot,
+                      rank_tokens, rows, slots, wcnt);
     if (wave < nitems)
         store_item_bf16<KG, U, MULTI>(first, stage, rows, wave / nseg, wave % nseg, H8, R);
     for (int item = wave + kRankWaves; item < nitems; item += kRankWaves) {
@@ -352,8 +402,12 @@ __global__ __launch_bounds__(kRankTile, 8) void rank_layout_dispatch_bf16_kernel
     }
 }
 
-template <int KV, int KG, int U, bool MULTI>
-__global__ __launch_bounds__(kRankTile) void rank_layout_dispatch_fp8_kernel(
+#ifndef EP_RANKS_FP8_WAVES
+#define EP_RANKS_FP8_WAVES 4     // wavefronts per SIMD the fused FP8 rank kernel is built for
+#endif
+
+template <int KV, int RQ, int KG, int U, bool MULTI>
+__global__ __launch_bounds__(kRankTile, EP_RANKS_FP8_WAVES) void rank_layout_dispatch_fp8_kernel(
     const u32x4 *__restrict__ x, const int32_t *__restrict__ idx, int32_t *__restrict__ rank_slot,
     int32_t *__restrict__ rank_tokens, u32x4 *__restrict__ stage_q,
     float *__restrict__ stage_scale, int T, int H, int K, int E, int R, int TT, int nseg)
@@ -364,9 +418,15 @@ __global__ __launch_bounds__(kRankTile) void rank_layout_dispatch_fp8_kernel(
     const int wave = wave_uniform(threadIdx.x / kWave);
     const int t0 = blockIdx.x * TT, nt = min(TT, T - t0);
     const int nitems = nt * nseg;
-    rank_tile<KV>(idx, t0, nt, T, K, E, R, blockIdx.x == gridDim.x - 1, rank_slot, rank_tokens,
-                  rows, slots, wcnt);
-    for (int item = wave; item < nitems; item += kRankWaves) {
+    // the first item's token row is loaded before the layout (it needs no slot) and cast after
+    RawPieceFp8<U> first;
+    if (wave < nitems) first = load_item_fp8<U>(x, t0 + wave / nseg, wave % nseg, H);
+    rank_tile<KV, RQ>(idx, t0, nt, T, K, E, R, blockIdx.x == gridDim.x - 1, rank_slot,
+                      rank_tokens, rows, slots, wcnt);
+    if (wave < nitems)
+        store_item_fp8<KG, U, MULTI>(cast_item_fp8<U>(first), stage_q, stage_scale, rows,
+                                     wave / nseg, wave % nseg, H, R);
+    for (int item = wave + kRankWaves; item < nitems; item += kRankWaves) {
         const int tl = item / nseg;
         dispatch_item_fp8<KG, U, MULTI>(x, stage_q, stage_scale, rows, t0 + tl, tl,
                                         item - tl * nseg, H, R);
@@ -808,19 +868,39 @@ dim3 grid_for(int T, int tpb) { return dim3(ceil_div(T, tpb)); }
 // launchers
 // ------------------------------------------------------------------------------------------
 
+namespace {
+
+// Counting form of rank_prefix_wave: packed per-lane counts in RQ words of 4 ranks (R <= 4 RQ)
+// while they cannot overflow, else ballots.
+int pick_rq(int T, int R)
+{
+    if (T > kPackedRankMaxT) return 0;
+    return R <= 4 ? 1 : R <= 16 ? 4 : 0;
+}
+
+}  // namespace
+
 hipError_t launch_rank_layout(const ep_shape_t &s, const int32_t *idx, int32_t *rank_slot,
                               int32_t *rank_tokens, hipStream_t stream)
 {
     const dim3 grid(s.T > 0 ? ceil_div(s.T, kRankTile) : 1), block(kRankTile);
-#define EP_LAUNCH_RL(KV)                                                                        \
-    return launch(rank_layout_kernel<KV>, grid, block, 0, stream, idx, s.T, s.K, s.E, s.R,      \
+    const int rq = pick_rq(s.T, s.R);
+#define EP_LAUNCH_RL_RQ(KV, RQ)                                                                 \
+    return launch(rank_layout_kernel<KV, RQ>, grid, block, 0, stream, idx, s.T, s.K, s.E, s.R,  \
                   rank_slot, rank_tokens)
+#define EP_LAUNCH_RL(KV)                                                                        \
+    do {                                                                                        \
+        if (rq == 1) EP_LAUNCH_RL_RQ(KV, 1);                                                    \
+        if (rq == 4) EP_LAUNCH_RL_RQ(KV, 4);                                                    \
+        EP_LAUNCH_RL_RQ(KV, 0);                                                                 \
+    } while (0)
     if (s.K == 4) EP_LAUNCH_RL(1);
     if (s.K == 8) EP_LAUNCH_RL(2);
     if (s.K == 12) EP_LAUNCH_RL(3);
     if (s.K == 16) EP_LAUNCH_RL(4);
     EP_LAUNCH_RL(0);
 #undef EP_LAUNCH_RL
+#undef EP_LAUNCH_RL_RQ
 }
 
 hipError_t launch_dispatch_ranks_bf16(const ep_shape_t &s, const uint16_t *x,
@@ -890,18 +970,47 @@ int pick_tt_ranks(int T, int R, bool fp8)
     return tt;
 }
 
+template <int KV, int U, int RQ>
+hipError_t launch_rank_dispatch_bf16_rq(const ep_shape_t &s, const u32x4 *x, const int32_t *idx,
+                                        int32_t *rank_slot, int32_t *rank_tokens, u32x4 *stage,
+                                        hipStream_t stream)
+{
+    const int H8 = s.H / 8, nseg = ceil_div(H8, U * kWave), TT = pick_tt_ranks(s.T, s.R, false);
+    const dim3 grid(s.T > 0 ? ceil_div(s.T, TT) : 1), block(kRankTile);
+#define EP_LAUNCH_RLD(KG, MULTI)                                                                \
+    return launch(rank_layout_dispatch_bf16_kernel<KV, RQ, KG, U, MULTI>, grid, block, 0,      \
+                  stream, x, idx, rank_slot, rank_tokens, stage, s.T, H8, s.K, s.E, s.R, TT,    \
+                  nseg)
+    EP_BY_K(s.R, EP_LAUNCH_RLD);
+#undef EP_LAUNCH_RLD
+}
+
 template <int KV, int U>
 hipError_t launch_rank_dispatch_bf16(const ep_shape_t &s, const u32x4 *x, const int32_t *idx,
                                      int32_t *rank_slot, int32_t *rank_tokens, u32x4 *stage,
                                      hipStream_t stream)
 {
-    const int H8 = s.H / 8, nseg = ceil_div(H8, U * kWave), TT = pick_tt_ranks(s.T, s.R, false);
+    const int rq = pick_rq(s.T, s.R);
+    if (rq == 1)
+        return launch_rank_dispatch_bf16_rq<KV, U, 1>(s, x, idx, rank_slot, rank_tokens, stage, stream);
+    if (rq == 4)
+        return launch_rank_dispatch_bf16_rq<KV, U, 4>(s, x, idx, rank_slot, rank_tokens, stage, stream);
+    return launch_rank_dispatch_bf16_rq<KV, U, 0>(s, x, idx, rank_slot, rank_tokens, stage, stream);
+}
+
+template <int KV, int U, int RQ>
+hipError_t launch_rank_dispatch_fp8_rq(const ep_shape_t &s, const u32x4 *x, const int32_t *idx,
+                                       int32_t *rank_slot, int32_t *rank_tokens, u32x4 *stage_q,
+                                       float *stage_scale, hipStream_t stream)
+{
+    const int nseg = ceil_div(s.H, U * 16 * kWave), TT = pick_tt_ranks(s.T, s.R, true);
     const dim3 grid(s.T > 0 ? ceil_div(s.T, TT) : 1), block(kRankTile);
-#define EP_LAUNCH_RLD(KG, MULTI)                                                                \
-    return launch(rank_layout_dispatch_bf16_kernel<KV, KG, U, MULTI>, grid, block, 0, stream,  \
-                  x, idx, rank_slot, rank_tokens, stage, s.T, H8, s.K, s.E, s.R, TT, nseg)
-    EP_BY_K(s.R, EP_LAUNCH_RLD);
-#undef EP_LAUNCH_RLD
+#define EP_LAUNCH_RLQ(KG, MULTI)                                                                \
+    return launch(rank_layout_dispatch_fp8_kernel<KV, RQ, KG, U, MULTI>, grid, block, 0,       \
+                  stream, x, idx, rank_slot, rank_tokens, stage_q, stage_scale, s.T, s.H, s.K,  \
+                  s.E, s.R, TT, nseg)
+    EP_BY_K(s.R, EP_LAUNCH_RLQ);
+#undef EP_LAUNCH_RLQ
 }
 
 template <int KV, int U>
@@ -909,14 +1018,15 @@ hipError_t launch_rank_dispatch_fp8(const ep_shape_t &s, const u32x4 *x, const i
                                     int32_t *rank_slot, int32_t *rank_tokens, u32x4 *stage_q,
                                     float *stage_scale, hipStream_t stream)
 {
-    const int nseg = ceil_div(s.H, U * 16 * kWave), TT = pick_tt_ranks(s.T, s.R, true);
-    const dim3 grid(s.T > 0 ? ceil_div(s.T, TT) : 1), block(kRankTile);
-#define EP_LAUNCH_RLQ(KG, MULTI)                                                                \
-    return launch(rank_layout_dispatch_fp8_kernel<KV, KG, U, MULTI>, grid, block, 0, stream,   \
-                  x, idx, rank_slot, rank_tokens, stage_q, stage_scale, s.T, s.H, s.K, s.E,     \
-                  s.R, TT, nseg)
-    EP_BY_K(s.R, EP_LAUNCH_RLQ);
-#undef EP_LAUNCH_RLQ
+    const int rq = pick_rq(s.T, s.R);
+    if (rq == 1)
+        return launch_rank_dispatch_fp8_rq<KV, U, 1>(s, x, idx, rank_slot, rank_tokens, stage_q,
+                                                     stage_scale, stream);
+    if (rq == 4)
+        return launch_rank_dispatch_fp8_rq<KV, U, 4>(s, x, idx, rank_slot, rank_tokens, stage_q,
+                                                     stage_scale, stream);
+    return launch_rank_dispatch_fp8_rq<KV, U, 0>(s, x, idx, rank_slot, rank_tokens, stage_q,
+                                                 stage_scale, stream);
 }
 
 template <int KV>

@@ -270,8 +270,8 @@ int ep_combine_packed(const ep_shape_t *shape, int32_t rows, const uint16_t *y,
  * per-rank partial rounded to bf16 (the precision a rank would send back) and the partials
  * summed in fp32 in ascending rank, which is bit-identical to ep_combine when R = 1.
  *
- * Common requirements (else EP_ERR_UNSUPPORTED): R <= EP_MAX_RANKS, R*T <= INT32_MAX; the
- * row-buffer alignment and H rules of the one-stage calls.
+ * Common requirements (else EP_ERR_UNSUPPORTED): R <= EP_MAX_RANKS, E <= EP_MAX_EXPERTS,
+ * R*T <= INT32_MAX; the row-buffer alignment and H rules of the one-stage calls.
  */
 
 /*

@@ -113,6 +113,8 @@ def test_two_stage_calls_reject_bad_arguments(lib):
     assert lib.ep_rank_layout(shape(), A16, A16, None, None) == B.EP_ERR_INVALID
     assert lib.ep_rank_layout(shape(T=1 << 28, K=1, R=16), A16, A16, A16, None) == B.EP_ERR_UNSUPPORTED
     assert "R*T" in lib.ep_last_error().decode()
+    assert lib.ep_rank_layout(shape(E=2048, R=16), A16, A16, A16, None) == B.EP_ERR_UNSUPPORTED
+    assert "EP_MAX_EXPERTS" in lib.ep_last_error().decode()
     assert lib.ep_dispatch_ranks(shape(**many_ranks), A16, A16, A16, None) == B.EP_ERR_UNSUPPORTED
     assert lib.ep_dispatch_ranks(shape(), A16, A16, A16 + 2, None) == B.EP_ERR_ALIGN
     assert lib.ep_dispatch_ranks(shape(H=12), A16, A16, A16, None) == B.EP_ERR_UNSUPPORTED
