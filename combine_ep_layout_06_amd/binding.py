@@ -34,6 +34,7 @@ EXPORTED = ("ep_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_layout_dispatch",
             "ep_combine_ranks", "ep_combine_reduce", "ep_layout_packed", "ep_dispatch_packed",
             "ep_dispatch_packed_fp8", "ep_layout_dispatch_packed", "ep_layout_dispatch_packed_fp8",
             "ep_combine_packed", "ep_check_e4m3_conversion", "ep_last_launches",
+            "ep_layout_workspace_bytes", "ep_layout_dispatch_ws", "ep_layout_dispatch_fp8_ws",
             "ep_error_string", "ep_last_error", "ep_version")
 
 
@@ -101,10 +102,14 @@ def load_library():
         L.ep_layout_dispatch_packed_fp8.argtypes = [sp, i32, i32] + [vp] * 11
         L.ep_check_e4m3_conversion.argtypes = [ctypes.c_uint32, ctypes.c_uint32, vp, vp, vp]
         L.ep_last_launches.argtypes = [ctypes.POINTER(EpLaunchRecord), ctypes.c_int]
+        L.ep_layout_dispatch_ws.argtypes = [sp] + [vp] * 10 + [ctypes.c_size_t, vp]
+        L.ep_layout_dispatch_fp8_ws.argtypes = [sp] + [vp] * 11 + [ctypes.c_size_t, vp]
         for fn in EXPORTED:
             if fn.startswith("ep_") and fn not in ("ep_error_string", "ep_last_error",
-                                                   "ep_version"):
+                                                   "ep_version", "ep_layout_workspace_bytes"):
                 getattr(L, fn).restype = ctypes.c_int
+        L.ep_layout_workspace_bytes.argtypes = [sp]
+        L.ep_layout_workspace_bytes.restype = ctypes.c_size_t
         L.ep_error_string.argtypes = [ctypes.c_int]
         L.ep_error_string.restype = ctypes.c_char_p
         L.ep_last_error.argtypes = []
@@ -316,6 +321,64 @@ def ep_layout_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, recv: torch.Tens
     _need(recv, "recv", _bf16(recv), E * C * H, dev)
     sh = _shape(T, H, E, K, C, R)
     _call("ep_layout_dispatch", sh, x, topk_idx, *_layout_ts(lay), recv, stream=stream)
+    return lay
+
+
+def layout_workspace_bytes(T: int, K: int, E: int) -> int:
+    """Bytes of workspace the _ws calls need for T tokens, top-K, E experts."""
+    return int(load_library().ep_layout_workspace_bytes(ctypes.byref(_shape(T, 1, E, K, 1, 1))))
+
+
+def _workspace(workspace, T, K, E, dev):
+    need = layout_workspace_bytes(T, K, E)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace: must be a contiguous tensor on the batch's device")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def ep_layout_dispatch_ws(x: torch.Tensor, topk_idx: torch.Tensor, recv: torch.Tensor, E: int,
+                          C: int, R: int, *, workspace=None, slot=None, expert_count=None,
+                          expert_offset=None, rank_count=None, rank_offset=None, stats=None,
+                          stream=None):
+    """ep_layout_dispatch in two launches through a workspace (chunk histograms): the same
+    outputs, faster on large batches. ``workspace``: a device tensor of at least
+    layout_workspace_bytes(T, K, E) bytes (allocated here if not given)."""
+    dev = x.device
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    lay = _layout_outputs(dev, T, K, E, R, slot, expert_count, expert_offset, rank_count,
+                          rank_offset, stats)
+    _need(x, "x", _bf16(x), T * H, dev)
+    _need(topk_idx, "topk_idx", torch.int32, T * K, dev)
+    _need(recv, "recv", _bf16(recv), E * C * H, dev)
+    ws, nbytes = _workspace(workspace, T, K, E, dev)
+    sh = _shape(T, H, E, K, C, R)
+    _call("ep_layout_dispatch_ws", sh, x, topk_idx, *_layout_ts(lay), recv, ws, nbytes,
+          stream=stream)
+    return lay
+
+
+def ep_layout_dispatch_fp8_ws(x: torch.Tensor, topk_idx: torch.Tensor, recv_q: torch.Tensor,
+                              recv_scale: torch.Tensor, E: int, C: int, R: int, *,
+                              workspace=None, slot=None, expert_count=None, expert_offset=None,
+                              rank_count=None, rank_offset=None, stats=None, stream=None):
+    """ep_layout_dispatch_fp8 in two launches through a workspace (see ep_layout_dispatch_ws)."""
+    dev = x.device
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    lay = _layout_outputs(dev, T, K, E, R, slot, expert_count, expert_offset, rank_count,
+                          rank_offset, stats)
+    _need(x, "x", _bf16(x), T * H, dev)
+    _need(topk_idx, "topk_idx", torch.int32, T * K, dev)
+    _need(recv_q, "recv_q", recv_q.dtype if recv_q.dtype in (torch.uint8, torch.float8_e4m3fn)
+          else torch.uint8, E * C * H, dev)
+    _need(recv_scale, "recv_scale", torch.float32, E * C * (H // EP_FP8_BLOCK), dev)
+    ws, nbytes = _workspace(workspace, T, K, E, dev)
+    sh = _shape(T, H, E, K, C, R)
+    _call("ep_layout_dispatch_fp8_ws", sh, x, topk_idx, *_layout_ts(lay), recv_q, recv_scale,
+          ws, nbytes, stream=stream)
     return lay
 
 

@@ -152,6 +152,78 @@ int ep_layout_dispatch_fp8(const ep_shape_t *shape, const uint16_t *x, const int
                       "ep_layout_dispatch_fp8");
 }
 
+namespace {
+
+// The workspace of the chunked layout: present, large enough and 16-byte aligned.
+int check_workspace(const ep_shape_t *shape, const void *workspace, size_t workspace_bytes,
+                    const char *fn)
+{
+    const size_t need = ep::layout_workspace_bytes(*shape);
+    if (need > 0 && !workspace) return fail(EP_ERR_INVALID, std::string(fn) + ": workspace is NULL");
+    if (workspace_bytes < need)
+        return fail(EP_ERR_INVALID, std::string(fn) + ": workspace_bytes " +
+                                        std::to_string(workspace_bytes) + " below the " +
+                                        std::to_string(need) + " this shape needs");
+    if (!aligned(workspace, 16))
+        return fail(EP_ERR_ALIGN, std::string(fn) + ": workspace must be 16-byte aligned");
+    return EP_OK;
+}
+
+}  // namespace
+
+size_t ep_layout_workspace_bytes(const ep_shape_t *shape)
+{
+    if (!shape || shape->T < 0 || shape->K < 1 || shape->E < 1 ||
+        (int64_t)shape->T * shape->K > INT32_MAX)
+        return 0;
+    return ep::layout_workspace_bytes(*shape);
+}
+
+int ep_layout_dispatch_ws(const ep_shape_t *shape, const uint16_t *x, const int32_t *topk_idx,
+                          int32_t *slot, int32_t *expert_count, int32_t *expert_offset,
+                          int32_t *rank_count, int32_t *rank_offset, int32_t *stats,
+                          uint16_t *recv, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream)
+{
+    const char *fn = "ep_layout_dispatch_ws";
+    if (int rc = check_layout_args(shape, topk_idx, slot, expert_count, expert_offset, stats, fn))
+        return rc;
+    if (int rc = check_rows(shape, fn, 8)) return rc;
+    if (shape->T > 0 && (!x || !recv))
+        return fail(EP_ERR_INVALID, "ep_layout_dispatch_ws: NULL required pointer");
+    if (!aligned(x, 16) || !aligned(recv, 16))
+        return fail(EP_ERR_ALIGN, "ep_layout_dispatch_ws: x and recv must be 16-byte aligned");
+    if (int rc = check_workspace(shape, workspace, workspace_bytes, fn)) return rc;
+    const ep::LayoutOut o{slot, expert_count, expert_offset, rank_count, rank_offset, stats};
+    return hip_status(ep::launch_layout_dispatch_bf16_chunked(
+                          *shape, x, topk_idx, o, recv, static_cast<int32_t *>(workspace), stream),
+                      fn);
+}
+
+int ep_layout_dispatch_fp8_ws(const ep_shape_t *shape, const uint16_t *x,
+                              const int32_t *topk_idx, int32_t *slot, int32_t *expert_count,
+                              int32_t *expert_offset, int32_t *rank_count, int32_t *rank_offset,
+                              int32_t *stats, uint8_t *recv_q, float *recv_scale,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    const char *fn = "ep_layout_dispatch_fp8_ws";
+    if (int rc = check_layout_args(shape, topk_idx, slot, expert_count, expert_offset, stats, fn))
+        return rc;
+    if (int rc = check_rows(shape, fn, EP_FP8_BLOCK)) return rc;
+    if (shape->T > 0 && (!x || !recv_q || !recv_scale))
+        return fail(EP_ERR_INVALID, "ep_layout_dispatch_fp8_ws: NULL required pointer");
+    if (!aligned(x, 16) || !aligned(recv_q, 16) || !aligned(recv_scale, 4))
+        return fail(EP_ERR_ALIGN, "ep_layout_dispatch_fp8_ws: x and recv_q must be 16-byte "
+                                  "aligned, recv_scale 4-byte aligned");
+    if (int rc = check_workspace(shape, workspace, workspace_bytes, fn)) return rc;
+    const ep::LayoutOut o{slot, expert_count, expert_offset, rank_count, rank_offset, stats};
+    return hip_status(ep::launch_layout_dispatch_fp8_chunked(*shape, x, topk_idx, o, recv_q,
+                                                             recv_scale,
+                                                             static_cast<int32_t *>(workspace),
+                                                             stream),
+                      fn);
+}
+
 int ep_dispatch(const ep_shape_t *shape, const uint16_t *x, const int32_t *topk_idx,
                 const int32_t *slot, uint16_t *recv, hipStream_t stream)
 {

@@ -40,11 +40,12 @@ namespace ep {
 
 namespace {
 
-template <int KG, int U, bool MULTI>
+// CHUNKED: step 1 of the layout reads the chunk histograms in `hist` (see ep_layout_tile.h).
+template <int KG, int U, bool MULTI, bool CHUNKED>
 __global__ __launch_bounds__(kTileThreads) void layout_dispatch_bf16_kernel(
     const u32x4 *__restrict__ x, const int32_t *__restrict__ idx, LayoutOut o,
     u32x4 *__restrict__ recv, int T, int H8, int E, int C, int K, int R, int nbits, int lg_nc,
-    int TT, int nseg)
+    int TT, int nseg, const int32_t *__restrict__ hist)
 {
     extern __shared__ __align__(16) int32_t lds[];
     __shared__ int32_t rows[kTileThreads];
@@ -59,8 +60,9 @@ __global__ __launch_bounds__(kTileThreads) void layout_dispatch_bf16_kernel(
     // layout's own loads (which the layout waits for in full), so both round trips overlap
     RowPiece<U> first;
     if (wave < nitems) first = load_item_bf16<U>(x, t0 + wave / nseg, wave % nseg, H8);
-    const TileIds ids = layout_tile_loads(idx, TK, t0 * K, TT * K);
-    layout_tile(ids, idx, TK, E, C, nbits, t0 * K, TT * K, last, lds, m, o.slot, rows);
+    const TileIds ids = layout_tile_loads<false, CHUNKED>(idx, TK, t0 * K, TT * K);
+    layout_tile<false, CHUNKED>(ids, idx, TK, E, C, nbits, t0 * K, TT * K, last, lds, m, o.slot,
+                                rows, 1, 0, hist);
     if (wave < nitems)
         store_item_bf16<KG, U, MULTI>(first, recv, rows, wave / nseg, wave % nseg, H8, K);
     for (int item = wave + kTileWaves; item < nitems; item += kTileWaves) {
@@ -70,11 +72,11 @@ __global__ __launch_bounds__(kTileThreads) void layout_dispatch_bf16_kernel(
     if (last) layout_finish<false>(TK, E, C, R, lds, m, o);
 }
 
-template <int KG, int U, bool MULTI>
+template <int KG, int U, bool MULTI, bool CHUNKED>
 __global__ __launch_bounds__(kTileThreads, EP_FUSED_FP8_WAVES) void layout_dispatch_fp8_kernel(
     const u32x4 *__restrict__ x, const int32_t *__restrict__ idx, LayoutOut o,
     u32x4 *__restrict__ recv_q, float *__restrict__ recv_scale, int T, int H, int E, int C,
-    int K, int R, int nbits, int lg_nc, int TT, int nseg)
+    int K, int R, int nbits, int lg_nc, int TT, int nseg, const int32_t *__restrict__ hist)
 {
     extern __shared__ __align__(16) int32_t lds[];
     __shared__ int32_t rows[kTileThreads];
@@ -90,10 +92,11 @@ __global__ __launch_bounds__(kTileThreads, EP_FUSED_FP8_WAVES) void layout_dispa
     // kernel takes 6.3 us against 6.6 us without the early loads, at T = 4096 the same 19.2 us
     // (issued before the own ids, they measured 18.6 -> 19.2 us there; cast before the layout,
     // 19.0 -> 19.8 us)
-    const TileIds ids = layout_tile_loads(idx, TK, t0 * K, TT * K);
+    const TileIds ids = layout_tile_loads<false, CHUNKED>(idx, TK, t0 * K, TT * K);
     RawPieceFp8<U> first;
     if (wave < nitems) first = load_item_fp8<U>(x, t0 + wave / nseg, wave % nseg, H);
-    layout_tile(ids, idx, TK, E, C, nbits, t0 * K, TT * K, last, lds, m, o.slot, rows);
+    layout_tile<false, CHUNKED>(ids, idx, TK, E, C, nbits, t0 * K, TT * K, last, lds, m, o.slot,
+                                rows, 1, 0, hist);
     if (wave < nitems)
         store_item_fp8<KG, U, MULTI>(cast_item_fp8<U>(first), recv_q, recv_scale, rows,
                                      wave / nseg, wave % nseg, H, K);
@@ -329,24 +332,25 @@ int pick_u(int TT, int H8)
     return u >= 4 ? 4 : (u >= 2 ? 2 : 1);
 }
 
-template <int U>
+template <int U, bool CHUNKED>
 hipError_t launch_bf16_u(const ep_shape_t &s, const u32x4 *x, const int32_t *idx,
                          const LayoutOut &o, u32x4 *recv, int H8, int TT, int nseg,
-                         hipStream_t stream)
+                         const int32_t *hist, hipStream_t stream)
 {
     const dim3 grid(s.T > 0 ? ceil_div(s.T, TT) : 1), block(kTileThreads);
     const int nbits = expert_bits(s.E), lg_nc = layout_lg_nc(s.E);
     const size_t lds = layout_lds_bytes(s.E, lg_nc);
 #define EP_LAUNCH_FUSED_BF16(KG, MULTI)                                                         \
-    return launch(layout_dispatch_bf16_kernel<KG, U, MULTI>, grid, block, lds, stream, x, idx,  \
-                  o, recv, s.T, H8, s.E, s.C, s.K, s.R, nbits, lg_nc, TT, nseg)
+    return launch(layout_dispatch_bf16_kernel<KG, U, MULTI, CHUNKED>, grid, block, lds, stream, \
+                  x, idx, o, recv, s.T, H8, s.E, s.C, s.K, s.R, nbits, lg_nc, TT, nseg, hist)
     EP_BY_K(s.K, EP_LAUNCH_FUSED_BF16);
 #undef EP_LAUNCH_FUSED_BF16
 }
 
-template <int U>
+template <int U, bool CHUNKED>
 hipError_t launch_fp8_u(const ep_shape_t &s, const u32x4 *x, const int32_t *idx,
-                        const LayoutOut &o, u32x4 *recv_q, float *recv_scale, hipStream_t stream)
+                        const LayoutOut &o, u32x4 *recv_q, float *recv_scale,
+                        const int32_t *hist, hipStream_t stream)
 {
     const int TT = pick_tt(s.T, s.K, true);
     const int nseg = ceil_div(s.H, U * 16 * kWave);
@@ -354,10 +358,39 @@ hipError_t launch_fp8_u(const ep_shape_t &s, const u32x4 *x, const int32_t *idx,
     const int nbits = expert_bits(s.E), lg_nc = layout_lg_nc(s.E);
     const size_t lds = layout_lds_bytes(s.E, lg_nc);
 #define EP_LAUNCH_FUSED_FP8(KG, MULTI)                                                          \
-    return launch(layout_dispatch_fp8_kernel<KG, U, MULTI>, grid, block, lds, stream, x, idx,  \
-                  o, recv_q, recv_scale, s.T, s.H, s.E, s.C, s.K, s.R, nbits, lg_nc, TT, nseg)
+    return launch(layout_dispatch_fp8_kernel<KG, U, MULTI, CHUNKED>, grid, block, lds, stream,  \
+                  x, idx, o, recv_q, recv_scale, s.T, s.H, s.E, s.C, s.K, s.R, nbits, lg_nc,    \
+                  TT, nseg, hist)
     EP_BY_K(s.K, EP_LAUNCH_FUSED_FP8);
 #undef EP_LAUNCH_FUSED_FP8
+}
+
+template <bool CHUNKED>
+hipError_t launch_fused_bf16(const ep_shape_t &s, const uint16_t *x, const int32_t *idx,
+                             const LayoutOut &o, uint16_t *recv, const int32_t *hist,
+                             hipStream_t stream)
+{
+    const int H8 = s.H / 8;
+    const int TT = pick_tt(s.T, s.K, false);
+    const int U = pick_u(TT, H8);
+    const int nseg = ceil_div(H8, U * kWave);
+    const u32x4 *xv = reinterpret_cast<const u32x4 *>(x);
+    u32x4 *rv = reinterpret_cast<u32x4 *>(recv);
+    if (U >= 4) return launch_bf16_u<4, CHUNKED>(s, xv, idx, o, rv, H8, TT, nseg, hist, stream);
+    if (U == 2) return launch_bf16_u<2, CHUNKED>(s, xv, idx, o, rv, H8, TT, nseg, hist, stream);
+    return launch_bf16_u<1, CHUNKED>(s, xv, idx, o, rv, H8, TT, nseg, hist, stream);
+}
+
+template <bool CHUNKED>
+hipError_t launch_fused_fp8(const ep_shape_t &s, const uint16_t *x, const int32_t *idx,
+                            const LayoutOut &o, uint8_t *recv_q, float *recv_scale,
+                            const int32_t *hist, hipStream_t stream)
+{
+    const u32x4 *xv = reinterpret_cast<const u32x4 *>(x);
+    u32x4 *qv = reinterpret_cast<u32x4 *>(recv_q);
+    if (pick_u_fp8(s.T, s.H) == 2)
+        return launch_fp8_u<2, CHUNKED>(s, xv, idx, o, qv, recv_scale, hist, stream);
+    return launch_fp8_u<1, CHUNKED>(s, xv, idx, o, qv, recv_scale, hist, stream);
 }
 
 }  // namespace
@@ -366,15 +399,25 @@ hipError_t launch_layout_dispatch_bf16(const ep_shape_t &s, const uint16_t *x,
                                        const int32_t *idx, const LayoutOut &o, uint16_t *recv,
                                        hipStream_t stream)
 {
-    const int H8 = s.H / 8;
-    const int TT = pick_tt(s.T, s.K, false);
-    const int U = pick_u(TT, H8);
-    const int nseg = ceil_div(H8, U * kWave);
-    const u32x4 *xv = reinterpret_cast<const u32x4 *>(x);
-    u32x4 *rv = reinterpret_cast<u32x4 *>(recv);
-    if (U >= 4) return launch_bf16_u<4>(s, xv, idx, o, rv, H8, TT, nseg, stream);
-    if (U == 2) return launch_bf16_u<2>(s, xv, idx, o, rv, H8, TT, nseg, stream);
-    return launch_bf16_u<1>(s, xv, idx, o, rv, H8, TT, nseg, stream);
+    return launch_fused_bf16<false>(s, x, idx, o, recv, nullptr, stream);
+}
+
+hipError_t launch_layout_dispatch_bf16_chunked(const ep_shape_t &s, const uint16_t *x,
+                                               const int32_t *idx, const LayoutOut &o,
+                                               uint16_t *recv, int32_t *hist,
+                                               hipStream_t stream)
+{
+    if (hipError_t e = launch_layout_chunk_hist(s, idx, hist, stream)) return e;
+    return launch_fused_bf16<true>(s, x, idx, o, recv, hist, stream);
+}
+
+hipError_t launch_layout_dispatch_fp8_chunked(const ep_shape_t &s, const uint16_t *x,
+                                              const int32_t *idx, const LayoutOut &o,
+                                              uint8_t *recv_q, float *recv_scale, int32_t *hist,
+                                              hipStream_t stream)
+{
+    if (hipError_t e = launch_layout_chunk_hist(s, idx, hist, stream)) return e;
+    return launch_fused_fp8<true>(s, x, idx, o, recv_q, recv_scale, hist, stream);
 }
 
 namespace {
@@ -431,10 +474,7 @@ hipError_t launch_layout_dispatch_fp8(const ep_shape_t &s, const uint16_t *x, co
                                       const LayoutOut &o, uint8_t *recv_q, float *recv_scale,
                                       hipStream_t stream)
 {
-    const u32x4 *xv = reinterpret_cast<const u32x4 *>(x);
-    u32x4 *qv = reinterpret_cast<u32x4 *>(recv_q);
-    if (pick_u_fp8(s.T, s.H) == 2) return launch_fp8_u<2>(s, xv, idx, o, qv, recv_scale, stream);
-    return launch_fp8_u<1>(s, xv, idx, o, qv, recv_scale, stream);
+    return launch_fused_fp8<false>(s, x, idx, o, recv_q, recv_scale, nullptr, stream);
 }
 
 // The fused packed kernels hold a second histogram in LDS; beyond this size (E above ~320)

@@ -94,6 +94,21 @@ hipError_t launch_layout_dispatch_fp8(const ep_shape_t &s, const uint16_t *x, co
                                       const LayoutOut &o, uint8_t *recv_q, float *recv_scale,
                                       hipStream_t stream);
 
+// The chunked form (large batches): chunk histograms into `hist` (layout_workspace_bytes:
+// one histogram of E + 2 words per 4096 pairs), then the fused kernel reading them. Same
+// outputs as the single launch.
+size_t layout_workspace_bytes(const ep_shape_t &s);
+hipError_t launch_layout_chunk_hist(const ep_shape_t &s, const int32_t *idx, int32_t *hist,
+                                    hipStream_t stream);
+hipError_t launch_layout_dispatch_bf16_chunked(const ep_shape_t &s, const uint16_t *x,
+                                               const int32_t *idx, const LayoutOut &o,
+                                               uint16_t *recv, int32_t *hist,
+                                               hipStream_t stream);
+hipError_t launch_layout_dispatch_fp8_chunked(const ep_shape_t &s, const uint16_t *x,
+                                              const int32_t *idx, const LayoutOut &o,
+                                              uint8_t *recv_q, float *recv_scale, int32_t *hist,
+                                              hipStream_t stream);
+
 hipError_t launch_combine(const ep_shape_t &s, const uint16_t *y, const int32_t *idx,
                           const int32_t *slot, const float *w, uint16_t *out,
                           hipStream_t stream, RowMap map = RowMap());

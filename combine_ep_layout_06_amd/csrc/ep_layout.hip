@@ -24,7 +24,50 @@ __global__ __launch_bounds__(kTileThreads) void layout_kernel(const int32_t *__r
     if (last) layout_finish<PACKED>(TK, E, C, R, lds, m, o);
 }
 
+// Histogram of each chunk of kLayoutChunk pairs: hist[c][b] = pairs of chunk c in bin b (the
+// E experts, then invalid, then unrouted), B = E + 2 words per chunk. One workgroup per chunk,
+// one 16-byte vector of ids per lane (the last, partial vector one id at a time).
+__global__ __launch_bounds__(kTileThreads) void layout_chunk_hist_kernel(
+    const int32_t *__restrict__ idx, int TK, int E, int32_t *__restrict__ hist)
+{
+    __shared__ int32_t h[EP_MAX_EXPERTS + 2];
+    const int tid = threadIdx.x, B = E + 2;
+    for (int k = tid; k < B; k += kTileThreads) h[k] = 0;
+    const int64_t p = (int64_t)blockIdx.x * kLayoutChunk + 4 * tid;   // kLayoutChunk = 4 * 1024
+    int4 v = int4{-1, -1, -1, -1};
+    if (p + 3 < TK) {
+        v = reinterpret_cast<const int4 *>(idx)[p / 4];
+    } else if (p < TK) {
+        v.x = idx[p];
+        if (p + 1 < TK) v.y = idx[p + 1];
+        if (p + 2 < TK) v.z = idx[p + 2];
+    }
+    __syncthreads();
+    const int64_t n = TK - p < 4 ? TK - p : 4;
+    const int e4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        if (c < n) atomicAdd(&h[layout_bin(e4[c], E)], 1);
+    __syncthreads();
+    for (int k = tid; k < B; k += kTileThreads) hist[(size_t)blockIdx.x * B + k] = h[k];
+}
+
 }  // namespace
+
+size_t layout_workspace_bytes(const ep_shape_t &s)
+{
+    const int64_t TK = (int64_t)s.T * s.K;
+    return (size_t)layout_chunks((int)TK) * (size_t)(s.E + 2) * sizeof(int32_t);
+}
+
+hipError_t launch_layout_chunk_hist(const ep_shape_t &s, const int32_t *idx, int32_t *hist,
+                                    hipStream_t stream)
+{
+    const int TK = s.T * s.K;
+    if (TK == 0) return hipSuccess;
+    return launch(layout_chunk_hist_kernel, dim3(layout_chunks(TK)), dim3(kTileThreads), 0,
+                  stream, idx, TK, s.E, hist);
+}
 
 hipError_t launch_layout(const ep_shape_t &s, const int32_t *idx, const LayoutOut &o,
                          hipStream_t stream)

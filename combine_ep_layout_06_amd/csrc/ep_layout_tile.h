@@ -36,6 +36,13 @@
 // (each id of the batch still costs one atomic). Step 3 then yields each expert's total, and
 // every workgroup scans the counts rounded up to the alignment into the packed offsets itself.
 //
+// CHUNKED (large batches, with a workspace): a first launch (layout_chunk_hist_kernel) writes
+// the histogram of every chunk of kLayoutChunk pairs to the workspace. Step 1 then adds, per
+// bin, the histograms of the chunks before the tile's chunk (lanes split over bins and chunks,
+// plain loads and adds) and counts only the earlier ids of its own chunk (at most one 16-byte
+// vector per lane). A workgroup's step 1 reads (T*K / kLayoutChunk) * (E + 2) words instead of
+// up to T*K ids; the results are the same.
+//
 // LDS is the launch's dynamic shared memory, carved by layout_lds_map(E, lg_nc); its size grows
 // with E (17 KB at E = 128, 140 KB at E = 1024).
 #pragma once
@@ -48,6 +55,12 @@ namespace ep {
 constexpr int kTileThreads = 1024;
 constexpr int kTileWaves = kTileThreads / kWave;
 constexpr int kPrefixVec = 8;      // 16-byte id vectors per lane issued up front in step 0
+constexpr int kLayoutChunk = 4096; // CHUNKED: pairs per chunk histogram (one vector per lane)
+static_assert(kLayoutChunk == 4 * kTileThreads, "a chunk is one 16-byte id vector per lane");
+
+// Chunks of kLayoutChunk pairs in a batch of TK pairs (the CHUNKED workspace holds one histogram
+// of E + 2 bins per chunk).
+__host__ __device__ inline int layout_chunks(int TK) { return (TK + kLayoutChunk - 1) / kLayoutChunk; }
 constexpr int kHistWords = (EP_MAX_EXPERTS + 2) * 16;   // budget of the replicated histogram
 
 // Copies per bin of the replicated histogram (a power of two, 16..64). More copies spread the
@@ -149,7 +162,7 @@ __device__ __forceinline__ OtherVecs other_vecs(int TK, int tile_begin, int P)
     return o;
 }
 
-template <bool ALL = false>
+template <bool ALL = false, bool CHUNKED = false>
 __device__ __forceinline__ TileIds layout_tile_loads(const int32_t *__restrict__ idx, int TK,
                                                      int tile_begin, int P)
 {
@@ -160,7 +173,16 @@ __device__ __forceinline__ TileIds layout_tile_loads(const int32_t *__restrict__
     t.tail = -1;
     // a batch is issued only if some lane of the wavefront needs it: the load pipe of a CU
     // moves ~64 bytes per clock, so clamped duplicates would still cost issue time
-    if constexpr (ALL) {
+    if constexpr (CHUNKED) {
+        // the earlier vectors of the tile's own chunk: fewer than kLayoutChunk / 4 = 1024
+        const int cb4 = (tile_begin / kLayoutChunk) * (kLayoutChunk / 4);
+        const int nv = tile_begin / 4 - cb4;
+        const int wave_q0 = __builtin_amdgcn_readfirstlane(tid & ~(kWave - 1));
+        const int4 *idx4 = reinterpret_cast<const int4 *>(idx);
+#pragma unroll
+        for (int u = 0; u < kPrefixVec; ++u) t.v[u] = int4{0, 0, 0, 0};
+        if (wave_q0 < nv && tid < nv) t.v[0] = idx4[cb4 + tid];
+    } else if constexpr (ALL) {
         const int tp = (TK / 4) * 4 + tid;      // a tail id past the tile
         if (tid < TK % 4 && tp >= tile_begin + P) t.tail = idx[tp];
         const OtherVecs ov = other_vecs(TK, tile_begin, P);
@@ -198,19 +220,34 @@ __device__ __forceinline__ TileIds layout_tile_loads(const int32_t *__restrict__
 // ALL: also counts the later tiles, and rows[k] = off[e] + slot, the pair's row in a packed
 // buffer of rows_cap rows with each expert's count rounded up to `align` (-1 if not kept or
 // past the buffer); the packed offsets are left in LDS at m.off.
-template <bool ALL = false>
+template <bool ALL = false, bool CHUNKED = false>
 __device__ __forceinline__ void layout_tile(const TileIds &ids, const int32_t *__restrict__ idx,
                                             int TK, int E, int C, int nbits, int tile_begin,
                                             int P, bool last, int32_t *lds,
                                             const LayoutLdsMap &m,
                                             int32_t *__restrict__ slot, int32_t *rows,
-                                            int align = 1, int rows_cap = 0)
+                                            int align = 1, int rows_cap = 0,
+                                            const int32_t *__restrict__ chunk_hist = nullptr)
 {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const int B = m.B, NC = 1 << m.lg_nc;
     int32_t *wcnt = lds + m.wcnt, *hist = lds + m.hist, *base = lds + m.base;
+
+    // CHUNKED: lane k = j*B + b sums bin b of the chunks j, j + J, j + 2J, ... before the
+    // tile's chunk (J = kTileThreads / B chunks side by side); the first pass is loaded before
+    // the LDS clear. With B > kTileThreads (E >= 1023) a few lanes take a second bin after it.
+    int csum = 0;
+    const int nchunk = tile_begin / kLayoutChunk;
+    const int J = B <= kTileThreads ? kTileThreads / B : 1;
+    if constexpr (CHUNKED) {
+        if (tid < J * B) {
+            const int b = tid % B;
+#pragma unroll 4
+            for (int cc = tid / B; cc < nchunk; cc += J) csum += chunk_hist[(size_t)cc * B + b];
+        }
+    }
 
     // zero the per-wavefront counts and the histogram copies (adjacent, 16-byte aligned)
     {
@@ -223,7 +260,20 @@ __device__ __forceinline__ void layout_tile(const TileIds &ids, const int32_t *_
     // 1. earlier tiles into the replicated histogram. Vectors past the prefix were clamped to
     //    its last one; their counts are skipped.
     const int copy = lane & (NC - 1);
-    if constexpr (ALL) {
+    if constexpr (CHUNKED) {
+        if (csum) atomicAdd(&hist[((tid % B) << m.lg_nc) + copy], csum);
+        for (int k = tid + kTileThreads; k < J * B; k += kTileThreads) {
+            int sum = 0;
+            for (int cc = k / B; cc < nchunk; cc += J) sum += chunk_hist[(size_t)cc * B + k % B];
+            if (sum) atomicAdd(&hist[((k % B) << m.lg_nc) + copy], sum);
+        }
+        const int nv = tile_begin / 4 - nchunk * (kLayoutChunk / 4);
+        if (tid < nv) {
+            const int e4[4] = {ids.v[0].x, ids.v[0].y, ids.v[0].z, ids.v[0].w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) atomicAdd(&hist[(layout_bin(e4[c], E) << m.lg_nc) + copy], 1);
+        }
+    } else if constexpr (ALL) {
         // every other vector: the earlier ones into hist, the later ones into the second
         // histogram, then the last TK % 4 ids if they come after the tile
         const OtherVecs ov = other_vecs(TK, tile_begin, P);

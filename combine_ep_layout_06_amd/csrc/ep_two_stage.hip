@@ -39,6 +39,15 @@
 #ifndef EP_RANKS_FUSED_TT
 #define EP_RANKS_FUSED_TT 0      // tokens per tile of the fused rank layout + stage 1
 #endif
+#ifndef EP_CR_NT_LOAD
+#define EP_CR_NT_LOAD 1          // partial combine: non-temporal expert-row loads
+#endif
+#ifndef EP_CR_NT_STORE
+#define EP_CR_NT_STORE 1         // partial combine: non-temporal partial-row stores
+#endif
+#ifndef EP_CR_U
+#define EP_CR_U 0                // partial combine: chunks per lane (0 = as the other kernels)
+#endif
 
 namespace ep {
 
@@ -645,7 +654,7 @@ __device__ __forceinline__ void combine_ranks_item(const PairLds &L, const u32x4
         wj[g] = __int_as_float(wave_uniform(__float_as_int(L.w[k])));
         const u32x4 *src = y + (size_t)(yr[g] >= 0 ? yr[g] : 0) * H8;
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[g][u] = load16<true>(src + cidx[u]);
+        for (int u = 0; u < U; ++u) v[g][u] = load16<EP_CR_NT_LOAD>(src + cidx[u]);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -669,7 +678,7 @@ __device__ __forceinline__ void combine_ranks_item(const PairLds &L, const u32x4
         u32x4 *dst = part + (size_t)pr[g] * H8;
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if (cok[u]) store16<true>(dst + cidx[u], pack_bf16(acc[u]));
+            if (cok[u]) store16<EP_CR_NT_STORE>(dst + cidx[u], pack_bf16(acc[u]));
     }
 }
 
@@ -1131,7 +1140,7 @@ hipError_t launch_combine_ranks(const ep_shape_t &s, const uint16_t *y, const in
 {
     const int H8 = s.H / 8;
     const bool seq = s.K > 8;
-    const int U = seq ? 1 : pick_u(s.T, H8);
+    const int U = seq ? 1 : EP_CR_U ? EP_CR_U : pick_u(s.T, H8);
     const int nseg = ceil_div(H8, U * kWave);
     const int tpb = pick_tpb(s.T, s.K, s.R);
     const dim3 grid = grid_for(s.T, tpb), block(kThreads);

@@ -29,6 +29,7 @@
 #ifndef EP_MI355X_EP_H
 #define EP_MI355X_EP_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -161,6 +162,41 @@ int ep_layout_dispatch_fp8(const ep_shape_t *shape, const uint16_t *x, const int
                            int32_t *slot, int32_t *expert_count, int32_t *expert_offset,
                            int32_t *rank_count, int32_t *rank_offset, int32_t *stats,
                            uint8_t *recv_q, float *recv_scale, hipStream_t stream);
+
+/*
+ * Large batches: the layout with a workspace.
+ *
+ * In ep_layout_dispatch every workgroup counts all the pairs before its tile, so the layout's
+ * work grows with the square of T*K. The _ws calls split it: a first launch writes the
+ * histogram of every chunk of 4096 pairs to a caller-provided workspace, and each tile of the
+ * fused layout + dispatch then adds the histograms of the chunks before its own and counts
+ * only the earlier pairs of its own chunk. Every output is bit-identical to ep_layout_dispatch
+ * (ep_layout_dispatch_fp8); the second launch pays off on large batches (on MI355X from about
+ * T*K = 2^16 pairs; below that the single launch is faster).
+ *
+ * ep_layout_workspace_bytes -- bytes the _ws calls need for this shape:
+ *   ceil(T*K / 4096) * (E + 2) * 4 (0 for T*K = 0 or an invalid shape). Host only.
+ * ep_layout_dispatch_ws / ep_layout_dispatch_fp8_ws -- the arguments of ep_layout_dispatch
+ *   (ep_layout_dispatch_fp8), then:
+ *   workspace       device memory owned by the caller, 16-byte aligned (else EP_ERR_ALIGN),
+ *                   at least ep_layout_workspace_bytes(shape) bytes (else EP_ERR_INVALID);
+ *                   overwritten by the call; nothing needs to be in it beforehand. Two calls
+ *                   in flight at once need two workspaces.
+ *   workspace_bytes its size.
+ */
+size_t ep_layout_workspace_bytes(const ep_shape_t *shape);
+
+int ep_layout_dispatch_ws(const ep_shape_t *shape, const uint16_t *x, const int32_t *topk_idx,
+                          int32_t *slot, int32_t *expert_count, int32_t *expert_offset,
+                          int32_t *rank_count, int32_t *rank_offset, int32_t *stats,
+                          uint16_t *recv, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+int ep_layout_dispatch_fp8_ws(const ep_shape_t *shape, const uint16_t *x,
+                              const int32_t *topk_idx, int32_t *slot, int32_t *expert_count,
+                              int32_t *expert_offset, int32_t *rank_count, int32_t *rank_offset,
+                              int32_t *stats, uint8_t *recv_q, float *recv_scale,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * ep_combine -- top-k weighted gather-reduce of expert outputs back onto each token.

@@ -143,9 +143,11 @@ class Case:
         sc.view(E * C, NB).index_fill_(0, rows, SENTINEL_F32)
         assert int((q != SENTINEL8).sum()) == 0 and int((sc != SENTINEL_F32).sum()) == 0
 
-    def check_fused(self, fp8: bool, full: bool):
-        """ep_layout_dispatch[_fp8]: every layout output bit-equal to the oracle's, and the
-        receive buffers exactly as the separate dispatch must leave them."""
+    def check_fused(self, fp8: bool, full: bool, ws: bool = False, workspace=None):
+        """ep_layout_dispatch[_fp8] (ws: the two-launch form with a workspace,
+        ep_layout_dispatch[_fp8]_ws): every layout output bit-equal to the oracle's, and the
+        receive buffers exactly as the separate dispatch must leave them. ``workspace`` (ws
+        only): a device tensor to use, e.g. one holding stale data from another call."""
         E, C, H, R = self.E, self.C, self.H, self.R
         i, s = kept_pairs(self.lay)
         e = self.idx.reshape(-1)[i]
@@ -154,10 +156,18 @@ class Case:
             NB = H // 128
             q = torch.full((E, C, H), SENTINEL8, dtype=torch.uint8, device=dev())
             sc = torch.full((E, C, NB), SENTINEL_F32, dtype=torch.float32, device=dev())
-            g = B.ep_layout_dispatch_fp8(self.x_d, self.idx_d, q, sc, E, C, R)
+            if ws:
+                g = B.ep_layout_dispatch_fp8_ws(self.x_d, self.idx_d, q, sc, E, C, R,
+                                                workspace=workspace)
+            else:
+                g = B.ep_layout_dispatch_fp8(self.x_d, self.idx_d, q, sc, E, C, R)
         else:
             recv = torch.full((E, C, H), SENTINEL16, dtype=torch.int16, device=dev())
-            g = B.ep_layout_dispatch(self.x_d, self.idx_d, recv, E, C, R)
+            if ws:
+                g = B.ep_layout_dispatch_ws(self.x_d, self.idx_d, recv, E, C, R,
+                                            workspace=workspace)
+            else:
+                g = B.ep_layout_dispatch(self.x_d, self.idx_d, recv, E, C, R)
         torch.cuda.synchronize()
         check_layout(self.idx, E, C, R, g)
         if fp8:

@@ -176,6 +176,31 @@ def test_fused_layout_expand_calls_reject_bad_arguments(lib):
               None) == B.EP_ERR_UNSUPPORTED
 
 
+def test_layout_workspace_calls(lib):
+    """ep_layout_workspace_bytes: one histogram of E + 2 words per 4096 pairs; the _ws calls
+    reject a missing, short or misaligned workspace (and everything ep_layout_dispatch does)."""
+    wsb = lib.ep_layout_workspace_bytes
+    assert wsb(shape(T=4096, K=8, E=128)) == 8 * 130 * 4
+    assert wsb(shape(T=4097, K=8, E=96)) == 9 * 98 * 4
+    assert wsb(shape(T=0)) == 0 and wsb(None) == 0 and wsb(shape(T=-1)) == 0
+    lay = (A16,) * 7                  # topk_idx, slot, count, offset, rank_count, rank_offset, stats
+    need = wsb(shape())
+    ws = lib.ep_layout_dispatch_ws
+    assert ws(shape(), A16, *lay, A16, None, need, None) == B.EP_ERR_INVALID
+    assert "workspace is NULL" in lib.ep_last_error().decode()
+    assert ws(shape(), A16, *lay, A16, A16, need - 1, None) == B.EP_ERR_INVALID
+    assert "below" in lib.ep_last_error().decode()
+    assert ws(shape(), A16, *lay, A16, A16 + 4, need, None) == B.EP_ERR_ALIGN
+    assert ws(shape(), A16 + 2, *lay, A16, A16, need, None) == B.EP_ERR_ALIGN
+    assert ws(shape(H=12), A16, *lay, A16, A16, need, None) == B.EP_ERR_UNSUPPORTED
+    assert ws(shape(E=2048, R=16), A16, *lay, A16, A16, 1 << 30, None) == B.EP_ERR_UNSUPPORTED
+    wq = lib.ep_layout_dispatch_fp8_ws
+    assert wq(shape(), A16, *lay, A16, A16, None, need, None) == B.EP_ERR_INVALID
+    assert wq(shape(), A16, *lay, A16, A16 + 2, A16, need, None) == B.EP_ERR_ALIGN
+    assert wq(shape(H=1000), A16, *lay, A16, A16, A16, need, None) == B.EP_ERR_UNSUPPORTED
+    assert wq(shape(), A16, *lay, A16, A16, A16, need - 4, None) == B.EP_ERR_INVALID
+
+
 def test_check_e4m3_conversion_rejects_bad_arguments(lib):
     chk = lib.ep_check_e4m3_conversion
     assert chk(0, 16, None, A16, None) == B.EP_ERR_INVALID

@@ -459,3 +459,71 @@ def test_combine_nan_and_inf_rows():
     assert np.array_equal(G.to_np(part).view(np.uint16)[r_i, p_i], wp[r_i, p_i])
     assert np.array_equal(G.to_np(out2).view(np.uint16),
                           oracle.combine_reduce(wp, orl["rank_slot"]))
+
+
+# the layout with a workspace (chunk histograms of 4096 pairs): shapes whose tiles start in
+# every position of a chunk, tiles that straddle chunk boundaries (K = 6, 5), a batch that is
+# one chunk exactly or one pair more, a ragged last vector (T*K % 4 != 0), E at its maximum
+# (E + 2 = 1026 bins: more bins than lanes), drops, unrouted and invalid ids
+WS_SMALL = [
+    # T, H, E, K, C, R
+    (512, 128, 16, 8, 300, 4),        # T*K = 4096: one chunk
+    (513, 128, 16, 8, 300, 4),        # 4104: a second chunk of 8 pairs
+    (1367, 256, 64, 6, 90, 8),        # 8202: K = 6, tiles of 8 tokens cross chunk boundaries
+    (2459, 128, 32, 5, 500, 4),       # 12295: K = 5, T*K % 4 = 3
+    (3000, 256, 1024, 8, 40, 8),      # E = 1024: 1026 bins
+    (4099, 256, 16, 4, 1100, 4),      # ragged last tile
+    (9000, 128, 128, 8, 700, 16),     # 72000 pairs, 18 chunks, drops
+]
+
+
+@pytest.mark.parametrize("T,H,E,K,C,R", WS_SMALL)
+def test_layout_dispatch_with_workspace(T, H, E, K, C, R):
+    print(f"[parity] layout+dispatch with workspace T={T} H={H} E={E} K={K} C={C} R={R}",
+          flush=True)
+    case = G.Case.random(T, H, E, K, C, R, seed=T + K)
+    case.check_fused(fp8=False, full=True, ws=True)
+    if H % 128 == 0:
+        case.check_fused(fp8=True, full=True, ws=True)
+
+
+@pytest.mark.parametrize("name", ["decode_fp8", "skew_zipf_c256", "prefill_bf16", "prefill_fp8"])
+def test_config_layout_dispatch_with_workspace(name):
+    """The workspace form on the full workloads, both dispatch dtypes, with a workspace that
+    holds stale data (the call must not depend on its contents)."""
+    cfg = W.get_config(name)
+    print(f"[parity] workspace form {name}", flush=True)
+    case = G.Case.from_config(cfg)
+    n = B.layout_workspace_bytes(cfg.T, cfg.K, cfg.E)
+    stale = torch.full((n,), 0x5A, dtype=torch.uint8, device=G.dev())
+    case.check_fused(fp8=False, full=False, ws=True, workspace=stale)
+    stale.fill_(0xC3)
+    case.check_fused(fp8=True, full=False, ws=True, workspace=stale)
+
+
+def test_layout_dispatch_with_workspace_many_pairs():
+    """2^17 pairs (32 chunks), E at its maximum, drops: the chunk sums over many chunks."""
+    cfg = W.EpConfig("max_e_ws", T=16384, H=128, E=B.EP_MAX_EXPERTS, K=8, C=100, R=8)
+    inp = W.make_inputs(cfg)
+    case = G.Case(cfg.T, cfg.H, cfg.E, cfg.K, cfg.C, cfg.R, inp["x"], inp["topk_idx"],
+                  inp["topk_w"])
+    assert case.lay["stats"]["dropped"] > 0
+    case.check_fused(fp8=False, full=False, ws=True)
+    case.check_fused(fp8=True, full=False, ws=True)
+
+
+def test_layout_dispatch_with_workspace_empty():
+    E, C, R, H = 16, 4, 4, 256
+    idx = torch.zeros((0, 8), dtype=torch.int32, device="cuda")
+    x = torch.zeros((0, H), dtype=torch.int16, device="cuda")
+    recv = torch.full((E, C, H), G.SENTINEL16, dtype=torch.int16, device="cuda")
+    g = B.ep_layout_dispatch_ws(x, idx, recv, E, C, R, workspace=torch.empty(0, dtype=torch.uint8,
+                                                                              device="cuda"),
+                                expert_count=torch.full((E,), 7, dtype=torch.int32, device="cuda"))
+    q = torch.full((E, C, H), G.SENTINEL8, dtype=torch.uint8, device="cuda")
+    sc = torch.full((E, C, H // 128), G.SENTINEL_F32, dtype=torch.float32, device="cuda")
+    g8 = B.ep_layout_dispatch_fp8_ws(x, idx, q, sc, E, C, R)
+    torch.cuda.synchronize()
+    assert G.to_np(g["expert_count"]).tolist() == [0] * E
+    assert G.to_np(g["stats"]).tolist() == [0, 0, 0, 0] == G.to_np(g8["stats"]).tolist()
+    assert int((recv != G.SENTINEL16).sum()) == 0 and int((q != G.SENTINEL8).sum()) == 0
