@@ -35,7 +35,7 @@ EXPORTED = ("ep_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_layout_dispatch",
             "ep_dispatch_packed_fp8", "ep_layout_dispatch_packed", "ep_layout_dispatch_packed_fp8",
             "ep_combine_packed", "ep_check_e4m3_conversion", "ep_last_launches",
             "ep_layout_workspace_bytes", "ep_layout_dispatch_ws", "ep_layout_dispatch_fp8_ws",
-            "ep_error_string", "ep_last_error", "ep_version")
+            "ep_layout_dispatch_noalloc", "ep_error_string", "ep_last_error", "ep_version")
 
 
 class EpShape(ctypes.Structure):
@@ -104,6 +104,7 @@ def load_library():
         L.ep_last_launches.argtypes = [ctypes.POINTER(EpLaunchRecord), ctypes.c_int]
         L.ep_layout_dispatch_ws.argtypes = [sp] + [vp] * 10 + [ctypes.c_size_t, vp]
         L.ep_layout_dispatch_fp8_ws.argtypes = [sp] + [vp] * 11 + [ctypes.c_size_t, vp]
+        L.ep_layout_dispatch_noalloc.argtypes = [sp] + [vp] * 10
         for fn in EXPORTED:
             if fn.startswith("ep_") and fn not in ("ep_error_string", "ep_last_error",
                                                    "ep_version", "ep_layout_workspace_bytes"):
@@ -357,6 +358,26 @@ def ep_layout_dispatch_ws(x: torch.Tensor, topk_idx: torch.Tensor, recv: torch.T
     sh = _shape(T, H, E, K, C, R)
     _call("ep_layout_dispatch_ws", sh, x, topk_idx, *_layout_ts(lay), recv, ws, nbytes,
           stream=stream)
+    return lay
+
+
+def ep_layout_dispatch_noalloc(x: torch.Tensor, topk_idx: torch.Tensor, recv: torch.Tensor,
+                               E: int, C: int, R: int, *, slot=None, expert_count=None,
+                               expert_offset=None, rank_count=None, rank_offset=None, stats=None,
+                               stream=None):
+    """ep_layout_dispatch_ws with the library's static scratch as the workspace (no workspace
+    argument; the C call allocates nothing). Pass every output to allocate nothing here
+    either."""
+    dev = x.device
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    lay = _layout_outputs(dev, T, K, E, R, slot, expert_count, expert_offset, rank_count,
+                          rank_offset, stats)
+    _need(x, "x", _bf16(x), T * H, dev)
+    _need(topk_idx, "topk_idx", torch.int32, T * K, dev)
+    _need(recv, "recv", _bf16(recv), E * C * H, dev)
+    sh = _shape(T, H, E, K, C, R)
+    _call("ep_layout_dispatch_noalloc", sh, x, topk_idx, *_layout_ts(lay), recv, stream=stream)
     return lay
 
 

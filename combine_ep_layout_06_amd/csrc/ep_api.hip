@@ -3,6 +3,7 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "ep.h"
@@ -154,6 +155,36 @@ int ep_layout_dispatch_fp8(const ep_shape_t *shape, const uint16_t *x, const int
 
 namespace {
 
+// The static scratch of ep_layout_dispatch_noalloc: device memory of the library itself, one
+// copy per GPU, held until the process ends. In host code `scratch` is only a stand-in for the
+// symbol; its device address on the current GPU comes from hipGetSymbolAddress, once per
+// device, and only that address is passed to kernels.
+constexpr size_t kScratchBytes = size_t(1) << 20;
+__device__ __align__(256) int32_t scratch[kScratchBytes / sizeof(int32_t)];
+
+constexpr int kScratchDevices = 64;
+void *g_scratch_ptr[kScratchDevices];
+hipError_t g_scratch_status[kScratchDevices];
+std::once_flag g_scratch_once[kScratchDevices];
+
+// This device's address of `scratch` (looked up on the first call on the device, with the
+// device current).
+int scratch_on_current_device(void **ptr, const char *fn)
+{
+    int dev = -1;
+    if (hipError_t e = hipGetDevice(&dev)) return hip_status(e, fn);
+    if (dev < 0 || dev >= kScratchDevices)
+        return fail(EP_ERR_UNSUPPORTED, std::string(fn) + ": device ordinal " +
+                                            std::to_string(dev) + " beyond the library's " +
+                                            std::to_string(kScratchDevices));
+    std::call_once(g_scratch_once[dev], [dev] {
+        g_scratch_status[dev] = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+    });
+    if (g_scratch_status[dev] != hipSuccess) return hip_status(g_scratch_status[dev], fn);
+    *ptr = g_scratch_ptr[dev];
+    return EP_OK;
+}
+
 // The workspace of the chunked layout: present, large enough and 16-byte aligned.
 int check_workspace(const ep_shape_t *shape, const void *workspace, size_t workspace_bytes,
                     const char *fn)
@@ -221,6 +252,35 @@ int ep_layout_dispatch_fp8_ws(const ep_shape_t *shape, const uint16_t *x,
                                                              recv_scale,
                                                              static_cast<int32_t *>(workspace),
                                                              stream),
+                      fn);
+}
+
+int ep_layout_dispatch_noalloc(const ep_shape_t *shape, const uint16_t *x,
+                               const int32_t *topk_idx, int32_t *slot, int32_t *expert_count,
+                               int32_t *expert_offset, int32_t *rank_count, int32_t *rank_offset,
+                               int32_t *stats, uint16_t *recv, hipStream_t stream)
+{
+    const char *fn = "ep_layout_dispatch_noalloc";
+    if (int rc = check_layout_args(shape, topk_idx, slot, expert_count, expert_offset, stats, fn))
+        return rc;
+    if (int rc = check_rows(shape, fn, 8)) return rc;
+    if (shape->T > 0 && (!x || !recv))
+        return fail(EP_ERR_INVALID, "ep_layout_dispatch_noalloc: NULL required pointer");
+    if (!aligned(x, 16) || !aligned(recv, 16))
+        return fail(EP_ERR_ALIGN, "ep_layout_dispatch_noalloc: x and recv must be 16-byte aligned");
+    const size_t need = ep::layout_workspace_bytes(*shape);
+    if (need > kScratchBytes)
+        return fail(EP_ERR_UNSUPPORTED, "ep_layout_dispatch_noalloc: this shape needs " +
+                                            std::to_string(need) +
+                                            " bytes of workspace, more than the library's "
+                                            "static scratch of " +
+                                            std::to_string(kScratchBytes) +
+                                            " (use ep_layout_dispatch_ws)");
+    void *ws = nullptr;
+    if (int rc = scratch_on_current_device(&ws, fn)) return rc;
+    const ep::LayoutOut o{slot, expert_count, expert_offset, rank_count, rank_offset, stats};
+    return hip_status(ep::launch_layout_dispatch_bf16_chunked(*shape, x, topk_idx, o, recv,
+                                                              static_cast<int32_t *>(ws), stream),
                       fn);
 }
 

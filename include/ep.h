@@ -199,6 +199,23 @@ int ep_layout_dispatch_fp8_ws(const ep_shape_t *shape, const uint16_t *x,
                               void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * ep_layout_dispatch_noalloc -- ep_layout_dispatch_ws without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The chunk histograms go to the library's own static
+ * scratch: 1 MiB of device memory per GPU, set aside when the library is loaded and held until
+ * the process ends; the call itself allocates nothing. A shape whose
+ * ep_layout_workspace_bytes exceeds 1 MiB (T*K above 4096 * floor(262144 / (E + 2)) pairs;
+ * 8.2 M pairs at E = 128) is rejected with EP_ERR_UNSUPPORTED. Arguments and outputs are those
+ * of ep_layout_dispatch, and the outputs are bit-identical to it. Every call on a GPU uses that
+ * GPU's one scratch, so two calls that overlap on one GPU (different streams, no ordering)
+ * race; calls on one stream are ordered and safe. Nothing in the scratch needs to be zero.
+ */
+int ep_layout_dispatch_noalloc(const ep_shape_t *shape, const uint16_t *x,
+                               const int32_t *topk_idx, int32_t *slot, int32_t *expert_count,
+                               int32_t *expert_offset, int32_t *rank_count, int32_t *rank_offset,
+                               int32_t *stats, uint16_t *recv, hipStream_t stream);
+
+/*
  * ep_combine -- top-k weighted gather-reduce of expert outputs back onto each token.
  *
  * Combine gathers the expert outputs and reduces them with the top-k weights on the token's

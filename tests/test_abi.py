@@ -201,6 +201,20 @@ def test_layout_workspace_calls(lib):
     assert wq(shape(), A16, *lay, A16, A16, A16, need - 4, None) == B.EP_ERR_INVALID
 
 
+def test_layout_dispatch_noalloc_rejects_beyond_its_scratch(lib):
+    """The static scratch holds 1 MiB: a shape whose workspace would be larger is rejected
+    (on the host, before any HIP call); so are the arguments ep_layout_dispatch rejects."""
+    na = lib.ep_layout_dispatch_noalloc
+    lay = (A16,) * 7
+    big = dict(T=1 << 21, K=8, E=128, C=4096, R=16)               # 4096 chunks of 130 words
+    assert lib.ep_layout_workspace_bytes(shape(**big)) > 1 << 20
+    assert na(shape(**big), A16, *lay, A16, None) == B.EP_ERR_UNSUPPORTED
+    assert "static scratch" in lib.ep_last_error().decode()
+    assert na(shape(), A16 + 2, *lay, A16, None) == B.EP_ERR_ALIGN
+    assert na(shape(), A16, *lay, None, None) == B.EP_ERR_INVALID
+    assert na(shape(H=12), A16, *lay, A16, None) == B.EP_ERR_UNSUPPORTED
+
+
 def test_check_e4m3_conversion_rejects_bad_arguments(lib):
     chk = lib.ep_check_e4m3_conversion
     assert chk(0, 16, None, A16, None) == B.EP_ERR_INVALID
