@@ -20,7 +20,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle_ep.so")
+# EP_ORACLE_LIB selects another build of ep_oracle.c (the sanitizer build of the tests)
+_LIB_PATH = os.environ.get("EP_ORACLE_LIB") or os.path.join(_HERE, "liboracle_ep.so")
 _lib = None
 
 _i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")

@@ -18,15 +18,21 @@ LIB = os.path.join(HERE, "liboracle_ep.so")
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
           "-Wall", "-Wextra", "-Werror"]
 
+# The sanitizer build (a test runs the oracle's tests against it): gcc's AddressSanitizer and
+# UndefinedBehaviorSanitizer, any finding fatal. CPU code only.
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=undefined"]
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = ["gcc", *CFLAGS, SRC, "-o", tmp, "-lm"]
+
+def build(verbose: bool = False, sanitize: bool = False, out: str | None = None) -> str:
+    out = out or LIB
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = ["gcc", *CFLAGS, *(SANITIZE_FLAGS if sanitize else []), SRC, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -44,7 +44,20 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
+
+/* Zeroed heap buffer of n elements of sz bytes (at least one); the oracle stops on failure. */
+static void *xcalloc(size_t n, size_t sz)
+{
+    void *p = calloc(n > 0 ? n : 1, sz);
+    if (!p) {
+        fprintf(stderr, "oracle: out of memory\n");
+        abort();
+    }
+    return p;
+}
 
 /* ----------------------------------------------------------------------------------------- */
 /* Number formats                                                                             */
@@ -176,8 +189,7 @@ void oracle_layout(int T, int K, int E, int C, int R, const int32_t *topk_idx, i
                    int32_t *count, int32_t *offset, int32_t *rank_count, int32_t *rank_offset,
                    int32_t *stats, int32_t *raw)
 {
-    int32_t demand[E > 0 ? E : 1];
-    for (int e = 0; e < E; ++e) demand[e] = 0;
+    int32_t *demand = xcalloc((size_t)E, sizeof *demand);
     int32_t kept = 0, dropped = 0, unrouted = 0, invalid = 0;
     long n = (long)T * K;
     for (long i = 0; i < n; ++i) {
@@ -205,6 +217,7 @@ void oracle_layout(int T, int K, int E, int C, int R, const int32_t *topk_idx, i
         run += s;
     }
     stats[0] = kept; stats[1] = dropped; stats[2] = unrouted; stats[3] = invalid;
+    free(demand);
 }
 
 /* A pair takes part in dispatch/combine only if its expert id and slot address a row of the
@@ -276,8 +289,8 @@ void oracle_dispatch_fp8(int T, int H, int E, int K, int C, const uint16_t *x,
                          float *recv_scale)
 {
     int NB = H / 128;
-    uint8_t q[H > 0 ? H : 1];
-    float sc[NB > 0 ? NB : 1];
+    uint8_t *q = xcalloc((size_t)H, sizeof *q);
+    float *sc = xcalloc((size_t)NB, sizeof *sc);
     for (int t = 0; t < T; ++t) {
         quantise_token(H, x + (long)t * H, q, sc);
         for (int j = 0; j < K; ++j) {
@@ -289,6 +302,8 @@ void oracle_dispatch_fp8(int T, int H, int E, int K, int C, const uint16_t *x,
             memcpy(recv_scale + r * NB, sc, (size_t)NB * sizeof(float));
         }
     }
+    free(q);
+    free(sc);
 }
 
 /* ----------------------------------------------------------------------------------------- */
@@ -364,8 +379,8 @@ void oracle_dispatch_ranks_fp8(int T, int H, int R, const uint16_t *x, const int
                                uint8_t *stage_q, float *stage_scale)
 {
     int NB = H / 128;
-    uint8_t q[H > 0 ? H : 1];
-    float sc[NB > 0 ? NB : 1];
+    uint8_t *q = xcalloc((size_t)H, sizeof *q);
+    float *sc = xcalloc((size_t)NB, sizeof *sc);
     for (int t = 0; t < T; ++t) {
         quantise_token(H, x + (long)t * H, q, sc);
         for (int r = 0; r < R; ++r) {
@@ -375,6 +390,8 @@ void oracle_dispatch_ranks_fp8(int T, int H, int R, const uint16_t *x, const int
             memcpy(stage_scale + ((long)r * T + p) * NB, sc, (size_t)NB * sizeof(float));
         }
     }
+    free(q);
+    free(sc);
 }
 
 /* Stage 2 of dispatch, the rank's own expansion: for every kept pair i = t*K + j of expert e
@@ -536,8 +553,8 @@ void oracle_dispatch_packed_fp8(int T, int H, int E, int K, int C, int rows, con
                                 const int32_t *offset, uint8_t *recv_q, float *recv_scale)
 {
     int NB = H / 128;
-    uint8_t q[H > 0 ? H : 1];
-    float sc[NB > 0 ? NB : 1];
+    uint8_t *q = xcalloc((size_t)H, sizeof *q);
+    float *sc = xcalloc((size_t)NB, sizeof *sc);
     for (int t = 0; t < T; ++t) {
         quantise_token(H, x + (long)t * H, q, sc);
         for (int j = 0; j < K; ++j) {
@@ -548,6 +565,8 @@ void oracle_dispatch_packed_fp8(int T, int H, int E, int K, int C, int rows, con
             memcpy(recv_scale + r * NB, sc, (size_t)NB * sizeof(float));
         }
     }
+    free(q);
+    free(sc);
 }
 
 /* Combine from the packed layout: as oracle_combine with y[e][slot] at row offset[e] + slot. */
