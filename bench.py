@@ -146,9 +146,11 @@ def run_starts(args):
 
 
 def roctx_ranges():
-    """(push, pop) of ROCm's roctx range API, or None if the library is not there."""
+    """(push, pop) of ROCm's roctx range API, or None if the library is not there. The
+    rocprofiler-sdk library comes first: rocprofv3 --marker-trace records its ranges."""
     import ctypes
-    for name in ("libroctx64.so", "libroctx64.so.4", "/opt/rocm/lib/libroctx64.so"):
+    for name in ("librocprofiler-sdk-roctx.so", "/opt/rocm/lib/librocprofiler-sdk-roctx.so",
+                 "libroctx64.so", "/opt/rocm/lib/libroctx64.so"):
         try:
             L = ctypes.CDLL(name)
         except OSError:

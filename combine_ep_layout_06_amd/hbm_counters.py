@@ -1,0 +1,246 @@
+"""HBM traffic of the benchmark's kernels from rocprofv3 counters, and kernel-trace summaries.
+
+``python -m combine_ep_layout_06_amd.hbm_counters collect --out DIR`` runs, for each workload
+and for a plain 256 MiB device copy (``bench.py --only copy_probe``), one rocprofv3 pass per
+counter (FETCH_SIZE, then WRITE_SIZE; each in a process of its own under a time limit).
+
+``python -m combine_ep_layout_06_amd.hbm_counters summarize --out DIR`` reads those passes and
+writes ``profiles/hbm_traffic.json`` (the record bench.py reads for ``roofline.traffic``) and one
+markdown table per workload. Per kernel, the median KiB per dispatch of each counter is scaled
+by the factor that makes the same counter read the known size of the copy, and set beside the
+kernel's algorithmic bytes (accounting.py). A record holds the SHA-256 of the kernel's sources,
+so the benchmark stops using it once they change.
+
+``python -m combine_ep_layout_06_amd.hbm_counters trace --csv FILE`` prints the per-kernel
+duration summary of a ``rocprofv3 --kernel-trace`` CSV as a markdown table; ``steps --csv FILE
+...`` the durations and gaps of the benchmark step's two kernels in each trace.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+COUNTERS = ("FETCH_SIZE", "WRITE_SIZE")
+WORKLOADS = ("prefill_bf16", "prefill_fp8")
+COPY_BYTES = 256 << 20
+
+# the kernels of the benchmark step, the name fragment that finds them in a trace, and the
+# sources whose hash keys the record
+KERNELS = {
+    "combine": ("combine_kernel", ["combine_ep_layout_06_amd/csrc/ep_combine.hip",
+                                   "combine_ep_layout_06_amd/csrc/ep_device.h",
+                                   "combine_ep_layout_06_amd/csrc/ep_internal.h"]),
+    "layout_dispatch": ("layout_dispatch_", ["combine_ep_layout_06_amd/csrc/ep_fused.hip",
+                                             "combine_ep_layout_06_amd/csrc/ep_layout_tile.h",
+                                             "combine_ep_layout_06_amd/csrc/ep_dispatch_item.h",
+                                             "combine_ep_layout_06_amd/csrc/ep_device.h",
+                                             "combine_ep_layout_06_amd/csrc/ep_internal.h"]),
+}
+
+
+def sources_sha256(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def pass_dir(out, counter, wl):
+    return os.path.join(out, f"pmc_{counter}_{wl}")
+
+
+def collect_command(out, counter, wl, display=False):
+    """The rocprofv3 pass; display: with $R for the repository root and plain python3."""
+    py, bench = (("python3", "$R/bench.py") if display
+                 else (sys.executable, os.path.join(ROOT, "bench.py")))
+    return ["timeout", "-s", "KILL", "120", "rocprofv3", "--pmc", counter, "-d",
+            pass_dir(out, counter, wl), "-o", wl, "--output-format", "csv", "--", py, bench,
+            "--only", wl, "--steps", "12", "--warmup", "4"]
+
+
+def collect(out):
+    os.makedirs(out, exist_ok=True)
+    for wl in ("copy_probe",) + WORKLOADS:
+        for counter in COUNTERS:
+            cmd = collect_command(out, counter, wl)
+            print("[counters] " + " ".join(cmd), flush=True)
+            res = subprocess.run(cmd, cwd="/tmp")
+            if res.returncode != 0:
+                print(f"[counters] pass failed with {res.returncode}", flush=True)
+                return res.returncode
+    return 0
+
+
+def read_counter(out, counter, wl):
+    """Kernel name -> list of the counter's value (KiB) per dispatch."""
+    files = glob.glob(os.path.join(pass_dir(out, counter, wl), "**", "*counter_collection.csv"),
+                      recursive=True)
+    per = {}
+    for path in files:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return per
+
+
+def pick(per, fragment):
+    """The values of the kernels whose name holds the fragment (one kernel per workload)."""
+    vals = [v for k, vs in per.items() if fragment in k for v in vs]
+    return vals
+
+
+def summarize(out, json_path, md_dir):
+    sys.path.insert(0, ROOT)
+    from combine_ep_layout_06_amd import accounting as A
+    from combine_ep_layout_06_amd import workloads as W
+
+    copy = {c: statistics.median(pick(read_counter(out, c, "copy_probe"), "")) for c in COUNTERS}
+    scale = {c: (COPY_BYTES / 1024) / copy[c] for c in COUNTERS}
+    records, tables = [], {}
+    for wl in WORKLOADS:
+        cfg = W.get_config(wl)
+        assert cfg.C >= cfg.T and cfg.route == "uniform"   # no drops: every pair is kept
+        n_kept = cfg.T * cfg.K
+        alg = {"combine": A.combine_bytes(cfg.T, cfg.K, cfg.H, n_kept),
+               "layout_dispatch": A.layout_bytes(cfg.T, cfg.K)
+               + A.dispatch_bytes(cfg.T, cfg.K, cfg.H, n_kept, cfg.fp8)}
+        rows = []
+        for kernel, (frag, srcs) in KERNELS.items():
+            v = {c: pick(read_counter(out, c, wl), frag) for c in COUNTERS}
+            if not v["FETCH_SIZE"] or not v["WRITE_SIZE"]:
+                continue
+            fk, wk = statistics.median(v["FETCH_SIZE"]), statistics.median(v["WRITE_SIZE"])
+            traffic = int(round((fk * scale["FETCH_SIZE"] + wk * scale["WRITE_SIZE"]) * 1024))
+            records.append({"kernel": kernel, "workload": wl,
+                            "launches_sampled": [len(v["FETCH_SIZE"]), len(v["WRITE_SIZE"])],
+                            "fetch_kib": fk, "write_kib": wk,
+                            "fetch_scale": round(scale["FETCH_SIZE"], 5),
+                            "write_scale": round(scale["WRITE_SIZE"], 5),
+                            "traffic_bytes": traffic, "algorithmic_bytes": alg[kernel],
+                            "sources": srcs, "sources_sha256": sources_sha256(srcs)})
+            rows.append((kernel, fk, scale["FETCH_SIZE"], wk, scale["WRITE_SIZE"], traffic,
+                         alg[kernel]))
+        tables[wl] = (cfg, rows)
+    rec = {"what": "HBM bytes per launch: median FETCH_SIZE and WRITE_SIZE (KiB per dispatch) "
+                   "over the sampled launches, each scaled by the factor that makes the same "
+                   "counter read the known size of a plain 256 MiB device copy (copy_probe). "
+                   "The benchmark reports traffic only while the kernel's sources still hash "
+                   "to sources_sha256. Written by combine_ep_layout_06_amd/hbm_counters.py.",
+           "copy_probe": {"bytes": COPY_BYTES, "fetch_kib": copy["FETCH_SIZE"],
+                          "write_kib": copy["WRITE_SIZE"]},
+           "commands": [" ".join(collect_command("$OUT", c, "<wl>", display=True))
+                        for c in COUNTERS]
+                       + ["<wl> in {copy_probe, " + ", ".join(WORKLOADS) + "}; run from /tmp"],
+           "records": records}
+    with open(json_path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    for wl, (cfg, rows) in tables.items():
+        lines = [f"# HBM traffic per launch: {wl} (T={cfg.T}, H={cfg.H}, E={cfg.E}, K={cfg.K}, "
+                 f"C={cfg.C}, {'FP8' if cfg.fp8 else 'bf16'} dispatch)", "",
+                 "rocprofv3 counter passes, one counter per run, median KiB per dispatch over "
+                 "the sampled launches, each scaled by the factor that makes the counter read "
+                 f"the known size of a plain 256 MiB device copy (FETCH_SIZE reads "
+                 f"{copy['FETCH_SIZE']:.1f} KiB, WRITE_SIZE {copy['WRITE_SIZE']:.1f} KiB for "
+                 f"{COPY_BYTES // 1024} KiB).", "",
+                 "Commands (run from /tmp; the package module prints and runs them):", "", "```",
+                 "python3 -m combine_ep_layout_06_amd.hbm_counters collect --out $OUT", *rec["commands"],
+                 "python3 -m combine_ep_layout_06_amd.hbm_counters summarize --out $OUT",
+                 "```", "",
+                 "| kernel | FETCH_SIZE KiB | x scale | WRITE_SIZE KiB | x scale | HBM bytes | "
+                 "algorithmic bytes | ratio |", "|---|---|---|---|---|---|---|---|"]
+        for kernel, fk, fs, wk, ws, traffic, alg in rows:
+            lines.append(f"| {kernel} | {fk:.1f} | {fs:.5f} | {wk:.1f} | {ws:.5f} | "
+                         f"{traffic:,} | {alg:,} | {traffic / alg:.3f} |")
+        with open(os.path.join(md_dir, f"hbm_counters_{wl}.md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+    return 0
+
+
+def trace_table(path, top=0):
+    """Per-kernel duration summary of a --kernel-trace CSV (us), as markdown rows."""
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "").replace("void ", "")
+            key = (name.split("(")[0].replace("ep::", ""), int(r["Grid_Size_X"]),
+                   int(r["Workgroup_Size_X"]))
+            per.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                                           / 1e3)
+    rows = sorted(per.items(), key=lambda kv: -sum(kv[1]))
+    out = ["| kernel | grid (lanes) | workgroup | launches | mean | median | min | max |",
+           "|---|---|---|---|---|---|---|---|"]
+    for (name, grid, wg), ts in rows[:top or None]:
+        out.append(f"| {name[:70]} | {grid} | {wg} | {len(ts)} | {statistics.fmean(ts):.2f} | "
+                   f"{statistics.median(ts):.2f} | {min(ts):.2f} | {max(ts):.2f} |")
+    return "\n".join(out)
+
+
+def step_table(paths):
+    """Per trace: the step's two kernels (a fused layout + dispatch launch followed by a combine
+    launch) and the gaps around them, median and min over the steps, as markdown rows. A step
+    that follows a fill (the cold protocol) also gives the gap from the fill's end to the
+    first kernel's start."""
+    out = ["| trace | steps | fill end -> first kernel | layout + dispatch | gap | combine | "
+           "first start -> combine end |", "|---|---|---|---|---|---|---|"]
+    for path in paths:
+        ks = []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                n = r["Kernel_Name"]
+                kind = ("ld" if "layout_dispatch_" in n else "cb" if "combine_kernel" in n
+                        else "fill" if "FillFunctor" in n else "other")
+                ks.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), kind))
+        ks.sort()
+        cols = {"fill": [], "ld": [], "gap": [], "cb": [], "span": []}
+        for i in range(len(ks) - 1):
+            (s0, e0, k0), (s1, e1, k1) = ks[i], ks[i + 1]
+            if k0 != "ld" or k1 != "cb":
+                continue
+            cols["ld"].append((e0 - s0) / 1e3)
+            cols["cb"].append((e1 - s1) / 1e3)
+            cols["gap"].append((s1 - e0) / 1e3)
+            cols["span"].append((e1 - s0) / 1e3)
+            if i > 0 and ks[i - 1][2] == "fill":
+                cols["fill"].append((s0 - ks[i - 1][1]) / 1e3)
+        f = lambda v: f"{statistics.median(v):.2f} ({min(v):.2f})" if v else "-"
+        out.append(f"| {os.path.basename(os.path.dirname(path))} | {len(cols['ld'])} | "
+                   f"{f(cols['fill'])} | {f(cols['ld'])} | {f(cols['gap'])} | {f(cols['cb'])} | "
+                   f"{f(cols['span'])} |")
+    return "\n".join(out)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("action", choices=("collect", "summarize", "trace", "steps"))
+    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "pmc"))
+    ap.add_argument("--json", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"))
+    ap.add_argument("--md-dir", default=os.path.join(ROOT, "profiles"))
+    ap.add_argument("--csv", default=None, nargs="+")
+    ap.add_argument("--top", type=int, default=0)
+    a = ap.parse_args()
+    if a.action == "collect":
+        return collect(a.out)
+    if a.action == "summarize":
+        return summarize(a.out, a.json, a.md_dir)
+    if a.action == "steps":
+        print(step_table(a.csv))
+        return 0
+    print(trace_table(a.csv[0], a.top))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
