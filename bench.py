@@ -85,6 +85,7 @@ def parse():
 START_FIGURES = (
     ("prefill_bf16 us_per_step", ("us_per_step",)),
     ("prefill_bf16 cold us_median", ("cold_single_shot", "us_median")),
+    ("prefill_bf16 cold read-flush us_median", ("cold_single_shot_read_flush", "us_median")),
     ("prefill_fp8 us_per_step", ("prefill_fp8", "us_per_step")),
     ("prefill_fp8 cold us_median", ("prefill_fp8", "cold_single_shot", "us_median")),
     ("decode_bf16 us_single_shot_median", ("t128_us", "decode_bf16", "us_single_shot_median")),
@@ -330,19 +331,26 @@ class Workload:
         return ev0.elapsed_time(ev1) / steps, wall / steps * 1e3
 
     @gc_paused
-    def single_shot(self, samples, flush, step=None):
+    def single_shot(self, samples, flush, step=None, read_flush=False):
         """Single-shot latency of one step, cold: each sample first overwrites `flush` (2 GiB,
         beyond every cache level) outside the event pair. While that fill runs, the host has
         already enqueued the event pair and the step's three launches, so the pair measures
         the GPU-side time of the step including the gaps between its kernels, not host-side
-        launch overhead."""
+        launch overhead. With read_flush the 2 GiB are read (summed) instead of written: the
+        caches then hold none of the step's data and none of the fill's dirty lines, which a
+        written flush leaves for the step to write back."""
         torch = self.torch
         step = step or self.step
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        sink = torch.empty((), dtype=torch.int64, device=flush.device)
+        words = flush.view(torch.int64)
         ts = []
         for k in range(samples):
             torch.cuda.synchronize()
-            flush.fill_(k & 0x7F)
+            if read_flush:
+                torch.sum(words, dim=0, out=sink)
+            else:
+                flush.fill_(k & 0x7F)
             ev0.record()
             step(k)
             ev1.record()
@@ -890,6 +898,13 @@ def main():
             # any of the step's data (the pipelined loop above reuses the layer's buffers)
             ss = wl.single_shot(args.latency_samples, flush)
             r["cold_single_shot"] = {
+                "flush": "2 GiB written before each sample",
+                "us_median": round(statistics.median(ss), 3),
+                "us_min": round(min(ss), 3), "us_max": round(max(ss), 3),
+                "hbm_frac": round(alg / (statistics.median(ss) * 1e-6) / A.HBM_PEAK_BYTES_PER_S, 4)}
+            ss = wl.single_shot(args.latency_samples, flush, read_flush=True)
+            r["cold_single_shot_read_flush"] = {
+                "flush": "2 GiB read before each sample (no dirty lines left in the caches)",
                 "us_median": round(statistics.median(ss), 3),
                 "us_min": round(min(ss), 3), "us_max": round(max(ss), 3),
                 "hbm_frac": round(alg / (statistics.median(ss) * 1e-6) / A.HBM_PEAK_BYTES_PER_S, 4)}
@@ -960,7 +975,8 @@ def main():
         c, _, rr, _, _ = results[name]
         keys = ("us_per_step", "wall_us_per_step", "replayed_step", "us_single_shot_median",
                 "graph_us_single_shot_median", "logical_GBps", "hbm_frac", "cold_single_shot",
-                "kernel_avg_us", "three_call_step", "launches", "fixture_sha256")
+                "cold_single_shot_read_flush", "kernel_avg_us", "three_call_step", "launches",
+                "fixture_sha256")
         return {k: rr[k] for k in keys if k in rr}
 
     line = {
@@ -984,6 +1000,8 @@ def main():
         "hbm_roofline_frac_by_protocol": {
             "primary": "cold_single_shot",
             "cold_single_shot": (r.get("cold_single_shot") or {}).get("hbm_frac"),
+            "cold_single_shot_read_flush":
+                (r.get("cold_single_shot_read_flush") or {}).get("hbm_frac"),
             "rotating_all_buffers": (r.get("rotating_all_buffers") or {}).get("hbm_frac"),
             "pipelined_warm": r["hbm_frac"],
             "pipelined_warm_note": "K steps back to back over persistent layer buffers: part "
@@ -992,6 +1010,7 @@ def main():
         "kernel_avg_us": r["kernel_avg_us"],
         "kernel_GBps": r["kernel_GBps"],
         "cold_single_shot": r.get("cold_single_shot"),
+        "cold_single_shot_read_flush": r.get("cold_single_shot_read_flush"),
         "rotating_all_buffers": r.get("rotating_all_buffers"),
         "three_call_step": r.get("three_call_step"),
         "replayed_step": r.get("replayed_step"),
