@@ -117,6 +117,10 @@ __global__ __launch_bounds__(kTileThreads, EP_FUSED_FP8_WAVES) void layout_dispa
 // SIMD (47 VGPRs, 78 SGPRs: two 1024-lane workgroups per CU). Prefill bf16 (T = 4096, R = 16):
 // 48.6 us against 6.7 + 44.8 us for the layout and the expansion apart; half rows per item
 // spill under that bound (60.1 us), and without it one workgroup fits per CU (49.6 us).
+// The staged row of a pair depends only on its id and rank_slot, so the first item's loads
+// could go out before the layout, as the one-stage kernels do with x; measured on MI355X this
+// gains under 2% on bf16 (48.5 -> 47.7 us with 4 of 8 pairs early, the 8-pair form spills) and
+// costs FP8 6 to 20% (22.1 -> 23.4 / 26.8 us), so the loads stay after the layout.
 template <int KG, int U, bool MULTI>
 __global__ __launch_bounds__(kTileThreads, 8) void layout_expand_bf16_kernel(
     const u32x4 *__restrict__ stage, const int32_t *__restrict__ idx,

@@ -343,6 +343,18 @@ def test_two_stage_empty_and_unrouted():
     torch.cuda.synchronize()
     assert G.to_np(lx["expert_count"]).tolist() == [0] * 8
     assert (G.to_np(recv).view(np.uint16) == np.uint16(S16)).all()
+    # the same for FP8: zero counts and stats, nothing copied
+    rq = torch.full((8, 2, 256), S8, dtype=torch.uint8, device="cuda")
+    rs = torch.full((8, 2, 2), SF, dtype=torch.float32, device="cuda")
+    lq = B.ep_layout_dispatch_expand_fp8(torch.zeros((4, 0, 256), dtype=torch.uint8, device="cuda"),
+                                         torch.zeros((4, 0, 2), dtype=torch.float32, device="cuda"),
+                                         idx, torch.zeros((0, 4), dtype=torch.int32, device="cuda"),
+                                         rq, rs, 8, 2,
+                                         stats=torch.full((4,), 7, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert G.to_np(lq["expert_count"]).tolist() == [0] * 8
+    assert G.to_np(lq["stats"]).tolist() == [0, 0, 0, 0]
+    assert int((rq != S8).sum()) == 0 and int((rs != SF).sum()) == 0
     # every id unrouted or invalid: nothing is sent anywhere, the output is +0
     ts = TwoStage(16, 64, 8, 4, 4, 4, np.where(np.arange(64).reshape(16, 4) % 2, -1, 9)
                   .astype(np.int32), W.f32_to_bf16_bits(np.ones((16, 64), np.float32)),
