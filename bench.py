@@ -24,9 +24,10 @@ outputs, as an MoE layer does. A variant where every batch also has its own buff
 reported beside it. Decode-like latency is single-shot: each sample first overwrites 2 GiB
 (beyond every cache) outside the event pair, then times one step (median of the samples).
 
-``--starts N`` repeats all of this in N fresh processes, the order of the four step configs
-rotated by one place per start, and reports the median start with each figure's per-start
-median, min, max and coefficient of variation.
+``--starts N`` (default 3; 1 with ``--only``) repeats all of this in N fresh processes, the
+order of the four step configs rotated by one place per start, and reports the median start
+with each figure's per-start median, min, max and coefficient of variation. ``--starts 1``
+runs in this process.
 
 ``--gpus N`` with N > 1 is refused: the benchmark measures one GPU; the library has no
 inter-GPU transport.
@@ -60,10 +61,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget for the oracle's CPU baseline")
-    ap.add_argument("--starts", type=int, default=1,
+    ap.add_argument("--starts", type=int, default=None,
                     help="run the benchmark in this many fresh processes, one after another, "
                          "each with the config order rotated by one more place, and report the "
-                         "median over the starts (with min, max and CV per config)")
+                         "median over the starts (with min, max and CV per config); default 3, "
+                         "1 with --only")
     ap.add_argument("--rotate", type=int, default=0,
                     help="rotate the order of the four step configs by this many places")
     ap.add_argument("--only", default=None,
@@ -131,7 +133,8 @@ def run_starts(args):
     import subprocess
     lines = []
     for k in range(args.starts):
-        cmd = [sys.executable, os.path.abspath(__file__), "--steps", str(args.steps),
+        cmd = [sys.executable, os.path.abspath(__file__), "--starts", "1",
+               "--steps", str(args.steps),
                "--warmup", str(args.warmup), "--workload", args.workload,
                "--latency-samples", str(args.latency_samples),
                "--cpu-seconds", str(args.cpu_seconds), "--rotate", str(k)]
@@ -812,6 +815,8 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path has no "
               "inter-GPU transport).", file=sys.stderr)
         sys.exit(2)
+    if args.starts is None:
+        args.starts = 1 if args.only else 3
     if args.starts > 1:
         if args.only:
             print("--starts and --only do not combine", file=sys.stderr)

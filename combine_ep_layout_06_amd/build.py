@@ -3,7 +3,8 @@
 ``python -m combine_ep_layout_06_amd.build`` (or ``build()``) compiles every source under
 ``csrc/`` with hipcc for gfx950, one process per source in parallel, and links them into
 ``combine_ep_layout_06_amd/libep_mi355x.so``. Extra ``-D`` definitions (launch-shape overrides)
-can be passed with ``defines``.
+can be passed with ``defines`` (command line: ``-D EP_NAME=VALUE``, and ``--out`` for a variant
+library elsewhere, which the binding loads when ``EP_MI355X_LIB`` names it).
 
 The same compilation writes ``kernel_resources.json`` beside the library: per kernel (mangled
 symbol), the compiler's own resource report (scalar and vector registers, spills, LDS, the
@@ -103,5 +104,23 @@ def build(out: str = LIB, defines: dict | None = None, verbose: bool = False) ->
     return out
 
 
+def main(argv=None) -> int:
+    import argparse
+    ap = argparse.ArgumentParser(description="build the gfx950 library")
+    ap.add_argument("--out", default=LIB, help="library path (default: the package's own)")
+    ap.add_argument("-D", dest="defines", action="append", default=[], metavar="NAME=VALUE",
+                    help="a launch-shape override, e.g. -D EP_FUSED_TT=16 (repeatable)")
+    ap.add_argument("-v", "--verbose", action="store_true")
+    a = ap.parse_args(argv)
+    defines = {}
+    for d in a.defines:
+        name, sep, value = d.partition("=")
+        if not re.fullmatch(r"EP_[A-Z0-9_]+", name) or not sep or not value:
+            ap.error(f"-D {d}: expected EP_NAME=VALUE")
+        defines[name] = value
+    print(build(os.path.abspath(a.out), defines or None, a.verbose))
+    return 0
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    sys.exit(main())

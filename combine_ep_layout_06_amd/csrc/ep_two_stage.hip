@@ -48,6 +48,9 @@
 #ifndef EP_CR_U
 #define EP_CR_U 0                // partial combine: chunks per lane (0 = as the other kernels)
 #endif
+#ifndef EP_RANKS_FP8_U
+#define EP_RANKS_FP8_U 0         // fused FP8 rank kernel: 16-channel pieces per lane (0 = auto)
+#endif
 
 namespace ep {
 
@@ -970,7 +973,10 @@ namespace {
 // Tokens per fused tile: at most one wavefront's worth (one lane per token ranks the tile),
 // TT*R <= kRankTile staged rows; on prefill-sized batches 8 for bf16 rows (two workgroups per
 // CU, each wavefront copying one half row: 24.8 us at T = 4096 against 25.8 us with 16 tokens
-// and whole rows) and 16 for FP8 rows (one workgroup per CU); 4 on small batches.
+// and whole rows) and 16 for FP8 rows (one workgroup per CU); 4 on small batches. FP8 at
+// T = 4096, R = 3: 13.4 us with two 16-channel pieces per lane and 16-token tiles; with one
+// piece per lane the kernel fits two workgroups per CU (60 VGPRs, 64 SGPRs), but measured
+// 14.1 us at 8-token tiles and 14.2 us at 16; two pieces with 8-token tiles 15.8 us.
 int pick_tt_ranks(int T, int R, bool fp8)
 {
     int tt = EP_RANKS_FUSED_TT ? EP_RANKS_FUSED_TT : (T >= 2048 ? (fp8 ? 16 : 8) : 4);
@@ -1060,7 +1066,7 @@ hipError_t launch_rank_dispatch_fp8_kv(const ep_shape_t &s, const uint16_t *x,
 {
     const u32x4 *xv = reinterpret_cast<const u32x4 *>(x);
     u32x4 *qv = reinterpret_cast<u32x4 *>(stage_q);
-    if (pick_u_fp8(s.T, s.H) == 2)
+    if ((EP_RANKS_FP8_U ? EP_RANKS_FP8_U : pick_u_fp8(s.T, s.H)) == 2)
         return launch_rank_dispatch_fp8<KV, 2>(s, xv, idx, rank_slot, rank_tokens, qv,
                                                stage_scale, stream);
     return launch_rank_dispatch_fp8<KV, 1>(s, xv, idx, rank_slot, rank_tokens, qv, stage_scale,

@@ -11,6 +11,11 @@ by the factor that makes the same counter read the known size of the copy, and s
 kernel's algorithmic bytes (accounting.py). A record holds the SHA-256 of the kernel's sources,
 so the benchmark stops using it once they change.
 
+``collect-detail`` and ``detail`` do the same for two more passes per workload: the L2's
+write requests to memory (all, and those of 64 bytes; the rest are 32 bytes) and the mean
+number of wavefronts resident per CU over each dispatch, written to
+``profiles/launch_counters_prefill.md``.
+
 ``python -m combine_ep_layout_06_amd.hbm_counters trace --csv FILE`` prints the per-kernel
 duration summary of a ``rocprofv3 --kernel-trace`` CSV as a markdown table; ``steps --csv FILE
 ...`` the durations and gaps of the benchmark step's two kernels in each trace.
@@ -47,6 +52,14 @@ KERNELS = {
 }
 
 
+# counter groups of the detail passes, each within one pass's per-block limits (TCC: 2 of 4;
+# SQ: 4 of 8 with the accumulation's own counter; GRBM: 1 of 2)
+DETAIL_PASSES = {
+    "wrreq": ("TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum"),
+    "occupancy": ("MeanOccupancyPerCU", "SQ_WAVES", "SQ_BUSY_CU_CYCLES"),
+}
+
+
 def sources_sha256(paths):
     h = hashlib.sha256()
     for p in paths:
@@ -59,32 +72,45 @@ def pass_dir(out, counter, wl):
     return os.path.join(out, f"pmc_{counter}_{wl}")
 
 
-def collect_command(out, counter, wl, display=False):
-    """The rocprofv3 pass; display: with $R for the repository root and plain python3."""
+def collect_command(out, counter, wl, display=False, counters=None):
+    """The rocprofv3 pass (counters: the pass's counters, default the one named counter);
+    display: with $R for the repository root and plain python3."""
     py, bench = (("python3", "$R/bench.py") if display
                  else (sys.executable, os.path.join(ROOT, "bench.py")))
-    return ["timeout", "-s", "KILL", "120", "rocprofv3", "--pmc", counter, "-d",
-            pass_dir(out, counter, wl), "-o", wl, "--output-format", "csv", "--", py, bench,
-            "--only", wl, "--steps", "12", "--warmup", "4"]
+    return ["timeout", "-s", "KILL", "120", "rocprofv3", "--pmc", *(counters or (counter,)),
+            "-d", pass_dir(out, counter, wl), "-o", wl, "--output-format", "csv", "--", py,
+            bench, "--only", wl, "--steps", "12", "--warmup", "4"]
+
+
+def run_passes(passes):
+    """Runs (pass name, workload, counters) passes one by one; stops at the first failure."""
+    for name, wl, counters, out in passes:
+        cmd = collect_command(out, name, wl, counters=counters)
+        print("[counters] " + " ".join(cmd), flush=True)
+        res = subprocess.run(cmd, cwd="/tmp")
+        if res.returncode != 0:
+            print(f"[counters] pass failed with {res.returncode}", flush=True)
+            return res.returncode
+    return 0
 
 
 def collect(out):
     os.makedirs(out, exist_ok=True)
-    for wl in ("copy_probe",) + WORKLOADS:
-        for counter in COUNTERS:
-            cmd = collect_command(out, counter, wl)
-            print("[counters] " + " ".join(cmd), flush=True)
-            res = subprocess.run(cmd, cwd="/tmp")
-            if res.returncode != 0:
-                print(f"[counters] pass failed with {res.returncode}", flush=True)
-                return res.returncode
-    return 0
+    return run_passes([(c, wl, None, out) for wl in ("copy_probe",) + WORKLOADS
+                       for c in COUNTERS])
 
 
-def read_counter(out, counter, wl):
-    """Kernel name -> list of the counter's value (KiB) per dispatch."""
-    files = glob.glob(os.path.join(pass_dir(out, counter, wl), "**", "*counter_collection.csv"),
-                      recursive=True)
+def collect_detail(out):
+    os.makedirs(out, exist_ok=True)
+    return run_passes([(name, wl, counters, out) for wl in WORKLOADS
+                       for name, counters in DETAIL_PASSES.items()])
+
+
+def read_counter(out, counter, wl, pass_name=None):
+    """Kernel name -> list of the counter's value per dispatch (pass_name: the pass that
+    collected it, default the counter's own)."""
+    files = glob.glob(os.path.join(pass_dir(out, pass_name or counter, wl), "**",
+                                   "*counter_collection.csv"), recursive=True)
     per = {}
     for path in files:
         with open(path) as f:
@@ -169,6 +195,46 @@ def summarize(out, json_path, md_dir):
     return 0
 
 
+def detail(out, md_dir):
+    """Median per dispatch of each detail counter for the step's kernels, as a markdown file."""
+    sys.path.insert(0, ROOT)
+    from combine_ep_layout_06_amd import workloads as W
+
+    lines = ["# Write requests and occupancy per launch: prefill_bf16 and prefill_fp8", "",
+             "rocprofv3 counter passes over the benchmark's step (12 timed + 4 warmup steps, "
+             "median per dispatch). TCC_EA0_WRREQ_sum counts the L2's write requests to memory, "
+             "TCC_EA0_WRREQ_64B_sum those that carry 64 bytes (the others carry 32); "
+             "MeanOccupancyPerCU is the mean number of wavefronts resident per CU over the "
+             "dispatch (a 1024-lane workgroup is 16 wavefronts); SQ_BUSY_CU_CYCLES the summed "
+             "busy cycles of the CUs.", "",
+             "Commands (run from /tmp; the package module prints and runs them):", "", "```",
+             "python3 -m combine_ep_layout_06_amd.hbm_counters collect-detail --out $OUT",
+             *[" ".join(collect_command("$OUT", name, "<wl>", display=True, counters=c))
+               for name, c in DETAIL_PASSES.items()],
+             "<wl> in {" + ", ".join(WORKLOADS) + "}; run from /tmp",
+             "python3 -m combine_ep_layout_06_amd.hbm_counters detail --out $OUT",
+             "```", "",
+             "| workload | kernel | dispatches | WRREQ | WRREQ 64 B | bytes they carry | "
+             "mean waves per CU | waves | busy CU cycles |", "|---|---|---|---|---|---|---|---|---|"]
+    for wl in WORKLOADS:
+        cfg = W.get_config(wl)
+        for kernel, (frag, _) in KERNELS.items():
+            v = {c: pick(read_counter(out, c, wl, name), frag)
+                 for name, cs in DETAIL_PASSES.items() for c in cs}
+            if not all(v.values()):
+                continue
+            m = {c: statistics.median(x) for c, x in v.items()}
+            wr, w64 = m["TCC_EA0_WRREQ_sum"], m["TCC_EA0_WRREQ_64B_sum"]
+            carried = (wr - w64) * 32 + w64 * 64
+            lines.append(f"| {wl} ({'FP8' if cfg.fp8 else 'bf16'}) | {kernel} | "
+                         f"{len(v['TCC_EA0_WRREQ_sum'])} | {wr:,.0f} | {w64:,.0f} | "
+                         f"{carried:,.0f} | {m['MeanOccupancyPerCU']:.1f} | "
+                         f"{m['SQ_WAVES']:,.0f} | {m['SQ_BUSY_CU_CYCLES']:,.0f} |")
+    with open(os.path.join(md_dir, "launch_counters_prefill.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return 0
+
+
 def trace_table(path, top=0):
     """Per-kernel duration summary of a --kernel-trace CSV (us), as markdown rows."""
     per = {}
@@ -224,7 +290,8 @@ def step_table(paths):
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("action", choices=("collect", "summarize", "trace", "steps"))
+    ap.add_argument("action", choices=("collect", "summarize", "collect-detail", "detail",
+                                       "trace", "steps"))
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "pmc"))
     ap.add_argument("--json", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"))
     ap.add_argument("--md-dir", default=os.path.join(ROOT, "profiles"))
@@ -235,6 +302,10 @@ def main():
         return collect(a.out)
     if a.action == "summarize":
         return summarize(a.out, a.json, a.md_dir)
+    if a.action == "collect-detail":
+        return collect_detail(a.out)
+    if a.action == "detail":
+        return detail(a.out, a.md_dir)
     if a.action == "steps":
         print(step_table(a.csv))
         return 0

@@ -56,3 +56,34 @@ def test_missing_figures_are_left_out_and_no_lines_is_an_error(bench):
     assert out["starts"]["n"] == 1 and "prefill_bf16 us_per_step" not in out["starts"]
     with pytest.raises(ValueError):
         bench.aggregate_starts([])
+
+
+def test_default_is_three_starts_and_each_child_runs_one(bench, monkeypatch, capsys):
+    import json
+    import subprocess
+    import sys
+
+    monkeypatch.setattr(sys, "argv", ["bench.py"])
+    assert bench.parse().starts is None              # main() turns None into 3, or 1 with --only
+    calls = []
+
+    class Done:
+        returncode = 0
+
+        def __init__(self, value):
+            self.stdout = "[noise]\n" + json.dumps(line(value, 52.0, 12.0)) + "\n"
+
+    def fake_run(cmd, **kw):
+        calls.append(cmd)
+        return Done(5000.0 + len(calls))
+
+    monkeypatch.setattr(subprocess, "run", fake_run)
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--steps", "7", "--warmup", "2"])
+    bench.main()
+    out = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
+    assert len(calls) == 3 and out["starts"]["n"] == 3
+    for k, cmd in enumerate(calls):
+        assert cmd[cmd.index("--starts") + 1] == "1"          # a child never forks again
+        assert cmd[cmd.index("--rotate") + 1] == str(k)
+        assert cmd[cmd.index("--steps") + 1] == "7"
+        assert ("--no-cpu-baseline" in cmd) == (k > 0)         # only the first times the oracle
