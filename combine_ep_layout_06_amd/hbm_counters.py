@@ -14,7 +14,9 @@ so the benchmark stops using it once they change.
 ``collect-detail`` and ``detail`` do the same for two more passes per workload: the L2's
 write requests to memory (all, and those of 64 bytes; the rest are 32 bytes) and the mean
 number of wavefronts resident per CU over each dispatch, written to
-``profiles/launch_counters_prefill.md``.
+``profiles/launch_counters_prefill.md``; and three memory-path passes on the bf16 step (wave
+and instruction counts, L2 hits, misses and DRAM credit stalls, L2 read latency), written to
+``profiles/memory_path_counters_prefill_bf16.md``.
 
 ``python -m combine_ep_layout_06_amd.hbm_counters trace --csv FILE`` prints the per-kernel
 duration summary of a ``rocprofv3 --kernel-trace`` CSV as a markdown table; ``steps --csv FILE
@@ -57,6 +59,16 @@ KERNELS = {
 DETAIL_PASSES = {
     "wrreq": ("TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum"),
     "occupancy": ("MeanOccupancyPerCU", "SQ_WAVES", "SQ_BUSY_CU_CYCLES"),
+}
+# memory-path passes on the bf16 prefill step (SQ: 8 of 8; TCC: 4 of 4; TA 2, TCP 3 of 4)
+MEMORY_WORKLOAD = "prefill_bf16"
+MEMORY_PASSES = {
+    "diag1": ("SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VMEM",
+              "SQ_INST_LEVEL_VMEM", "SQ_INSTS_VMEM_RD", "SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_VALU"),
+    "diag2": ("TCC_HIT_sum", "TCC_MISS_sum", "TCC_EA0_RDREQ_sum",
+              "TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum"),
+    "diag3": ("TA_BUSY_avr", "TA_ADDR_STALLED_BY_TC_CYCLES_sum", "TCP_PENDING_STALL_CYCLES_sum",
+              "TCP_TCC_READ_REQ_LATENCY_sum", "TCP_TCC_READ_REQ_sum"),
 }
 
 
@@ -103,7 +115,9 @@ def collect(out):
 def collect_detail(out):
     os.makedirs(out, exist_ok=True)
     return run_passes([(name, wl, counters, out) for wl in WORKLOADS
-                       for name, counters in DETAIL_PASSES.items()])
+                       for name, counters in DETAIL_PASSES.items()]
+                      + [(name, MEMORY_WORKLOAD, counters, out)
+                         for name, counters in MEMORY_PASSES.items()])
 
 
 def read_counter(out, counter, wl, pass_name=None):
@@ -231,6 +245,51 @@ def detail(out, md_dir):
                          f"{carried:,.0f} | {m['MeanOccupancyPerCU']:.1f} | "
                          f"{m['SQ_WAVES']:,.0f} | {m['SQ_BUSY_CU_CYCLES']:,.0f} |")
     with open(os.path.join(md_dir, "launch_counters_prefill.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return memory_detail(out, md_dir)
+
+
+def memory_detail(out, md_dir):
+    """The memory-path passes: every counter per kernel (median per dispatch), and the ratios
+    that locate combine's limit, as a markdown file."""
+    wl = MEMORY_WORKLOAD
+    med = {k: {} for k in KERNELS}
+    for name, cs in MEMORY_PASSES.items():
+        for c in cs:
+            for kernel, (frag, _) in KERNELS.items():
+                v = pick(read_counter(out, c, wl, name), frag)
+                if v:
+                    med[kernel][c] = statistics.median(v)
+    if not all(med.values()):
+        return 0
+    lines = [f"# Memory-path counters: {wl} step kernels (T=4096, H=2048, E=128, K=8)", "",
+             "Three rocprofv3 counter passes, each its own run of the benchmark on the one "
+             "workload (12 timed steps after 4 warm-up steps); median per dispatch over the "
+             "sampled launches of each kernel. Commands (R = repository root, run from /tmp; "
+             "`python3 -m combine_ep_layout_06_amd.hbm_counters collect-detail` runs them, "
+             "`detail` writes this file):", "", "```",
+             *[" ".join(collect_command("$OUT", name, wl, display=True, counters=c))
+               for name, c in MEMORY_PASSES.items()], "```", "",
+             "| counter | layout_dispatch | combine |", "|---|---|---|"]
+    for c in sorted({c for cs in MEMORY_PASSES.values() for c in cs}):
+        a, b = med["layout_dispatch"].get(c), med["combine"].get(c)
+        lines.append(f"| {c} | {a:,.0f} | {b:,.0f} |")
+    cb, ld = med["combine"], med["layout_dispatch"]
+    ratio = lambda m, a, b: m[a] / m[b] if m.get(b) else float("nan")
+    lines += ["", "Ratios:", "",
+              f"* L2 read latency under load (TCP_TCC_READ_REQ_LATENCY_sum / TCP_TCC_READ_REQ_sum):"
+              f" combine {ratio(cb, 'TCP_TCC_READ_REQ_LATENCY_sum', 'TCP_TCC_READ_REQ_sum'):,.0f}"
+              f" cycles, layout_dispatch "
+              f"{ratio(ld, 'TCP_TCC_READ_REQ_LATENCY_sum', 'TCP_TCC_READ_REQ_sum'):,.0f}.",
+              f"* DRAM credit stalls per DRAM read request: combine "
+              f"{ratio(cb, 'TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum', 'TCC_EA0_RDREQ_sum'):.2f}, "
+              f"layout_dispatch "
+              f"{ratio(ld, 'TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum', 'TCC_EA0_RDREQ_sum'):.2f}.",
+              f"* L2 miss rate (TCC_MISS_sum / (TCC_HIT_sum + TCC_MISS_sum)): combine "
+              f"{cb['TCC_MISS_sum'] / (cb['TCC_HIT_sum'] + cb['TCC_MISS_sum']):.2f}, "
+              f"layout_dispatch "
+              f"{ld['TCC_MISS_sum'] / (ld['TCC_HIT_sum'] + ld['TCC_MISS_sum']):.2f}."]
+    with open(os.path.join(md_dir, f"memory_path_counters_{wl}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     return 0
 
