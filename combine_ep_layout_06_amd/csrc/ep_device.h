@@ -149,4 +149,23 @@ __device__ __forceinline__ float group8_max(float v)
     return __int_as_float(x);   // inputs are non-negative floats: integer order = value order
 }
 
+// The tile this workgroup takes. Workgroups go to the 8 XCDs round-robin (blockIdx mod 8), some
+// XCDs write more slowly than others, and a tile's layout pass grows with its position.
+// ORDER = 1: the odd XCDs take the first half of the tiles (the cheaper layouts) and the even
+// ones the second half; ORDER = 2 the other way round; each XCD's tiles interleaved with its
+// three peers'. A bijection on [0, gridDim.x) when gridDim.x is a multiple of 8, else the
+// identity; ORDER = 0: the identity.
+template <int ORDER>
+__device__ __forceinline__ int xcd_tile()
+{
+    if constexpr (ORDER != 0) {
+        const int n = gridDim.x, b = blockIdx.x;
+        if ((n & 7) != 0) return b;
+        const int x = b & 7, i = b >> 3;
+        const bool first_half = (x & 1) == (ORDER == 1 ? 1 : 0);
+        return (first_half ? 0 : n / 2) + 4 * i + (x >> 1);
+    }
+    return blockIdx.x;
+}
+
 }  // namespace ep

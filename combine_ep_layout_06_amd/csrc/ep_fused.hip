@@ -36,6 +36,26 @@
 #define EP_FUSED_FP8_WAVES 8
 #endif
 
+// Order of the tiles over the XCDs in each fused kernel (xcd_tile, ep_device.h). All keep the
+// identity. The bf16 layout + dispatch at T = 4096 ran 25.4-25.6 us with order 1 against
+// 26.0-26.3 us in one allocation of the benchmark's buffers, but 27.4 against 25.3 us (step
+// 53.1-53.5 against 51.7 us) when the buffers sat elsewhere (the benchmark's other config
+// orders): which XCDs write slowly depends on where the written rows lie. The FP8 one: 18.2-18.8
+// us with the identity, 18.6-18.8 with order 1, 19.3-19.4 with order 2. The layout + expansion
+// kernels: bf16 48.7 us all three ways; FP8 22.0 us with the identity, 22.4 and 23.0 us.
+#ifndef EP_FUSED_BF16_XCD_ORDER
+#define EP_FUSED_BF16_XCD_ORDER 0
+#endif
+#ifndef EP_FUSED_FP8_XCD_ORDER
+#define EP_FUSED_FP8_XCD_ORDER 0
+#endif
+#ifndef EP_EXPAND_BF16_XCD_ORDER
+#define EP_EXPAND_BF16_XCD_ORDER 0
+#endif
+#ifndef EP_EXPAND_FP8_XCD_ORDER
+#define EP_EXPAND_FP8_XCD_ORDER 0
+#endif
+
 namespace ep {
 
 namespace {
@@ -51,8 +71,9 @@ __global__ __launch_bounds__(kTileThreads) void layout_dispatch_bf16_kernel(
     __shared__ int32_t rows[kTileThreads];
     const LayoutLdsMap m = layout_lds_map(E, lg_nc);
     const int TK = T * K;
-    const bool last = blockIdx.x == gridDim.x - 1;
-    const int t0 = blockIdx.x * TT;
+    const int tile = xcd_tile<EP_FUSED_BF16_XCD_ORDER>();
+    const bool last = tile == (int)gridDim.x - 1;
+    const int t0 = tile * TT;
     const int nt = min(TT, T - t0);
     const int wave = wave_uniform(threadIdx.x / kWave);
     const int nitems = nt * nseg;
@@ -82,8 +103,9 @@ __global__ __launch_bounds__(kTileThreads, EP_FUSED_FP8_WAVES) void layout_dispa
     __shared__ int32_t rows[kTileThreads];
     const LayoutLdsMap m = layout_lds_map(E, lg_nc);
     const int TK = T * K;
-    const bool last = blockIdx.x == gridDim.x - 1;
-    const int t0 = blockIdx.x * TT;
+    const int tile = xcd_tile<EP_FUSED_FP8_XCD_ORDER>();
+    const bool last = tile == (int)gridDim.x - 1;
+    const int t0 = tile * TT;
     const int nt = min(TT, T - t0);
     const int wave = wave_uniform(threadIdx.x / kWave);
     const int nitems = nt * nseg;
@@ -131,8 +153,9 @@ __global__ __launch_bounds__(kTileThreads, 8) void layout_expand_bf16_kernel(
     __shared__ int32_t rows[kTileThreads];
     const LayoutLdsMap m = layout_lds_map(E, lg_nc);
     const int TK = T * K;
-    const bool last = blockIdx.x == gridDim.x - 1;
-    const int t0 = blockIdx.x * TT;
+    const int tile = xcd_tile<EP_EXPAND_BF16_XCD_ORDER>();
+    const bool last = tile == (int)gridDim.x - 1;
+    const int t0 = tile * TT;
     const int nt = min(TT, T - t0);
     const int wave = wave_uniform(threadIdx.x / kWave);
     const int lane = threadIdx.x & (kWave - 1);
@@ -194,8 +217,9 @@ __global__ __launch_bounds__(kTileThreads, 8) void layout_expand_fp8_kernel(
     __shared__ int32_t rows[kTileThreads];
     const LayoutLdsMap m = layout_lds_map(E, lg_nc);
     const int TK = T * K;
-    const bool last = blockIdx.x == gridDim.x - 1;
-    const int t0 = blockIdx.x * TT;
+    const int tile = xcd_tile<EP_EXPAND_FP8_XCD_ORDER>();
+    const bool last = tile == (int)gridDim.x - 1;
+    const int t0 = tile * TT;
     const int nt = min(TT, T - t0);
     const int wave = wave_uniform(threadIdx.x / kWave);
     const int lane = threadIdx.x & (kWave - 1);

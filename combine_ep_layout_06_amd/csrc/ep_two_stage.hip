@@ -48,6 +48,15 @@
 #ifndef EP_CR_U
 #define EP_CR_U 0                // partial combine: chunks per lane (0 = as the other kernels)
 #endif
+// Fused rank kernels: tile order over the XCDs (xcd_tile). At T = 4096 the FP8 one (R = 3,
+// 16-token tiles) takes 12.7-13.0 us with ORDER = 1 against 13.4 us with the identity; the bf16
+// one (R = 16) 23.7-23.9 us either way, 25.0 us with ORDER = 2.
+#ifndef EP_RANKS_BF16_XCD_ORDER
+#define EP_RANKS_BF16_XCD_ORDER 0
+#endif
+#ifndef EP_RANKS_FP8_XCD_ORDER
+#define EP_RANKS_FP8_XCD_ORDER 1
+#endif
 #ifndef EP_RANKS_FP8_U
 #define EP_RANKS_FP8_U 0         // fused FP8 rank kernel: 16-channel pieces per lane (0 = auto)
 #endif
@@ -399,12 +408,13 @@ __global__ __launch_bounds__(kRankTile, 8) void rank_layout_dispatch_bf16_kernel
     __shared__ int32_t rows[kRankTile];
     __shared__ int32_t slots[kRankTile];
     const int wave = wave_uniform(threadIdx.x / kWave);
-    const int t0 = blockIdx.x * TT, nt = min(TT, T - t0);
+    const int tile = xcd_tile<EP_RANKS_BF16_XCD_ORDER>();
+    const int t0 = tile * TT, nt = min(TT, T - t0);
     const int nitems = nt * nseg;
     // the first item's row loads need no slot: issued before the layout's loads
     RowPiece<U> first;
     if (wave < nitems) first = load_item_bf16<U>(x, t0 + wave / nseg, wave % nseg, H8);
-    rank_tile<KV, RQ>(idx, t0, nt, T, K, E, R, blockIdx.x == gridDim.x - 1, rank_slot,
+    rank_tile<KV, RQ>(idx, t0, nt, T, K, E, R, tile == (int)gridDim.x - 1, rank_slot,
                       rank_tokens, rows, slots, wcnt);
     if (wave < nitems)
         store_item_bf16<KG, U, MULTI>(first, stage, rows, wave / nseg, wave % nseg, H8, R);
@@ -428,12 +438,13 @@ __global__ __launch_bounds__(kRankTile, EP_RANKS_FP8_WAVES) void rank_layout_dis
     __shared__ int32_t rows[kRankTile];
     __shared__ int32_t slots[kRankTile];
     const int wave = wave_uniform(threadIdx.x / kWave);
-    const int t0 = blockIdx.x * TT, nt = min(TT, T - t0);
+    const int tile = xcd_tile<EP_RANKS_FP8_XCD_ORDER>();
+    const int t0 = tile * TT, nt = min(TT, T - t0);
     const int nitems = nt * nseg;
     // the first item's token row is loaded before the layout (it needs no slot) and cast after
     RawPieceFp8<U> first;
     if (wave < nitems) first = load_item_fp8<U>(x, t0 + wave / nseg, wave % nseg, H);
-    rank_tile<KV, RQ>(idx, t0, nt, T, K, E, R, blockIdx.x == gridDim.x - 1, rank_slot,
+    rank_tile<KV, RQ>(idx, t0, nt, T, K, E, R, tile == (int)gridDim.x - 1, rank_slot,
                       rank_tokens, rows, slots, wcnt);
     if (wave < nitems)
         store_item_fp8<KG, U, MULTI>(cast_item_fp8<U>(first), stage_q, stage_scale, rows,
