@@ -43,11 +43,14 @@
 #define EP_CR_NT_LOAD 1          // partial combine: non-temporal expert-row loads
 #endif
 #ifndef EP_CR_NT_STORE
-#define EP_CR_NT_STORE 1         // partial combine: non-temporal partial-row stores
+#define EP_CR_NT_STORE 0         // partial combine: non-temporal partial-row stores
 #endif
 #ifndef EP_CR_U
 #define EP_CR_U 0                // partial combine: chunks per lane (0 = as the other kernels)
 #endif
+#ifndef EP_RED_CACHED_BYTES
+#define EP_RED_CACHED_BYTES (64 << 20)  // final reduce: partial buffers up to this size are read
+#endif                                  // through the caches, larger ones non-temporally
 // Fused rank kernels: tile order over the XCDs (xcd_tile). At T = 4096 the FP8 one (R = 3,
 // 16-token tiles) takes 12.7-13.0 us with ORDER = 1 against 13.4 us with the identity; the bf16
 // one (R = 16) 23.7-23.9 us either way, 25.0 us with ORDER = 2.
@@ -762,7 +765,9 @@ __global__ __launch_bounds__(kThreads) void combine_ranks_kernel(
 constexpr int kZeroChunks = 4096;
 __device__ u32x4 g_zero_row[kZeroChunks];
 
-template <int KG, int U, bool MULTI, bool ZROW>
+// NTL: the partial rows are loaded non-temporally (a partial buffer too large to stay in the
+// last-level cache between the partial combine and this kernel).
+template <int KG, int U, bool MULTI, bool ZROW, bool NTL>
 __global__ __launch_bounds__(kThreads) void combine_reduce_kernel(
     const u32x4 *__restrict__ part, const int32_t *__restrict__ rank_slot,
     u32x4 *__restrict__ out, int T, int H8, int R, int Q, int tpb, int nseg)
@@ -825,7 +830,7 @@ __global__ __launch_bounds__(kThreads) void combine_reduce_kernel(
                         wg[g] = 1.0f;
                     }
 #pragma unroll
-                    for (int u = 0; u < U; ++u) v[g][u] = load16<true>(src + cidx[u]);
+                    for (int u = 0; u < U; ++u) v[g][u] = load16<NTL>(src + cidx[u]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1157,7 +1162,11 @@ hipError_t launch_combine_ranks(const ep_shape_t &s, const uint16_t *y, const in
 {
     const int H8 = s.H / 8;
     const bool seq = s.K > 8;
-    const int U = seq ? 1 : EP_CR_U ? EP_CR_U : pick_u(s.T, H8);
+    // at most half rows (two chunks per lane, 100 VGPRs, 4 wavefronts per SIMD), with plain
+    // partial-row stores: at T = 4096 44.4 against 50.7 us with whole rows and non-temporal
+    // stores (bf16, R = 16; pass 136.8-137.4 against 138.8-139.1 us), FP8 (R = 3) 35.2 against
+    // 36.0 us; whole rows with plain stores, or one chunk per lane, measured in between
+    const int U = seq ? 1 : EP_CR_U ? EP_CR_U : min(pick_u(s.T, H8), 2);
     const int nseg = ceil_div(H8, U * kWave);
     const int tpb = pick_tpb(s.T, s.K, s.R);
     const dim3 grid = grid_for(s.T, tpb), block(kThreads);
@@ -1194,16 +1203,26 @@ hipError_t launch_combine_reduce(const ep_shape_t &s, const uint16_t *part,
     const dim3 grid = grid_for(s.T, tpb), block(kThreads);
     const u32x4 *pv = reinterpret_cast<const u32x4 *>(part);
     u32x4 *ov = reinterpret_cast<u32x4 *>(out);
-#define EP_LAUNCH_RD_Z(KG, MULTI, Z)                                                            \
+    // the partial combine's plain stores leave a small partial buffer in the last-level cache:
+    // at T = 4096, H = 2048 the FP8 workload's R = 3 (50 MB of rows) reduces in 13.5 against
+    // 13.9 us and its pass takes 78.9-79.4 against 81.9-82.3 us read through the caches, while
+    // the bf16 workload's R = 16 (268 MB) is faster read non-temporally (22.6 against 23.8 us)
+    const bool ntl = (size_t)s.R * s.T * s.H * sizeof(uint16_t) > (size_t)EP_RED_CACHED_BYTES;
+#define EP_LAUNCH_RD_ZN(KG, MULTI, Z, N)                                                        \
     do {                                                                                        \
         if (U >= 4)                                                                             \
-            return launch(combine_reduce_kernel<KG, 4, MULTI, Z>, grid, block, 0, stream, pv,    \
+            return launch(combine_reduce_kernel<KG, 4, MULTI, Z, N>, grid, block, 0, stream, pv, \
                           rank_slot, ov, s.T, H8, s.R, Q, tpb, nseg);                           \
         if (U == 2)                                                                             \
-            return launch(combine_reduce_kernel<KG, 2, MULTI, Z>, grid, block, 0, stream, pv,    \
+            return launch(combine_reduce_kernel<KG, 2, MULTI, Z, N>, grid, block, 0, stream, pv, \
                           rank_slot, ov, s.T, H8, s.R, Q, tpb, nseg);                           \
-        return launch(combine_reduce_kernel<KG, 1, MULTI, Z>, grid, block, 0, stream, pv,        \
+        return launch(combine_reduce_kernel<KG, 1, MULTI, Z, N>, grid, block, 0, stream, pv,     \
                       rank_slot, ov, s.T, H8, s.R, Q, tpb, nseg);                               \
+    } while (0)
+#define EP_LAUNCH_RD_Z(KG, MULTI, Z)                                                            \
+    do {                                                                                        \
+        if (ntl) EP_LAUNCH_RD_ZN(KG, MULTI, Z, true);                                           \
+        EP_LAUNCH_RD_ZN(KG, MULTI, Z, false);                                                   \
     } while (0)
 #define EP_LAUNCH_RD(KG, MULTI)                                                                 \
     do {                                                                                        \
@@ -1216,6 +1235,7 @@ hipError_t launch_combine_reduce(const ep_shape_t &s, const uint16_t *part,
     EP_BY_K(Q, EP_LAUNCH_RD);
 #undef EP_LAUNCH_RD
 #undef EP_LAUNCH_RD_Z
+#undef EP_LAUNCH_RD_ZN
 }
 
 }  // namespace ep
