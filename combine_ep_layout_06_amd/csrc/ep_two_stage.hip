@@ -48,6 +48,9 @@
 #ifndef EP_CR_U
 #define EP_CR_U 0                // partial combine: chunks per lane (0 = as the other kernels)
 #endif
+#ifndef EP_EXPAND_NT_STORE
+#define EP_EXPAND_NT_STORE 1     // expansion: non-temporal expert-row stores (see ep_fused.hip)
+#endif
 #ifndef EP_RED_CACHED_BYTES
 #define EP_RED_CACHED_BYTES (64 << 20)  // final reduce: partial buffers up to this size are read
 #endif                                  // through the caches, larger ones non-temporally
@@ -561,7 +564,7 @@ __global__ __launch_bounds__(kThreads) void expand_bf16_kernel(
                     u32x4 *dst = recv + (size_t)d[g] * H8;
 #pragma unroll
                     for (int u = 0; u < U; ++u)
-                        if (cok[u]) store16<EP_DISPATCH_NT_STORE>(dst + cidx[u], v[g][u]);
+                        if (cok[u]) store16<EP_EXPAND_NT_STORE>(dst + cidx[u], v[g][u]);
                 }
             }
         }
@@ -612,7 +615,7 @@ __global__ __launch_bounds__(kThreads) void expand_fp8_kernel(
 #pragma unroll
                 for (int g = 0; g < KG; ++g) {
                     if (d[g] < 0) continue;
-                    if (act) recv_q[(size_t)d[g] * H16 + cq] = q[g];
+                    if (act) store16<EP_EXPAND_NT_STORE>(recv_q + (size_t)d[g] * H16 + cq, q[g]);
                     if (lead) recv_scale[(size_t)d[g] * NB + cs] = sc[g];
                 }
             }
