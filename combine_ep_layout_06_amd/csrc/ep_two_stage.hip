@@ -1168,7 +1168,8 @@ hipError_t launch_combine_ranks(const ep_shape_t &s, const uint16_t *y, const in
     // at most half rows (two chunks per lane, 100 VGPRs, 4 wavefronts per SIMD), with plain
     // partial-row stores: at T = 4096 44.4 against 50.7 us with whole rows and non-temporal
     // stores (bf16, R = 16; pass 136.8-137.4 against 138.8-139.1 us), FP8 (R = 3) 35.2 against
-    // 36.0 us; whole rows with plain stores, or one chunk per lane, measured in between
+    // 36.0 us; whole rows with plain stores, or one chunk per lane, measured in between. Four
+    // tokens per group (pick_tpb) stay: 1, 2 and 8 measured 45.9, 44.9-45.0 and 46.2 us (bf16)
     const int U = seq ? 1 : EP_CR_U ? EP_CR_U : min(pick_u(s.T, H8), 2);
     const int nseg = ceil_div(H8, U * kWave);
     const int tpb = pick_tpb(s.T, s.K, s.R);
