@@ -157,6 +157,39 @@ __device__ __forceinline__ RawPieceFp8<U> load_item_fp8(const u32x4 *__restrict_
     return r;
 }
 
+// The same loads with no branch: every lane loads (a lane past the row reads the row's first
+// chunk), so a caller that issued loads before this one can wait for those alone while these
+// are in flight. zero_past_row() must be applied before the cast.
+template <int U>
+__device__ __forceinline__ RawPieceFp8<U> load_item_fp8_nobranch(const u32x4 *__restrict__ x,
+                                                                 int t, int seg, int H)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    RawPieceFp8<U> r;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int h0 = fp8_channel(seg, u, U, lane);
+        r.act[u] = h0 < H;
+        const u32x4 *src = x + (size_t)t * (H / 8) + (r.act[u] ? h0 / 8 : 0);
+        r.a[u] = load16<EP_DISPATCH_NT_LOAD>(src);
+        r.b[u] = load16<EP_DISPATCH_NT_LOAD>(src + 1);
+    }
+    return r;
+}
+
+// Zeros in the pieces past the row, as load_item_fp8 leaves them.
+template <int U>
+__device__ __forceinline__ RawPieceFp8<U> zero_past_row(RawPieceFp8<U> r)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+        r.a[u] = r.act[u] ? r.a[u] : z;
+        r.b[u] = r.act[u] ? r.b[u] : z;
+    }
+    return r;
+}
+
 // All 64 lanes take part (a block amax is a DPP max over 8 lanes).
 template <int U>
 __device__ __forceinline__ QuantPiece<U> cast_item_fp8(const RawPieceFp8<U> &r)

@@ -63,6 +63,17 @@
 #ifndef EP_RANKS_FP8_XCD_ORDER
 #define EP_RANKS_FP8_XCD_ORDER 1
 #endif
+// Fused rank kernels: the layout's id loads go out first and the first item's row loads
+// after them with no branch, so the layout waits for the ids alone while the rows are in flight
+// (a wavefront's loads complete in order; with the rows first, or under a branch, the compiler
+// waits for all of them). From per-workgroup stamps, the layout phase of the FP8 kernel had
+// taken 4.0-4.9 us, mostly the row loads, against a 3.7 us copy phase. At T = 4096: FP8 (R = 3)
+// 12.4-12.5 against 12.8 us, bf16 (R = 16) 23.4-23.5 against 23.8 us. The one-stage fused
+// kernels measured slower in the same arrangement (bf16 26.2-26.6 against 26.0 us with the id
+// loads also branch-free, FP8 20.9 against 18.1 us) and keep theirs.
+#ifndef EP_RANKS_IDS_FIRST
+#define EP_RANKS_IDS_FIRST 1
+#endif
 #ifndef EP_RANKS_FP8_U
 #define EP_RANKS_FP8_U 0         // fused FP8 rank kernel: 16-channel pieces per lane (0 = auto)
 #endif
@@ -132,6 +143,28 @@ __device__ __forceinline__ int wave_total(int v)
 // fields hold up to 255, so 63 passes.
 constexpr int kPackedRankMaxT = 63 * kRankBatch * kRankTile;
 
+// One pass of rank_prefix_wave's loads: this lane's tokens q0 + (b0 + b) * kRankTile,
+// b < kRankBatch, as KV 16-byte id vectors each; a batch is loaded only if some token of the
+// wavefront in it lies before t0 (wavefront-uniform), the others read as -1 (no expert).
+template <int KV>
+__device__ __forceinline__ void rank_batch_loads(const int32_t *__restrict__ idx, int b0, int t0,
+                                                 int K, int4 (&v)[kRankBatch][KV])
+{
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int q0 = wave * kWave + lane;
+#pragma unroll
+    for (int b = 0; b < kRankBatch; ++b) {
+#pragma unroll
+        for (int j = 0; j < KV; ++j) v[b][j] = int4{-1, -1, -1, -1};
+        if ((b0 + b) * kRankTile + wave * kWave < t0) {        // wavefront-uniform
+            const int q = min(q0 + (b0 + b) * kRankTile, t0 - 1);
+#pragma unroll
+            for (int j = 0; j < KV; ++j)
+                v[b][j] = reinterpret_cast<const int4 *>(idx + (size_t)q * K)[j];
+        }
+    }
+}
+
 // Per-rank counts of the tokens [0, t0) in this wavefront's share (tokens wave*64 + lane +
 // b*kRankTile): kRankBatch tokens per lane are loaded together (16-byte id vectors when
 // KV > 0). Lane r returns rank r's total.
@@ -139,9 +172,12 @@ constexpr int kPackedRankMaxT = 63 * kRankBatch * kRankTile;
 // packed 8-bit fields, one 24-bit multiply and a mask per 4 ranks and token (spread4); one
 // wave sum per rank at the end. RQ = 0: per rank and batch one ballot and a scalar popcount
 // (any R <= 64).
-template <int KV, int RQ>
+// PRE (KV > 0): the first pass's vectors were loaded beforehand (rank_batch_loads with b0 = 0)
+// and are passed in `first`.
+template <int KV, int RQ, bool PRE = false>
 __device__ __forceinline__ int rank_prefix_wave(const int32_t *__restrict__ idx, int t0, int K,
-                                                int E, uint32_t magic, int R)
+                                                int E, uint32_t magic, int R,
+                                                const int4 (*first)[KV > 0 ? KV : 1] = nullptr)
 {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int q0 = wave * kWave + lane;
@@ -154,16 +190,13 @@ __device__ __forceinline__ int rank_prefix_wave(const int32_t *__restrict__ idx,
         uint64_t m[kRankBatch];
         if constexpr (KV > 0) {
             int4 v[kRankBatch][KV];
+            if (PRE && b0 == 0) {
 #pragma unroll
-            for (int b = 0; b < kRankBatch; ++b) {
+                for (int b = 0; b < kRankBatch; ++b)
 #pragma unroll
-                for (int j = 0; j < KV; ++j) v[b][j] = int4{-1, -1, -1, -1};
-                if ((b0 + b) * kRankTile + wave * kWave < t0) {        // wavefront-uniform
-                    const int q = min(q0 + (b0 + b) * kRankTile, t0 - 1);
-#pragma unroll
-                    for (int j = 0; j < KV; ++j)
-                        v[b][j] = reinterpret_cast<const int4 *>(idx + (size_t)q * K)[j];
-                }
+                    for (int j = 0; j < KV; ++j) v[b][j] = first[b][j];
+            } else {
+                rank_batch_loads<KV>(idx, b0, t0, K, v);
             }
 #pragma unroll
             for (int b = 0; b < kRankBatch; ++b)
@@ -357,15 +390,43 @@ __global__ __launch_bounds__(kThreads) void dispatch_ranks_fp8_kernel(
 // earlier tokens, then copies (or quantises and copies) the tile's rows to their staging rows
 // ------------------------------------------------------------------------------------------
 
+// The global loads of rank_tile for KV > 0, issued before the workgroup's other loads so that
+// the layout waits only for them (a wavefront's loads complete in order): wavefront 0's ids of
+// the tile's own tokens (lane tl: token t0 + tl) and the first pass of earlier tokens.
+template <int KV>
+struct RankTileIds {
+    int4 own[KV > 0 ? KV : 1];
+    int4 v[kRankBatch][KV > 0 ? KV : 1];
+};
+
+template <int KV>
+__device__ __forceinline__ RankTileIds<KV> rank_tile_loads(const int32_t *__restrict__ idx,
+                                                           int t0, int nt, int K)
+{
+    RankTileIds<KV> ids;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+#pragma unroll
+    for (int j = 0; j < KV; ++j) ids.own[j] = int4{-1, -1, -1, -1};
+    if (wave == 0 && lane < nt) {
+#pragma unroll
+        for (int j = 0; j < KV; ++j)
+            ids.own[j] = reinterpret_cast<const int4 *>(idx + (size_t)(t0 + lane) * K)[j];
+    }
+    rank_batch_loads<KV>(idx, 0, t0, K, ids.v);
+    return ids;
+}
+
 // Rank layout of the tile [t0, t0 + nt), nt <= kWave, in a workgroup of kRankTile lanes:
 // rank_slot rows of the tile (coalesced, through LDS), rows[tl*R + r] = r*T + slot or -1 in
-// LDS for the copies, and rank_tokens in the last workgroup. Ends with a barrier.
-template <int KV, int RQ>
+// LDS for the copies, and rank_tokens in the last workgroup. Ends with a barrier. PRE (KV > 0):
+// the ids were loaded by rank_tile_loads and are passed in `pre`.
+template <int KV, int RQ, bool PRE = false>
 __device__ __forceinline__ void rank_tile(const int32_t *__restrict__ idx, int t0, int nt, int T,
                                           int K, int E, int R, bool last,
                                           int32_t *__restrict__ rank_slot,
                                           int32_t *__restrict__ rank_tokens, int32_t *rows,
-                                          int32_t *slots, int32_t (*wcnt)[EP_MAX_RANKS])
+                                          int32_t *slots, int32_t (*wcnt)[EP_MAX_RANKS],
+                                          const RankTileIds<KV> *pre = nullptr)
 {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const uint32_t magic = rank_magic(E / R);
@@ -375,13 +436,14 @@ __device__ __forceinline__ void rank_tile(const int32_t *__restrict__ idx, int t
         if constexpr (KV > 0) {
             int4 v[KV];
 #pragma unroll
-            for (int j = 0; j < KV; ++j) v[j] = reinterpret_cast<const int4 *>(idx + (size_t)t * K)[j];
+            for (int j = 0; j < KV; ++j)
+                v[j] = PRE ? pre->own[j] : reinterpret_cast<const int4 *>(idx + (size_t)t * K)[j];
             own = ranks_of(v, KV, E, magic);
         } else {
             own = token_ranks_any(idx, t, K, E, magic);
         }
     }
-    const int acc = rank_prefix_wave<KV, RQ>(idx, t0, K, E, magic, R);
+    const int acc = rank_prefix_wave<KV, RQ, PRE>(idx, t0, K, E, magic, R, PRE ? pre->v : nullptr);
     if (lane < R) wcnt[wave][lane] = acc;
     __syncthreads();
     if (wave == 0) {
@@ -417,11 +479,17 @@ __global__ __launch_bounds__(kRankTile, 8) void rank_layout_dispatch_bf16_kernel
     const int tile = xcd_tile<EP_RANKS_BF16_XCD_ORDER>();
     const int t0 = tile * TT, nt = min(TT, T - t0);
     const int nitems = nt * nseg;
-    // the first item's row loads need no slot: issued before the layout's loads
-    RowPiece<U> first;
-    if (wave < nitems) first = load_item_bf16<U>(x, t0 + wave / nseg, wave % nseg, H8);
-    rank_tile<KV, RQ>(idx, t0, nt, T, K, E, R, tile == (int)gridDim.x - 1, rank_slot,
-                      rank_tokens, rows, slots, wcnt);
+    // the ids first, then the first item's row loads (they need no slot), so that the layout
+    // waits for the ids only while the rows are in flight
+    constexpr bool kPre = KV > 0 && RQ > 0 && EP_RANKS_IDS_FIRST;
+    RankTileIds<KV> ids;
+    if constexpr (kPre) ids = rank_tile_loads<KV>(idx, t0, nt, K);
+    // (issued by every wavefront, those without an item repeating the last one, so that the
+    // number of loads behind the ids is the same on every path and the wait for the ids is exact)
+    const int fi = min(wave, nitems - 1);
+    const RowPiece<U> first = load_item_bf16<U>(x, t0 + fi / nseg, fi % nseg, H8);
+    rank_tile<KV, RQ, kPre>(idx, t0, nt, T, K, E, R, tile == (int)gridDim.x - 1, rank_slot,
+                            rank_tokens, rows, slots, wcnt, &ids);
     if (wave < nitems)
         store_item_bf16<KG, U, MULTI>(first, stage, rows, wave / nseg, wave % nseg, H8, R);
     for (int item = wave + kRankWaves; item < nitems; item += kRankWaves) {
@@ -447,14 +515,20 @@ __global__ __launch_bounds__(kRankTile, EP_RANKS_FP8_WAVES) void rank_layout_dis
     const int tile = xcd_tile<EP_RANKS_FP8_XCD_ORDER>();
     const int t0 = tile * TT, nt = min(TT, T - t0);
     const int nitems = nt * nseg;
-    // the first item's token row is loaded before the layout (it needs no slot) and cast after
-    RawPieceFp8<U> first;
-    if (wave < nitems) first = load_item_fp8<U>(x, t0 + wave / nseg, wave % nseg, H);
-    rank_tile<KV, RQ>(idx, t0, nt, T, K, E, R, tile == (int)gridDim.x - 1, rank_slot,
-                      rank_tokens, rows, slots, wcnt);
+    // the ids first, then the first item's token row (it needs no slot; cast after the
+    // layout), so that the layout waits for the ids only while the row is in flight
+    constexpr bool kPre = KV > 0 && RQ > 0 && EP_RANKS_IDS_FIRST;
+    RankTileIds<KV> ids;
+    if constexpr (kPre) ids = rank_tile_loads<KV>(idx, t0, nt, K);
+    // (issued by every wavefront, those without an item repeating the last one, so that the
+    // number of loads behind the ids is the same on every path and the wait for the ids is exact)
+    const int fi = min(wave, nitems - 1);
+    const RawPieceFp8<U> first = load_item_fp8_nobranch<U>(x, t0 + fi / nseg, fi % nseg, H);
+    rank_tile<KV, RQ, kPre>(idx, t0, nt, T, K, E, R, tile == (int)gridDim.x - 1, rank_slot,
+                            rank_tokens, rows, slots, wcnt, &ids);
     if (wave < nitems)
-        store_item_fp8<KG, U, MULTI>(cast_item_fp8<U>(first), stage_q, stage_scale, rows,
-                                     wave / nseg, wave % nseg, H, R);
+        store_item_fp8<KG, U, MULTI>(cast_item_fp8<U>(zero_past_row<U>(first)), stage_q,
+                                     stage_scale, rows, wave / nseg, wave % nseg, H, R);
     for (int item = wave + kRankWaves; item < nitems; item += kRankWaves) {
         const int tl = item / nseg;
         dispatch_item_fp8<KG, U, MULTI>(x, stage_q, stage_scale, rows, t0 + tl, tl,
@@ -1099,6 +1173,8 @@ hipError_t launch_rank_layout_dispatch_bf16(const ep_shape_t &s, const uint16_t 
                                             int32_t *rank_tokens, uint16_t *stage,
                                             hipStream_t stream)
 {
+    // no tokens: nothing to copy, and the fused kernel's row loads would have no row to read
+    if (s.T == 0) return launch_rank_layout(s, idx, rank_slot, rank_tokens, stream);
     if (s.K == 8)
         return launch_rank_dispatch_bf16_kv<2>(s, x, idx, rank_slot, rank_tokens, stage, stream);
     return launch_rank_dispatch_bf16_kv<0>(s, x, idx, rank_slot, rank_tokens, stage, stream);
@@ -1109,6 +1185,7 @@ hipError_t launch_rank_layout_dispatch_fp8(const ep_shape_t &s, const uint16_t *
                                            int32_t *rank_tokens, uint8_t *stage_q,
                                            float *stage_scale, hipStream_t stream)
 {
+    if (s.T == 0) return launch_rank_layout(s, idx, rank_slot, rank_tokens, stream);
     if (s.K == 8)
         return launch_rank_dispatch_fp8_kv<2>(s, x, idx, rank_slot, rank_tokens, stage_q,
                                               stage_scale, stream);
