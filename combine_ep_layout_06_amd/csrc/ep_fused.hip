@@ -117,11 +117,12 @@ __global__ __launch_bounds__(kTileThreads, EP_FUSED_FP8_WAVES) void layout_dispa
     const int nt = min(TT, T - t0);
     const int wave = wave_uniform(threadIdx.x / kWave);
     const int nitems = nt * nseg;
-    // the first item's row loads go out right after the tile's own ids and before the layout's
-    // loads of the earlier ids, and the cast waits until after the layout: at T = 128 the fused
-    // kernel takes 6.3 us against 6.6 us without the early loads, at T = 4096 the same 19.2 us
-    // (issued before the own ids, they measured 18.6 -> 19.2 us there; cast before the layout,
-    // 19.0 -> 19.8 us)
+    // the first item's row loads go out after the layout's id loads, and the cast waits until
+    // after the layout: at T = 128 the fused kernel takes 6.3 us against 6.6 us without the
+    // early loads (issued before the ids, at T = 4096 they measured 18.6 -> 19.2 us; cast
+    // before the layout, 19.0 -> 19.8 us). The row loads sit under a branch (wavefronts with an
+    // item), so the layout's waits cover them too; loading them with no branch, which lets the
+    // layout wait for the ids alone, measured slower (20.9 against 18.1 us at T = 4096).
     const TileIds ids = layout_tile_loads<false, CHUNKED>(idx, TK, t0 * K, TT * K);
     RawPieceFp8<U> first;
     if (wave < nitems) first = load_item_fp8<U>(x, t0 + wave / nseg, wave % nseg, H);
