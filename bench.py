@@ -621,13 +621,14 @@ def brief_launch(r):
     return d
 
 
-def counter_traffic(kernel, workload):
+def counter_traffic(kernel, workload, root=None):
     """HBM bytes per launch of `kernel` on `workload` from the committed counter record
     (profiles/hbm_traffic.json: rocprofv3 FETCH_SIZE and WRITE_SIZE passes, each scaled by what
     the same counter reads for a plain device copy of known size). None if there is no record
-    or the kernel's sources changed since the counters were taken."""
+    or the kernel's sources changed since the counters were taken. `root`: the repository (the
+    one holding this file by default)."""
     import hashlib
-    root = os.path.dirname(os.path.abspath(__file__))
+    root = root or os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(root, "profiles", "hbm_traffic.json")
     try:
         with open(path) as f:
