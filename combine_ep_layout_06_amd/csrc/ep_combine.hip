@@ -20,11 +20,13 @@
 // loads before issuing the next one. Loads of y and stores of out are non-temporal: each byte
 // is touched once (non-temporal loads measured ~25% faster here).
 //
-// Measured on MI355X, this kernel reaches ~94% of a bare probe of the same access pattern
-// (eight random 4 KiB rows read per contiguous row written); a per-wavefront variant that
+// Measured on MI355X, this kernel reaches ~95% of a bare probe of the same access pattern
+// (eight random 4 KiB rows read per contiguous row written, rows precomputed, the same rows
+// re-read after a 2 GiB fill: 22.9 against 24.0 us at T = 4096); a per-wavefront variant that
 // prefetched the next token's metadata through scalar loads instead of LDS staging was no
-// faster, and neither was a wave-uniform branch around each pair's fold in place of the
-// per-element select.
+// faster, nor was one wavefront per item with the metadata in lanes and no LDS at all (26.4-
+// 26.5 against 26.2-26.6 us in the benchmark, 3.90 against 4.02 us at T = 128), nor a
+// wave-uniform branch around each pair's fold in place of the per-element select.
 #include "ep_device.h"
 #include "ep_internal.h"
 
