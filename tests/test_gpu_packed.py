@@ -114,6 +114,7 @@ SMALL = [
                                       # the call runs as two launches
     (40, 256, 300, 256, 20, 3),       # K = EP_MAX_TOPK
     (600, 256, 32, 6, 40, 4),         # 512 <= T < 1024: fused tiles of two tokens
+    (40, 32896, 6, 3, 12, 3),         # rows longer than the combine's zero row
 ]
 
 

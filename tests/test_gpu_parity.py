@@ -85,6 +85,8 @@ SMALL = [
     (2051, 256, 16, 4, 700, 4),       # fused tiles of 4 tokens (bf16) and 16 (FP8) with a
                                       # 3-token last tile
     (4099, 256, 16, 4, 1100, 4),      # bf16 fused tiles of 8 tokens, a 3-token last tile
+    (40, 32896, 6, 3, 12, 3),         # H/8 = 4112 chunks, longer than the combine's zero row:
+                                      # dropped pairs take the per-pair select
     (4100, 512, 64, 8, 200, 8),       # whole-row combine items folding rows in groups of two
                                       # with drops, unrouted and invalid ids
     (40, 256, 300, 256, 20, 3),       # K = EP_MAX_TOPK: 32 pair groups per token, full tiles

@@ -178,6 +178,7 @@ SMALL = [
     (9000, 64, 32, 8, 4000, 8),       # rank layout past five tiles: the batched prefix loop
     (6000, 64, 24, 6, 3000, 6),       # the same with K = 6 (ids one at a time)
     (40, 256, 300, 256, 20, 3),       # K = EP_MAX_TOPK
+    (40, 32896, 6, 3, 12, 3),         # rows longer than the zero row: the reduce's select
 ]
 
 
