@@ -1063,6 +1063,24 @@ hipError_t launch_dispatch_ranks_fp8(const ep_shape_t &s, const uint16_t *x,
 
 namespace {
 
+// Pair groups of the staging copy for R ranks, limited to the ones the rank counters' form RQ
+// can meet: pick_rq gives RQ = 1 only for R <= 4 and RQ = 4 only for 4 < R <= 16; RQ = 0 (the
+// ballots) means R > 16 or a batch past kPackedRankMaxT, and takes the looping form of groups
+// of 8, which serves any R. Other pairings are never built.
+#define EP_BY_R(RQ, R, LAUNCH)                                                                  \
+    do {                                                                                        \
+        if constexpr (RQ == 1) {                                                                \
+            if ((R) > 2) LAUNCH(4, false);                                                      \
+            if ((R) > 1) LAUNCH(2, false);                                                      \
+            LAUNCH(1, false);                                                                   \
+        } else if constexpr (RQ == 4) {                                                         \
+            if ((R) > 8) LAUNCH(8, true);                                                       \
+            LAUNCH(8, false);                                                                   \
+        } else {                                                                                \
+            LAUNCH(8, true);                                                                    \
+        }                                                                                       \
+    } while (0)
+
 // Tokens per fused tile: at most one wavefront's worth (one lane per token ranks the tile),
 // TT*R <= kRankTile staged rows; on prefill-sized batches 8 for bf16 rows (two workgroups per
 // CU, each wavefront copying one half row: 24.8 us at T = 4096 against 25.8 us with 16 tokens
@@ -1089,7 +1107,7 @@ hipError_t launch_rank_dispatch_bf16_rq(const ep_shape_t &s, const u32x4 *x, con
     return launch(rank_layout_dispatch_bf16_kernel<KV, RQ, KG, U, MULTI>, grid, block, 0,      \
                   stream, x, idx, rank_slot, rank_tokens, stage, s.T, H8, s.K, s.E, s.R, TT,    \
                   nseg)
-    EP_BY_K(s.R, EP_LAUNCH_RLD);
+    EP_BY_R(RQ, s.R, EP_LAUNCH_RLD);
 #undef EP_LAUNCH_RLD
 }
 
@@ -1117,7 +1135,7 @@ hipError_t launch_rank_dispatch_fp8_rq(const ep_shape_t &s, const u32x4 *x, cons
     return launch(rank_layout_dispatch_fp8_kernel<KV, RQ, KG, U, MULTI>, grid, block, 0,       \
                   stream, x, idx, rank_slot, rank_tokens, stage_q, stage_scale, s.T, s.H, s.K,  \
                   s.E, s.R, TT, nseg)
-    EP_BY_K(s.R, EP_LAUNCH_RLQ);
+    EP_BY_R(RQ, s.R, EP_LAUNCH_RLQ);
 #undef EP_LAUNCH_RLQ
 }
 
@@ -1258,9 +1276,12 @@ hipError_t launch_combine_ranks(const ep_shape_t &s, const uint16_t *y, const in
                       rank_slot, w, pv, s.T, H8, s.E, s.C, s.K, s.R, tpb, nseg);
 #define EP_LAUNCH_CR(KG)                                                                        \
     do {                                                                                        \
-        if (U >= 4)                                                                             \
-            return launch(combine_ranks_kernel<KG, 4, false>, grid, block, 0, stream, yv, idx,   \
-                          slot, rank_slot, w, pv, s.T, H8, s.E, s.C, s.K, s.R, tpb, nseg);      \
+        if constexpr (EP_CR_U >= 4) {                                                           \
+            if (U >= 4)                                                                         \
+                return launch(combine_ranks_kernel<KG, 4, false>, grid, block, 0, stream, yv,    \
+                              idx, slot, rank_slot, w, pv, s.T, H8, s.E, s.C, s.K, s.R, tpb,    \
+                              nseg);                                                            \
+        }                                                                                       \
         if (U == 2)                                                                             \
             return launch(combine_ranks_kernel<KG, 2, false>, grid, block, 0, stream, yv, idx,   \
                           slot, rank_slot, w, pv, s.T, H8, s.E, s.C, s.K, s.R, tpb, nseg);      \
@@ -1288,35 +1309,51 @@ hipError_t launch_combine_reduce(const ep_shape_t &s, const uint16_t *part,
     // at T = 4096, H = 2048 the FP8 workload's R = 3 (50 MB of rows) reduces in 13.5 against
     // 13.9 us and its pass takes 78.9-79.4 against 81.9-82.3 us read through the caches, while
     // the bf16 workload's R = 16 (268 MB) is faster read non-temporally (22.6 against 23.8 us)
-    const bool ntl = (size_t)s.R * s.T * s.H * sizeof(uint16_t) > (size_t)EP_RED_CACHED_BYTES;
+    // rows longer than the zero row (over 64 KiB each) are always read non-temporally
+    const bool ntl = H8 > kZeroChunks ||
+                     (size_t)s.R * s.T * s.H * sizeof(uint16_t) > (size_t)EP_RED_CACHED_BYTES;
+#define EP_LAUNCH_RD_UZN(KG, UU, MULTI, Z, N)                                                   \
+    return launch(combine_reduce_kernel<KG, UU, MULTI, Z, N>, grid, block, 0, stream, pv,        \
+                  rank_slot, ov, s.T, H8, s.R, Q, tpb, nseg)
 #define EP_LAUNCH_RD_ZN(KG, MULTI, Z, N)                                                        \
     do {                                                                                        \
-        if (U >= 4)                                                                             \
-            return launch(combine_reduce_kernel<KG, 4, MULTI, Z, N>, grid, block, 0, stream, pv, \
-                          rank_slot, ov, s.T, H8, s.R, Q, tpb, nseg);                           \
-        if (U == 2)                                                                             \
-            return launch(combine_reduce_kernel<KG, 2, MULTI, Z, N>, grid, block, 0, stream, pv, \
-                          rank_slot, ov, s.T, H8, s.R, Q, tpb, nseg);                           \
-        return launch(combine_reduce_kernel<KG, 1, MULTI, Z, N>, grid, block, 0, stream, pv,     \
-                      rank_slot, ov, s.T, H8, s.R, Q, tpb, nseg);                               \
+        if (U >= 4) EP_LAUNCH_RD_UZN(KG, 4, MULTI, Z, N);                                       \
+        if (U == 2) EP_LAUNCH_RD_UZN(KG, 2, MULTI, Z, N);                                       \
+        EP_LAUNCH_RD_UZN(KG, 1, MULTI, Z, N);                                                   \
     } while (0)
-#define EP_LAUNCH_RD_Z(KG, MULTI, Z)                                                            \
+#define EP_LAUNCH_RD4_ZN(KG, MULTI, Z, N) EP_LAUNCH_RD_UZN(KG, 4, MULTI, Z, N)
+#define EP_LAUNCH_RD12_ZN(KG, MULTI, Z, N)                                                      \
     do {                                                                                        \
-        if (ntl) EP_LAUNCH_RD_ZN(KG, MULTI, Z, true);                                           \
-        EP_LAUNCH_RD_ZN(KG, MULTI, Z, false);                                                   \
+        if (U == 2) EP_LAUNCH_RD_UZN(KG, 2, MULTI, Z, N);                                       \
+        EP_LAUNCH_RD_UZN(KG, 1, MULTI, Z, N);                                                   \
     } while (0)
-#define EP_LAUNCH_RD(KG, MULTI)                                                                 \
+// ZN: the launch for one zero-row / load-policy pair (with every chunk count, or some)
+#define EP_LAUNCH_RD_SEL(ZN, KG, MULTI)                                                         \
     do {                                                                                        \
-        if (H8 <= kZeroChunks) EP_LAUNCH_RD_Z(KG, MULTI, true);                                 \
-        EP_LAUNCH_RD_Z(KG, MULTI, false);                                                       \
+        if (H8 <= kZeroChunks) {                                                                \
+            if (ntl) ZN(KG, MULTI, true, true);                                                 \
+            ZN(KG, MULTI, true, false);                                                         \
+        }                                                                                       \
+        ZN(KG, MULTI, false, true);                                                             \
     } while (0)
-    // whole-row items (U = 4) fold a list of 5..8 partials as two groups of four: 118 VGPRs,
-    // 4 wavefronts per SIMD (22.6 against 23.5 us with one group of eight at T = 4096, R = 16)
-    if (Q > 4 && Q <= 8 && U >= 4) EP_LAUNCH_RD(4, true);
-    EP_BY_K(Q, EP_LAUNCH_RD);
+#define EP_LAUNCH_RD(KG, MULTI) EP_LAUNCH_RD_SEL(EP_LAUNCH_RD_ZN, KG, MULTI)
+    // lists of 5..8 partials: whole-row items (U = 4) fold them as two groups of four (118
+    // VGPRs, 4 wavefronts per SIMD: 22.6 against 23.5 us with one group of eight at T = 4096,
+    // R = 16), narrower items as one group of eight
+    if (Q > 8) EP_LAUNCH_RD(8, true);
+    if (Q > 4) {
+        if (U >= 4) EP_LAUNCH_RD_SEL(EP_LAUNCH_RD4_ZN, 4, true);
+        EP_LAUNCH_RD_SEL(EP_LAUNCH_RD12_ZN, 8, false);
+    }
+    if (Q > 2) EP_LAUNCH_RD(4, false);
+    if (Q > 1) EP_LAUNCH_RD(2, false);
+    EP_LAUNCH_RD(1, false);
 #undef EP_LAUNCH_RD
-#undef EP_LAUNCH_RD_Z
+#undef EP_LAUNCH_RD_SEL
+#undef EP_LAUNCH_RD12_ZN
+#undef EP_LAUNCH_RD4_ZN
 #undef EP_LAUNCH_RD_ZN
+#undef EP_LAUNCH_RD_UZN
 }
 
 }  // namespace ep
