@@ -20,7 +20,8 @@ and instruction counts, L2 hits, misses and DRAM credit stalls, L2 read latency)
 
 ``python -m combine_ep_layout_06_amd.hbm_counters trace --csv FILE`` prints the per-kernel
 duration summary of a ``rocprofv3 --kernel-trace`` CSV as a markdown table; ``steps --csv FILE
-...`` the durations and gaps of the benchmark step's two kernels in each trace.
+...`` the durations and gaps of the benchmark step's two kernels in each trace; ``coverage
+--csv FILE ...`` how many of the kernels the build holds the traces launched, and which never.
 """
 from __future__ import annotations
 
@@ -313,6 +314,39 @@ def trace_table(path, top=0):
     return "\n".join(out)
 
 
+def coverage_table(paths):
+    """The kernels the build holds (``kernel_resources.json`` beside the library) against the
+    ones the --kernel-trace CSVs launched, as markdown: counts, then every kernel never
+    launched (names demangled with c++filt)."""
+    with open(os.path.join(PKG, "kernel_resources.json")) as f:
+        mangled = sorted(json.load(f)["kernels"])
+    names = subprocess.run(["c++filt"], input="\n".join(mangled), capture_output=True,
+                           text=True, check=True).stdout.splitlines()
+    short = lambda n: n.replace("(anonymous namespace)::", "").split("(")[0].strip()
+    built = {short(n) for n in names}
+    launched = {}
+    for path in paths:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                k = short(r["Kernel_Name"])
+                if k in built:
+                    launched[k] = launched.get(k, 0) + 1
+    never = sorted(built - set(launched))
+    fams = {}
+    for k in built:
+        fam = k.split("<")[0].replace("void ", "").replace("ep::", "")
+        n_l = fams.setdefault(fam, [0, 0])
+        n_l[0] += 1
+        n_l[1] += k in launched
+    out = [f"{len(built)} kernels built, {len(launched)} launched at least once, "
+           f"{len(never)} never launched; {sum(launched.values())} launches of them in all.", "",
+           "| kernel template | built | launched |", "|---|---|---|"]
+    out += [f"| {fam} | {b} | {l} |" for fam, (b, l) in sorted(fams.items())]
+    if never:
+        out += ["", "Never launched:", ""] + [f"- {k}" for k in never]
+    return "\n".join(out)
+
+
 def step_table(paths):
     """Per trace: the step's two kernels (a fused layout + dispatch launch followed by a combine
     launch) and the gaps around them, median and min over the steps, as markdown rows. A step
@@ -350,7 +384,7 @@ def step_table(paths):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("action", choices=("collect", "summarize", "collect-detail", "detail",
-                                       "trace", "steps"))
+                                       "trace", "steps", "coverage"))
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "pmc"))
     ap.add_argument("--json", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"))
     ap.add_argument("--md-dir", default=os.path.join(ROOT, "profiles"))
@@ -367,6 +401,9 @@ def main():
         return detail(a.out, a.md_dir)
     if a.action == "steps":
         print(step_table(a.csv))
+        return 0
+    if a.action == "coverage":
+        print(coverage_table(a.csv))
         return 0
     print(trace_table(a.csv[0], a.top))
     return 0
