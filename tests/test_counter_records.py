@@ -105,3 +105,31 @@ def test_bench_uses_a_record_only_while_the_sources_match(bench, tmp_path):
     assert bench.counter_traffic("combine", "prefill_fp8", root=str(root)) is None
     src.write_text("kernel v2\n")                     # the kernel changed since the counters
     assert bench.counter_traffic("combine", "prefill_bf16", root=str(root)) is None
+
+
+def test_coverage_table_counts_built_and_launched(H, tmp_path):
+    """coverage: the build's kernel list against a trace; a kernel the trace never launched is
+    named, foreign kernels (torch's) are ignored."""
+    import shutil
+    if shutil.which("c++filt") is None or not os.path.exists(
+            os.path.join(ROOT, "combine_ep_layout_06_amd", "kernel_resources.json")):
+        pytest.skip("needs c++filt and a built kernel_resources.json")
+    import subprocess
+    with open(os.path.join(ROOT, "combine_ep_layout_06_amd", "kernel_resources.json")) as f:
+        mangled = sorted(json.load(f)["kernels"])
+    names = subprocess.run(["c++filt"], input="\n".join(mangled), capture_output=True,
+                           text=True, check=True).stdout.splitlines()
+    trace = tmp_path / "t_kernel_trace.csv"
+    with open(trace, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name"])
+        w.writeheader()
+        for n in names[1:]:                       # every kernel but the first, twice
+            w.writerow({"Kernel_Name": n})
+            w.writerow({"Kernel_Name": n})
+        w.writerow({"Kernel_Name": "void at::native::vectorized_elementwise_kernel<4>(int)"})
+    text = H.coverage_table([str(trace)])
+    n = len(set(names))
+    assert text.splitlines()[0] == (f"{n} kernels built, {n - 1} launched at least once, "
+                                    f"1 never launched; {2 * (n - 1)} launches of them in all.")
+    missing = names[0].replace("(anonymous namespace)::", "").split("(")[0].strip()
+    assert text.splitlines()[-1] == f"- {missing}"
