@@ -9,6 +9,11 @@ library elsewhere, which the binding loads when ``EP_MI355X_LIB`` names it).
 The same compilation writes ``kernel_resources.json`` beside the library: per kernel (mangled
 symbol), the compiler's own resource report (scalar and vector registers, spills, LDS, the
 wavefronts per SIMD it allows), for recording beside measurements.
+
+``build(out, sanitize=True)`` builds a library for checking the host code on the CPU: the host
+side under AddressSanitizer and UndefinedBehaviorSanitizer (clang's runtime, which the process
+that loads it must preload), the device side unoptimised to keep the build short. It is for the
+host argument checks only and never launches a kernel that matters.
 """
 from __future__ import annotations
 
@@ -35,6 +40,15 @@ HIPCC_FLAGS = [
     # no packed-fp32 instructions (v_pk_*_f32) in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+
+# host code under ASan and UBSan, each flag for the host compilation only; device code at -O0
+SANITIZE_FLAGS = [
+    "-O1", "-Xarch_device", "-O0",
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all",
+]
+SANITIZE_LINK_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                       "-shared-libasan"]
 
 # the compiler's per-kernel resource remarks
 _REMARK = re.compile(r"remark:\s+(Function Name|TotalSGPRs|VGPRs|AGPRs|ScratchSize \[bytes/lane\]"
@@ -64,9 +78,10 @@ def parse_resources(text: str) -> dict:
     return out
 
 
-def _compile(src: str, obj: str, defines: dict | None, verbose: bool):
-    cmd = [hipcc(), *HIPCC_FLAGS, "-Rpass-analysis=kernel-resource-usage", f"-I{INCLUDE}",
-           f"-I{CSRC}"]
+def _compile(src: str, obj: str, defines: dict | None, verbose: bool, sanitize: bool = False):
+    cmd = [hipcc(), *HIPCC_FLAGS]
+    cmd += SANITIZE_FLAGS if sanitize else ["-Rpass-analysis=kernel-resource-usage"]
+    cmd += [f"-I{INCLUDE}", f"-I{CSRC}"]
     cmd += [f"-D{k}={v}" for k, v in (defines or {}).items()]
     cmd += ["-c", src, "-o", obj]
     if verbose:
@@ -75,7 +90,10 @@ def _compile(src: str, obj: str, defines: dict | None, verbose: bool):
     return src, res
 
 
-def build(out: str = LIB, defines: dict | None = None, verbose: bool = False) -> str:
+def build(out: str = LIB, defines: dict | None = None, verbose: bool = False,
+          sanitize: bool = False) -> str:
+    if sanitize and os.path.abspath(out) == LIB:
+        raise ValueError("a sanitized build goes elsewhere than the package's library")
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     objdir = os.path.join(os.path.dirname(out), "_build", os.path.basename(out) + ".obj")
     os.makedirs(objdir, exist_ok=True)
@@ -83,13 +101,15 @@ def build(out: str = LIB, defines: dict | None = None, verbose: bool = False) ->
     jobs = max(1, min(len(sources), os.cpu_count() or 1, 16))
     resources = {}
     with cf.ThreadPoolExecutor(jobs) as pool:
-        for src, res in pool.map(lambda a: _compile(*a, defines, verbose), zip(sources, objs)):
+        for src, res in pool.map(lambda a: _compile(*a, defines, verbose, sanitize),
+                                 zip(sources, objs)):
             if res.returncode != 0:
                 sys.stderr.write(res.stdout + res.stderr)
                 raise RuntimeError(f"hipcc failed ({res.returncode}) on {src}")
             resources.update(parse_resources(res.stderr))
     tmp = out + f".tmp{os.getpid()}"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC",
+           *(SANITIZE_LINK_FLAGS if sanitize else []), *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -97,7 +117,7 @@ def build(out: str = LIB, defines: dict | None = None, verbose: bool = False) ->
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed ({res.returncode}) linking {out}")
     os.replace(tmp, out)
-    if out == LIB:
+    if out == LIB and not sanitize:
         with open(RESOURCES + ".tmp", "w") as f:
             json.dump({"arch": ARCH, "kernels": resources}, f, indent=1, sort_keys=True)
         os.replace(RESOURCES + ".tmp", RESOURCES)
