@@ -353,7 +353,8 @@ def step_table(paths):
     that follows a fill (the cold protocol) also gives the gap from the fill's end to the
     first kernel's start."""
     out = ["| trace | steps | fill end -> first kernel | layout + dispatch | gap | combine | "
-           "first start -> combine end |", "|---|---|---|---|---|---|---|"]
+           "first start -> combine end | combine end -> next step |",
+           "|---|---|---|---|---|---|---|---|"]
     for path in paths:
         ks = []
         with open(path) as f:
@@ -363,7 +364,7 @@ def step_table(paths):
                         else "fill" if "FillFunctor" in n else "other")
                 ks.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), kind))
         ks.sort()
-        cols = {"fill": [], "ld": [], "gap": [], "cb": [], "span": []}
+        cols = {"fill": [], "ld": [], "gap": [], "cb": [], "span": [], "next": []}
         for i in range(len(ks) - 1):
             (s0, e0, k0), (s1, e1, k1) = ks[i], ks[i + 1]
             if k0 != "ld" or k1 != "cb":
@@ -374,10 +375,12 @@ def step_table(paths):
             cols["span"].append((e1 - s0) / 1e3)
             if i > 0 and ks[i - 1][2] == "fill":
                 cols["fill"].append((s0 - ks[i - 1][1]) / 1e3)
+            if i + 2 < len(ks) and ks[i + 2][2] == "ld":     # back to back: the next step's start
+                cols["next"].append((ks[i + 2][0] - e1) / 1e3)
         f = lambda v: f"{statistics.median(v):.2f} ({min(v):.2f})" if v else "-"
         out.append(f"| {os.path.basename(os.path.dirname(path))} | {len(cols['ld'])} | "
                    f"{f(cols['fill'])} | {f(cols['ld'])} | {f(cols['gap'])} | {f(cols['cb'])} | "
-                   f"{f(cols['span'])} |")
+                   f"{f(cols['span'])} | {f(cols['next'])} |")
     return "\n".join(out)
 
 
