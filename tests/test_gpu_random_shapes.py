@@ -2,8 +2,8 @@
 
 Each case draws a shape inside the library's limits (T up to ~5000, H any multiple of 8 or of
 128, E up to 1024 split over R ranks from 1 to 64, K from 1 to 20, a capacity between 30% and
-130% of the mean demand) and random ids in [-2, E] (duplicates, unrouted and invalid ids), then
-runs every call family on it and compares every output with the oracle in full: the one-stage
+130% of the mean demand, a packed alignment of 1, 3, 8, 64 or 100) and random ids in [-2, E]
+(duplicates, unrouted and invalid ids), then runs every call family on it and compares every output with the oracle in full: the one-stage
 dispatch (bf16 and, where H allows, FP8), the fused layout + dispatch with and without a
 workspace, combine, the packed layout at a random alignment, and the two-stage path. The fixed
 cases of the other parity tests pick shapes on purpose; these pick the odd ones nobody chose
@@ -38,7 +38,9 @@ def draw(i):
         C //= 2
     while T > 1 and (R * T * H * 2 > BYTES_MAX or E * C * H * 2 > BYTES_MAX):
         T //= 2
-    align = int(rng.choice([1, 8, 64]))
+    # packed alignment, powers of two or not, with its padding rows within the byte bound
+    aligns = [a for a in (1, 3, 8, 64, 100) if E * (a - 1) * H * 2 <= BYTES_MAX // 2]
+    align = int(rng.choice(aligns))
     return T, H, E, K, C, R, align
 
 
@@ -77,8 +79,9 @@ def test_random_shape(i):
 
 def test_draws_cover_the_odd_cases():
     """The draw covers what the fixed lists do not: K not a power of two, H not a multiple of
-    128, and ranks that are not a power of two."""
+    128, ranks and packed alignments that are not powers of two."""
     shapes = [draw(i) for i in range(N_CASES)]
     assert any(K not in (1, 2, 4, 8, 16) for _, _, _, K, _, _, _ in shapes)
     assert any(H % 128 for _, H, _, _, _, _, _ in shapes)
     assert any(R & (R - 1) for _, _, _, _, _, R, _ in shapes)
+    assert any(A & (A - 1) for _, _, _, _, _, _, A in shapes)
